@@ -1,0 +1,178 @@
+/*
+ * cp.h -- C ABI of the MI355X depth-loop library (libcpms.so).
+ *
+ * The library runs the depth loop of a codec-TTS code predictor: per frame an
+ * input projection, then n_positions depth positions, each walked through every
+ * decoder layer (qkv, attention, o, gate/up, down), a code head and a draw at
+ * every position after the first, and n_positions code embeddings whose sum is
+ * returned with the codes.  This is the frame of the mstar pull request
+ * "Qwen3-TTS: Run the 1.7B Depth Loop as One Persistent Kernel on Hopper"
+ * (#1183), section "How it works"; the outputs are the ones its section
+ * "Testing" compares (codes, embedding sums, KV cache, logits).
+ *
+ * Two executors compute bitwise-identical frames from the same task bodies:
+ *   CP_EXEC_PERSISTENT  one launch of one workgroup per compute unit that walks
+ *                       a static per-workgroup task list and hands data between
+ *                       phases through counters in device memory;
+ *   CP_EXEC_PER_PHASE   one launch per phase (the unfused comparison).
+ *
+ * Conventions for every call:
+ *   - every call returns a cp_status; no exception or abort crosses the ABI;
+ *   - "device" pointers are HIP device allocations on the plan's device;
+ *     "host" pointers are ordinary process memory;
+ *   - sizes are element counts unless a name says bytes;
+ *   - matrices are row-major [out][in], the layout of nn.Linear;
+ *   - the activation type of a plan (dtype) is also the storage type of its
+ *     weights, input hidden and KV outputs: IEEE fp32, or bf16 as 16-bit words.
+ */
+#ifndef CP_H
+#define CP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CP_ABI_VERSION 1
+
+typedef enum {
+  CP_OK = 0,
+  CP_ERR_INVALID_ARGUMENT = 1, /* NULL where a pointer is required, rows out of range, ... */
+  CP_ERR_UNSUPPORTED = 2,      /* shape, dtype or setting this build does not run */
+  CP_ERR_NOT_CORESIDENT = 3,   /* the persistent grid cannot be resident all at once */
+  CP_ERR_OUT_OF_MEMORY = 4,
+  CP_ERR_HIP = 5,              /* a HIP runtime call failed; see cp_plan_last_error */
+  CP_ERR_DEVICE_TIMEOUT = 6    /* a device-side wait gave up (reported by cp_plan_device_status) */
+} cp_status;
+
+typedef enum { CP_DTYPE_F32 = 0, CP_DTYPE_BF16 = 1 } cp_dtype;
+typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
+
+/* Plan flags. */
+#define CP_FLAG_TRACE 0x1u /* record per-task timestamps (persistent executor) */
+
+/* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
+ * head_dim 64 or 128; n_q_heads a multiple of n_kv_heads; hidden, input_dim,
+ * intermediate and vocab multiples of 64; 2 <= n_positions <= 16;
+ * 1 <= max_rows <= 64. */
+typedef struct {
+  int32_t abi_version;  /* CP_ABI_VERSION */
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t input_dim;    /* width of the input hidden that the input projection maps to hidden */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate; /* SwiGLU width */
+  int32_t n_positions;  /* depth positions per frame; n_positions - 1 heads and draws */
+  int32_t vocab;        /* codes per codebook */
+  int32_t max_rows;     /* rows (independent requests) a frame may carry */
+  int32_t dtype;        /* cp_dtype */
+  float rms_eps;        /* RMSNorm epsilon, e.g. 1e-6 */
+  float rope_theta;     /* RoPE base, e.g. 1e4 */
+  int32_t exec;         /* cp_exec */
+  uint32_t flags;       /* CP_FLAG_* */
+} cp_config;
+
+/* Weights, read only inside cp_plan_create: the plan copies and repacks them,
+ * so the caller may free them afterwards.  Single matrices are device
+ * pointers; per-layer, per-table and per-head lists are HOST arrays of device
+ * pointers. */
+typedef struct {
+  const void* w_in;               /* [hidden][input_dim] input projection */
+  const void* const* embed;       /* n_positions x [vocab][hidden]; table j embeds code j */
+  const void* const* attn_norm;   /* n_layers x [hidden] */
+  const void* const* w_qkv;       /* n_layers x [(nq + 2 nkv) head_dim][hidden]; rows q heads | k heads | v heads */
+  const void* const* w_o;         /* n_layers x [hidden][nq head_dim] */
+  const void* const* mlp_norm;    /* n_layers x [hidden] */
+  const void* const* w_gate;      /* n_layers x [intermediate][hidden] */
+  const void* const* w_up;        /* n_layers x [intermediate][hidden] */
+  const void* const* w_down;      /* n_layers x [hidden][intermediate] */
+  const void* final_norm;         /* [hidden] */
+  const void* const* w_head;      /* (n_positions - 1) x [vocab][hidden]; entry j-1 is head j */
+} cp_weights;
+
+/* One frame's inputs and outputs: all device pointers, borrowed until the
+ * frame's stream work completes. */
+typedef struct {
+  int32_t rows;              /* 1 .. max_rows */
+  const void* hidden_in;     /* [rows][input_dim], dtype */
+  const int32_t* code0;      /* [rows] code 0 (from outside the loop), each in [0, vocab) */
+  /* Sampling, [rows] each.  All five NULL: greedy for every row.  Some but not
+   * all NULL: CP_ERR_INVALID_ARGUMENT.  Per-row values never fail on the
+   * device: temperature <= 0 is greedy; top_k <= 0 or >= vocab is no top-k
+   * cut; top_p >= 1 is no top-p cut, top_p <= 0 keeps the best token only. */
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  const uint64_t* seed;
+  uint64_t* offset;          /* in/out: advanced by n_positions - 1 in place */
+  int32_t* codes;            /* out [rows][n_positions - 1], codes 1 .. n_positions-1 */
+  float* embsum;             /* out [rows][hidden]: fp32 sum of the n_positions code embeddings */
+  float* logits;             /* optional out [rows][n_positions - 1][vocab] (fp32) */
+  void* k_cache;             /* optional out [n_layers][rows][n_kv_heads][n_positions][head_dim], dtype, post-RoPE */
+  void* v_cache;             /* optional out, same layout */
+  uint64_t* trace;           /* optional out, cp_plan_info.trace_words words (needs CP_FLAG_TRACE) */
+} cp_frame_io;
+
+typedef struct {
+  int32_t n_phases;          /* dependent phases of one frame */
+  int32_t n_tasks;           /* tasks over all workgroups */
+  int32_t n_workgroups;      /* persistent grid size (one per compute unit) */
+  int32_t lds_bytes;         /* dynamic LDS per workgroup */
+  int64_t weight_bytes_per_frame; /* algorithmic weight bytes one frame reads */
+  int64_t packed_weight_bytes;    /* device bytes of the repacked weights */
+  int64_t scratch_bytes;          /* device bytes of plan-owned scratch */
+  int64_t trace_words;            /* uint64 words a traced frame writes */
+  int32_t cu_count;
+  int32_t max_tasks_per_workgroup;
+} cp_plan_info;
+
+typedef struct cp_plan cp_plan; /* opaque, owned by the library */
+
+/* Validates cfg, checks that the persistent grid is co-resident on
+ * hip_device (CP_ERR_NOT_CORESIDENT otherwise), repacks the weights, builds
+ * the per-workgroup task lists and allocates all scratch.  On success *out
+ * owns the plan; on failure *out is NULL. */
+cp_status cp_plan_create(const cp_config* cfg, const cp_weights* w, int hip_device, cp_plan** out);
+
+/* Enqueues one frame on hip_stream (a hipStream_t; NULL = default stream) and
+ * returns without waiting.  Checks io on the host first and enqueues nothing
+ * on an error.  The call allocates nothing and never synchronises, so it may
+ * be captured into a HIP graph.  Frames of one plan must be stream-ordered:
+ * the persistent executor holds every compute unit while it runs, and two of
+ * its frames in flight at once on one device could wait on each other. */
+cp_status cp_frame_run(cp_plan* plan, const cp_frame_io* io, void* hip_stream);
+
+/* Frees everything the plan owns.  NULL is accepted. */
+cp_status cp_plan_destroy(cp_plan* plan);
+
+cp_status cp_plan_query(const cp_plan* plan, cp_plan_info* info);
+
+/* Synchronises the plan's device and reports CP_ERR_DEVICE_TIMEOUT if a
+ * device-side wait gave up since the plan was created, else CP_OK. */
+cp_status cp_plan_device_status(cp_plan* plan);
+
+const char* cp_status_string(cp_status s);
+
+/* Text of the last error recorded on the plan ("" if none). */
+const char* cp_plan_last_error(const cp_plan* plan);
+
+/* Text of the last error of a cp_plan_create or cp_schedule_check call that
+ * failed (per calling thread). */
+const char* cp_last_create_error(void);
+
+/* Builds the per-workgroup task lists cfg would get on a device of cu_count
+ * compute units and checks their invariants, touching no device: every wait
+ * points to a counter group that only earlier phases signal; every counter
+ * receives exactly its per-frame count; every workgroup's list is in phase
+ * order.  On success fills n_phases, n_tasks, n_workgroups and
+ * max_tasks_per_workgroup of info (other fields zero).  For tests and
+ * planning tools; cp_plan_create runs the same checks. */
+cp_status cp_schedule_check(const cp_config* cfg, int cu_count, cp_plan_info* info);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

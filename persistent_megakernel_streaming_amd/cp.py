@@ -1,0 +1,223 @@
+"""Thin ctypes binding of libcpms.so (include/cp.h).
+
+Argument marshalling only: every step of the depth loop runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library is not built, importing this module raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcpms.so")
+
+CP_OK = 0
+STATUS = {0: "CP_OK", 1: "CP_ERR_INVALID_ARGUMENT", 2: "CP_ERR_UNSUPPORTED", 3: "CP_ERR_NOT_CORESIDENT",
+          4: "CP_ERR_OUT_OF_MEMORY", 5: "CP_ERR_HIP", 6: "CP_ERR_DEVICE_TIMEOUT"}
+CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
+CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
+CP_FLAG_TRACE = 1
+ABI_VERSION = 1
+
+_VP = C.c_void_p
+
+
+class Config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("abi_version", "n_layers", "hidden", "input_dim", "n_q_heads",
+                                          "n_kv_heads", "head_dim", "intermediate", "n_positions", "vocab",
+                                          "max_rows", "dtype")] + [
+        ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("exec", C.c_int32), ("flags", C.c_uint32)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("w_in", _VP), ("embed", C.POINTER(_VP)), ("attn_norm", C.POINTER(_VP)),
+                ("w_qkv", C.POINTER(_VP)), ("w_o", C.POINTER(_VP)), ("mlp_norm", C.POINTER(_VP)),
+                ("w_gate", C.POINTER(_VP)), ("w_up", C.POINTER(_VP)), ("w_down", C.POINTER(_VP)),
+                ("final_norm", _VP), ("w_head", C.POINTER(_VP))]
+
+
+class FrameIO(C.Structure):
+    _fields_ = [("rows", C.c_int32), ("hidden_in", _VP), ("code0", _VP), ("temperature", _VP),
+                ("top_k", _VP), ("top_p", _VP), ("seed", _VP), ("offset", _VP), ("codes", _VP),
+                ("embsum", _VP), ("logits", _VP), ("k_cache", _VP), ("v_cache", _VP), ("trace", _VP)]
+
+
+class PlanInfo(C.Structure):
+    _fields_ = [("n_phases", C.c_int32), ("n_tasks", C.c_int32), ("n_workgroups", C.c_int32),
+                ("lds_bytes", C.c_int32), ("weight_bytes_per_frame", C.c_int64),
+                ("packed_weight_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("trace_words", C.c_int64),
+                ("cu_count", C.c_int32), ("max_tasks_per_workgroup", C.c_int32)]
+
+
+class CpError(RuntimeError):
+    def __init__(self, status, msg=""):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run persistent_megakernel_streaming_amd.build")
+    lib = C.CDLL(LIB_PATH)
+    lib.cp_plan_create.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.c_int, C.POINTER(C.c_void_p)]
+    lib.cp_frame_run.argtypes = [C.c_void_p, C.POINTER(FrameIO), C.c_void_p]
+    lib.cp_plan_destroy.argtypes = [C.c_void_p]
+    lib.cp_plan_query.argtypes = [C.c_void_p, C.POINTER(PlanInfo)]
+    lib.cp_plan_device_status.argtypes = [C.c_void_p]
+    lib.cp_status_string.argtypes = [C.c_int]
+    lib.cp_status_string.restype = C.c_char_p
+    lib.cp_plan_last_error.argtypes = [C.c_void_p]
+    lib.cp_plan_last_error.restype = C.c_char_p
+    lib.cp_last_create_error.restype = C.c_char_p
+    lib.cp_schedule_check.argtypes = [C.POINTER(Config), C.c_int, C.POINTER(PlanInfo)]
+    for f in ("cp_plan_create", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
+              "cp_schedule_check"):
+        getattr(lib, f).restype = C.c_int
+    return lib
+
+
+_lib = load_library()
+
+
+def lib():
+    return _lib
+
+
+def make_config(cfg, max_rows=None, exec_mode="persistent", flags=0) -> Config:
+    """A cp_config for a synth.DepthLoopConfig-like object."""
+    return Config(abi_version=ABI_VERSION, n_layers=cfg.n_layers, hidden=cfg.hidden, input_dim=cfg.input_dim,
+                  n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
+                  intermediate=cfg.intermediate, n_positions=cfg.n_positions, vocab=cfg.vocab,
+                  max_rows=cfg.rows if max_rows is None else max_rows,
+                  dtype=CP_DTYPE_BF16 if cfg.dtype == "bf16" else CP_DTYPE_F32,
+                  rms_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
+                  exec=CP_EXEC_PER_PHASE if exec_mode == "per_phase" else CP_EXEC_PERSISTENT, flags=flags)
+
+
+def schedule_check(cfg, cu_count=256, max_rows=None):
+    """Builds and checks the task lists for a device of cu_count CUs (host only)."""
+    c = make_config(cfg, max_rows=max_rows)
+    info = PlanInfo()
+    st = _lib.cp_schedule_check(C.byref(c), int(cu_count), C.byref(info))
+    if st != CP_OK:
+        raise CpError(st, _lib.cp_last_create_error().decode())
+    return info
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def upload_weights(cfg, w: dict, device="cuda"):
+    """Copies stored weights (numpy, storage type; bf16 as uint16 bits) to the device."""
+    import torch
+    out = {}
+    for k, v in w.items():
+        a = np.ascontiguousarray(v)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        out[k] = torch.from_numpy(a).to(device)
+    return out
+
+
+class Plan:
+    """A cp_plan.  ``weights``: device tensors keyed as synth.make_weights names them."""
+
+    def __init__(self, cfg, weights: dict, exec_mode="persistent", max_rows=None, device=0, flags=0):
+        self.cfg = cfg
+        self._c = make_config(cfg, max_rows=max_rows, exec_mode=exec_mode, flags=flags)
+        L, P = cfg.n_layers, cfg.n_positions
+
+        def arr(names):
+            a = (C.c_void_p * len(names))(*[weights[n].data_ptr() for n in names])
+            return C.cast(a, C.POINTER(C.c_void_p)), a
+
+        keep = []
+        fields = {}
+        for key, names in (("embed", [f"embed.{j}" for j in range(P)]),
+                           ("attn_norm", [f"attn_norm.{l}" for l in range(L)]),
+                           ("w_qkv", [f"w_qkv.{l}" for l in range(L)]),
+                           ("w_o", [f"w_o.{l}" for l in range(L)]),
+                           ("mlp_norm", [f"mlp_norm.{l}" for l in range(L)]),
+                           ("w_gate", [f"w_gate.{l}" for l in range(L)]),
+                           ("w_up", [f"w_up.{l}" for l in range(L)]),
+                           ("w_down", [f"w_down.{l}" for l in range(L)]),
+                           ("w_head", [f"w_head.{j}" for j in range(1, P)])):
+            fields[key], a = arr(names)
+            keep.append(a)
+        self._w = Weights(w_in=weights["w_in"].data_ptr(), final_norm=weights["final_norm"].data_ptr(), **fields)
+        h = C.c_void_p()
+        st = _lib.cp_plan_create(C.byref(self._c), C.byref(self._w), int(device), C.byref(h))
+        if st != CP_OK:
+            raise CpError(st, _lib.cp_last_create_error().decode())
+        self._h = h
+        self._keep = keep
+
+    def info(self) -> PlanInfo:
+        i = PlanInfo()
+        self._check(_lib.cp_plan_query(self._h, C.byref(i)))
+        return i
+
+    def _check(self, st):
+        if st != CP_OK:
+            raise CpError(st, _lib.cp_plan_last_error(self._h).decode())
+
+    def run(self, io: dict, stream=None):
+        """Enqueues one frame.  ``io`` maps cp_frame_io field names to device
+        tensors (``rows`` to an int); the call does not wait."""
+        import torch
+        f = FrameIO(rows=int(io["rows"]))
+        for k in ("hidden_in", "code0", "temperature", "top_k", "top_p", "seed", "offset", "codes", "embsum",
+                  "logits", "k_cache", "v_cache", "trace"):
+            t = io.get(k)
+            if t is not None:
+                setattr(f, k, t.data_ptr())
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        self._check(_lib.cp_frame_run(self._h, C.byref(f), C.c_void_p(s)))
+
+    def device_status(self):
+        self._check(_lib.cp_plan_device_status(self._h))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.cp_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def make_io(cfg, inputs: dict, rows=None, device="cuda", logits=True, kv=False):
+    """Device frame I/O for synth.make_inputs output."""
+    import torch
+    rows = inputs["rows"] if rows is None else rows
+    hid = np.ascontiguousarray(inputs["hidden"][:rows])
+    if hid.dtype == np.uint16:
+        hid = hid.view(np.int16)
+    io = {
+        "rows": rows,
+        "hidden_in": torch.from_numpy(hid).to(device),
+        "code0": torch.from_numpy(np.ascontiguousarray(inputs["code0"][:rows])).to(device),
+        "codes": torch.full((rows, cfg.n_positions - 1), -1, dtype=torch.int32, device=device),
+        "embsum": torch.zeros((rows, cfg.hidden), dtype=torch.float32, device=device),
+    }
+    if logits:
+        io["logits"] = torch.zeros((rows, cfg.n_positions - 1, cfg.vocab), dtype=torch.float32, device=device)
+    if kv:
+        et = torch.int16 if cfg.dtype == "bf16" else torch.float32
+        shape = (cfg.n_layers, rows, cfg.n_kv_heads, cfg.n_positions, cfg.head_dim)
+        io["k_cache"] = torch.zeros(shape, dtype=et, device=device)
+        io["v_cache"] = torch.zeros(shape, dtype=et, device=device)
+    if "temperature" in inputs:
+        io["temperature"] = torch.from_numpy(np.ascontiguousarray(inputs["temperature"][:rows])).to(device)
+        io["top_k"] = torch.from_numpy(np.ascontiguousarray(inputs["top_k"][:rows])).to(device)
+        io["top_p"] = torch.from_numpy(np.ascontiguousarray(inputs["top_p"][:rows])).to(device)
+        io["seed"] = torch.from_numpy(np.ascontiguousarray(inputs["seed"][:rows]).view(np.int64)).to(device)
+        io["offset"] = torch.from_numpy(np.ascontiguousarray(inputs["offset"][:rows]).view(np.int64)).to(device)
+    return io

@@ -1,0 +1,118 @@
+// Internal layout shared by the host planner (cp_plan.cpp) and the device code
+// (cp_kernels.hip).  Nothing here crosses the C ABI.
+#pragma once
+#include <stdint.h>
+
+namespace cpms {
+
+// Task kinds, one per phase type of the frame.
+enum TaskType : uint8_t {
+  T_INPROJ = 1,  // input projection tile (split-K partial, last arriver reduces)
+  T_EMBED0 = 2,  // embedding of code 0 for one row
+  T_QKV = 3,     // RMSNorm + qkv projection tile + RoPE
+  T_ATTN = 4,    // attention for one kv head and a group of rows
+  T_O = 5,       // o projection split-K partial (+ residual by the last arriver)
+  T_GU = 6,      // RMSNorm + stacked gate/up tile + SwiGLU
+  T_DOWN = 7,    // down projection split-K partial (+ residual by the last arriver)
+  T_HEAD = 8,    // final RMSNorm + code head tile + per-tile argmax candidates
+  T_DRAW = 9,    // draw + embedding for one row
+};
+
+constexpr int kMaxWaits = 4;
+constexpr uint32_t kNone = 0xffffffffu;
+constexpr int kTileN = 16;          // output slots per projection tile
+constexpr int kMaxRows = 64;
+constexpr int kThreads = 256;       // 4 waves per workgroup
+constexpr int kSlotBytes = 64 * 1024;  // one weight-tile slot in LDS (two slots)
+constexpr int kMiscLds = 4096;
+constexpr int kLdsBytes = 2 * kSlotBytes + kMiscLds;
+constexpr int kCtrStride = 32;      // uint32 words between sub-counters (128 B)
+
+// A group of sub-counters: a phase (or part of one) signals it, a later task
+// waits on it.  Producer i adds to sub-counter i % nsub; each sub-counter
+// receives per_sub adds per frame, so a frame's epoch e is complete at
+// per_sub * e.
+struct CtrGroup {
+  uint32_t base;     // index of the first sub-counter (in units of kCtrStride words)
+  uint16_t nsub;
+  uint16_t per_sub;
+};
+
+struct Task {
+  uint8_t type;
+  uint8_t split;     // split-K index
+  uint8_t nsplit;    // split-K ways (1: not split)
+  uint8_t nwait;
+  uint16_t layer;
+  uint16_t pos;
+  uint32_t tile;     // projection n-tile, attention (kv head, row group), row
+  uint32_t wait[kMaxWaits];  // counter groups to wait on
+  uint32_t sig;      // counter group signalled at completion (kNone: none)
+  uint32_t sig_slot; // producer index within sig
+  uint32_t tctr;     // split-K tile counter (kNone if not split)
+  uint32_t w_off;    // byte offset of the packed weight tile
+  uint32_t w_bytes;  // its size (multiple of 1 KiB), 0 for tasks without weights
+  uint32_t phase;    // global phase index
+};
+
+struct DevPlan {
+  // shapes
+  int L, H, Din, nq, nkv, d, I, P, V, Rmax;
+  int gq;             // q heads per kv head
+  int attn_rows;      // rows per attention task
+  int n_head_tiles;   // vocab / 16
+  int bf16;           // activation type
+  float eps;
+  float attn_scale;   // 1 / sqrt(head_dim)
+  uint32_t spin_limit;
+  int n_wg;
+  int n_tasks;
+  // task lists
+  const Task* tasks;            // all tasks, grouped by workgroup
+  const uint32_t* wg_begin;     // [n_wg + 1]
+  const CtrGroup* groups;
+  uint32_t* ctr;                // sub-counters and split-K tile counters
+  uint32_t* state;              // [0] epoch, [32] done counter, [64] error word
+  // weights (plan-owned copies)
+  const uint8_t* wblob;         // packed projection tiles
+  const void* gains;            // [2L + 1][H]: attn_norm[l], mlp_norm[l], final_norm
+  const void* embed;            // [P][V][H]
+  const float* rope;            // [P][d/2][2]: cos, sin
+  // activations and scratch (act = dtype)
+  void* xin;                    // [P][Rmax][H] position inputs
+  // Buffers below marked [2] are doubled by position parity: positions 0
+  // and 1 can be in flight at the same time.
+  void* hres;                   // [2][2][Rmax][H] residual after down, by layer parity
+  void* hmid;                   // [2][Rmax][H] residual after o
+  void* qbuf;                   // [2][Rmax][nq d]
+  void* abuf;                   // [2][Rmax][nq d] attention output
+  void* mbuf;                   // [2][Rmax][I] SwiGLU output
+  void* kc;                     // [L][Rmax][nkv][P][d]
+  void* vc;
+  float* part;                  // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16]
+  float* zbuf;                  // [Rmax][V] logits of the current head
+  uint2* cand;                  // [Rmax][n_head_tiles] (value bits, index)
+  uint64_t* trace;              // plan-owned trace staging (unused if no trace)
+  int trace_on;
+  int n_o_split, n_d_split, n_in_split;
+  uint64_t part_o_off, part_d_off, part_in_off;  // float offsets into part
+  uint64_t part_stride;                          // floats of one split-K buffer
+};
+
+struct DevFrame {
+  int rows;
+  int sampled;
+  const void* hidden_in;
+  const int32_t* code0;
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  const uint64_t* seed;
+  uint64_t* offset;
+  int32_t* codes;
+  float* embsum;
+  float* logits;
+  uint64_t* trace;
+};
+
+}  // namespace cpms

@@ -1,0 +1,716 @@
+// Device code of the depth-loop library: the task bodies, the persistent
+// executor and the one-launch-per-phase executor.
+//
+// The frame and its phases follow mstar pull request #1183 ("Qwen3-TTS: Run
+// the 1.7B Depth Loop as One Persistent Kernel on Hopper"), section "How it
+// works": one resident workgroup per compute unit walks a static task list; a
+// task waits on counters in device memory, runs one tile and signals a
+// counter; attention waits only on the qkv tiles of its own kv head; o and
+// down split their K loop and add the partial sums in a fixed order, with no
+// atomics on data, so a frame is bit-identical from run to run.  The megakernel
+// pattern itself (resident blocks, counter dependencies that only point to
+// earlier work, prefetching weights before waiting) is the one of the handbook
+// chapter "The gaps between kernels: PDL and megakernels", section
+// "Megakernels: the whole forward pass in one kernel".
+//
+// Hand-off between workgroups (MI355X has eight XCDs, each with its own L2):
+// every value one workgroup writes and another reads is stored and loaded with
+// the agent-coherent cache policy (sc1), the writer waits for its stores to
+// complete before it adds to a counter, and the reader polls the counter with
+// agent-scope atomic loads.  No L2 write-back or invalidate is needed, because
+// no cross-workgroup value is ever held in a non-coherent cache line.
+// Weights and inputs never change during a frame and use the ordinary path.
+#include <hip/hip_runtime.h>
+
+#include "cp_device.h"
+
+namespace cpms {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kSC1 = 16;  // buffer cache policy bit: coherent at agent scope
+
+// ------------------------------------------------------------------ memory helpers
+
+// A raw buffer resource over [p, p + bytes): loads past the end return zero,
+// stores past the end are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld16c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1); }
+__device__ __forceinline__ u32x2 ld8c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSC1); }
+__device__ __forceinline__ uint32_t ld4c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSC1); }
+__device__ __forceinline__ uint32_t ld2c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kSC1); }
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t ld2(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+__device__ __forceinline__ void st16c(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSC1); }
+__device__ __forceinline__ void st8c(rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kSC1); }
+__device__ __forceinline__ void st4c(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kSC1); }
+__device__ __forceinline__ void st2c(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, kSC1); }
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ------------------------------------------------------------------ numerics
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Element e of a 16-byte chunk as float.
+template <int BF>
+__device__ __forceinline__ float chunk_elem(const u32x4& v, int e) {
+  if constexpr (BF) return bf2f((v[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+  else return __uint_as_float(v[e]);
+}
+
+// Rounds to the activation type and returns the stored bits.
+template <int BF>
+__device__ __forceinline__ uint32_t to_act(float f) {
+  if constexpr (BF) return f2bf(f);
+  else return __float_as_uint(f);
+}
+template <int BF>
+__device__ __forceinline__ float act_val(float f) {
+  if constexpr (BF) return bf2f(f2bf(f));
+  else return f;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// (value, index) that wins an argmax: larger value, then lower index.
+__device__ __forceinline__ bool beats(float v, uint32_t i, float bv, uint32_t bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// ------------------------------------------------------------------ sync
+
+__device__ __forceinline__ uint32_t ld_ctr(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 0 waits until every sub-counter of the task's groups has reached its
+// share of this frame's target; the rest of the workgroup waits at the barrier.
+// A wait gives up after spin_limit polls and raises the error word, so a
+// broken schedule ends the kernel instead of hanging it.
+__device__ __forceinline__ void wait_deps(const DevPlan& pl, const Task& tk, uint32_t epoch) {
+  if (threadIdx.x < 64 && tk.nwait) {
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < kMaxWaits; ++k) {
+      if (k >= tk.nwait) break;
+      const CtrGroup gp = pl.groups[tk.wait[k]];
+      const uint32_t target = (uint32_t)gp.per_sub * epoch;
+      if (lane < gp.nsub) {
+        const uint32_t* c = pl.ctr + (size_t)(gp.base + lane) * kCtrStride;
+        uint32_t spins = 0;
+        while (ld_ctr(c) < target) {
+          if (++spins > pl.spin_limit) {
+            __hip_atomic_store(pl.state + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          if ((spins & 1023u) == 0 && ld_ctr(pl.state + 64)) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Every wave waits for its own stores, then one thread adds to the group.
+__device__ __forceinline__ void signal_group(const DevPlan& pl, uint32_t grp, uint32_t slot, bool persistent) {
+  wait_vm();
+  __syncthreads();
+  if (persistent && threadIdx.x == 0 && grp != kNone) {
+    const CtrGroup gp = pl.groups[grp];
+    __hip_atomic_fetch_add(pl.ctr + (size_t)(gp.base + slot % gp.nsub) * kCtrStride, 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ------------------------------------------------------------------ weights -> LDS
+
+// Direct-to-LDS copy of the task's packed weight tile: each wave moves 1 KiB
+// chunks (64 lanes x 16 B) with global_load_lds_dwordx4.
+__device__ __forceinline__ void issue_tile(const DevPlan& pl, const Task& tk, uint8_t* slot) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t nch = tk.w_bytes >> 10;
+  const uint8_t* src = pl.wblob + tk.w_off;
+  for (uint32_t c = wave; c < nch; c += 4) {
+    __builtin_amdgcn_global_load_lds((const void*)(src + c * 1024 + lane * 16),
+                                     (void __attribute__((address_space(3)))*)(slot + c * 1024), 16, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------------ projections
+
+enum Epi { EPI_QKV, EPI_GU, EPI_HEAD, EPI_PART };
+
+// The MFMA step for one 16-byte chunk of K per lane.
+template <int BF>
+__device__ __forceinline__ f32x4 mma(const u32x4& w, const u32x4& x, f32x4 acc) {
+  if constexpr (BF) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, x), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w[e]), __uint_as_float(x[e]), acc, 0, 0, 0);
+    return acc;
+  }
+}
+
+template <int BF>
+__device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t epoch,
+                          uint8_t* slot, uint32_t* misc, bool persistent) {
+  constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
+  constexpr int E = 16 / ESZ;         // elements per 16-byte chunk
+  constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane >> 4, rl = lane & 15;
+  const int row = wave * 16 + rl;
+  const int rows = fr.rows;
+  const bool wave_live = wave * 16 < rows;
+  const bool live = row < rows;
+  const int H = pl.H, Rmax = pl.Rmax;
+  const int l = tk.layer, p = tk.pos;
+
+  // Operand source, K range, norm and epilogue of this task kind.
+  const void* xsrc;
+  uint32_t xbytes, ld;  // buffer bytes and row stride (elements)
+  int k0 = 0, kt;
+  int gain_row = -1;    // row of the gain table, -1: no norm
+  int nb = 1;
+  Epi epi;
+  const void* resid = nullptr;  // residual (EPI_PART)
+  void* out = nullptr;          // output (EPI_PART)
+  uint64_t part_off = 0;
+  // Buffers that two positions in flight at once (0 and 1) would share are
+  // doubled and picked by position parity.
+  const int par = p & 1;
+  const uint32_t hbytes = (uint32_t)Rmax * H * ESZ;
+  const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * pl.d * ESZ;
+  uint8_t* hres = (uint8_t*)pl.hres + (size_t)par * 2 * hbytes;   // [layer parity]
+  uint8_t* hmid = (uint8_t*)pl.hmid + (size_t)par * hbytes;
+  const uint8_t* layer_in = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
+  switch (tk.type) {
+    case T_QKV:
+      xsrc = layer_in; xbytes = hbytes; ld = H; kt = H; gain_row = 2 * l; epi = EPI_QKV; break;
+    case T_GU:
+      xsrc = hmid; xbytes = hbytes; ld = H; kt = H; gain_row = 2 * l + 1; nb = 2; epi = EPI_GU; break;
+    case T_HEAD:
+      xsrc = hres + (size_t)((pl.L - 1) & 1) * hbytes; xbytes = hbytes; ld = H; kt = H;
+      gain_row = 2 * pl.L; epi = EPI_HEAD; break;
+    case T_O:
+      xsrc = (const uint8_t*)pl.abuf + (size_t)par * qdbytes; ld = pl.nq * pl.d; xbytes = qdbytes;
+      kt = (int)ld / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART; resid = layer_in; out = hmid;
+      part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; break;
+    case T_DOWN:
+      xsrc = (const uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ; ld = pl.I; xbytes = (uint32_t)Rmax * ld * ESZ;
+      kt = pl.I / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART; resid = hmid;
+      out = hres + (size_t)(l & 1) * hbytes; part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; break;
+    default:  // T_INPROJ
+      xsrc = fr.hidden_in; ld = pl.Din; xbytes = (uint32_t)fr.rows * ld * ESZ; kt = pl.Din / tk.nsplit;
+      k0 = tk.split * kt; epi = EPI_PART; out = pl.xin; part_off = pl.part_in_off; break;
+  }
+  const int nck = kt * ESZ / 64;  // 16-byte chunks per lane (<= 32)
+
+  // Activation rows straight from memory into the B operand registers.
+  const rsrc_t rx = make_rsrc(xsrc, xbytes);
+  u32x4 xa[32];
+  const uint32_t xoff = ((uint32_t)row * ld + k0 + q * E) * ESZ;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    if (c < nck) xa[c] = (wave_live && live) ? ld16c(rx, xoff + c * 64) : u32x4{0, 0, 0, 0};
+  }
+  wait_vm();        // activations and this wave's share of the weight tile have landed
+  __syncthreads();  // every wave's share of the tile is in LDS
+
+  if (wave_live) {
+    if (gain_row >= 0) {
+      // RMSNorm of the full row: float sum of squares per lane in K order,
+      // then across the four lane groups in a fixed tree.
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (c < nck)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float x = chunk_elem<BF>(xa[c], e);
+            ss += x * x;
+          }
+      ss += shfl_xor_f(ss, 16);
+      ss += shfl_xor_f(ss, 32);
+      const float rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
+      const rsrc_t rg = make_rsrc((const uint8_t*)pl.gains + (size_t)gain_row * H * ESZ, (uint32_t)H * ESZ);
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        if (c < nck) {
+          const u32x4 g = ld16(rg, (uint32_t)(c * KS + q * E) * ESZ);
+          u32x4 o;
+          if constexpr (BF) {
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+              const float t0 = chunk_elem<1>(xa[c], 2 * w2) * rinv, t1 = chunk_elem<1>(xa[c], 2 * w2 + 1) * rinv;
+              const float v0 = t0 * chunk_elem<1>(g, 2 * w2), v1 = t1 * chunk_elem<1>(g, 2 * w2 + 1);
+              o[w2] = f2bf(v0) | (f2bf(v1) << 16);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float t = __uint_as_float(xa[c][e]) * rinv;
+              o[e] = __float_as_uint(t * __uint_as_float(g[e]));
+            }
+          }
+          xa[c] = live ? o : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+
+    // K loop: weights from the LDS tile (fragment order), activations from registers.
+    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    const uint8_t* wt = slot + lane * 16;
+    if (nb == 1) {
+      // two accumulators on alternating chunks, added once at the end
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        if (c < nck) {
+          const u32x4 w = *(const u32x4*)(wt + c * 1024);
+          if (c & 1) acc1 = mma<BF>(w, xa[c], acc1);
+          else acc0 = mma<BF>(w, xa[c], acc0);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + acc1[v];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        if (c < nck) {
+          const u32x4 wg = *(const u32x4*)(wt + (2 * c) * 1024);
+          const u32x4 wu = *(const u32x4*)(wt + (2 * c + 1) * 1024);
+          acc0 = mma<BF>(wg, xa[c], acc0);
+          acc1 = mma<BF>(wu, xa[c], acc1);
+        }
+      }
+    }
+
+    // Lane (q, rl) holds output slots 4q .. 4q+3 of row `row`.
+    if (epi == EPI_QKV) {
+      const int d = pl.d, th = d / 16, gq = pl.gq, nkv = pl.nkv;
+      const int tpg = (gq + 2) * th;
+      const int g = tk.tile / tpg, lt = tk.tile % tpg;
+      const uint32_t kvoff = (uint32_t)(((l * Rmax + row) * nkv + g) * pl.P + p) * d;
+      const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * pl.P * d * ESZ;
+      if (live) {
+        if (lt < (gq + 1) * th) {
+          // q or k head: slots (4q + v) hold rotary pairs 8 tih + 2q + (v >> 1), half v & 1
+          const int tih = lt % th;
+          const bool isq = lt < gq * th;
+          const int hq = g * gq + lt / th;
+          const int i0 = 8 * tih + 2 * q;
+          float y[4];
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const float x1 = acc0[2 * pr], x2 = acc0[2 * pr + 1];
+            const float cs = pl.rope[(p * (d / 2) + i0 + pr) * 2], sn = pl.rope[(p * (d / 2) + i0 + pr) * 2 + 1];
+            y[2 * pr] = x1 * cs - x2 * sn;
+            y[2 * pr + 1] = x2 * cs + x1 * sn;
+          }
+          // dims i0, i0 + 1 (first halves) and i0 + d/2, i0 + d/2 + 1 (second halves)
+          rsrc_t r;
+          uint32_t base;
+          if (isq) {
+            r = make_rsrc((uint8_t*)pl.qbuf + (size_t)par * qdbytes, qdbytes);
+            base = (uint32_t)(row * pl.nq * d + hq * d);
+          } else {
+            r = make_rsrc(pl.kc, kvbytes);
+            base = kvoff;
+          }
+          if constexpr (BF) {
+            st4c(r, (base + i0) * 2, f2bf(y[0]) | (f2bf(y[2]) << 16));
+            st4c(r, (base + i0 + d / 2) * 2, f2bf(y[1]) | (f2bf(y[3]) << 16));
+          } else {
+            st8c(r, (base + i0) * 4, u32x2{__float_as_uint(y[0]), __float_as_uint(y[2])});
+            st8c(r, (base + i0 + d / 2) * 4, u32x2{__float_as_uint(y[1]), __float_as_uint(y[3])});
+          }
+        } else {
+          const int tih = lt - (gq + 1) * th;
+          const rsrc_t r = make_rsrc(pl.vc, kvbytes);
+          const uint32_t o = (kvoff + 16 * tih + 4 * q) * ESZ;
+          if constexpr (BF) st8c(r, o, u32x2{f2bf(acc0[0]) | (f2bf(acc0[1]) << 16), f2bf(acc0[2]) | (f2bf(acc0[3]) << 16)});
+          else st16c(r, o, u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
+        }
+      }
+    } else if (epi == EPI_GU) {
+      if (live) {
+        float m[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gv = acc0[v], uv = acc1[v];
+          m[v] = (gv / (1.0f + expf(-gv))) * uv;
+        }
+        const rsrc_t r = make_rsrc((uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ, (uint32_t)Rmax * pl.I * ESZ);
+        const uint32_t o = (uint32_t)(row * pl.I + 16 * tk.tile + 4 * q) * ESZ;
+        if constexpr (BF) st8c(r, o, u32x2{f2bf(m[0]) | (f2bf(m[1]) << 16), f2bf(m[2]) | (f2bf(m[3]) << 16)});
+        else st16c(r, o, u32x4{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])});
+      }
+    } else if (epi == EPI_HEAD) {
+      const int V = pl.V;
+      const uint32_t n0 = 16 * tk.tile + 4 * q;
+      if (live) {
+        const u32x4 z = {__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])};
+        st16c(make_rsrc(pl.zbuf, (uint32_t)Rmax * V * 4), (uint32_t)(row * V + n0) * 4, z);
+        if (fr.logits)
+          st16c(make_rsrc(fr.logits, (uint32_t)rows * (pl.P - 1) * V * 4), (uint32_t)((row * (pl.P - 1) + (p - 1)) * V + n0) * 4, z);
+      }
+      // best (value, index) of the tile for this row
+      float bv = acc0[0];
+      uint32_t bi = n0;
+#pragma unroll
+      for (int v = 1; v < 4; ++v)
+        if (beats(acc0[v], n0 + v, bv, bi)) { bv = acc0[v]; bi = n0 + v; }
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        const float ov = shfl_xor_f(bv, m);
+        const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
+        if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (live && q == 0)
+        st8c(make_rsrc(pl.cand, (uint32_t)Rmax * pl.n_head_tiles * 8), (uint32_t)(row * pl.n_head_tiles + tk.tile) * 8,
+             u32x2{__float_as_uint(bv), bi});
+    } else {  // EPI_PART: fp32 partial of this split
+      if (live) {
+        const uint32_t o = (uint32_t)(((tk.tile * tk.nsplit + tk.split) * Rmax + row) * 16 + 4 * q) * 4;
+        st16c(make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4), o,
+              u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
+      }
+    }
+  }
+
+  if (epi != EPI_PART) {
+    signal_group(pl, tk.sig, tk.sig_slot, persistent);
+    return;
+  }
+
+  // Split-K: the last of the nsplit tasks of this tile to arrive adds the
+  // partials in split order (then the residual) and stores the tile.
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(pl.ctr + (size_t)tk.tctr * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    misc[0] = (old == (uint32_t)tk.nsplit * epoch - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (misc[0] == 0) return;  // uniform across the workgroup
+
+  {
+    const int t = threadIdx.x;  // 64 rows x 4 column quads
+    const int r = t >> 2, c4 = (t & 3) * 4;
+    if (r < rows) {
+      const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4);
+      f32x4 s = {0, 0, 0, 0};
+      for (int sp = 0; sp < tk.nsplit; ++sp) {
+        const u32x4 v = ld16c(rp, (uint32_t)(((tk.tile * tk.nsplit + sp) * Rmax + r) * 16 + c4) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(v[e]);
+      }
+      const uint32_t eo = (uint32_t)(r * H + 16 * tk.tile + c4) * ESZ;
+      if (resid) {
+        const rsrc_t rr = make_rsrc(resid, hbytes);
+        if constexpr (BF) {
+          const u32x2 h = ld8c(rr, eo);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[e] = s[e] + bf2f((h[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+        } else {
+          const u32x4 h = ld16c(rr, eo);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(h[e]);
+        }
+      }
+      const rsrc_t ro = make_rsrc(out, hbytes);
+      if constexpr (BF) st8c(ro, eo, u32x2{f2bf(s[0]) | (f2bf(s[1]) << 16), f2bf(s[2]) | (f2bf(s[3]) << 16)});
+      else st16c(ro, eo, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3])});
+    }
+  }
+  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+}
+
+// ------------------------------------------------------------------ attention
+
+// One kv head g for a group of rows: every (row, q head of g) pair is one
+// wave's work.  Scores: lane (t, c) takes position t and a quarter c of the
+// head dimension; softmax over t <= p in float; output: lane owns d/64 dims.
+template <int BF>
+__device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent) {
+  constexpr int ESZ = BF ? 2 : 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d = pl.d, gq = pl.gq, nkv = pl.nkv, P = pl.P, Rmax = pl.Rmax;
+  const int l = tk.layer, p = tk.pos;
+  const int ngroups = Rmax / pl.attn_rows;
+  const int g = tk.tile / ngroups, rg = tk.tile % ngroups;
+  const int npairs = pl.attn_rows * gq;
+  const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * d * ESZ;
+  const rsrc_t rq = make_rsrc((uint8_t*)pl.qbuf + (size_t)(p & 1) * qdbytes, qdbytes);
+  const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ;
+  const rsrc_t rk = make_rsrc(pl.kc, kvbytes), rv = make_rsrc(pl.vc, kvbytes);
+  const rsrc_t ra = make_rsrc((uint8_t*)pl.abuf + (size_t)(p & 1) * qdbytes, qdbytes);
+  const int t = lane >> 2, c = lane & 3;
+  const int dq = d / 4;                  // dims per score lane
+  const int nchunk = dq * ESZ / 16;      // 16-byte chunks per score lane (2, 4 or 8)
+  const int dpl = d / 64;                // output dims per lane (1 or 2)
+  for (int pi = wave; pi < npairs; pi += 4) {
+    const int row = rg * pl.attn_rows + pi / gq;
+    const int hq = g * gq + pi % gq;
+    if (row >= fr.rows) continue;  // wave-uniform
+    const uint32_t kvrow = (uint32_t)((l * Rmax + row) * nkv + g) * P;
+    // scores
+    float dot = 0.f;
+    if (t <= p) {
+      const uint32_t qo = (uint32_t)(row * pl.nq * d + hq * d + c * dq) * ESZ;
+      const uint32_t ko = (uint32_t)((kvrow + t) * d + c * dq) * ESZ;
+      u32x4 qv[8], kv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < nchunk) { qv[i] = ld16c(rq, qo + i * 16); kv[i] = ld16c(rk, ko + i * 16); }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < nchunk)
+#pragma unroll
+          for (int e = 0; e < 16 / ESZ; ++e) dot += chunk_elem<BF>(qv[i], e) * chunk_elem<BF>(kv[i], e);
+    }
+    dot += shfl_xor_f(dot, 1);
+    dot += shfl_xor_f(dot, 2);
+    const float s = (t <= p) ? dot * pl.attn_scale : -INFINITY;
+    float m = s;
+#pragma unroll
+    for (int k = 4; k <= 32; k <<= 1) m = fmaxf(m, shfl_xor_f(m, k));
+    const float e = (t <= p) ? expf(s - m) : 0.f;
+    float sum = e;
+#pragma unroll
+    for (int k = 4; k <= 32; k <<= 1) sum += shfl_xor_f(sum, k);
+    const float w = e / sum;
+    // output: sum over t in ascending order
+    float o0 = 0.f, o1 = 0.f;
+    const uint32_t dbase = (uint32_t)(lane * dpl);
+    for (int tt = 0; tt <= p; ++tt) {
+      const float wt = __shfl(w, tt * 4, 64);
+      const uint32_t vo = (uint32_t)((kvrow + tt) * d + dbase) * ESZ;
+      if constexpr (BF) {
+        if (dpl == 2) {
+          const uint32_t v = ld4c(rv, vo);
+          o0 += wt * bf2f(v & 0xffffu);
+          o1 += wt * bf2f(v >> 16);
+        } else {
+          o0 += wt * bf2f(ld2c(rv, vo));
+        }
+      } else {
+        if (dpl == 2) {
+          const u32x2 v = ld8c(rv, vo);
+          o0 += wt * __uint_as_float(v[0]);
+          o1 += wt * __uint_as_float(v[1]);
+        } else {
+          o0 += wt * __uint_as_float(ld4c(rv, vo));
+        }
+      }
+    }
+    const uint32_t ao = (uint32_t)(row * pl.nq * d + hq * d + dbase) * ESZ;
+    if constexpr (BF) {
+      if (dpl == 2) st4c(ra, ao, f2bf(o0) | (f2bf(o1) << 16));
+      else st2c(ra, ao, f2bf(o0));
+    } else {
+      if (dpl == 2) st8c(ra, ao, u32x2{__float_as_uint(o0), __float_as_uint(o1)});
+      else st4c(ra, ao, __float_as_uint(o0));
+    }
+  }
+  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+}
+
+// ------------------------------------------------------------------ draw + embed
+
+// Writes embedding row `code` of table j as the input of position j + 1 (when
+// there is one) and adds it to the row's fp32 embedding sum.
+template <int BF>
+__device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr, int j, int row, int code, bool first) {
+  constexpr int ESZ = BF ? 2 : 4;
+  const int H = pl.H, V = pl.V;
+  const rsrc_t re = make_rsrc(pl.embed, (uint32_t)pl.P * V * H * ESZ);
+  const rsrc_t rs = make_rsrc(fr.embsum, (uint32_t)fr.rows * H * 4);
+  const rsrc_t rx = make_rsrc(pl.xin, (uint32_t)pl.P * pl.Rmax * H * ESZ);
+  const uint32_t ebase = (uint32_t)((j * V + code) * H);
+  const uint32_t xbase = (uint32_t)(((j + 1) * pl.Rmax + row) * H);
+  for (int k = threadIdx.x * 4; k < H; k += kThreads * 4) {
+    float ev[4];
+    if constexpr (BF) {
+      const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(re, (ebase + k) * 2, 0, 0);
+      ev[0] = bf2f(e[0] & 0xffffu); ev[1] = bf2f(e[0] >> 16); ev[2] = bf2f(e[1] & 0xffffu); ev[3] = bf2f(e[1] >> 16);
+      if (j + 1 < pl.P) st8c(rx, (xbase + k) * 2, e);
+    } else {
+      const u32x4 e = ld16(re, (ebase + k) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ev[i] = __uint_as_float(e[i]);
+      if (j + 1 < pl.P) st16c(rx, (xbase + k) * 4, e);
+    }
+    const uint32_t so = (uint32_t)(row * H + k) * 4;
+    u32x4 sv;
+    if (first) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(ev[i]);
+    } else {
+      sv = ld16c(rs, so);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(__uint_as_float(sv[i]) + ev[i]);
+    }
+    st16c(rs, so, sv);
+  }
+}
+
+template <int BF>
+__device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent) {
+  const int row = (int)tk.tile;
+  if (row < fr.rows) {
+    int code = fr.code0[row];
+    code = code < 0 ? 0 : (code >= pl.V ? pl.V - 1 : code);
+    embed_row<BF>(pl, fr, 0, row, code, true);
+  }
+  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+}
+
+template <int BF>
+__device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t* misc, bool persistent) {
+  const int row = (int)tk.tile, p = tk.pos;
+  if (row < fr.rows) {
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const rsrc_t rc = make_rsrc(pl.cand, (uint32_t)pl.Rmax * pl.n_head_tiles * 8);
+      float bv = -INFINITY;
+      uint32_t bi = 0xffffffffu;
+      for (int i = lane; i < pl.n_head_tiles; i += 64) {
+        const u32x2 cv = ld8c(rc, (uint32_t)(row * pl.n_head_tiles + i) * 8);
+        const float v = __uint_as_float(cv[0]);
+        if (beats(v, cv[1], bv, bi)) { bv = v; bi = cv[1]; }
+      }
+#pragma unroll
+      for (int m = 1; m <= 32; m <<= 1) {
+        const float ov = shfl_xor_f(bv, m);
+        const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
+        if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (lane == 0) {
+        misc[1] = bi < (uint32_t)pl.V ? bi : 0u;
+        st4c(make_rsrc(fr.codes, (uint32_t)fr.rows * (pl.P - 1) * 4), (uint32_t)(row * (pl.P - 1) + p - 1) * 4, misc[1]);
+      }
+    }
+    __syncthreads();
+    embed_row<BF>(pl, fr, p, row, (int)misc[1], false);
+  }
+  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+}
+
+// ------------------------------------------------------------------ executors
+
+template <int BF>
+__device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t epoch,
+                                         uint8_t* slot, uint32_t* misc, bool persistent) {
+  switch (tk.type) {
+    case T_ATTN: attn_task<BF>(pl, fr, tk, persistent); break;
+    case T_EMBED0: embed0_task<BF>(pl, fr, tk, persistent); break;
+    case T_DRAW: draw_task<BF>(pl, fr, tk, misc, persistent); break;
+    default: proj_task<BF>(pl, fr, tk, epoch, slot, misc, persistent); break;
+  }
+}
+
+template <int BF>
+__global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
+  extern __shared__ __align__(1024) uint8_t lds[];
+  uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
+  const uint32_t epoch = ld_ctr(pl.state);
+  const uint32_t b = pl.wg_begin[blockIdx.x], e = pl.wg_begin[blockIdx.x + 1];
+  for (uint32_t i = b; i < e; ++i) {
+    const Task tk = pl.tasks[i];
+    uint8_t* slot = lds + ((i - b) & 1) * kSlotBytes;
+    if (tk.w_bytes) issue_tile(pl, tk, slot);  // lands while the workgroup waits
+    wait_deps(pl, tk, epoch);
+    run_task<BF>(pl, fr, tk, epoch, slot, misc, true);
+  }
+  // The last workgroup to finish moves the plan to the next frame.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(pl.state + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)pl.n_wg * epoch - 1)
+      __hip_atomic_store(pl.state, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int BF>
+__global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame fr, const Task* tasks) {
+  extern __shared__ __align__(1024) uint8_t lds[];
+  uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
+  const uint32_t epoch = ld_ctr(pl.state);
+  const Task tk = tasks[blockIdx.x];
+  if (tk.w_bytes) issue_tile(pl, tk, lds);
+  run_task<BF>(pl, fr, tk, epoch, lds, misc, false);
+}
+
+__global__ void bump_epoch_kernel(uint32_t* state) {
+  const uint32_t e = ld_ctr(state);
+  __hip_atomic_store(state, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace cpms
+
+// ------------------------------------------------------------------ host-side launchers
+
+namespace cpms {
+
+const void* persistent_kernel_ptr(int bf16) {
+  return bf16 ? (const void*)persistent_kernel<1> : (const void*)persistent_kernel<0>;
+}
+
+hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s) {
+  if (pl.bf16)
+    hipLaunchKernelGGL(persistent_kernel<1>, dim3(pl.n_wg), dim3(kThreads), kLdsBytes, s, pl, fr);
+  else
+    hipLaunchKernelGGL(persistent_kernel<0>, dim3(pl.n_wg), dim3(kThreads), kLdsBytes, s, pl, fr);
+  return hipGetLastError();
+}
+
+hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const Task* tasks, int n, hipStream_t s) {
+  if (pl.bf16)
+    hipLaunchKernelGGL(phase_kernel<1>, dim3(n), dim3(kThreads), kLdsBytes, s, pl, fr, tasks);
+  else
+    hipLaunchKernelGGL(phase_kernel<0>, dim3(n), dim3(kThreads), kLdsBytes, s, pl, fr, tasks);
+  return hipGetLastError();
+}
+
+hipError_t launch_bump_epoch(uint32_t* state, hipStream_t s) {
+  hipLaunchKernelGGL(bump_epoch_kernel, dim3(1), dim3(1), 0, s, state);
+  return hipGetLastError();
+}
+
+hipError_t set_kernel_attributes() {
+  hipError_t e;
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
+  if ((e = hipFuncSetAttribute((const void*)phase_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
+  return hipFuncSetAttribute((const void*)phase_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+}
+
+int occupancy_per_cu(int bf16) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bf16 ? persistent_kernel<1> : persistent_kernel<0>, kThreads,
+                                                   kLdsBytes) != hipSuccess)
+    return -1;
+  return n;
+}
+
+}  // namespace cpms

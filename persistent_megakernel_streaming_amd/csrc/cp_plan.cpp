@@ -1,0 +1,833 @@
+// Host side of the depth-loop library: configuration checks, the co-residency
+// check, weight repacking, the static per-workgroup task lists and the C ABI
+// declared in include/cp.h.
+//
+// The schedule follows mstar pull request #1183 ("Qwen3-TTS: Run the 1.7B
+// Depth Loop as One Persistent Kernel on Hopper"), section "How it works":
+// the host builds a static task list per workgroup; a frame is the input
+// projection, qkv / attention / o / gate-up / down per layer and position,
+// a head per position after the first, and 16 embedding steps (15 after a
+// draw); attention waits per kv head; o and down split K across workgroups
+// and add the partials in a fixed order.  Deadlock freedom follows the rules
+// of the handbook chapter "The gaps between kernels: PDL and megakernels",
+// section "Megakernels": the grid is no larger than what is resident at once,
+// and every wait points to work that comes earlier in the global phase order,
+// which is also the order of every workgroup's own list.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cp.h"
+#include "cp_device.h"
+
+namespace cpms {
+const void* persistent_kernel_ptr(int bf16);
+hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s);
+hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const Task* tasks, int n, hipStream_t s);
+hipError_t launch_bump_epoch(uint32_t* state, hipStream_t s);
+hipError_t set_kernel_attributes();
+int occupancy_per_cu(int bf16);
+}  // namespace cpms
+
+using namespace cpms;
+
+struct cp_plan {
+  cp_config cfg{};
+  int device = 0;
+  int cu_count = 0;
+  DevPlan dp{};
+  std::vector<Task> tasks;              // grouped by workgroup
+  std::vector<uint32_t> wg_begin;
+  std::vector<Task> phase_tasks;        // grouped by phase (per-phase executor)
+  std::vector<uint32_t> phase_begin;
+  std::vector<CtrGroup> groups;
+  uint32_t n_ctr = 0;
+  int n_phases = 0;
+  int max_tasks_wg = 0;
+  Task* d_phase_tasks = nullptr;
+  std::vector<void*> allocs;
+  int64_t packed_bytes = 0, scratch_bytes = 0, weight_bytes_frame = 0;
+  std::string err;
+};
+
+static thread_local std::string g_create_err;
+
+namespace {
+
+#define HIPCHK(plan, call)                                                                   \
+  do {                                                                                       \
+    hipError_t e_ = (call);                                                                  \
+    if (e_ != hipSuccess) {                                                                  \
+      (plan)->err = std::string(#call) + ": " + hipGetErrorString(e_);                       \
+      return CP_ERR_HIP;                                                                     \
+    }                                                                                        \
+  } while (0)
+
+cp_status fail(cp_plan* p, cp_status s, const std::string& msg) {
+  p->err = msg;
+  return s;
+}
+
+uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------- planning
+
+struct Builder {
+  cp_plan* P;
+  int n_wg;
+  std::vector<std::vector<Task>> per_wg;
+  std::vector<std::vector<Task>> per_phase;
+  uint32_t next_ctr = 0;
+
+  uint32_t group(int count, int max_sub = 16) {
+    // a group of nsub sub-counters, each receiving count / nsub adds per frame
+    int nsub = std::min(max_sub, count);
+    while (count % nsub) --nsub;
+    CtrGroup g{next_ctr, (uint16_t)nsub, (uint16_t)(count / nsub)};
+    next_ctr += nsub;
+    P->groups.push_back(g);
+    return (uint32_t)P->groups.size() - 1;
+  }
+  uint32_t counter() { return next_ctr++; }
+
+  // Appends one phase; wg_of maps a task's index in the phase to a workgroup.
+  void phase(std::vector<Task> ts, const std::vector<int>& wg_of) {
+    const uint32_t ph = (uint32_t)per_phase.size();
+    for (size_t i = 0; i < ts.size(); ++i) {
+      ts[i].phase = ph;
+      per_wg[wg_of[i] % n_wg].push_back(ts[i]);
+    }
+    per_phase.push_back(std::move(ts));
+  }
+};
+
+Task make_task(uint8_t type, int l, int p, uint32_t tile) {
+  Task t{};
+  t.type = type;
+  t.layer = (uint16_t)l;
+  t.pos = (uint16_t)p;
+  t.tile = tile;
+  t.nsplit = 1;
+  t.sig = kNone;
+  t.tctr = kNone;
+  for (auto& w : t.wait) w = kNone;
+  return t;
+}
+
+void add_wait(Task& t, uint32_t g) { t.wait[t.nwait++] = g; }
+
+// Spreads n tasks over the workgroups starting at a rotating offset.
+std::vector<int> spread(int n, int n_wg, int& rot) {
+  std::vector<int> m(n);
+  for (int i = 0; i < n; ++i) m[i] = (rot + i) % n_wg;
+  rot = (rot + n) % n_wg;
+  return m;
+}
+
+// Split-K tasks (tile t, split s): the nsplit partners of a tile share an XCD
+// (workgroups are dealt to XCDs round-robin by id) when the phase fills the grid.
+std::vector<int> split_map(int tiles, int nsplit, int n_wg, int& rot) {
+  std::vector<int> m(tiles * nsplit);
+  if (tiles * nsplit == n_wg && n_wg % 8 == 0 && tiles % 8 == 0) {
+    for (int t = 0; t < tiles; ++t)
+      for (int s = 0; s < nsplit; ++s) m[t * nsplit + s] = ((t / 8) * nsplit + s) * 8 + (t % 8);
+    return m;
+  }
+  return spread(tiles * nsplit, n_wg, rot);
+}
+
+}  // namespace
+
+// Repacks one projection tile: rows[16 * nb] source rows (host), K range
+// [k0, k0 + kt).  Output order: chunk step c, row block b, lane, element -- the
+// order in which a wave's 64 lanes read MFMA A fragments (lane l: row l % 16,
+// elements (l / 16) * E .. + E of the step).
+static void pack_tile(std::vector<uint8_t>& blob, const std::vector<const uint8_t*>& rows, int k0, int kt, int esz) {
+  const int E = 16 / esz, KS = 4 * E, nb = (int)rows.size() / 16;
+  for (int c = 0; c < kt / KS; ++c)
+    for (int b = 0; b < nb; ++b)
+      for (int lane = 0; lane < 64; ++lane) {
+        const uint8_t* src = rows[16 * b + lane % 16] + (size_t)(k0 + c * KS + (lane / 16) * E) * esz;
+        blob.insert(blob.end(), src, src + 16);
+      }
+}
+
+static cp_status validate(const cp_config* c, std::string& msg) {
+  if (c->abi_version != CP_ABI_VERSION) { msg = "abi_version mismatch"; return CP_ERR_UNSUPPORTED; }
+  if (c->n_layers < 1 || c->hidden < 1 || c->input_dim < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 1 || c->intermediate < 1 || c->n_positions < 1 || c->vocab < 1 || c->max_rows < 1) {
+    msg = "non-positive size";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  if (c->dtype != CP_DTYPE_F32 && c->dtype != CP_DTYPE_BF16) { msg = "dtype"; return CP_ERR_UNSUPPORTED; }
+  if (c->exec != CP_EXEC_PERSISTENT && c->exec != CP_EXEC_PER_PHASE) { msg = "exec"; return CP_ERR_UNSUPPORTED; }
+  const int esz = c->dtype == CP_DTYPE_BF16 ? 2 : 4;
+  if (c->head_dim != 64 && c->head_dim != 128) { msg = "head_dim must be 64 or 128"; return CP_ERR_UNSUPPORTED; }
+  if (c->n_q_heads % c->n_kv_heads) { msg = "n_q_heads must be a multiple of n_kv_heads"; return CP_ERR_UNSUPPORTED; }
+  if (c->n_positions < 2 || c->n_positions > 16) { msg = "n_positions must be in 2..16"; return CP_ERR_UNSUPPORTED; }
+  if (c->max_rows > kMaxRows) { msg = "max_rows must be <= 64"; return CP_ERR_UNSUPPORTED; }
+  if (c->hidden % 64 || c->input_dim % 64 || c->intermediate % 64 || c->vocab % 64) {
+    msg = "hidden, input_dim, intermediate and vocab must be multiples of 64";
+    return CP_ERR_UNSUPPORTED;
+  }
+  if (c->hidden * esz > 2048) { msg = "hidden too large for register-resident rows"; return CP_ERR_UNSUPPORTED; }
+  if ((c->n_q_heads * c->head_dim / 4) * esz > 2048 || (c->intermediate / 4) * esz > 2048 ||
+      (c->input_dim / 4) * esz > 2048) {
+    msg = "split-K slice too large";
+    return CP_ERR_UNSUPPORTED;
+  }
+  if (c->n_q_heads % 4) { msg = "n_q_heads must be a multiple of 4"; return CP_ERR_UNSUPPORTED; }
+  // an o split (n_q_heads / 4 heads) must read at most kMaxWaits kv heads
+  const int gq = c->n_q_heads / c->n_kv_heads, hps = c->n_q_heads / 4;
+  if ((hps - 1) / gq + 2 > kMaxWaits && hps / gq > kMaxWaits) { msg = "kv grouping not supported"; return CP_ERR_UNSUPPORTED; }
+  if (c->flags & ~CP_FLAG_TRACE) { msg = "unknown flag"; return CP_ERR_UNSUPPORTED; }
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) { msg = "rms_eps / rope_theta"; return CP_ERR_INVALID_ARGUMENT; }
+  return CP_OK;
+}
+
+static cp_status build_schedule(cp_plan* P) {
+  const cp_config& c = P->cfg;
+  const int L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, d = c.head_dim;
+  const int I = c.intermediate, Pn = c.n_positions, V = c.vocab, R = c.max_rows;
+  const int gq = nq / nkv;
+  const int n_wg = P->cu_count;
+  Builder B{P, n_wg, std::vector<std::vector<Task>>(n_wg), {}, 0};
+  const int ht = H / 16, qkv_tiles = (nq + 2 * nkv) * d / 16, tpg = (gq + 2) * d / 16;
+  const int gu_tiles = I / 16, head_tiles = V / 16;
+  const int ns_o = 4, ns_d = 4, ns_in = 4;
+  int ar = std::max(1, 4 / gq);
+  while (R % ar) --ar;
+  const int agroups = R / ar;
+  P->dp.attn_rows = ar;
+  P->dp.n_o_split = ns_o;
+  P->dp.n_d_split = ns_d;
+  P->dp.n_in_split = ns_in;
+  const int gu_per_split = gu_tiles / ns_d;
+  int rot = 0;
+
+  // input projection (split-K) and code-0 embedding: no waits
+  const uint32_t g_inp = B.group(ht);
+  {
+    std::vector<Task> ts;
+    for (int t = 0; t < ht; ++t) {
+      const uint32_t tc = B.counter();
+      for (int s = 0; s < ns_in; ++s) {
+        Task k = make_task(T_INPROJ, 0, 0, t);
+        k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_in; k.tctr = tc; k.sig = g_inp; k.sig_slot = t;
+        ts.push_back(k);
+      }
+    }
+    B.phase(ts, split_map(ht, ns_in, n_wg, rot));
+  }
+  const uint32_t g_emb0 = B.group(R);
+  {
+    std::vector<Task> ts;
+    for (int r = 0; r < R; ++r) {
+      Task k = make_task(T_EMBED0, 0, 0, r);
+      k.sig = g_emb0; k.sig_slot = r;
+      ts.push_back(k);
+    }
+    B.phase(ts, spread(R, n_wg, rot));
+  }
+
+  std::vector<std::vector<uint32_t>> g_qkv(Pn * L);  // [p * L + l][g]
+  uint32_t g_prev_draw = kNone;
+  for (int p = 0; p < Pn; ++p) {
+    uint32_t g_layer_in = (p == 0) ? g_inp : (p == 1 ? g_emb0 : g_prev_draw);
+    for (int l = 0; l < L; ++l) {
+      // qkv
+      std::vector<uint32_t>& gq_groups = g_qkv[p * L + l];
+      for (int g = 0; g < nkv; ++g) gq_groups.push_back(B.group(tpg, 4));
+      {
+        std::vector<Task> ts;
+        for (int t = 0; t < qkv_tiles; ++t) {
+          Task k = make_task(T_QKV, l, p, t);
+          add_wait(k, g_layer_in);
+          k.sig = gq_groups[t / tpg]; k.sig_slot = t % tpg;
+          ts.push_back(k);
+        }
+        B.phase(ts, spread(qkv_tiles, n_wg, rot));
+      }
+      // Position 0 has no head: the residual after its last layer feeds
+      // nothing, so only the last layer's qkv (its K/V) is computed there.
+      if (p == 0 && l == L - 1) break;
+      // attention, per kv head
+      std::vector<uint32_t> g_att(nkv);
+      for (int g = 0; g < nkv; ++g) g_att[g] = B.group(agroups, 4);
+      {
+        std::vector<Task> ts;
+        for (int g = 0; g < nkv; ++g)
+          for (int rg = 0; rg < agroups; ++rg) {
+            Task k = make_task(T_ATTN, l, p, g * agroups + rg);
+            add_wait(k, gq_groups[g]);
+            if (p == 1) add_wait(k, g_qkv[0 * L + l][g]);  // position 0's K/V of this layer
+            k.sig = g_att[g]; k.sig_slot = rg;
+            ts.push_back(k);
+          }
+        B.phase(ts, spread(nkv * agroups, n_wg, rot));
+      }
+      // o (split-K over q heads; a split waits only on the kv heads it reads)
+      const uint32_t g_o = B.group(ht);
+      {
+        std::vector<Task> ts;
+        const int hps = nq / ns_o;
+        for (int t = 0; t < ht; ++t) {
+          const uint32_t tc = B.counter();
+          for (int s = 0; s < ns_o; ++s) {
+            Task k = make_task(T_O, l, p, t);
+            k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_o; k.tctr = tc; k.sig = g_o; k.sig_slot = t;
+            for (int g = (s * hps) / gq; g <= (s * hps + hps - 1) / gq; ++g) add_wait(k, g_att[g]);
+            ts.push_back(k);
+          }
+        }
+        B.phase(ts, split_map(ht, ns_o, n_wg, rot));
+      }
+      // gate/up
+      std::vector<uint32_t> g_gu(ns_d);
+      for (int s = 0; s < ns_d; ++s) g_gu[s] = B.group(gu_per_split, 4);
+      {
+        std::vector<Task> ts;
+        for (int t = 0; t < gu_tiles; ++t) {
+          Task k = make_task(T_GU, l, p, t);
+          add_wait(k, g_o);
+          k.sig = g_gu[t / gu_per_split]; k.sig_slot = t % gu_per_split;
+          ts.push_back(k);
+        }
+        B.phase(ts, spread(gu_tiles, n_wg, rot));
+      }
+      // down (split-K over the intermediate; a split waits on the gate/up
+      // tiles of its slice)
+      const uint32_t g_down = B.group(ht);
+      {
+        std::vector<Task> ts;
+        for (int t = 0; t < ht; ++t) {
+          const uint32_t tc = B.counter();
+          for (int s = 0; s < ns_d; ++s) {
+            Task k = make_task(T_DOWN, l, p, t);
+            k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_d; k.tctr = tc; k.sig = g_down; k.sig_slot = t;
+            add_wait(k, g_gu[s]);
+            ts.push_back(k);
+          }
+        }
+        B.phase(ts, split_map(ht, ns_d, n_wg, rot));
+      }
+      g_layer_in = g_down;
+    }
+    if (p == 0) continue;
+    // head p and draw p
+    const uint32_t g_head = B.group(head_tiles);
+    {
+      std::vector<Task> ts;
+      for (int t = 0; t < head_tiles; ++t) {
+        Task k = make_task(T_HEAD, L - 1, p, t);
+        add_wait(k, g_layer_in);
+        k.sig = g_head; k.sig_slot = t;
+        ts.push_back(k);
+      }
+      B.phase(ts, spread(head_tiles, n_wg, rot));
+    }
+    const uint32_t g_draw = B.group(R);
+    {
+      std::vector<Task> ts;
+      for (int r = 0; r < R; ++r) {
+        Task k = make_task(T_DRAW, L - 1, p, r);
+        add_wait(k, g_head);
+        k.sig = g_draw; k.sig_slot = r;
+        ts.push_back(k);
+      }
+      B.phase(ts, spread(R, n_wg, rot));
+    }
+    g_prev_draw = g_draw;
+  }
+
+  P->n_ctr = B.next_ctr;
+  P->n_phases = (int)B.per_phase.size();
+  P->tasks.clear();
+  P->wg_begin.assign(1, 0);
+  P->max_tasks_wg = 0;
+  for (auto& v : B.per_wg) {
+    P->tasks.insert(P->tasks.end(), v.begin(), v.end());
+    P->wg_begin.push_back((uint32_t)P->tasks.size());
+    P->max_tasks_wg = std::max(P->max_tasks_wg, (int)v.size());
+  }
+  P->phase_tasks.clear();
+  P->phase_begin.assign(1, 0);
+  for (auto& v : B.per_phase) {
+    P->phase_tasks.insert(P->phase_tasks.end(), v.begin(), v.end());
+    P->phase_begin.push_back((uint32_t)P->phase_tasks.size());
+  }
+  return CP_OK;
+}
+
+// Checks the schedule invariants that deadlock freedom and correctness rest
+// on: waits only point to groups signalled by earlier phases; every group
+// receives exactly its per-frame count; each workgroup's list is in phase
+// order; weight tiles fit an LDS slot and the packed blob.
+static cp_status check_schedule(cp_plan* P) {
+  const size_t ng = P->groups.size();
+  std::vector<int> first_sig(ng, INT32_MAX), last_sig(ng, -1);
+  std::vector<int64_t> count(ng, 0);
+  std::vector<std::vector<int>> slot_count(ng);
+  for (size_t g = 0; g < ng; ++g) slot_count[g].assign(P->groups[g].nsub, 0);
+  std::vector<int> split_seen;
+  for (const Task& t : P->phase_tasks) {
+    if (t.sig != kNone) {
+      if (t.sig >= ng) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: bad signal group");
+      first_sig[t.sig] = std::min(first_sig[t.sig], (int)t.phase);
+      last_sig[t.sig] = std::max(last_sig[t.sig], (int)t.phase);
+      // split-K tasks signal once per tile (by the last arriver)
+      if (t.nsplit == 1 || t.split == 0) {
+        count[t.sig] += 1;
+        slot_count[t.sig][t.sig_slot % P->groups[t.sig].nsub] += 1;
+      }
+    }
+    if (t.w_bytes > (uint32_t)kSlotBytes || t.w_bytes % 1024) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: weight tile too large");
+    if ((int64_t)t.w_off + t.w_bytes > P->packed_bytes) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: tile outside blob");
+    if (t.tctr != kNone && t.tctr >= P->n_ctr) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: bad tile counter");
+  }
+  for (size_t g = 0; g < ng; ++g) {
+    const CtrGroup& G = P->groups[g];
+    if (count[g] != (int64_t)G.nsub * G.per_sub) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: group count mismatch");
+    for (int s = 0; s < G.nsub; ++s)
+      if (slot_count[g][s] != G.per_sub) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: sub-counter count mismatch");
+    if (G.base + G.nsub > P->n_ctr) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: counter out of range");
+  }
+  for (const Task& t : P->phase_tasks)
+    for (int k = 0; k < t.nwait; ++k) {
+      if (t.wait[k] >= ng) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: bad wait group");
+      if (last_sig[t.wait[k]] >= (int)t.phase) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: wait on a later phase");
+    }
+  for (size_t w = 0; w + 1 < P->wg_begin.size(); ++w)
+    for (uint32_t i = P->wg_begin[w] + 1; i < P->wg_begin[w + 1]; ++i)
+      if (P->tasks[i].phase < P->tasks[i - 1].phase) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: list out of order");
+  return CP_OK;
+}
+
+// ---------------------------------------------------------------- weights
+
+static cp_status fetch(cp_plan* P, const void* dptr, size_t bytes, std::vector<uint8_t>& out) {
+  if (!dptr) return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL weight pointer");
+  out.resize(bytes);
+  HIPCHK(P, hipMemcpy(out.data(), dptr, bytes, hipMemcpyDeviceToHost));
+  return CP_OK;
+}
+
+static cp_status alloc(cp_plan* P, void** p, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    P->err = std::string("hipMalloc: ") + hipGetErrorString(e);
+    return CP_ERR_OUT_OF_MEMORY;
+  }
+  P->allocs.push_back(*p);
+  P->scratch_bytes += (int64_t)bytes;
+  return CP_OK;
+}
+
+#define TRY(x)                     \
+  do {                             \
+    cp_status s_ = (x);            \
+    if (s_ != CP_OK) return s_;    \
+  } while (0)
+
+static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
+  const cp_config& c = P->cfg;
+  const int L = c.n_layers, H = c.hidden, Din = c.input_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const int d = c.head_dim, I = c.intermediate, Pn = c.n_positions, V = c.vocab;
+  const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
+  const int gq = nq / nkv, th = d / 16, tpg = (gq + 2) * th, qkv_tiles = nkv * tpg, ht = H / 16;
+  const int ns_o = P->dp.n_o_split, ns_d = P->dp.n_d_split, ns_in = P->dp.n_in_split;
+  const int qd = nq * d;
+  std::vector<uint8_t> blob;
+  blob.reserve((size_t)esz * ((size_t)L * ((nq + 2 * nkv) * d * H + H * qd + 3 * I * H) + (size_t)(Pn - 1) * V * H + (size_t)H * Din));
+  // offsets [l][kind][tile][split]
+  std::vector<uint32_t> off_qkv(L * qkv_tiles), off_o(L * ht * ns_o), off_gu(L * (I / 16)), off_d(L * ht * ns_d);
+  std::vector<uint32_t> off_head((Pn - 1) * (V / 16)), off_in(ht * ns_in);
+  std::vector<uint8_t> m, m2;
+  auto rowp = [&](const std::vector<uint8_t>& mat, int cols, int r) { return mat.data() + (size_t)r * cols * esz; };
+  auto check_size = [&]() { return blob.size() < 0xffffffffull; };
+  if (!w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->attn_norm || !w->mlp_norm || !w->embed ||
+      !w->w_head)
+    return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL weight list");
+  for (int l = 0; l < L; ++l) {
+    TRY(fetch(P, w->w_qkv[l], (size_t)(nq + 2 * nkv) * d * H * esz, m));
+    for (int t = 0; t < qkv_tiles; ++t) {
+      const int g = t / tpg, lt = t % tpg;
+      std::vector<const uint8_t*> rows(16);
+      for (int j = 0; j < 16; ++j) {
+        const int qq = j / 4, v = j % 4;
+        int r;
+        if (lt < (gq + 1) * th) {
+          const int tih = lt % th;
+          const int dim = 8 * tih + 2 * qq + (v >> 1) + (v & 1) * (d / 2);  // rotary pair layout
+          r = (lt < gq * th) ? (g * gq + lt / th) * d + dim : qd + g * d + dim;
+        } else {
+          r = qd + nkv * d + g * d + 16 * (lt - (gq + 1) * th) + j;
+        }
+        rows[j] = rowp(m, H, r);
+      }
+      off_qkv[l * qkv_tiles + t] = (uint32_t)blob.size();
+      pack_tile(blob, rows, 0, H, esz);
+    }
+    TRY(fetch(P, w->w_o[l], (size_t)H * qd * esz, m));
+    for (int t = 0; t < ht; ++t)
+      for (int s = 0; s < ns_o; ++s) {
+        std::vector<const uint8_t*> rows(16);
+        for (int j = 0; j < 16; ++j) rows[j] = rowp(m, qd, 16 * t + j);
+        off_o[(l * ht + t) * ns_o + s] = (uint32_t)blob.size();
+        pack_tile(blob, rows, s * (qd / ns_o), qd / ns_o, esz);
+      }
+    TRY(fetch(P, w->w_gate[l], (size_t)I * H * esz, m));
+    TRY(fetch(P, w->w_up[l], (size_t)I * H * esz, m2));
+    for (int t = 0; t < I / 16; ++t) {
+      std::vector<const uint8_t*> rows(32);
+      for (int j = 0; j < 16; ++j) {
+        rows[j] = rowp(m, H, 16 * t + j);
+        rows[16 + j] = rowp(m2, H, 16 * t + j);
+      }
+      off_gu[l * (I / 16) + t] = (uint32_t)blob.size();
+      pack_tile(blob, rows, 0, H, esz);
+    }
+    TRY(fetch(P, w->w_down[l], (size_t)H * I * esz, m));
+    for (int t = 0; t < ht; ++t)
+      for (int s = 0; s < ns_d; ++s) {
+        std::vector<const uint8_t*> rows(16);
+        for (int j = 0; j < 16; ++j) rows[j] = rowp(m, I, 16 * t + j);
+        off_d[(l * ht + t) * ns_d + s] = (uint32_t)blob.size();
+        pack_tile(blob, rows, s * (I / ns_d), I / ns_d, esz);
+      }
+    if (!check_size()) return fail(P, CP_ERR_UNSUPPORTED, "packed weights exceed 4 GiB");
+  }
+  for (int j = 1; j < Pn; ++j) {
+    TRY(fetch(P, w->w_head[j - 1], (size_t)V * H * esz, m));
+    for (int t = 0; t < V / 16; ++t) {
+      std::vector<const uint8_t*> rows(16);
+      for (int i = 0; i < 16; ++i) rows[i] = rowp(m, H, 16 * t + i);
+      off_head[(j - 1) * (V / 16) + t] = (uint32_t)blob.size();
+      pack_tile(blob, rows, 0, H, esz);
+    }
+  }
+  TRY(fetch(P, w->w_in, (size_t)H * Din * esz, m));
+  for (int t = 0; t < ht; ++t)
+    for (int s = 0; s < ns_in; ++s) {
+      std::vector<const uint8_t*> rows(16);
+      for (int j = 0; j < 16; ++j) rows[j] = rowp(m, Din, 16 * t + j);
+      off_in[t * ns_in + s] = (uint32_t)blob.size();
+      pack_tile(blob, rows, s * (Din / ns_in), Din / ns_in, esz);
+    }
+  if (!check_size()) return fail(P, CP_ERR_UNSUPPORTED, "packed weights exceed 4 GiB");
+
+  // attach tiles to tasks
+  auto attach = [&](Task& t) {
+    switch (t.type) {
+      case T_QKV: t.w_off = off_qkv[t.layer * qkv_tiles + t.tile]; t.w_bytes = 16 * H * esz; break;
+      case T_O: t.w_off = off_o[(t.layer * ht + t.tile) * ns_o + t.split]; t.w_bytes = 16 * (qd / ns_o) * esz; break;
+      case T_GU: t.w_off = off_gu[t.layer * (I / 16) + t.tile]; t.w_bytes = 32 * H * esz; break;
+      case T_DOWN: t.w_off = off_d[(t.layer * ht + t.tile) * ns_d + t.split]; t.w_bytes = 16 * (I / ns_d) * esz; break;
+      case T_HEAD: t.w_off = off_head[(t.pos - 1) * (V / 16) + t.tile]; t.w_bytes = 16 * H * esz; break;
+      case T_INPROJ: t.w_off = off_in[t.tile * ns_in + t.split]; t.w_bytes = 16 * (Din / ns_in) * esz; break;
+      default: t.w_off = 0; t.w_bytes = 0; break;
+    }
+  };
+  for (Task& t : P->tasks) attach(t);
+  for (Task& t : P->phase_tasks) attach(t);
+
+  void* dblob;
+  TRY(alloc(P, &dblob, blob.size()));
+  HIPCHK(P, hipMemcpy(dblob, blob.data(), blob.size(), hipMemcpyHostToDevice));
+  P->dp.wblob = (const uint8_t*)dblob;
+  P->packed_bytes = (int64_t)blob.size();
+
+  // norm gains [2L + 1][H], embedding tables [P][V][H], RoPE table [P][d/2][2]
+  std::vector<uint8_t> gains((size_t)(2 * L + 1) * H * esz);
+  for (int l = 0; l < L; ++l) {
+    TRY(fetch(P, w->attn_norm[l], (size_t)H * esz, m));
+    std::memcpy(gains.data() + (size_t)(2 * l) * H * esz, m.data(), (size_t)H * esz);
+    TRY(fetch(P, w->mlp_norm[l], (size_t)H * esz, m));
+    std::memcpy(gains.data() + (size_t)(2 * l + 1) * H * esz, m.data(), (size_t)H * esz);
+  }
+  TRY(fetch(P, w->final_norm, (size_t)H * esz, m));
+  std::memcpy(gains.data() + (size_t)(2 * L) * H * esz, m.data(), (size_t)H * esz);
+  void* dg;
+  TRY(alloc(P, &dg, gains.size()));
+  HIPCHK(P, hipMemcpy(dg, gains.data(), gains.size(), hipMemcpyHostToDevice));
+  P->dp.gains = dg;
+  void* de;
+  TRY(alloc(P, &de, (size_t)Pn * V * H * esz));
+  for (int j = 0; j < Pn; ++j) {
+    if (!w->embed[j]) return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL embedding table");
+    HIPCHK(P, hipMemcpy((uint8_t*)de + (size_t)j * V * H * esz, w->embed[j], (size_t)V * H * esz, hipMemcpyDeviceToDevice));
+  }
+  P->dp.embed = de;
+  std::vector<float> rope((size_t)Pn * (d / 2) * 2);
+  for (int p = 0; p < Pn; ++p)
+    for (int i = 0; i < d / 2; ++i) {
+      const double ang = (double)p * std::pow((double)c.rope_theta, -2.0 * i / (double)d);
+      rope[((size_t)p * (d / 2) + i) * 2] = (float)std::cos(ang);
+      rope[((size_t)p * (d / 2) + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  void* dr;
+  TRY(alloc(P, &dr, rope.size() * 4));
+  HIPCHK(P, hipMemcpy(dr, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
+  P->dp.rope = (const float*)dr;
+  int64_t wb = (int64_t)esz * ((int64_t)Pn * L * ((nq + 2 * nkv) * d * H + (int64_t)H * qd + 3LL * I * H) +
+                               (int64_t)(Pn - 1) * V * H + (int64_t)H * Din);
+  P->weight_bytes_frame = wb;
+  return CP_OK;
+}
+
+static cp_status alloc_scratch(cp_plan* P) {
+  const cp_config& c = P->cfg;
+  const int L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, d = c.head_dim;
+  const int I = c.intermediate, Pn = c.n_positions, V = c.vocab, R = c.max_rows;
+  const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
+  DevPlan& dp = P->dp;
+  void* p;
+  TRY(alloc(P, &p, (size_t)Pn * R * H * esz)); dp.xin = p;
+  TRY(alloc(P, &p, (size_t)2 * 2 * R * H * esz)); dp.hres = p;     // [parity][layer parity]
+  TRY(alloc(P, &p, (size_t)2 * R * H * esz)); dp.hmid = p;
+  TRY(alloc(P, &p, (size_t)2 * R * nq * d * esz)); dp.qbuf = p;
+  TRY(alloc(P, &p, (size_t)2 * R * nq * d * esz)); dp.abuf = p;
+  TRY(alloc(P, &p, (size_t)2 * R * I * esz)); dp.mbuf = p;
+  TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * esz)); dp.kc = p;
+  TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * esz)); dp.vc = p;
+  const size_t part_one = (size_t)(H / 16) * 4 * R * 16;  // floats per split-K phase buffer
+  TRY(alloc(P, &p, part_one * 5 * 4)); dp.part = (float*)p;          // o[2], down[2], in
+  dp.part_stride = part_one;
+  dp.part_o_off = 0;
+  dp.part_d_off = 2 * part_one;
+  dp.part_in_off = 4 * part_one;
+  TRY(alloc(P, &p, (size_t)R * V * 4)); dp.zbuf = (float*)p;
+  TRY(alloc(P, &p, (size_t)R * (V / 16) * 8)); dp.cand = (uint2*)p;
+  TRY(alloc(P, &p, (size_t)P->n_ctr * kCtrStride * 4)); dp.ctr = (uint32_t*)p;
+  HIPCHK(P, hipMemset(dp.ctr, 0, (size_t)P->n_ctr * kCtrStride * 4));
+  TRY(alloc(P, &p, 128 * 4)); dp.state = (uint32_t*)p;
+  std::vector<uint32_t> st(128, 0);
+  st[0] = 1;  // first frame is epoch 1
+  HIPCHK(P, hipMemcpy(dp.state, st.data(), st.size() * 4, hipMemcpyHostToDevice));
+  TRY(alloc(P, &p, P->tasks.size() * sizeof(Task))); dp.tasks = (const Task*)p;
+  HIPCHK(P, hipMemcpy(p, P->tasks.data(), P->tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
+  TRY(alloc(P, &p, P->wg_begin.size() * 4)); dp.wg_begin = (const uint32_t*)p;
+  HIPCHK(P, hipMemcpy(p, P->wg_begin.data(), P->wg_begin.size() * 4, hipMemcpyHostToDevice));
+  TRY(alloc(P, &p, P->phase_tasks.size() * sizeof(Task))); P->d_phase_tasks = (Task*)p;
+  HIPCHK(P, hipMemcpy(p, P->phase_tasks.data(), P->phase_tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
+  TRY(alloc(P, &p, P->groups.size() * sizeof(CtrGroup))); dp.groups = (const CtrGroup*)p;
+  HIPCHK(P, hipMemcpy(p, P->groups.data(), P->groups.size() * sizeof(CtrGroup), hipMemcpyHostToDevice));
+  return CP_OK;
+}
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" {
+
+const char* cp_status_string(cp_status s) {
+  switch (s) {
+    case CP_OK: return "ok";
+    case CP_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CP_ERR_UNSUPPORTED: return "unsupported";
+    case CP_ERR_NOT_CORESIDENT: return "persistent grid cannot be co-resident";
+    case CP_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case CP_ERR_HIP: return "HIP runtime error";
+    case CP_ERR_DEVICE_TIMEOUT: return "device-side wait timed out";
+  }
+  return "unknown status";
+}
+
+const char* cp_plan_last_error(const cp_plan* plan) { return plan ? plan->err.c_str() : ""; }
+const char* cp_last_create_error(void) { return g_create_err.c_str(); }
+
+cp_status cp_plan_destroy(cp_plan* plan) {
+  if (!plan) return CP_OK;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(plan->device);
+  for (void* p : plan->allocs) (void)hipFree(p);
+  (void)hipSetDevice(prev);
+  delete plan;
+  return CP_OK;
+}
+
+static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights* w, int dev) {
+  std::string msg;
+  cp_status s = validate(cfg, msg);
+  if (s != CP_OK) return fail(P, s, msg);
+  P->cfg = *cfg;
+  P->device = dev;
+  int ndev = 0;
+  HIPCHK(P, hipGetDeviceCount(&ndev));
+  if (dev < 0 || dev >= ndev) return fail(P, CP_ERR_INVALID_ARGUMENT, "no such device");
+  HIPCHK(P, hipSetDevice(dev));
+  hipDeviceProp_t prop;
+  HIPCHK(P, hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(P, CP_ERR_UNSUPPORTED, std::string("needs gfx950, found ") + prop.gcnArchName);
+  P->cu_count = prop.multiProcessorCount;
+  if ((size_t)prop.sharedMemPerBlock < (size_t)kLdsBytes)
+    return fail(P, CP_ERR_NOT_CORESIDENT, "not enough LDS per workgroup");
+  HIPCHK(P, set_kernel_attributes());
+  const int bf = cfg->dtype == CP_DTYPE_BF16;
+  if (occupancy_per_cu(bf) < 1) return fail(P, CP_ERR_NOT_CORESIDENT, "persistent kernel does not fit one CU");
+
+  DevPlan& dp = P->dp;
+  dp.L = cfg->n_layers; dp.H = cfg->hidden; dp.Din = cfg->input_dim; dp.nq = cfg->n_q_heads;
+  dp.nkv = cfg->n_kv_heads; dp.d = cfg->head_dim; dp.I = cfg->intermediate; dp.P = cfg->n_positions;
+  dp.V = cfg->vocab; dp.Rmax = cfg->max_rows; dp.gq = dp.nq / dp.nkv; dp.n_head_tiles = dp.V / 16;
+  dp.bf16 = bf; dp.eps = cfg->rms_eps; dp.attn_scale = (float)(1.0 / std::sqrt((double)cfg->head_dim));
+  dp.spin_limit = 1u << 22;
+  dp.n_wg = P->cu_count;
+  TRY(build_schedule(P));
+  TRY(pack_weights(P, w));
+  TRY(check_schedule(P));
+  dp.n_tasks = (int)P->tasks.size();
+  TRY(alloc_scratch(P));
+  HIPCHK(P, hipDeviceSynchronize());
+  return CP_OK;
+}
+
+cp_status cp_plan_create(const cp_config* cfg, const cp_weights* w, int hip_device, cp_plan** out) {
+  if (!out) return CP_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  g_create_err.clear();
+  if (!cfg || !w) {
+    g_create_err = "NULL config or weights";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  cp_plan* P = new cp_plan();
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  cp_status s = create_impl(P, cfg, w, hip_device);
+  (void)hipSetDevice(prev);
+  if (s != CP_OK) {
+    g_create_err = P->err;
+    cp_plan_destroy(P);
+    return s;
+  }
+  *out = P;
+  return CP_OK;
+}
+
+cp_status cp_schedule_check(const cp_config* cfg, int cu_count, cp_plan_info* info) {
+  g_create_err.clear();
+  if (!cfg || !info || cu_count < 1) {
+    g_create_err = "NULL argument or cu_count < 1";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  cp_plan P;
+  std::string msg;
+  cp_status s = validate(cfg, msg);
+  if (s == CP_OK) {
+    P.cfg = *cfg;
+    P.cu_count = cu_count;
+    P.packed_bytes = INT64_MAX;  // no weights: tile bounds are not checked here
+    s = build_schedule(&P);
+    if (s == CP_OK) s = check_schedule(&P);
+    msg = P.err;
+  }
+  if (s != CP_OK) {
+    g_create_err = msg;
+    return s;
+  }
+  std::memset(info, 0, sizeof *info);
+  info->n_phases = P.n_phases;
+  info->n_tasks = (int32_t)P.tasks.size();
+  info->n_workgroups = cu_count;
+  info->max_tasks_per_workgroup = P.max_tasks_wg;
+  return CP_OK;
+}
+
+cp_status cp_plan_query(const cp_plan* P, cp_plan_info* info) {
+  if (!P || !info) return CP_ERR_INVALID_ARGUMENT;
+  info->n_phases = P->n_phases;
+  info->n_tasks = (int32_t)P->tasks.size();
+  info->n_workgroups = P->cu_count;
+  info->lds_bytes = kLdsBytes;
+  info->weight_bytes_per_frame = P->weight_bytes_frame;
+  info->packed_weight_bytes = P->packed_bytes;
+  info->scratch_bytes = P->scratch_bytes;
+  info->trace_words = 0;
+  info->cu_count = P->cu_count;
+  info->max_tasks_per_workgroup = P->max_tasks_wg;
+  return CP_OK;
+}
+
+cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
+  if (!P || !io) return CP_ERR_INVALID_ARGUMENT;
+  const cp_config& c = P->cfg;
+  if (io->rows < 1 || io->rows > c.max_rows) return fail(P, CP_ERR_INVALID_ARGUMENT, "rows out of range");
+  if (!io->hidden_in || !io->code0 || !io->codes || !io->embsum)
+    return fail(P, CP_ERR_INVALID_ARGUMENT, "hidden_in, code0, codes and embsum are required");
+  const int nsamp = (io->temperature != nullptr) + (io->top_k != nullptr) + (io->top_p != nullptr) +
+                    (io->seed != nullptr) + (io->offset != nullptr);
+  if (nsamp != 0 && nsamp != 5) return fail(P, CP_ERR_INVALID_ARGUMENT, "sampling arrays must be all set or all NULL");
+  if (nsamp == 5) return fail(P, CP_ERR_UNSUPPORTED, "sampled draws are not built yet");
+  if (io->trace) return fail(P, CP_ERR_UNSUPPORTED, "tracing is not built yet");
+  DevFrame fr{};
+  fr.rows = io->rows;
+  fr.sampled = nsamp == 5;
+  fr.hidden_in = io->hidden_in;
+  fr.code0 = io->code0;
+  fr.temperature = io->temperature;
+  fr.top_k = io->top_k;
+  fr.top_p = io->top_p;
+  fr.seed = io->seed;
+  fr.offset = io->offset;
+  fr.codes = io->codes;
+  fr.embsum = io->embsum;
+  fr.logits = io->logits;
+  fr.trace = io->trace;
+  hipStream_t s = (hipStream_t)stream;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  if (prev != P->device) HIPCHK(P, hipSetDevice(P->device));
+  hipError_t e = hipSuccess;
+  if (c.exec == CP_EXEC_PERSISTENT) {
+    e = launch_persistent(P->dp, fr, s);
+  } else {
+    for (int ph = 0; ph < P->n_phases && e == hipSuccess; ++ph) {
+      const uint32_t b = P->phase_begin[ph], n = P->phase_begin[ph + 1] - b;
+      e = launch_phase(P->dp, fr, P->d_phase_tasks + b, (int)n, s);
+    }
+    if (e == hipSuccess) e = launch_bump_epoch(P->dp.state, s);
+  }
+  if (e == hipSuccess && (io->k_cache || io->v_cache)) {
+    const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
+    const size_t per_row = (size_t)c.n_kv_heads * c.n_positions * c.head_dim * esz;
+    for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
+      const size_t src = (size_t)l * c.max_rows * per_row, dst = (size_t)l * io->rows * per_row;
+      if (io->k_cache)
+        e = hipMemcpyAsync((uint8_t*)io->k_cache + dst, (const uint8_t*)P->dp.kc + src, io->rows * per_row,
+                           hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess && io->v_cache)
+        e = hipMemcpyAsync((uint8_t*)io->v_cache + dst, (const uint8_t*)P->dp.vc + src, io->rows * per_row,
+                           hipMemcpyDeviceToDevice, s);
+    }
+  }
+  if (prev != P->device) (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return CP_OK;
+}
+
+cp_status cp_plan_device_status(cp_plan* P) {
+  if (!P) return CP_ERR_INVALID_ARGUMENT;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(P->device);
+  uint32_t st[128];
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(st, P->dp.state, sizeof st, hipMemcpyDeviceToHost);
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("device status: ") + hipGetErrorString(e));
+  if (st[64]) return fail(P, CP_ERR_DEVICE_TIMEOUT, "a device-side wait gave up");
+  return CP_OK;
+}
+
+}  // extern "C"

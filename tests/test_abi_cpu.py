@@ -1,0 +1,72 @@
+"""Host-only checks of the C ABI library: it loads, exports every function
+include/cp.h declares, rejects bad arguments before touching a device, and its
+planner builds deadlock-free task lists (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from persistent_megakernel_streaming_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _cp():
+    from persistent_megakernel_streaming_amd import cp
+    return cp
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "cp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    cp = _cp()
+    names = _declared_functions()
+    assert "cp_plan_create" in names and "cp_frame_run" in names and "cp_plan_destroy" in names
+    for n in names:
+        assert hasattr(cp.lib(), n), n
+
+
+def test_status_strings_and_null_arguments():
+    cp = _cp()
+    lib = cp.lib()
+    for s in range(7):
+        assert lib.cp_status_string(s)
+    assert lib.cp_plan_create(None, None, 0, None) == 1
+    h = C.c_void_p()
+    c = cp.make_config(synth.CONFIGS["tiny_f32"])
+    assert lib.cp_plan_create(C.byref(c), None, 0, C.byref(h)) == 1 and not h.value
+    assert lib.cp_plan_destroy(None) == 0
+    assert lib.cp_frame_run(None, None, None) == 1
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(head_dim=96), 2), (dict(n_positions=17), 2), (dict(n_kv_heads=3), 2),
+    (dict(hidden=1000), 2), (dict(n_layers=0), 1), (dict(rows=65), 2),
+])
+def test_unsupported_shapes_are_refused_on_the_host(change, status):
+    cp = _cp()
+    rows = change.pop("rows", None)
+    cfg = synth.CONFIGS["l5_r1"].with_(**change)
+    c = cp.make_config(cfg, max_rows=rows)
+    info = cp.PlanInfo()
+    assert cp.lib().cp_schedule_check(C.byref(c), 256, C.byref(info)) == status
+    assert cp.lib().cp_last_create_error()
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "l5_r1", "l5_r64", "l10_r64"])
+@pytest.mark.parametrize("cus", [256, 64, 7])
+def test_schedule_invariants(name, cus):
+    cp = _cp()
+    cfg = synth.CONFIGS[name]
+    info = cp.schedule_check(cfg, cu_count=cus)
+    L, P = cfg.n_layers, cfg.n_positions
+    # 5 L P + 2 P phases (input projection, 15 heads, 16 embedding steps), less
+    # the four phases after position 0's last qkv, whose results nothing reads.
+    assert info.n_phases == 5 * L * P + 2 * P - 4
+    assert info.n_workgroups == cus
+    assert info.max_tasks_per_workgroup * cus >= info.n_tasks
