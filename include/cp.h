@@ -113,7 +113,10 @@ typedef struct {
   float* logits;             /* optional out [rows][n_positions - 1][vocab] (fp32) */
   void* k_cache;             /* optional out [n_layers][rows][n_kv_heads][n_positions][head_dim], dtype, post-RoPE */
   void* v_cache;             /* optional out, same layout */
-  uint64_t* trace;           /* optional out, cp_plan_info.trace_words words (needs CP_FLAG_TRACE) */
+  uint64_t* trace;           /* optional out, cp_plan_info.trace_words words (needs CP_FLAG_TRACE and the
+                                persistent executor): per task, in the order of cp_plan_task_table, six
+                                100 MHz timestamps -- task start, dependencies met, operands landed,
+                                body done, stores complete, signalled */
 } cp_frame_io;
 
 typedef struct {
@@ -144,6 +147,12 @@ cp_status cp_plan_create(const cp_config* cfg, const cp_weights* w, int hip_devi
  * the persistent executor holds every compute unit while it runs, and two of
  * its frames in flight at once on one device could wait on each other. */
 cp_status cp_frame_run(cp_plan* plan, const cp_frame_io* io, void* hip_stream);
+
+/* Writes 8 int32 per task, in trace order: phase index, task type (1 input
+ * projection, 2 code-0 embedding, 3 qkv, 4 attention, 5 o, 6 gate/up, 7 down,
+ * 8 head, 9 draw), layer, position, tile, split-K index, workgroup, index in
+ * the workgroup's list.  n_tasks must equal cp_plan_info.n_tasks. */
+cp_status cp_plan_task_table(const cp_plan* plan, int32_t* out, int64_t n_tasks);
 
 /* Frees everything the plan owns.  NULL is accepted. */
 cp_status cp_plan_destroy(cp_plan* plan);

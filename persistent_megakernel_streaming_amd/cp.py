@@ -73,8 +73,9 @@ def load_library():
     lib.cp_plan_last_error.restype = C.c_char_p
     lib.cp_last_create_error.restype = C.c_char_p
     lib.cp_schedule_check.argtypes = [C.POINTER(Config), C.c_int, C.POINTER(PlanInfo)]
+    lib.cp_plan_task_table.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
     for f in ("cp_plan_create", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
-              "cp_schedule_check"):
+              "cp_schedule_check", "cp_plan_task_table"):
         getattr(lib, f).restype = C.c_int
     return lib
 
@@ -177,6 +178,13 @@ class Plan:
                 setattr(f, k, t.data_ptr())
         s = torch.cuda.current_stream().cuda_stream if stream is None else stream
         self._check(_lib.cp_frame_run(self._h, C.byref(f), C.c_void_p(s)))
+
+    def task_table(self) -> np.ndarray:
+        """[n_tasks][8] int32: phase, type, layer, pos, tile, split, workgroup, index in list."""
+        n = self.info().n_tasks
+        out = np.zeros((n, 8), np.int32)
+        self._check(_lib.cp_plan_task_table(self._h, out.ctypes.data, n))
+        return out
 
     def device_status(self):
         self._check(_lib.cp_plan_device_status(self._h))

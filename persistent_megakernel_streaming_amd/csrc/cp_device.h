@@ -24,9 +24,10 @@ constexpr int kTileN = 16;          // output slots per projection tile
 constexpr int kMaxRows = 64;
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kSlotBytes = 64 * 1024;  // one weight-tile slot in LDS (two slots)
-constexpr int kMiscLds = 4096;
+constexpr int kMiscLds = 16384;  // flags, gain row, cross-wave reductions
 constexpr int kLdsBytes = 2 * kSlotBytes + kMiscLds;
 constexpr int kCtrStride = 32;      // uint32 words between sub-counters (128 B)
+constexpr int kTraceStamps = 6;     // timestamps per task in a traced frame
 
 // A group of sub-counters: a phase (or part of one) signals it, a later task
 // waits on it.  Producer i adds to sub-counter i % nsub; each sub-counter
@@ -62,6 +63,7 @@ struct DevPlan {
   int attn_rows;      // rows per attention task
   int n_head_tiles;   // vocab / 16
   int bf16;           // activation type
+  int unit_gains;     // every RMSNorm gain is exactly 1 (the gain product is skipped)
   float eps;
   float attn_scale;   // 1 / sqrt(head_dim)
   uint32_t spin_limit;

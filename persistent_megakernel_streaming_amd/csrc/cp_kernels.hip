@@ -55,15 +55,27 @@ __device__ __forceinline__ void st2c(rsrc_t r, uint32_t off, uint32_t v) { __bui
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Trace stamp k of the current task (100 MHz constant clock), thread 0 only.
+// tr is null when the plan does not trace.
+__device__ __forceinline__ void stamp(uint64_t* tr, int k) {
+  if (tr && threadIdx.x == 0) tr[k] = __builtin_amdgcn_s_memrealtime();
+}
+
 // ------------------------------------------------------------------ numerics
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float -> bf16, round to nearest even (NaN stays NaN).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const bf16x2 v = {(__bf16)f, (__bf16)0.0f};
+  return __builtin_bit_cast(uint32_t, v) & 0xffffu;
+}
+// Two floats -> packed bf16 pair (lo in bits 0..15), one conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element e of a 16-byte chunk as float.
@@ -128,27 +140,56 @@ __device__ __forceinline__ void wait_deps(const DevPlan& pl, const Task& tk, uin
 }
 
 // Every wave waits for its own stores, then one thread adds to the group.
-__device__ __forceinline__ void signal_group(const DevPlan& pl, uint32_t grp, uint32_t slot, bool persistent) {
+__device__ __forceinline__ void signal_group(const DevPlan& pl, uint32_t grp, uint32_t slot, bool persistent,
+                                             uint64_t* tr) {
+  stamp(tr, 3);
   wait_vm();
   __syncthreads();
+  stamp(tr, 4);
   if (persistent && threadIdx.x == 0 && grp != kNone) {
     const CtrGroup gp = pl.groups[grp];
     __hip_atomic_fetch_add(pl.ctr + (size_t)(gp.base + slot % gp.nsub) * kCtrStride, 1u,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  stamp(tr, 5);
 }
 
 // ------------------------------------------------------------------ weights -> LDS
 
-// Direct-to-LDS copy of the task's packed weight tile: each wave moves 1 KiB
-// chunks (64 lanes x 16 B) with global_load_lds_dwordx4.
-__device__ __forceinline__ void issue_tile(const DevPlan& pl, const Task& tk, uint8_t* slot) {
+// Byte offset of the gain row staged in the misc LDS region.
+constexpr int kGainLds = 1024;    // RMSNorm gain row (<= 2 KiB)
+constexpr int kRedSsLds = 4096;   // cross-wave sums of squares (256 B)
+constexpr int kRedAccLds = 8192;  // cross-wave MFMA accumulators (8 KiB)
+
+// Gain row (of the [2L + 1][H] table) a projection task normalises with, or -1.
+__device__ __forceinline__ int gain_row_of(const DevPlan& pl, const Task& tk) {
+  switch (tk.type) {
+    case T_QKV: return 2 * tk.layer;
+    case T_GU: return 2 * tk.layer + 1;
+    case T_HEAD: return 2 * pl.L;
+    default: return -1;
+  }
+}
+
+// Direct-to-LDS copies of the task's packed weight tile and, for normalising
+// tasks, its RMSNorm gain row: 1 KiB chunks (64 lanes x 16 B) with
+// global_load_lds_dwordx4, dealt round-robin to the four waves.
+__device__ __forceinline__ void issue_tile(const DevPlan& pl, const Task& tk, uint8_t* slot, uint8_t* misc) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t nch = tk.w_bytes >> 10;
   const uint8_t* src = pl.wblob + tk.w_off;
   for (uint32_t c = wave; c < nch; c += 4) {
     __builtin_amdgcn_global_load_lds((const void*)(src + c * 1024 + lane * 16),
                                      (void __attribute__((address_space(3)))*)(slot + c * 1024), 16, 0, 0);
+  }
+  const int gr = gain_row_of(pl, tk);
+  if (gr >= 0) {
+    const uint32_t gbytes = (uint32_t)pl.H * (pl.bf16 ? 2 : 4);  // <= 2 KiB
+    const uint8_t* gsrc = (const uint8_t*)pl.gains + (size_t)gr * gbytes;
+    for (uint32_t c = 3 - wave; c < (gbytes + 1023) / 1024; c += 4) {
+      __builtin_amdgcn_global_load_lds((const void*)(gsrc + c * 1024 + lane * 16),
+                                       (void __attribute__((address_space(3)))*)(misc + kGainLds + c * 1024), 16, 0, 0);
+    }
   }
 }
 
@@ -171,16 +212,13 @@ __device__ __forceinline__ f32x4 mma(const u32x4& w, const u32x4& x, f32x4 acc) 
 
 template <int BF>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t epoch,
-                          uint8_t* slot, uint32_t* misc, bool persistent) {
+                          uint8_t* slot, uint32_t* misc, bool persistent, uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 4, rl = lane & 15;
-  const int row = wave * 16 + rl;
   const int rows = fr.rows;
-  const bool wave_live = wave * 16 < rows;
-  const bool live = row < rows;
   const int H = pl.H, Rmax = pl.Rmax;
   const int l = tk.layer, p = tk.pos;
 
@@ -222,68 +260,125 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       xsrc = fr.hidden_in; ld = pl.Din; xbytes = (uint32_t)fr.rows * ld * ESZ; kt = pl.Din / tk.nsplit;
       k0 = tk.split * kt; epi = EPI_PART; out = pl.xin; part_off = pl.part_in_off; break;
   }
-  const int nck = kt * ESZ / 64;  // 16-byte chunks per lane (<= 32)
+  const int nck = kt * ESZ / 64;  // 16-byte chunks per lane over the task's K range
 
-  // Activation rows straight from memory into the B operand registers.
+  // Waves and row tiles: a wave owns 16 rows; with few rows the waves of a
+  // row tile split K and add their results through LDS in a fixed order.
+  const int nrt = (rows + 15) >> 4;                   // row tiles holding live rows (1..4)
+  const int wpr = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);  // waves per row tile
+  const int rt = wave / wpr, ks = wave % wpr;
+  const int ncw = nck / wpr;                          // chunks this wave handles (<= 32)
+  const int c0 = ks * ncw;
+  const int row = rt * 16 + rl;
+  const bool wave_live = rt < nrt;
+  const bool live = wave_live && row < rows;
+  float* red_ss = (float*)((uint8_t*)misc + kRedSsLds);      // [4 waves][16 rows]
+  f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);    // [4 waves][2][64 lanes]
+
+  // Activation rows straight from memory into the B operand registers; the
+  // residual of an unsplit o / down tile comes with them.
   const rsrc_t rx = make_rsrc(xsrc, xbytes);
   u32x4 xa[32];
-  const uint32_t xoff = ((uint32_t)row * ld + k0 + q * E) * ESZ;
+  const uint32_t xoff = ((uint32_t)row * ld + k0 + q * E) * ESZ + c0 * 64;
 #pragma unroll
   for (int c = 0; c < 32; ++c) {
-    if (c < nck) xa[c] = (wave_live && live) ? ld16c(rx, xoff + c * 64) : u32x4{0, 0, 0, 0};
+    if (c < ncw) xa[c] = live ? ld16c(rx, xoff + c * 64) : u32x4{0, 0, 0, 0};
+  }
+  const uint32_t eo = (uint32_t)(row * H + 16 * tk.tile + 4 * q) * ESZ;  // this lane's 4 output slots
+  u32x4 rv = {0, 0, 0, 0};
+  if (epi == EPI_PART && tk.nsplit == 1 && resid && live && ks == 0) {
+    const rsrc_t rr = make_rsrc(resid, hbytes);
+    if constexpr (BF) {
+      const u32x2 h = ld8c(rr, eo);
+      rv[0] = h[0]; rv[1] = h[1];
+    } else {
+      rv = ld16c(rr, eo);
+    }
+  }
+  // RoPE cos/sin of this lane's two rotary pairs (qkv tiles of q and k heads)
+  float rope_cs[2] = {1.f, 1.f}, rope_sn[2] = {0.f, 0.f};
+  if (tk.type == T_QKV) {
+    const int d = pl.d, th = d / 16, tpg = (pl.gq + 2) * th, lt = tk.tile % tpg;
+    if (lt < (pl.gq + 1) * th) {
+      const int i0 = 8 * (lt % th) + 2 * q;
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        rope_cs[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2];
+        rope_sn[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2 + 1];
+      }
+    }
   }
   wait_vm();        // activations and this wave's share of the weight tile have landed
   __syncthreads();  // every wave's share of the tile is in LDS
+  stamp(tr, 2);
 
-  if (wave_live) {
-    if (gain_row >= 0) {
-      // RMSNorm of the full row: float sum of squares per lane in K order,
-      // then across the four lane groups in a fixed tree.
-      float ss = 0.f;
+  if (gain_row >= 0) {
+    // RMSNorm of the full row: float sum of squares per lane in K order, then
+    // across the four lane groups and the waves of the row tile in a fixed order.
+    float ss = 0.f;
+    if (wave_live) {
 #pragma unroll
       for (int c = 0; c < 32; ++c)
-        if (c < nck)
+        if (c < ncw)
 #pragma unroll
           for (int e = 0; e < E; ++e) {
             const float x = chunk_elem<BF>(xa[c], e);
-            ss += x * x;
+            ss = fmaf(x, x, ss);
           }
       ss += shfl_xor_f(ss, 16);
       ss += shfl_xor_f(ss, 32);
-      const float rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
-      const rsrc_t rg = make_rsrc((const uint8_t*)pl.gains + (size_t)gain_row * H * ESZ, (uint32_t)H * ESZ);
+    }
+    if (wpr > 1) {
+      if (wave_live && q == 0) red_ss[wave * 16 + rl] = ss;
+      __syncthreads();
+      if (wave_live) {
+        ss = 0.f;
+        for (int k = 0; k < wpr; ++k) ss += red_ss[(rt * wpr + k) * 16 + rl];
+      }
+    }
+    const float rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
+    if (wave_live) {
+      const uint8_t* gl = (const uint8_t*)misc + kGainLds + c0 * 64;  // gain row staged with the tile
 #pragma unroll
       for (int c = 0; c < 32; ++c) {
-        if (c < nck) {
-          const u32x4 g = ld16(rg, (uint32_t)(c * KS + q * E) * ESZ);
+        if (c < ncw) {
           u32x4 o;
           if constexpr (BF) {
+            const u32x4 g = *(const u32x4*)(gl + (c * KS + q * E) * ESZ);
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {
-              const float t0 = chunk_elem<1>(xa[c], 2 * w2) * rinv, t1 = chunk_elem<1>(xa[c], 2 * w2 + 1) * rinv;
-              const float v0 = t0 * chunk_elem<1>(g, 2 * w2), v1 = t1 * chunk_elem<1>(g, 2 * w2 + 1);
-              o[w2] = f2bf(v0) | (f2bf(v1) << 16);
+              const uint32_t xw = xa[c][w2];
+              const float t0 = __uint_as_float(xw << 16) * rinv, t1 = __uint_as_float(xw & 0xffff0000u) * rinv;
+              if (pl.unit_gains) {
+                o[w2] = pack_bf16(t0, t1);
+              } else {
+                const uint32_t gw = g[w2];
+                o[w2] = pack_bf16(t0 * __uint_as_float(gw << 16), t1 * __uint_as_float(gw & 0xffff0000u));
+              }
             }
           } else {
+            const u32x4 g = *(const u32x4*)(gl + (c * KS + q * E) * ESZ);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float t = __uint_as_float(xa[c][e]) * rinv;
-              o[e] = __float_as_uint(t * __uint_as_float(g[e]));
+              o[e] = __float_as_uint(pl.unit_gains ? t : t * __uint_as_float(g[e]));
             }
           }
           xa[c] = live ? o : u32x4{0, 0, 0, 0};
         }
       }
     }
+  }
 
-    // K loop: weights from the LDS tile (fragment order), activations from registers.
-    f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    const uint8_t* wt = slot + lane * 16;
+  // K loop: weights from the LDS tile (fragment order), activations from registers.
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  if (wave_live) {
+    const uint8_t* wt = slot + lane * 16 + (size_t)c0 * nb * 1024;
     if (nb == 1) {
       // two accumulators on alternating chunks, added once at the end
 #pragma unroll
       for (int c = 0; c < 32; ++c) {
-        if (c < nck) {
+        if (c < ncw) {
           const u32x4 w = *(const u32x4*)(wt + c * 1024);
           if (c & 1) acc1 = mma<BF>(w, xa[c], acc1);
           else acc0 = mma<BF>(w, xa[c], acc0);
@@ -294,7 +389,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     } else {
 #pragma unroll
       for (int c = 0; c < 32; ++c) {
-        if (c < nck) {
+        if (c < ncw) {
           const u32x4 wg = *(const u32x4*)(wt + (2 * c) * 1024);
           const u32x4 wu = *(const u32x4*)(wt + (2 * c + 1) * 1024);
           acc0 = mma<BF>(wg, xa[c], acc0);
@@ -302,8 +397,33 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         }
       }
     }
+  }
+  if (wpr > 1) {
+    // K parts of a row tile: (((k0 + k1) + k2) + k3), in the wave of part 0
+    if (wave_live) {
+      red_acc[(wave * 2 + 0) * 64 + lane] = acc0;
+      if (nb == 2) red_acc[(wave * 2 + 1) * 64 + lane] = acc1;
+    }
+    __syncthreads();
+    if (wave_live && ks == 0) {
+      acc0 = red_acc[(rt * wpr * 2 + 0) * 64 + lane];
+      if (nb == 2) acc1 = red_acc[(rt * wpr * 2 + 1) * 64 + lane];
+      for (int k = 1; k < wpr; ++k) {
+        const f32x4 a = red_acc[((rt * wpr + k) * 2 + 0) * 64 + lane];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + a[v];
+        if (nb == 2) {
+          const f32x4 b = red_acc[((rt * wpr + k) * 2 + 1) * 64 + lane];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc1[v] = acc1[v] + b[v];
+        }
+      }
+    }
+  }
+  const bool epi_wave = wave_live && ks == 0;
 
-    // Lane (q, rl) holds output slots 4q .. 4q+3 of row `row`.
+  // Lane (q, rl) of an epilogue wave holds output slots 4q .. 4q+3 of row `row`.
+  if (epi_wave) {
     if (epi == EPI_QKV) {
       const int d = pl.d, th = d / 16, gq = pl.gq, nkv = pl.nkv;
       const int tpg = (gq + 2) * th;
@@ -321,7 +441,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
             const float x1 = acc0[2 * pr], x2 = acc0[2 * pr + 1];
-            const float cs = pl.rope[(p * (d / 2) + i0 + pr) * 2], sn = pl.rope[(p * (d / 2) + i0 + pr) * 2 + 1];
+            const float cs = rope_cs[pr], sn = rope_sn[pr];
             y[2 * pr] = x1 * cs - x2 * sn;
             y[2 * pr + 1] = x2 * cs + x1 * sn;
           }
@@ -336,8 +456,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
             base = kvoff;
           }
           if constexpr (BF) {
-            st4c(r, (base + i0) * 2, f2bf(y[0]) | (f2bf(y[2]) << 16));
-            st4c(r, (base + i0 + d / 2) * 2, f2bf(y[1]) | (f2bf(y[3]) << 16));
+            st4c(r, (base + i0) * 2, pack_bf16(y[0], y[2]));
+            st4c(r, (base + i0 + d / 2) * 2, pack_bf16(y[1], y[3]));
           } else {
             st8c(r, (base + i0) * 4, u32x2{__float_as_uint(y[0]), __float_as_uint(y[2])});
             st8c(r, (base + i0 + d / 2) * 4, u32x2{__float_as_uint(y[1]), __float_as_uint(y[3])});
@@ -346,7 +466,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           const int tih = lt - (gq + 1) * th;
           const rsrc_t r = make_rsrc(pl.vc, kvbytes);
           const uint32_t o = (kvoff + 16 * tih + 4 * q) * ESZ;
-          if constexpr (BF) st8c(r, o, u32x2{f2bf(acc0[0]) | (f2bf(acc0[1]) << 16), f2bf(acc0[2]) | (f2bf(acc0[3]) << 16)});
+          if constexpr (BF) st8c(r, o, u32x2{pack_bf16(acc0[0], acc0[1]), pack_bf16(acc0[2], acc0[3])});
           else st16c(r, o, u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
         }
       }
@@ -360,7 +480,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         }
         const rsrc_t r = make_rsrc((uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ, (uint32_t)Rmax * pl.I * ESZ);
         const uint32_t o = (uint32_t)(row * pl.I + 16 * tk.tile + 4 * q) * ESZ;
-        if constexpr (BF) st8c(r, o, u32x2{f2bf(m[0]) | (f2bf(m[1]) << 16), f2bf(m[2]) | (f2bf(m[3]) << 16)});
+        if constexpr (BF) st8c(r, o, u32x2{pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3])});
         else st16c(r, o, u32x4{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])});
       }
     } else if (epi == EPI_HEAD) {
@@ -387,7 +507,18 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       if (live && q == 0)
         st8c(make_rsrc(pl.cand, (uint32_t)Rmax * pl.n_head_tiles * 8), (uint32_t)(row * pl.n_head_tiles + tk.tile) * 8,
              u32x2{__float_as_uint(bv), bi});
-    } else {  // EPI_PART: fp32 partial of this split
+    } else if (tk.nsplit == 1) {  // EPI_PART, unsplit: residual add and store
+      if (live) {
+        f32x4 s = acc0;
+        if (resid) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[e] = s[e] + chunk_elem<BF>(rv, e);
+        }
+        const rsrc_t ro = make_rsrc(out, hbytes);
+        if constexpr (BF) st8c(ro, eo, u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])});
+        else st16c(ro, eo, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3])});
+      }
+    } else {  // EPI_PART, split: fp32 partial of this split
       if (live) {
         const uint32_t o = (uint32_t)(((tk.tile * tk.nsplit + tk.split) * Rmax + row) * 16 + 4 * q) * 4;
         st16c(make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4), o,
@@ -396,8 +527,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     }
   }
 
-  if (epi != EPI_PART) {
-    signal_group(pl, tk.sig, tk.sig_slot, persistent);
+  if (epi != EPI_PART || tk.nsplit == 1) {
+    signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
     return;
   }
 
@@ -418,31 +549,38 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     const int r = t >> 2, c4 = (t & 3) * 4;
     if (r < rows) {
       const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4);
-      f32x4 s = {0, 0, 0, 0};
-      for (int sp = 0; sp < tk.nsplit; ++sp) {
-        const u32x4 v = ld16c(rp, (uint32_t)(((tk.tile * tk.nsplit + sp) * Rmax + r) * 16 + c4) * 4);
+      // issue every load (partials and residual) before using any
+      const uint32_t ro_off = (uint32_t)(r * H + 16 * tk.tile + c4) * ESZ;
+      u32x4 pv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(v[e]);
-      }
-      const uint32_t eo = (uint32_t)(r * H + 16 * tk.tile + c4) * ESZ;
+      for (int sp = 0; sp < 4; ++sp)
+        if (sp < tk.nsplit) pv[sp] = ld16c(rp, (uint32_t)(((tk.tile * tk.nsplit + sp) * Rmax + r) * 16 + c4) * 4);
+      u32x4 hv = {0, 0, 0, 0};
       if (resid) {
         const rsrc_t rr = make_rsrc(resid, hbytes);
         if constexpr (BF) {
-          const u32x2 h = ld8c(rr, eo);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[e] = s[e] + bf2f((h[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+          const u32x2 h = ld8c(rr, ro_off);
+          hv[0] = h[0]; hv[1] = h[1];
         } else {
-          const u32x4 h = ld16c(rr, eo);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(h[e]);
+          hv = ld16c(rr, ro_off);
         }
       }
+      f32x4 s = {0, 0, 0, 0};
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp)
+        if (sp < tk.nsplit)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(pv[sp][e]);
+      if (resid) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = s[e] + chunk_elem<BF>(hv, e);
+      }
       const rsrc_t ro = make_rsrc(out, hbytes);
-      if constexpr (BF) st8c(ro, eo, u32x2{f2bf(s[0]) | (f2bf(s[1]) << 16), f2bf(s[2]) | (f2bf(s[3]) << 16)});
-      else st16c(ro, eo, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3])});
+      if constexpr (BF) st8c(ro, ro_off, u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])});
+      else st16c(ro, ro_off, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3])});
     }
   }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
 }
 
 // ------------------------------------------------------------------ attention
@@ -451,7 +589,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 // wave's work.  Scores: lane (t, c) takes position t and a quarter c of the
 // head dimension; softmax over t <= p in float; output: lane owns d/64 dims.
 template <int BF>
-__device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent) {
+__device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent,
+                                          uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d = pl.d, gq = pl.gq, nkv = pl.nkv, P = pl.P, Rmax = pl.Rmax;
@@ -473,21 +612,34 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     const int hq = g * gq + pi % gq;
     if (row >= fr.rows) continue;  // wave-uniform
     const uint32_t kvrow = (uint32_t)((l * Rmax + row) * nkv + g) * P;
+    // every load of the pair (Q, K and V for t <= p) is issued before any is used
+    const uint32_t dbase = (uint32_t)(lane * dpl);
+    u32x4 qv[8], kv[8];
+    const uint32_t qo = (uint32_t)(row * pl.nq * d + hq * d + c * dq) * ESZ;
+    const uint32_t ko = (uint32_t)((kvrow + t) * d + c * dq) * ESZ;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nchunk) {
+        qv[i] = ld16c(rq, qo + i * 16);
+        kv[i] = (t <= p) ? ld16c(rk, ko + i * 16) : u32x4{0, 0, 0, 0};
+      }
+    u32x2 vv[16];  // V[t][dbase .. dbase + dpl) for t = 0 .. 15
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      if (tt <= p) {
+        const uint32_t vo = (uint32_t)((kvrow + tt) * d + dbase) * ESZ;
+        if (ESZ * dpl == 8) vv[tt] = ld8c(rv, vo);
+        else if (ESZ * dpl == 4) vv[tt] = u32x2{ld4c(rv, vo), 0u};
+        else vv[tt] = u32x2{ld2c(rv, vo), 0u};
+      }
+    }
     // scores
     float dot = 0.f;
-    if (t <= p) {
-      const uint32_t qo = (uint32_t)(row * pl.nq * d + hq * d + c * dq) * ESZ;
-      const uint32_t ko = (uint32_t)((kvrow + t) * d + c * dq) * ESZ;
-      u32x4 qv[8], kv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < nchunk) { qv[i] = ld16c(rq, qo + i * 16); kv[i] = ld16c(rk, ko + i * 16); }
+    for (int i = 0; i < 8; ++i)
+      if (i < nchunk)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < nchunk)
-#pragma unroll
-          for (int e = 0; e < 16 / ESZ; ++e) dot += chunk_elem<BF>(qv[i], e) * chunk_elem<BF>(kv[i], e);
-    }
+        for (int e = 0; e < 16 / ESZ; ++e) dot += chunk_elem<BF>(qv[i], e) * chunk_elem<BF>(kv[i], e);
     dot += shfl_xor_f(dot, 1);
     dot += shfl_xor_f(dot, 2);
     const float s = (t <= p) ? dot * pl.attn_scale : -INFINITY;
@@ -501,38 +653,33 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     const float w = e / sum;
     // output: sum over t in ascending order
     float o0 = 0.f, o1 = 0.f;
-    const uint32_t dbase = (uint32_t)(lane * dpl);
-    for (int tt = 0; tt <= p; ++tt) {
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
       const float wt = __shfl(w, tt * 4, 64);
-      const uint32_t vo = (uint32_t)((kvrow + tt) * d + dbase) * ESZ;
-      if constexpr (BF) {
-        if (dpl == 2) {
-          const uint32_t v = ld4c(rv, vo);
-          o0 += wt * bf2f(v & 0xffffu);
-          o1 += wt * bf2f(v >> 16);
+      if (tt <= p) {
+        if constexpr (BF) {
+          if (dpl == 2) {
+            o0 += wt * bf2f(vv[tt][0] & 0xffffu);
+            o1 += wt * bf2f(vv[tt][0] >> 16);
+          } else {
+            o0 += wt * bf2f(vv[tt][0] & 0xffffu);
+          }
         } else {
-          o0 += wt * bf2f(ld2c(rv, vo));
-        }
-      } else {
-        if (dpl == 2) {
-          const u32x2 v = ld8c(rv, vo);
-          o0 += wt * __uint_as_float(v[0]);
-          o1 += wt * __uint_as_float(v[1]);
-        } else {
-          o0 += wt * __uint_as_float(ld4c(rv, vo));
+          o0 += wt * __uint_as_float(vv[tt][0]);
+          if (dpl == 2) o1 += wt * __uint_as_float(vv[tt][1]);
         }
       }
     }
     const uint32_t ao = (uint32_t)(row * pl.nq * d + hq * d + dbase) * ESZ;
     if constexpr (BF) {
-      if (dpl == 2) st4c(ra, ao, f2bf(o0) | (f2bf(o1) << 16));
+      if (dpl == 2) st4c(ra, ao, pack_bf16(o0, o1));
       else st2c(ra, ao, f2bf(o0));
     } else {
       if (dpl == 2) st8c(ra, ao, u32x2{__float_as_uint(o0), __float_as_uint(o1)});
       else st4c(ra, ao, __float_as_uint(o0));
     }
   }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
 }
 
 // ------------------------------------------------------------------ draw + embed
@@ -575,18 +722,20 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
 }
 
 template <int BF>
-__device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent) {
+__device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent,
+                                            uint64_t* tr) {
   const int row = (int)tk.tile;
   if (row < fr.rows) {
     int code = fr.code0[row];
     code = code < 0 ? 0 : (code >= pl.V ? pl.V - 1 : code);
     embed_row<BF>(pl, fr, 0, row, code, true);
   }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
 }
 
 template <int BF>
-__device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t* misc, bool persistent) {
+__device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t* misc,
+                                          bool persistent, uint64_t* tr) {
   const int row = (int)tk.tile, p = tk.pos;
   if (row < fr.rows) {
     if (threadIdx.x < 64) {
@@ -613,19 +762,19 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
     __syncthreads();
     embed_row<BF>(pl, fr, p, row, (int)misc[1], false);
   }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent);
+  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
 }
 
 // ------------------------------------------------------------------ executors
 
 template <int BF>
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t epoch,
-                                         uint8_t* slot, uint32_t* misc, bool persistent) {
+                                         uint8_t* slot, uint32_t* misc, bool persistent, uint64_t* tr) {
   switch (tk.type) {
-    case T_ATTN: attn_task<BF>(pl, fr, tk, persistent); break;
-    case T_EMBED0: embed0_task<BF>(pl, fr, tk, persistent); break;
-    case T_DRAW: draw_task<BF>(pl, fr, tk, misc, persistent); break;
-    default: proj_task<BF>(pl, fr, tk, epoch, slot, misc, persistent); break;
+    case T_ATTN: attn_task<BF>(pl, fr, tk, persistent, tr); break;
+    case T_EMBED0: embed0_task<BF>(pl, fr, tk, persistent, tr); break;
+    case T_DRAW: draw_task<BF>(pl, fr, tk, misc, persistent, tr); break;
+    default: proj_task<BF>(pl, fr, tk, epoch, slot, misc, persistent, tr); break;
   }
 }
 
@@ -637,10 +786,13 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
   const uint32_t b = pl.wg_begin[blockIdx.x], e = pl.wg_begin[blockIdx.x + 1];
   for (uint32_t i = b; i < e; ++i) {
     const Task tk = pl.tasks[i];
+    uint64_t* tr = pl.trace_on ? pl.trace + (size_t)i * kTraceStamps : nullptr;
+    stamp(tr, 0);
     uint8_t* slot = lds + ((i - b) & 1) * kSlotBytes;
-    if (tk.w_bytes) issue_tile(pl, tk, slot);  // lands while the workgroup waits
+    issue_tile(pl, tk, slot, (uint8_t*)misc);  // lands while the workgroup waits
     wait_deps(pl, tk, epoch);
-    run_task<BF>(pl, fr, tk, epoch, slot, misc, true);
+    stamp(tr, 1);
+    run_task<BF>(pl, fr, tk, epoch, slot, misc, true, tr);
   }
   // The last workgroup to finish moves the plan to the next frame.
   __syncthreads();
@@ -657,8 +809,8 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
   const uint32_t epoch = ld_ctr(pl.state);
   const Task tk = tasks[blockIdx.x];
-  if (tk.w_bytes) issue_tile(pl, tk, lds);
-  run_task<BF>(pl, fr, tk, epoch, lds, misc, false);
+  issue_tile(pl, tk, lds, (uint8_t*)misc);
+  run_task<BF>(pl, fr, tk, epoch, lds, misc, false, nullptr);
 }
 
 __global__ void bump_epoch_kernel(uint32_t* state) {

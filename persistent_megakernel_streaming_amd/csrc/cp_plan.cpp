@@ -67,6 +67,12 @@ namespace {
     }                                                                                        \
   } while (0)
 
+#define TRY(x)                  \
+  do {                          \
+    cp_status s_ = (x);         \
+    if (s_ != CP_OK) return s_; \
+  } while (0)
+
 cp_status fail(cp_plan* p, cp_status s, const std::string& msg) {
   p->err = msg;
   return s;
@@ -194,7 +200,46 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   return CP_OK;
 }
 
+// Split-K ways for o, down and the input projection.  With at most 16 rows a
+// frame is latency-bound: unsplit tiles (down in halves, to fit an LDS slot)
+// save the partial-sum hand-off.  With more rows the activation bytes each
+// workgroup reads dominate, and four ways cut them by four.  A choice must
+// keep the weight tile within one LDS slot, each wave's K share within 32
+// chunks, and every o split on whole kv heads.
+static cp_status choose_splits(cp_plan* P) {
+  const cp_config& c = P->cfg;
+  const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
+  const int R = c.max_rows;
+  const int nrt = (R + 15) / 16, wpr_min = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);
+  const int gq = c.n_q_heads / c.n_kv_heads;
+  auto ok = [&](int K, int ns) {
+    if (K % (16 * ns)) return false;
+    const int kt = K / ns;
+    const int nck = kt * esz / 64;
+    return kt * esz * 64 % 64 == 0 && nck % 4 == 0 && 16 * kt * esz <= kSlotBytes && nck / wpr_min <= 32;
+  };
+  const int order_lo[3] = {1, 2, 4}, order_hi[3] = {4, 2, 1};
+  const int* order = R <= 16 ? order_lo : order_hi;
+  int ns_o = 0, ns_d = 0, ns_in = 0;
+  for (int i = 0; i < 3 && !ns_o; ++i) {
+    const int ns = order[i];
+    if (c.n_q_heads % ns == 0 && (c.n_q_heads / ns) % gq == 0 && c.n_kv_heads % ns == 0 &&
+        ok(c.n_q_heads * c.head_dim, ns))
+      ns_o = ns;
+  }
+  for (int i = 0; i < 3 && !ns_d; ++i)
+    if ((c.intermediate / 16) % order[i] == 0 && ok(c.intermediate, order[i])) ns_d = order[i];
+  for (int i = 0; i < 3 && !ns_in; ++i)
+    if (ok(c.input_dim, order[i])) ns_in = order[i];
+  if (!ns_o || !ns_d || !ns_in) return fail(P, CP_ERR_UNSUPPORTED, "no split-K choice fits these shapes");
+  P->dp.n_o_split = ns_o;
+  P->dp.n_d_split = ns_d;
+  P->dp.n_in_split = ns_in;
+  return CP_OK;
+}
+
 static cp_status build_schedule(cp_plan* P) {
+  TRY(choose_splits(P));
   const cp_config& c = P->cfg;
   const int L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, d = c.head_dim;
   const int I = c.intermediate, Pn = c.n_positions, V = c.vocab, R = c.max_rows;
@@ -203,15 +248,13 @@ static cp_status build_schedule(cp_plan* P) {
   Builder B{P, n_wg, std::vector<std::vector<Task>>(n_wg), {}, 0};
   const int ht = H / 16, qkv_tiles = (nq + 2 * nkv) * d / 16, tpg = (gq + 2) * d / 16;
   const int gu_tiles = I / 16, head_tiles = V / 16;
-  const int ns_o = 4, ns_d = 4, ns_in = 4;
+  const int ns_o = P->dp.n_o_split, ns_d = P->dp.n_d_split, ns_in = P->dp.n_in_split;
   int ar = std::max(1, 4 / gq);
   while (R % ar) --ar;
   const int agroups = R / ar;
   P->dp.attn_rows = ar;
-  P->dp.n_o_split = ns_o;
-  P->dp.n_d_split = ns_d;
-  P->dp.n_in_split = ns_in;
   const int gu_per_split = gu_tiles / ns_d;
+  const int kv_per_osplit = nkv / ns_o;  // kv heads whose attention output one o split reads
   int rot = 0;
 
   // input projection (split-K) and code-0 embedding: no waits
@@ -219,7 +262,7 @@ static cp_status build_schedule(cp_plan* P) {
   {
     std::vector<Task> ts;
     for (int t = 0; t < ht; ++t) {
-      const uint32_t tc = B.counter();
+      const uint32_t tc = ns_in > 1 ? B.counter() : kNone;
       for (int s = 0; s < ns_in; ++s) {
         Task k = make_task(T_INPROJ, 0, 0, t);
         k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_in; k.tctr = tc; k.sig = g_inp; k.sig_slot = t;
@@ -260,9 +303,9 @@ static cp_status build_schedule(cp_plan* P) {
       // Position 0 has no head: the residual after its last layer feeds
       // nothing, so only the last layer's qkv (its K/V) is computed there.
       if (p == 0 && l == L - 1) break;
-      // attention, per kv head
-      std::vector<uint32_t> g_att(nkv);
-      for (int g = 0; g < nkv; ++g) g_att[g] = B.group(agroups, 4);
+      // attention, per kv head; it signals the group of the o split that reads it
+      std::vector<uint32_t> g_att(ns_o);
+      for (int s = 0; s < ns_o; ++s) g_att[s] = B.group(kv_per_osplit * agroups);
       {
         std::vector<Task> ts;
         for (int g = 0; g < nkv; ++g)
@@ -270,7 +313,7 @@ static cp_status build_schedule(cp_plan* P) {
             Task k = make_task(T_ATTN, l, p, g * agroups + rg);
             add_wait(k, gq_groups[g]);
             if (p == 1) add_wait(k, g_qkv[0 * L + l][g]);  // position 0's K/V of this layer
-            k.sig = g_att[g]; k.sig_slot = rg;
+            k.sig = g_att[g / kv_per_osplit]; k.sig_slot = (g % kv_per_osplit) * agroups + rg;
             ts.push_back(k);
           }
         B.phase(ts, spread(nkv * agroups, n_wg, rot));
@@ -279,13 +322,12 @@ static cp_status build_schedule(cp_plan* P) {
       const uint32_t g_o = B.group(ht);
       {
         std::vector<Task> ts;
-        const int hps = nq / ns_o;
         for (int t = 0; t < ht; ++t) {
-          const uint32_t tc = B.counter();
+          const uint32_t tc = ns_o > 1 ? B.counter() : kNone;
           for (int s = 0; s < ns_o; ++s) {
             Task k = make_task(T_O, l, p, t);
             k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_o; k.tctr = tc; k.sig = g_o; k.sig_slot = t;
-            for (int g = (s * hps) / gq; g <= (s * hps + hps - 1) / gq; ++g) add_wait(k, g_att[g]);
+            add_wait(k, g_att[s]);
             ts.push_back(k);
           }
         }
@@ -310,7 +352,7 @@ static cp_status build_schedule(cp_plan* P) {
       {
         std::vector<Task> ts;
         for (int t = 0; t < ht; ++t) {
-          const uint32_t tc = B.counter();
+          const uint32_t tc = ns_d > 1 ? B.counter() : kNone;
           for (int s = 0; s < ns_d; ++s) {
             Task k = make_task(T_DOWN, l, p, t);
             k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_d; k.tctr = tc; k.sig = g_down; k.sig_slot = t;
@@ -433,11 +475,6 @@ static cp_status alloc(cp_plan* P, void** p, size_t bytes) {
   return CP_OK;
 }
 
-#define TRY(x)                     \
-  do {                             \
-    cp_status s_ = (x);            \
-    if (s_ != CP_OK) return s_;    \
-  } while (0)
 
 static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
   const cp_config& c = P->cfg;
@@ -557,6 +594,13 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
   }
   TRY(fetch(P, w->final_norm, (size_t)H * esz, m));
   std::memcpy(gains.data() + (size_t)(2 * L) * H * esz, m.data(), (size_t)H * esz);
+  // All gains exactly 1: the kernel skips the gain product (x * 1 == x).
+  bool unit = true;
+  for (size_t i = 0; i < gains.size() / esz && unit; ++i) {
+    if (esz == 2) unit = ((const uint16_t*)gains.data())[i] == 0x3f80;
+    else unit = ((const uint32_t*)gains.data())[i] == 0x3f800000u;
+  }
+  P->dp.unit_gains = unit ? 1 : 0;
   void* dg;
   TRY(alloc(P, &dg, gains.size()));
   HIPCHK(P, hipMemcpy(dg, gains.data(), gains.size(), hipMemcpyHostToDevice));
@@ -620,6 +664,11 @@ static cp_status alloc_scratch(cp_plan* P) {
   HIPCHK(P, hipMemcpy(p, P->wg_begin.data(), P->wg_begin.size() * 4, hipMemcpyHostToDevice));
   TRY(alloc(P, &p, P->phase_tasks.size() * sizeof(Task))); P->d_phase_tasks = (Task*)p;
   HIPCHK(P, hipMemcpy(p, P->phase_tasks.data(), P->phase_tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
+  if (c.flags & CP_FLAG_TRACE) {
+    TRY(alloc(P, &p, P->tasks.size() * kTraceStamps * 8)); dp.trace = (uint64_t*)p;
+    HIPCHK(P, hipMemset(p, 0, P->tasks.size() * kTraceStamps * 8));
+    dp.trace_on = 1;
+  }
   TRY(alloc(P, &p, P->groups.size() * sizeof(CtrGroup))); dp.groups = (const CtrGroup*)p;
   HIPCHK(P, hipMemcpy(p, P->groups.data(), P->groups.size() * sizeof(CtrGroup), hipMemcpyHostToDevice));
   return CP_OK;
@@ -753,7 +802,7 @@ cp_status cp_plan_query(const cp_plan* P, cp_plan_info* info) {
   info->weight_bytes_per_frame = P->weight_bytes_frame;
   info->packed_weight_bytes = P->packed_bytes;
   info->scratch_bytes = P->scratch_bytes;
-  info->trace_words = 0;
+  info->trace_words = (P->cfg.flags & CP_FLAG_TRACE) ? (int64_t)P->tasks.size() * kTraceStamps : 0;
   info->cu_count = P->cu_count;
   info->max_tasks_per_workgroup = P->max_tasks_wg;
   return CP_OK;
@@ -769,7 +818,8 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
                     (io->seed != nullptr) + (io->offset != nullptr);
   if (nsamp != 0 && nsamp != 5) return fail(P, CP_ERR_INVALID_ARGUMENT, "sampling arrays must be all set or all NULL");
   if (nsamp == 5) return fail(P, CP_ERR_UNSUPPORTED, "sampled draws are not built yet");
-  if (io->trace) return fail(P, CP_ERR_UNSUPPORTED, "tracing is not built yet");
+  if (io->trace && !(c.flags & CP_FLAG_TRACE)) return fail(P, CP_ERR_INVALID_ARGUMENT, "trace needs CP_FLAG_TRACE");
+  if (io->trace && c.exec != CP_EXEC_PERSISTENT) return fail(P, CP_ERR_UNSUPPORTED, "trace needs the persistent executor");
   DevFrame fr{};
   fr.rows = io->rows;
   fr.sampled = nsamp == 5;
@@ -811,8 +861,22 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
                            hipMemcpyDeviceToDevice, s);
     }
   }
+  if (e == hipSuccess && io->trace)
+    e = hipMemcpyAsync(io->trace, P->dp.trace, P->tasks.size() * kTraceStamps * 8, hipMemcpyDeviceToDevice, s);
   if (prev != P->device) (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return CP_OK;
+}
+
+cp_status cp_plan_task_table(const cp_plan* P, int32_t* out, int64_t n_tasks) {
+  if (!P || !out || n_tasks != (int64_t)P->tasks.size()) return CP_ERR_INVALID_ARGUMENT;
+  for (size_t w = 0; w + 1 < P->wg_begin.size(); ++w)
+    for (uint32_t i = P->wg_begin[w]; i < P->wg_begin[w + 1]; ++i) {
+      const Task& t = P->tasks[i];
+      int32_t* o = out + (size_t)i * 8;
+      o[0] = (int32_t)t.phase; o[1] = t.type; o[2] = t.layer; o[3] = t.pos;
+      o[4] = (int32_t)t.tile; o[5] = t.split; o[6] = (int32_t)w; o[7] = (int32_t)(i - P->wg_begin[w]);
+    }
   return CP_OK;
 }
 
