@@ -53,9 +53,9 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
 #define CP_FLAG_TRACE 0x1u /* record per-task timestamps (persistent executor) */
 
 /* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
- * head_dim 64 or 128; n_q_heads a multiple of n_kv_heads; hidden, input_dim,
- * intermediate and vocab multiples of 64; 2 <= n_positions <= 16;
- * 1 <= max_rows <= 64. */
+ * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a
+ * multiple of 256 up to 1024; input_dim, intermediate and vocab multiples of
+ * 64; 2 <= n_positions <= 16; 1 <= max_rows <= 64. */
 typedef struct {
   int32_t abi_version;  /* CP_ABI_VERSION */
   int32_t n_layers;
@@ -114,9 +114,10 @@ typedef struct {
   void* k_cache;             /* optional out [n_layers][rows][n_kv_heads][n_positions][head_dim], dtype, post-RoPE */
   void* v_cache;             /* optional out, same layout */
   uint64_t* trace;           /* optional out, cp_plan_info.trace_words words (needs CP_FLAG_TRACE and the
-                                persistent executor): per task, in the order of cp_plan_task_table, six
+                                persistent executor): per task, in the order of cp_plan_task_table, eight
                                 100 MHz timestamps -- task start, dependencies met, operands landed,
-                                body done, stores complete, signalled */
+                                normalised, K loop done, epilogue issued, stores complete, signalled
+                                (stamps a task kind does not pass through are left as they were) */
 } cp_frame_io;
 
 typedef struct {

@@ -27,7 +27,7 @@ constexpr int kSlotBytes = 64 * 1024;  // one weight-tile slot in LDS (two slots
 constexpr int kMiscLds = 16384;  // flags, gain row, cross-wave reductions
 constexpr int kLdsBytes = 2 * kSlotBytes + kMiscLds;
 constexpr int kCtrStride = 32;      // uint32 words between sub-counters (128 B)
-constexpr int kTraceStamps = 6;     // timestamps per task in a traced frame
+constexpr int kTraceStamps = 8;     // timestamps per task in a traced frame
 
 // A group of sub-counters: a phase (or part of one) signals it, a later task
 // waits on it.  Producer i adds to sub-counter i % nsub; each sub-counter
@@ -92,6 +92,7 @@ struct DevPlan {
   void* kc;                     // [L][Rmax][nkv][P][d]
   void* vc;
   float* part;                  // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16]
+  float* ssq;                   // [P + 6][Rmax][H/16] sum-of-squares partials of residual rows
   float* zbuf;                  // [Rmax][V] logits of the current head
   uint2* cand;                  // [Rmax][n_head_tiles] (value bits, index)
   uint64_t* trace;              // plan-owned trace staging (unused if no trace)

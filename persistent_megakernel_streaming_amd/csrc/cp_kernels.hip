@@ -142,16 +142,16 @@ __device__ __forceinline__ void wait_deps(const DevPlan& pl, const Task& tk, uin
 // Every wave waits for its own stores, then one thread adds to the group.
 __device__ __forceinline__ void signal_group(const DevPlan& pl, uint32_t grp, uint32_t slot, bool persistent,
                                              uint64_t* tr) {
-  stamp(tr, 3);
+  stamp(tr, 5);
   wait_vm();
   __syncthreads();
-  stamp(tr, 4);
+  stamp(tr, 6);
   if (persistent && threadIdx.x == 0 && grp != kNone) {
     const CtrGroup gp = pl.groups[grp];
     __hip_atomic_fetch_add(pl.ctr + (size_t)(gp.base + slot % gp.nsub) * kCtrStride, 1u,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  stamp(tr, 5);
+  stamp(tr, 7);
 }
 
 // ------------------------------------------------------------------ weights -> LDS
@@ -210,23 +210,42 @@ __device__ __forceinline__ f32x4 mma(const u32x4& w, const u32x4& x, f32x4 acc) 
   }
 }
 
+// Sum of squares of a residual row comes from its producers as H/16 partials
+// (one per 16-column tile, in tile order); ssq slot ids: position inputs
+// 0 .. P-1, residual after down P + 2*parity + layer parity, residual after o
+// P + 4 + parity.
+__device__ __forceinline__ float* ssq_slot(const DevPlan& pl, int slot) {
+  return pl.ssq + (size_t)slot * pl.Rmax * (pl.H / 16);
+}
+
+// Sum of squares of the four values a lane stores, added over the `span`
+// lanes (xor distances `first`, `2 first`, ...) that share one 16-column tile.
+__device__ __forceinline__ float tile_ssq(const float (&v)[4], int first, int span) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s = fmaf(v[e], v[e], s);
+  for (int m = first; m < first * span; m <<= 1) s += shfl_xor_f(s, m);
+  return s;
+}
+
 template <int BF>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t epoch,
-                          uint8_t* slot, uint32_t* misc, bool persistent, uint64_t* tr) {
+                                          uint8_t* slot, uint32_t* misc, bool persistent, uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 4, rl = lane & 15;
   const int rows = fr.rows;
-  const int H = pl.H, Rmax = pl.Rmax;
+  const int H = pl.H, Rmax = pl.Rmax, P = pl.P;
   const int l = tk.layer, p = tk.pos;
 
   // Operand source, K range, norm and epilogue of this task kind.
   const void* xsrc;
   uint32_t xbytes, ld;  // buffer bytes and row stride (elements)
   int k0 = 0, kt;
-  int gain_row = -1;    // row of the gain table, -1: no norm
+  int in_ssq = -1;      // ssq slot of a normalised input (-1: no norm)
+  int out_ssq = -1;     // ssq slot of a residual output (EPI_PART)
   int nb = 1;
   Epi epi;
   const void* resid = nullptr;  // residual (EPI_PART)
@@ -240,49 +259,56 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   uint8_t* hres = (uint8_t*)pl.hres + (size_t)par * 2 * hbytes;   // [layer parity]
   uint8_t* hmid = (uint8_t*)pl.hmid + (size_t)par * hbytes;
   const uint8_t* layer_in = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
+  const int layer_in_ssq = (l == 0) ? p : P + 2 * par + ((l - 1) & 1);
   switch (tk.type) {
     case T_QKV:
-      xsrc = layer_in; xbytes = hbytes; ld = H; kt = H; gain_row = 2 * l; epi = EPI_QKV; break;
+      xsrc = layer_in; xbytes = hbytes; ld = H; kt = H; in_ssq = layer_in_ssq; epi = EPI_QKV; break;
     case T_GU:
-      xsrc = hmid; xbytes = hbytes; ld = H; kt = H; gain_row = 2 * l + 1; nb = 2; epi = EPI_GU; break;
+      xsrc = hmid; xbytes = hbytes; ld = H; kt = H; in_ssq = P + 4 + par; nb = 2; epi = EPI_GU; break;
     case T_HEAD:
       xsrc = hres + (size_t)((pl.L - 1) & 1) * hbytes; xbytes = hbytes; ld = H; kt = H;
-      gain_row = 2 * pl.L; epi = EPI_HEAD; break;
+      in_ssq = P + 2 * par + ((pl.L - 1) & 1); epi = EPI_HEAD; break;
     case T_O:
       xsrc = (const uint8_t*)pl.abuf + (size_t)par * qdbytes; ld = pl.nq * pl.d; xbytes = qdbytes;
       kt = (int)ld / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART; resid = layer_in; out = hmid;
-      part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; break;
+      out_ssq = P + 4 + par; part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; break;
     case T_DOWN:
       xsrc = (const uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ; ld = pl.I; xbytes = (uint32_t)Rmax * ld * ESZ;
       kt = pl.I / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART; resid = hmid;
-      out = hres + (size_t)(l & 1) * hbytes; part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; break;
+      out = hres + (size_t)(l & 1) * hbytes; out_ssq = P + 2 * par + (l & 1);
+      part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; break;
     default:  // T_INPROJ
       xsrc = fr.hidden_in; ld = pl.Din; xbytes = (uint32_t)fr.rows * ld * ESZ; kt = pl.Din / tk.nsplit;
-      k0 = tk.split * kt; epi = EPI_PART; out = pl.xin; part_off = pl.part_in_off; break;
+      k0 = tk.split * kt; epi = EPI_PART; out = pl.xin; out_ssq = 0; part_off = pl.part_in_off; break;
   }
   const int nck = kt * ESZ / 64;  // 16-byte chunks per lane over the task's K range
 
   // Waves and row tiles: a wave owns 16 rows; with few rows the waves of a
   // row tile split K and add their results through LDS in a fixed order.
   const int nrt = (rows + 15) >> 4;                   // row tiles holding live rows (1..4)
-  const int wpr = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);  // waves per row tile
+  int wpr = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);        // waves per row tile
+  while (wpr > 1 && nck % (4 * wpr)) wpr >>= 1;        // each wave takes whole groups of 4 chunks
   const int rt = wave / wpr, ks = wave % wpr;
-  const int ncw = nck / wpr;                          // chunks this wave handles (<= 32)
+  const int ncw = nck / wpr;                          // chunks this wave handles (a multiple of 4)
   const int c0 = ks * ncw;
   const int row = rt * 16 + rl;
   const bool wave_live = rt < nrt;
   const bool live = wave_live && row < rows;
-  float* red_ss = (float*)((uint8_t*)misc + kRedSsLds);      // [4 waves][16 rows]
   f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);    // [4 waves][2][64 lanes]
+  const uint32_t ssq_bytes = (uint32_t)Rmax * (H / 16) * 4;
 
-  // Activation rows straight from memory into the B operand registers; the
-  // residual of an unsplit o / down tile comes with them.
+  // Loads that do not depend on the K loop go out first: the sum-of-squares
+  // partials of a normalised input, the residual of an unsplit o / down tile
+  // and the RoPE angles of a qkv tile.
   const rsrc_t rx = make_rsrc(xsrc, xbytes);
-  u32x4 xa[32];
   const uint32_t xoff = ((uint32_t)row * ld + k0 + q * E) * ESZ + c0 * 64;
+  u32x4 ssv[4];
+  const int nsq = H / 64;  // partials per lane (H/16 partials over 4 lanes), <= 4
+  if (in_ssq >= 0) {
+    const rsrc_t rs = make_rsrc(ssq_slot(pl, in_ssq), ssq_bytes);
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    if (c < ncw) xa[c] = live ? ld16c(rx, xoff + c * 64) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i)
+      if (i * 4 < nsq) ssv[i] = live ? ld16c(rs, (uint32_t)(row * (H / 16) + q * nsq + 4 * i) * 4) : u32x4{0, 0, 0, 0};
   }
   const uint32_t eo = (uint32_t)(row * H + 16 * tk.tile + 4 * q) * ESZ;  // this lane's 4 output slots
   u32x4 rv = {0, 0, 0, 0};
@@ -295,7 +321,6 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       rv = ld16c(rr, eo);
     }
   }
-  // RoPE cos/sin of this lane's two rotary pairs (qkv tiles of q and k heads)
   float rope_cs[2] = {1.f, 1.f}, rope_sn[2] = {0.f, 0.f};
   if (tk.type == T_QKV) {
     const int d = pl.d, th = d / 16, tpg = (pl.gq + 2) * th, lt = tk.tile % tpg;
@@ -308,96 +333,99 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   }
-  wait_vm();        // activations and this wave's share of the weight tile have landed
+
+  // K loop over groups of four chunks: the next group's loads are in flight
+  // while the current one is scaled and multiplied.
+  u32x4 xa[4], xb[4];
+  auto load_group = [&](u32x4 (&x)[4], int g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = live ? ld16c(rx, xoff + (g * 4 + i) * 64) : u32x4{0, 0, 0, 0};
+  };
+  const int ng = ncw / 4;
+  if (wave_live) load_group(xa, 0);
+  wait_vm();        // this wave's share of the weight tile (and the first group) have landed
   __syncthreads();  // every wave's share of the tile is in LDS
   stamp(tr, 2);
 
-  if (gain_row >= 0) {
-    // RMSNorm of the full row: float sum of squares per lane in K order, then
-    // across the four lane groups and the waves of the row tile in a fixed order.
+  float rinv = 1.f;
+  if (in_ssq >= 0 && wave_live) {
     float ss = 0.f;
-    if (wave_live) {
 #pragma unroll
-      for (int c = 0; c < 32; ++c)
-        if (c < ncw)
+    for (int i = 0; i < 4; ++i)
+      if (i * 4 < nsq)
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float x = chunk_elem<BF>(xa[c], e);
-            ss = fmaf(x, x, ss);
-          }
-      ss += shfl_xor_f(ss, 16);
-      ss += shfl_xor_f(ss, 32);
-    }
-    if (wpr > 1) {
-      if (wave_live && q == 0) red_ss[wave * 16 + rl] = ss;
-      __syncthreads();
-      if (wave_live) {
-        ss = 0.f;
-        for (int k = 0; k < wpr; ++k) ss += red_ss[(rt * wpr + k) * 16 + rl];
-      }
-    }
-    const float rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
-    if (wave_live) {
-      const uint8_t* gl = (const uint8_t*)misc + kGainLds + c0 * 64;  // gain row staged with the tile
-#pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        if (c < ncw) {
-          u32x4 o;
-          if constexpr (BF) {
-            const u32x4 g = *(const u32x4*)(gl + (c * KS + q * E) * ESZ);
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-              const uint32_t xw = xa[c][w2];
-              const float t0 = __uint_as_float(xw << 16) * rinv, t1 = __uint_as_float(xw & 0xffff0000u) * rinv;
-              if (pl.unit_gains) {
-                o[w2] = pack_bf16(t0, t1);
-              } else {
-                const uint32_t gw = g[w2];
-                o[w2] = pack_bf16(t0 * __uint_as_float(gw << 16), t1 * __uint_as_float(gw & 0xffff0000u));
-              }
-            }
-          } else {
-            const u32x4 g = *(const u32x4*)(gl + (c * KS + q * E) * ESZ);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float t = __uint_as_float(xa[c][e]) * rinv;
-              o[e] = __float_as_uint(pl.unit_gains ? t : t * __uint_as_float(g[e]));
-            }
-          }
-          xa[c] = live ? o : u32x4{0, 0, 0, 0};
-        }
-      }
-    }
+        for (int e = 0; e < 4; ++e) ss += __uint_as_float(ssv[i][e]);
+    ss += shfl_xor_f(ss, 16);
+    ss += shfl_xor_f(ss, 32);
+    rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
   }
+  stamp(tr, 3);
 
-  // K loop: weights from the LDS tile (fragment order), activations from registers.
+  const bool norm = in_ssq >= 0;
+  const bool unit = pl.unit_gains != 0;
+  const uint8_t* gl = (const uint8_t*)misc + kGainLds + c0 * 64;  // gain row staged with the tile
+  const uint8_t* wt = slot + lane * 16 + (size_t)c0 * nb * 1024;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  if (wave_live) {
-    const uint8_t* wt = slot + lane * 16 + (size_t)c0 * nb * 1024;
-    if (nb == 1) {
-      // two accumulators on alternating chunks, added once at the end
+  // a = round(round(x * r) * g) in the activation type, then the MFMAs
+  auto process = [&](u32x4 (&x)[4], int g) {
+    u32x4 w[8];
 #pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        if (c < ncw) {
-          const u32x4 w = *(const u32x4*)(wt + c * 1024);
-          if (c & 1) acc1 = mma<BF>(w, xa[c], acc1);
-          else acc0 = mma<BF>(w, xa[c], acc0);
+    for (int i = 0; i < 4; ++i) {
+      w[2 * i] = *(const u32x4*)(wt + ((g * 4 + i) * nb) * 1024);
+      if (nb == 2) w[2 * i + 1] = *(const u32x4*)(wt + ((g * 4 + i) * nb + 1) * 1024);
+    }
+    if (norm) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 gv = *(const u32x4*)(gl + ((g * 4 + i) * KS + q * E) * ESZ);
+        u32x4 o;
+        if constexpr (BF) {
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            const uint32_t xw = x[i][w2];
+            const float t0 = __uint_as_float(xw << 16) * rinv, t1 = __uint_as_float(xw & 0xffff0000u) * rinv;
+            if (unit) {
+              o[w2] = pack_bf16(t0, t1);
+            } else {
+              const uint32_t gw = gv[w2];
+              o[w2] = pack_bf16(t0 * __uint_as_float(gw << 16), t1 * __uint_as_float(gw & 0xffff0000u));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = __uint_as_float(x[i][e]) * rinv;
+            o[e] = __float_as_uint(unit ? t : t * __uint_as_float(gv[e]));
+          }
         }
+        x[i] = live ? o : u32x4{0, 0, 0, 0};
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (nb == 1) {
+        if (i & 1) acc1 = mma<BF>(w[2 * i], x[i], acc1);
+        else acc0 = mma<BF>(w[2 * i], x[i], acc0);
+      } else {
+        acc0 = mma<BF>(w[2 * i], x[i], acc0);
+        acc1 = mma<BF>(w[2 * i + 1], x[i], acc1);
+      }
+    }
+  };
+  if (wave_live) {
+    for (int g = 0; g < ng; g += 2) {
+      if (g + 1 < ng) load_group(xb, g + 1);
+      process(xa, g);
+      if (g + 1 >= ng) break;
+      if (g + 2 < ng) load_group(xa, g + 2);
+      process(xb, g + 1);
+    }
+    if (nb == 1) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + acc1[v];
-    } else {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        if (c < ncw) {
-          const u32x4 wg = *(const u32x4*)(wt + (2 * c) * 1024);
-          const u32x4 wu = *(const u32x4*)(wt + (2 * c + 1) * 1024);
-          acc0 = mma<BF>(wg, xa[c], acc0);
-          acc1 = mma<BF>(wu, xa[c], acc1);
-        }
-      }
     }
   }
+  stamp(tr, 4);
   if (wpr > 1) {
     // K parts of a row tile: (((k0 + k1) + k2) + k3), in the wave of part 0
     if (wave_live) {
@@ -428,8 +456,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       const int d = pl.d, th = d / 16, gq = pl.gq, nkv = pl.nkv;
       const int tpg = (gq + 2) * th;
       const int g = tk.tile / tpg, lt = tk.tile % tpg;
-      const uint32_t kvoff = (uint32_t)(((l * Rmax + row) * nkv + g) * pl.P + p) * d;
-      const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * pl.P * d * ESZ;
+      const uint32_t kvoff = (uint32_t)(((l * Rmax + row) * nkv + g) * P + p) * d;
+      const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ;
       if (live) {
         if (lt < (gq + 1) * th) {
           // q or k head: slots (4q + v) hold rotary pairs 8 tih + 2q + (v >> 1), half v & 1
@@ -490,7 +518,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         const u32x4 z = {__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])};
         st16c(make_rsrc(pl.zbuf, (uint32_t)Rmax * V * 4), (uint32_t)(row * V + n0) * 4, z);
         if (fr.logits)
-          st16c(make_rsrc(fr.logits, (uint32_t)rows * (pl.P - 1) * V * 4), (uint32_t)((row * (pl.P - 1) + (p - 1)) * V + n0) * 4, z);
+          st16c(make_rsrc(fr.logits, (uint32_t)rows * (P - 1) * V * 4), (uint32_t)((row * (P - 1) + (p - 1)) * V + n0) * 4, z);
       }
       // best (value, index) of the tile for this row
       float bv = acc0[0];
@@ -507,16 +535,16 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       if (live && q == 0)
         st8c(make_rsrc(pl.cand, (uint32_t)Rmax * pl.n_head_tiles * 8), (uint32_t)(row * pl.n_head_tiles + tk.tile) * 8,
              u32x2{__float_as_uint(bv), bi});
-    } else if (tk.nsplit == 1) {  // EPI_PART, unsplit: residual add and store
-      if (live) {
-        f32x4 s = acc0;
-        if (resid) {
+    } else if (tk.nsplit == 1) {  // EPI_PART, unsplit: residual add, store, sum of squares
+      float h[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[e] = s[e] + chunk_elem<BF>(rv, e);
-        }
+      for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(resid ? acc0[e] + chunk_elem<BF>(rv, e) : acc0[e]);
+      const float sq = tile_ssq(h, 16, 4);
+      if (live) {
         const rsrc_t ro = make_rsrc(out, hbytes);
-        if constexpr (BF) st8c(ro, eo, u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])});
-        else st16c(ro, eo, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3])});
+        if constexpr (BF) st8c(ro, eo, u32x2{pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3])});
+        else st16c(ro, eo, u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]), __float_as_uint(h[3])});
+        if (q == 0) st4c(make_rsrc(ssq_slot(pl, out_ssq), ssq_bytes), (uint32_t)(row * (H / 16) + tk.tile) * 4, __float_as_uint(sq));
       }
     } else {  // EPI_PART, split: fp32 partial of this split
       if (live) {
@@ -547,37 +575,40 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   {
     const int t = threadIdx.x;  // 64 rows x 4 column quads
     const int r = t >> 2, c4 = (t & 3) * 4;
+    const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4);
+    // issue every load (partials and residual) before using any
+    const uint32_t ro_off = (uint32_t)(r * H + 16 * tk.tile + c4) * ESZ;
+    u32x4 pv[4];
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+      if (sp < tk.nsplit)
+        pv[sp] = r < rows ? ld16c(rp, (uint32_t)(((tk.tile * tk.nsplit + sp) * Rmax + r) * 16 + c4) * 4) : u32x4{0, 0, 0, 0};
+    u32x4 hv = {0, 0, 0, 0};
+    if (resid && r < rows) {
+      const rsrc_t rr = make_rsrc(resid, hbytes);
+      if constexpr (BF) {
+        const u32x2 h = ld8c(rr, ro_off);
+        hv[0] = h[0]; hv[1] = h[1];
+      } else {
+        hv = ld16c(rr, ro_off);
+      }
+    }
+    f32x4 s = {0, 0, 0, 0};
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+      if (sp < tk.nsplit)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(pv[sp][e]);
+    float h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(resid ? s[e] + chunk_elem<BF>(hv, e) : s[e]);
+    const float sq = tile_ssq(h, 1, 4);
     if (r < rows) {
-      const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4);
-      // issue every load (partials and residual) before using any
-      const uint32_t ro_off = (uint32_t)(r * H + 16 * tk.tile + c4) * ESZ;
-      u32x4 pv[4];
-#pragma unroll
-      for (int sp = 0; sp < 4; ++sp)
-        if (sp < tk.nsplit) pv[sp] = ld16c(rp, (uint32_t)(((tk.tile * tk.nsplit + sp) * Rmax + r) * 16 + c4) * 4);
-      u32x4 hv = {0, 0, 0, 0};
-      if (resid) {
-        const rsrc_t rr = make_rsrc(resid, hbytes);
-        if constexpr (BF) {
-          const u32x2 h = ld8c(rr, ro_off);
-          hv[0] = h[0]; hv[1] = h[1];
-        } else {
-          hv = ld16c(rr, ro_off);
-        }
-      }
-      f32x4 s = {0, 0, 0, 0};
-#pragma unroll
-      for (int sp = 0; sp < 4; ++sp)
-        if (sp < tk.nsplit)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(pv[sp][e]);
-      if (resid) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = s[e] + chunk_elem<BF>(hv, e);
-      }
       const rsrc_t ro = make_rsrc(out, hbytes);
-      if constexpr (BF) st8c(ro, ro_off, u32x2{pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])});
-      else st16c(ro, ro_off, u32x4{__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]), __float_as_uint(s[3])});
+      if constexpr (BF) st8c(ro, ro_off, u32x2{pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3])});
+      else st16c(ro, ro_off, u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]), __float_as_uint(h[3])});
+      if ((t & 3) == 0)
+        st4c(make_rsrc(ssq_slot(pl, out_ssq), ssq_bytes), (uint32_t)(r * (H / 16) + tk.tile) * 4, __float_as_uint(sq));
     }
   }
   signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
@@ -695,29 +726,34 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
   const rsrc_t rx = make_rsrc(pl.xin, (uint32_t)pl.P * pl.Rmax * H * ESZ);
   const uint32_t ebase = (uint32_t)((j * V + code) * H);
   const uint32_t xbase = (uint32_t)(((j + 1) * pl.Rmax + row) * H);
-  for (int k = threadIdx.x * 4; k < H; k += kThreads * 4) {
-    float ev[4];
-    if constexpr (BF) {
-      const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(re, (ebase + k) * 2, 0, 0);
-      ev[0] = bf2f(e[0] & 0xffffu); ev[1] = bf2f(e[0] >> 16); ev[2] = bf2f(e[1] & 0xffffu); ev[3] = bf2f(e[1] >> 16);
-      if (j + 1 < pl.P) st8c(rx, (xbase + k) * 2, e);
-    } else {
-      const u32x4 e = ld16(re, (ebase + k) * 4);
+  const bool feeds = j + 1 < pl.P;  // the row is the input of position j + 1
+  // thread t covers elements 4t .. 4t+3: four threads per 16-column tile
+  for (int k = threadIdx.x * 4; k < ((H + 1023) / 1024) * 1024; k += kThreads * 4) {
+    const bool in = k < H;
+    float ev[4] = {0.f, 0.f, 0.f, 0.f};
+    u32x4 sv = {0, 0, 0, 0};
+    if (in) {
+      if constexpr (BF) {
+        const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(re, (ebase + k) * 2, 0, 0);
+        ev[0] = bf2f(e[0] & 0xffffu); ev[1] = bf2f(e[0] >> 16); ev[2] = bf2f(e[1] & 0xffffu); ev[3] = bf2f(e[1] >> 16);
+        if (feeds) st8c(rx, (xbase + k) * 2, e);
+      } else {
+        const u32x4 e = ld16(re, (ebase + k) * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ev[i] = __uint_as_float(e[i]);
-      if (j + 1 < pl.P) st16c(rx, (xbase + k) * 4, e);
+        for (int i = 0; i < 4; ++i) ev[i] = __uint_as_float(e[i]);
+        if (feeds) st16c(rx, (xbase + k) * 4, e);
+      }
+      if (!first) sv = ld16c(rs, (uint32_t)(row * H + k) * 4);
     }
-    const uint32_t so = (uint32_t)(row * H + k) * 4;
-    u32x4 sv;
-    if (first) {
+    const float sq = tile_ssq(ev, 1, 4);
+    if (in) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(ev[i]);
-    } else {
-      sv = ld16c(rs, so);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(__uint_as_float(sv[i]) + ev[i]);
+      for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(first ? ev[i] : __uint_as_float(sv[i]) + ev[i]);
+      st16c(rs, (uint32_t)(row * H + k) * 4, sv);
+      if (feeds && (threadIdx.x & 3) == 0)
+        st4c(make_rsrc(ssq_slot(pl, j + 1), (uint32_t)pl.Rmax * (H / 16) * 4), (uint32_t)(row * (H / 16) + k / 16) * 4,
+             __float_as_uint(sq));
     }
-    st16c(rs, so, sv);
   }
 }
 

@@ -185,7 +185,7 @@ static cp_status validate(const cp_config* c, std::string& msg) {
     msg = "hidden, input_dim, intermediate and vocab must be multiples of 64";
     return CP_ERR_UNSUPPORTED;
   }
-  if (c->hidden * esz > 2048) { msg = "hidden too large for register-resident rows"; return CP_ERR_UNSUPPORTED; }
+  if (c->hidden % 256 || c->hidden > 1024) { msg = "hidden must be a multiple of 256, at most 1024"; return CP_ERR_UNSUPPORTED; }
   if ((c->n_q_heads * c->head_dim / 4) * esz > 2048 || (c->intermediate / 4) * esz > 2048 ||
       (c->input_dim / 4) * esz > 2048) {
     msg = "split-K slice too large";
@@ -650,6 +650,7 @@ static cp_status alloc_scratch(cp_plan* P) {
   dp.part_o_off = 0;
   dp.part_d_off = 2 * part_one;
   dp.part_in_off = 4 * part_one;
+  TRY(alloc(P, &p, (size_t)(Pn + 6) * R * (H / 16) * 4)); dp.ssq = (float*)p;
   TRY(alloc(P, &p, (size_t)R * V * 4)); dp.zbuf = (float*)p;
   TRY(alloc(P, &p, (size_t)R * (V / 16) * 8)); dp.cand = (uint2*)p;
   TRY(alloc(P, &p, (size_t)P->n_ctr * kCtrStride * 4)); dp.ctr = (uint32_t*)p;
