@@ -164,6 +164,16 @@ cp_status cp_plan_query(const cp_plan* plan, cp_plan_info* info);
  * device-side wait gave up since the plan was created, else CP_OK. */
 cp_status cp_plan_device_status(cp_plan* plan);
 
+/* Frame epochs.  Every word one workgroup hands to another carries the epoch
+ * of the frame that wrote it, so a reader can tell this frame's data from
+ * anything older.  Epochs count 1, 2, ... per frame (cp_frame_run) and wrap
+ * after 4194302 frames: the frame that reaches the limit also clears every
+ * tagged buffer, and the next frame is epoch 1 again.  cp_plan_set_epoch makes
+ * the plan's next frame run as `epoch` (1 <= epoch <= 4194302), so that the
+ * wrap can be exercised; it synchronises the device and returns
+ * CP_ERR_INVALID_ARGUMENT for an epoch outside that range. */
+cp_status cp_plan_set_epoch(cp_plan* plan, uint32_t epoch);
+
 const char* cp_status_string(cp_status s);
 
 /* Text of the last error recorded on the plan ("" if none). */

@@ -21,6 +21,7 @@ CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
 CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1
 ABI_VERSION = 1
+EPOCH_WRAP = (1 << 22) - 1  # epochs run 1 .. EPOCH_WRAP - 1
 
 _VP = C.c_void_p
 
@@ -74,8 +75,9 @@ def load_library():
     lib.cp_last_create_error.restype = C.c_char_p
     lib.cp_schedule_check.argtypes = [C.POINTER(Config), C.c_int, C.POINTER(PlanInfo)]
     lib.cp_plan_task_table.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
+    lib.cp_plan_set_epoch.argtypes = [C.c_void_p, C.c_uint32]
     for f in ("cp_plan_create", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
-              "cp_schedule_check", "cp_plan_task_table"):
+              "cp_schedule_check", "cp_plan_task_table", "cp_plan_set_epoch"):
         getattr(lib, f).restype = C.c_int
     return lib
 
@@ -185,6 +187,10 @@ class Plan:
         out = np.zeros((n, 8), np.int32)
         self._check(_lib.cp_plan_task_table(self._h, out.ctypes.data, n))
         return out
+
+    def set_epoch(self, epoch: int):
+        """Makes the next frame run as ``epoch`` (exercises the epoch wrap)."""
+        self._check(_lib.cp_plan_set_epoch(self._h, int(epoch)))
 
     def device_status(self):
         self._check(_lib.cp_plan_device_status(self._h))

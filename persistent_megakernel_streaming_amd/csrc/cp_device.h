@@ -39,22 +39,51 @@ struct CtrGroup {
   uint16_t per_sub;
 };
 
+constexpr uint32_t kKvPhase = 1023;  // tag phase of K/V cache words (each written once per frame)
+constexpr int kMaxPhases = 1023;     // phase ids must stay below kKvPhase
+// A tag is epoch * 1024 + phase in 32 bits, so epochs live in [1, kEpochWrap).
+// Before the epoch would reach kEpochWrap every tagged buffer is cleared and
+// the count restarts at 1 (epoch 0 is the tag of cleared memory).
+constexpr uint32_t kEpochWrap = (1u << 22) - 1;
+constexpr int kMaxClear = 16;
+
+struct Span {
+  void* p;
+  uint64_t bytes;  // a multiple of 8
+};
+
 struct Task {
   uint8_t type;
   uint8_t split;     // split-K index
   uint8_t nsplit;    // split-K ways (1: not split)
-  uint8_t nwait;
+  uint8_t pad0;
   uint16_t layer;
   uint16_t pos;
   uint32_t tile;     // projection n-tile, attention (kv head, row group), row
-  uint32_t wait[kMaxWaits];  // counter groups to wait on
-  uint32_t sig;      // counter group signalled at completion (kNone: none)
-  uint32_t sig_slot; // producer index within sig
-  uint32_t tctr;     // split-K tile counter (kNone if not split)
+  uint16_t phase;    // global phase index (tags this task's outputs)
+  uint16_t ph_in0;   // phase whose outputs are this task's main input
+  uint16_t ph_in1;   // phase of the residual input (o / down), else unused
+  uint16_t pad1;
   uint32_t w_off;    // byte offset of the packed weight tile
   uint32_t w_bytes;  // its size (multiple of 1 KiB), 0 for tasks without weights
-  uint32_t phase;    // global phase index
+  // Dependency description used only by the host validator: counter groups
+  // the task reads from and the group it completes.
+  uint32_t wait[kMaxWaits];
+  uint32_t nwait;
+  uint32_t sig;
+  uint32_t sig_slot;
 };
+
+// What a workgroup needs to run one task (24 bytes, six scalar registers):
+// the host's Task without the dependency bookkeeping its validator uses.
+struct DevTask {
+  uint8_t type, split, nsplit, pad0;
+  uint16_t layer, pos;
+  uint16_t tile, phase;
+  uint16_t ph_in0, ph_in1;
+  uint32_t w_off, w_bytes;
+};
+static_assert(sizeof(DevTask) == 24, "DevTask layout");
 
 struct DevPlan {
   // shapes
@@ -70,11 +99,9 @@ struct DevPlan {
   int n_wg;
   int n_tasks;
   // task lists
-  const Task* tasks;            // all tasks, grouped by workgroup
+  const DevTask* tasks;         // all tasks, grouped by workgroup
   const uint32_t* wg_begin;     // [n_wg + 1]
-  const CtrGroup* groups;
-  uint32_t* ctr;                // sub-counters and split-K tile counters
-  uint32_t* state;              // [0] epoch, [32] done counter, [64] error word
+  uint32_t* state;              // [0] epoch, [32] done counter, [64] error word, [96] clear pending
   // weights (plan-owned copies)
   const uint8_t* wblob;         // packed projection tiles
   const void* gains;            // [2L + 1][H]: attn_norm[l], mlp_norm[l], final_norm
@@ -82,8 +109,9 @@ struct DevPlan {
   const float* rope;            // [P][d/2][2]: cos, sin
   // activations and scratch (act = dtype)
   void* xin;                    // [P][Rmax][H] position inputs
-  // Buffers below marked [2] are doubled by position parity: positions 0
-  // and 1 can be in flight at the same time.
+  // Cross-workgroup buffers hold tagged 64-bit words (2 * dtype size bytes
+  // per element).  Buffers marked [2] are doubled by position parity:
+  // positions 0 and 1 can be in flight at the same time.
   void* hres;                   // [2][2][Rmax][H] residual after down, by layer parity
   void* hmid;                   // [2][Rmax][H] residual after o
   void* qbuf;                   // [2][Rmax][nq d]
@@ -91,20 +119,23 @@ struct DevPlan {
   void* mbuf;                   // [2][Rmax][I] SwiGLU output
   void* kc;                     // [L][Rmax][nkv][P][d]
   void* vc;
-  float* part;                  // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16]
-  float* ssq;                   // [P + 6][Rmax][H/16] sum-of-squares partials of residual rows
-  float* zbuf;                  // [Rmax][V] logits of the current head
-  uint2* cand;                  // [Rmax][n_head_tiles] (value bits, index)
+  uint64_t* part;               // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16] words
+  uint32_t* ssq;                // [P + 6][Rmax][H/16] words: sum-of-squares partials of residual rows
+  uint64_t* zbuf;               // [Rmax][V] words: logits of the current head
+  uint64_t* cand;               // [Rmax][n_head_tiles][2] words: (value, index) of each head tile
   uint64_t* trace;              // plan-owned trace staging (unused if no trace)
   int trace_on;
   int n_o_split, n_d_split, n_in_split;
-  uint64_t part_o_off, part_d_off, part_in_off;  // float offsets into part
-  uint64_t part_stride;                          // floats of one split-K buffer
+  uint64_t part_o_off, part_d_off, part_in_off;  // word offsets into part
+  uint64_t part_stride;                          // words of one split-K buffer
+  Span clear[kMaxClear];                         // every buffer that holds tagged words
+  int n_clear;
 };
 
 struct DevFrame {
   int rows;
   int sampled;
+  int defer_clear;  // K/V are copied out after the kernel: leave a wrap's clear to clear_pending_kernel
   const void* hidden_in;
   const int32_t* code0;
   const float* temperature;

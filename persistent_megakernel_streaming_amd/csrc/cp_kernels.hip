@@ -3,23 +3,26 @@
 //
 // The frame and its phases follow mstar pull request #1183 ("Qwen3-TTS: Run
 // the 1.7B Depth Loop as One Persistent Kernel on Hopper"), section "How it
-// works": one resident workgroup per compute unit walks a static task list; a
-// task waits on counters in device memory, runs one tile and signals a
-// counter; attention waits only on the qkv tiles of its own kv head; o and
-// down split their K loop and add the partial sums in a fixed order, with no
-// atomics on data, so a frame is bit-identical from run to run.  The megakernel
-// pattern itself (resident blocks, counter dependencies that only point to
-// earlier work, prefetching weights before waiting) is the one of the handbook
+// works": one resident workgroup per compute unit walks a static task list and
+// runs one tile per task; attention waits only on the qkv tiles of its own kv
+// head; o and down may split their K loop and add the partial sums in a fixed
+// order, with no atomics on data, so a frame is bit-identical from run to run.
+// The megakernel pattern itself (resident blocks, dependencies that only point
+// to earlier work, weights fetched before the wait) is the one of the handbook
 // chapter "The gaps between kernels: PDL and megakernels", section
 // "Megakernels: the whole forward pass in one kernel".
 //
-// Hand-off between workgroups (MI355X has eight XCDs, each with its own L2):
-// every value one workgroup writes and another reads is stored and loaded with
-// the agent-coherent cache policy (sc1), the writer waits for its stores to
-// complete before it adds to a counter, and the reader polls the counter with
-// agent-scope atomic loads.  No L2 write-back or invalidate is needed, because
-// no cross-workgroup value is ever held in a non-coherent cache line.
-// Weights and inputs never change during a frame and use the ordinary path.
+// Hand-off between workgroups.  MI355X has eight XCDs, each with its own L2,
+// and a 256-workgroup counter barrier with agent-scope acquire/release costs
+// several microseconds there.  Instead, every value one workgroup writes and
+// another reads is stored as 64-bit words {payload, tag}: the payload is two
+// bf16 (or one fp32) and the tag is epoch * 1024 + the writer's phase index.
+// Words are written with agent-coherent (sc1) stores whose 8-byte words are
+// single-copy atomic, and read with agent-coherent loads; a reader whose words
+// do not yet carry the tag it expects reloads them.  The data is its own ready
+// signal: there are no counters, no store-completion waits and no cache
+// write-back or invalidate on the path.  Weights, norms and embedding tables
+// never change during a frame and use ordinary loads and direct-to-LDS copies.
 #include <hip/hip_runtime.h>
 
 #include "cp_device.h"
@@ -30,9 +33,14 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kSC1 = 16;  // buffer cache policy bit: coherent at agent scope
+
+// LDS layout of the misc region (after the two weight-tile slots).
+constexpr int kGainLds = 1024;    // RMSNorm gain rows, two slots of 2 KiB
+constexpr int kRedAccLds = 8192;  // cross-wave MFMA accumulators (8 KiB)
 
 // ------------------------------------------------------------------ memory helpers
 
@@ -42,16 +50,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ u32x4 ld16c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1); }
-__device__ __forceinline__ u32x2 ld8c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSC1); }
-__device__ __forceinline__ uint32_t ld4c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSC1); }
-__device__ __forceinline__ uint32_t ld2c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kSC1); }
 __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld2(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+__device__ __forceinline__ u32x2 ld8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
 __device__ __forceinline__ void st16c(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSC1); }
 __device__ __forceinline__ void st8c(rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kSC1); }
-__device__ __forceinline__ void st4c(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kSC1); }
-__device__ __forceinline__ void st2c(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, kSC1); }
+__device__ __forceinline__ void st16(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
+__device__ __forceinline__ void st4(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0); }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -65,8 +69,6 @@ __device__ __forceinline__ void stamp(uint64_t* tr, int k) {
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
 // float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t f2bf(float f) {
   const bf16x2 v = {(__bf16)f, (__bf16)0.0f};
@@ -78,19 +80,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Element e of a 16-byte chunk as float.
+// Element e of a 16-byte payload chunk as float.
 template <int BF>
 __device__ __forceinline__ float chunk_elem(const u32x4& v, int e) {
   if constexpr (BF) return bf2f((v[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
   else return __uint_as_float(v[e]);
 }
 
-// Rounds to the activation type and returns the stored bits.
-template <int BF>
-__device__ __forceinline__ uint32_t to_act(float f) {
-  if constexpr (BF) return f2bf(f);
-  else return __float_as_uint(f);
-}
+// Rounds to the activation type (returns the rounded value as float).
 template <int BF>
 __device__ __forceinline__ float act_val(float f) {
   if constexpr (BF) return bf2f(f2bf(f));
@@ -104,65 +101,73 @@ __device__ __forceinline__ bool beats(float v, uint32_t i, float bv, uint32_t bi
   return v > bv || (v == bv && i < bi);
 }
 
-// ------------------------------------------------------------------ sync
+// ------------------------------------------------------------------ tagged words
 
-__device__ __forceinline__ uint32_t ld_ctr(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+__device__ __forceinline__ uint32_t tag_of(uint32_t epoch, uint32_t phase) { return (epoch << 10) | phase; }
 
-// Wave 0 waits until every sub-counter of the task's groups has reached its
-// share of this frame's target; the rest of the workgroup waits at the barrier.
-// A wait gives up after spin_limit polls and raises the error word, so a
+// A 16-byte load holds two tagged words: [payload, tag, payload, tag].
+__device__ __forceinline__ bool ll_ok(const u32x4& v, uint32_t tag) { return v[1] == tag && v[3] == tag; }
+
+// Payload of a 32-byte (four-word) chunk: 16 bytes of activations.
+__device__ __forceinline__ u32x4 ll_payload(const u32x4& a, const u32x4& b) { return u32x4{a[0], a[2], b[0], b[2]}; }
+
+// Tagged pair of payload words for a 16-byte store.
+__device__ __forceinline__ u32x4 ll_pair(uint32_t p0, uint32_t p1, uint32_t tag) { return u32x4{p0, tag, p1, tag}; }
+
+// Gives up a wait after spin_limit polls and raises the error word, so a
 // broken schedule ends the kernel instead of hanging it.
-__device__ __forceinline__ void wait_deps(const DevPlan& pl, const Task& tk, uint32_t epoch) {
-  if (threadIdx.x < 64 && tk.nwait) {
-    const int lane = threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < kMaxWaits; ++k) {
-      if (k >= tk.nwait) break;
-      const CtrGroup gp = pl.groups[tk.wait[k]];
-      const uint32_t target = (uint32_t)gp.per_sub * epoch;
-      if (lane < gp.nsub) {
-        const uint32_t* c = pl.ctr + (size_t)(gp.base + lane) * kCtrStride;
-        uint32_t spins = 0;
-        while (ld_ctr(c) < target) {
-          if (++spins > pl.spin_limit) {
-            __hip_atomic_store(pl.state + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          if ((spins & 1023u) == 0 && ld_ctr(pl.state + 64)) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
+struct Spin {
+  uint32_t n = 0;
+  __device__ __forceinline__ bool next(const DevPlan& pl) {
+    if (++n > pl.spin_limit) {
+      __hip_atomic_store(pl.state + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
     }
+    if ((n & 4095u) == 0 && __hip_atomic_load(pl.state + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
+    __builtin_amdgcn_s_sleep(1);
+    return true;
   }
-  __syncthreads();
+};
+
+// Polls N 16-byte tagged loads (already issued into v) until every word
+// carries `tag`; stale ones are reloaded from off(i).
+template <int N, typename Off>
+__device__ __forceinline__ void ll_poll(const DevPlan& pl, rsrc_t r, Off off, u32x4 (&v)[N], uint32_t tag,
+                                        bool active) {
+  if (!active) return;
+  Spin sp;
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok = ok && ll_ok(v[i], tag);
+    if (ok || !sp.next(pl)) break;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!ll_ok(v[i], tag)) v[i] = ld16c(r, off(i));
+  }
 }
 
-// Every wave waits for its own stores, then one thread adds to the group.
-__device__ __forceinline__ void signal_group(const DevPlan& pl, uint32_t grp, uint32_t slot, bool persistent,
-                                             uint64_t* tr) {
-  stamp(tr, 5);
-  wait_vm();
-  __syncthreads();
-  stamp(tr, 6);
-  if (persistent && threadIdx.x == 0 && grp != kNone) {
-    const CtrGroup gp = pl.groups[grp];
-    __hip_atomic_fetch_add(pl.ctr + (size_t)(gp.base + slot % gp.nsub) * kCtrStride, 1u,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The same for single tagged words (8-byte loads).
+template <int N, typename Off>
+__device__ __forceinline__ void ll_poll1(const DevPlan& pl, rsrc_t r, Off off, u32x2 (&v)[N], uint32_t tag,
+                                         bool active) {
+  if (!active) return;
+  Spin sp;
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok = ok && v[i][1] == tag;
+    if (ok || !sp.next(pl)) break;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (v[i][1] != tag) v[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off(i), 0, kSC1);
   }
-  stamp(tr, 7);
 }
 
 // ------------------------------------------------------------------ weights -> LDS
 
-// Byte offset of the gain row staged in the misc LDS region.
-constexpr int kGainLds = 1024;    // RMSNorm gain row (<= 2 KiB)
-constexpr int kRedSsLds = 4096;   // cross-wave sums of squares (256 B)
-constexpr int kRedAccLds = 8192;  // cross-wave MFMA accumulators (8 KiB)
-
 // Gain row (of the [2L + 1][H] table) a projection task normalises with, or -1.
-__device__ __forceinline__ int gain_row_of(const DevPlan& pl, const Task& tk) {
+__device__ __forceinline__ int gain_row_of(const DevPlan& pl, const DevTask& tk) {
   switch (tk.type) {
     case T_QKV: return 2 * tk.layer;
     case T_GU: return 2 * tk.layer + 1;
@@ -171,10 +176,10 @@ __device__ __forceinline__ int gain_row_of(const DevPlan& pl, const Task& tk) {
   }
 }
 
-// Direct-to-LDS copies of the task's packed weight tile and, for normalising
+// Direct-to-LDS copies of a task's packed weight tile and, for normalising
 // tasks, its RMSNorm gain row: 1 KiB chunks (64 lanes x 16 B) with
 // global_load_lds_dwordx4, dealt round-robin to the four waves.
-__device__ __forceinline__ void issue_tile(const DevPlan& pl, const Task& tk, uint8_t* slot, uint8_t* misc) {
+__device__ __forceinline__ void issue_tile(const DevPlan& pl, const DevTask& tk, uint8_t* slot, uint8_t* gain) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t nch = tk.w_bytes >> 10;
   const uint8_t* src = pl.wblob + tk.w_off;
@@ -188,10 +193,21 @@ __device__ __forceinline__ void issue_tile(const DevPlan& pl, const Task& tk, ui
     const uint8_t* gsrc = (const uint8_t*)pl.gains + (size_t)gr * gbytes;
     for (uint32_t c = 3 - wave; c < (gbytes + 1023) / 1024; c += 4) {
       __builtin_amdgcn_global_load_lds((const void*)(gsrc + c * 1024 + lane * 16),
-                                       (void __attribute__((address_space(3)))*)(misc + kGainLds + c * 1024), 16, 0, 0);
+                                       (void __attribute__((address_space(3)))*)(gain + c * 1024), 16, 0, 0);
     }
   }
 }
+
+// Where the next task's tile goes, and whether there is one.
+struct Next {
+  DevTask tk;  // loaded when the current task starts
+  bool valid;
+  uint8_t* slot;
+  uint8_t* gain;
+  __device__ __forceinline__ void issue(const DevPlan& pl) const {
+    if (valid) issue_tile(pl, tk, slot, gain);
+  }
+};
 
 // ------------------------------------------------------------------ projections
 
@@ -211,15 +227,15 @@ __device__ __forceinline__ f32x4 mma(const u32x4& w, const u32x4& x, f32x4 acc) 
 }
 
 // Sum of squares of a residual row comes from its producers as H/16 partials
-// (one per 16-column tile, in tile order); ssq slot ids: position inputs
-// 0 .. P-1, residual after down P + 2*parity + layer parity, residual after o
-// P + 4 + parity.
-__device__ __forceinline__ float* ssq_slot(const DevPlan& pl, int slot) {
-  return pl.ssq + (size_t)slot * pl.Rmax * (pl.H / 16);
+// (one per 16-column tile, tile order), stored as tagged words; ssq slot ids:
+// position inputs 0 .. P-1, residual after down P + 2*parity + layer parity,
+// residual after o P + 4 + parity.
+__device__ __forceinline__ uint32_t* ssq_slot(const DevPlan& pl, int slot) {
+  return pl.ssq + (size_t)slot * pl.Rmax * (pl.H / 16) * 2;
 }
 
 // Sum of squares of the four values a lane stores, added over the `span`
-// lanes (xor distances `first`, `2 first`, ...) that share one 16-column tile.
+// lanes (xor distances first, 2 first, ...) that share one 16-column tile.
 __device__ __forceinline__ float tile_ssq(const float (&v)[4], int first, int span) {
   float s = 0.f;
 #pragma unroll
@@ -228,24 +244,42 @@ __device__ __forceinline__ float tile_ssq(const float (&v)[4], int first, int sp
   return s;
 }
 
+// Stores four activation values as tagged words at byte offset off (element
+// index * ESZ * 2) of r.
 template <int BF>
-__device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, bool persistent, uint64_t* tr) {
+__device__ __forceinline__ void st_act4(rsrc_t r, uint32_t off, const float (&v)[4], uint32_t tag) {
+  if constexpr (BF) {
+    st16c(r, off, ll_pair(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), tag));
+  } else {
+    st16c(r, off, ll_pair(__float_as_uint(v[0]), __float_as_uint(v[1]), tag));
+    st16c(r, off + 16, ll_pair(__float_as_uint(v[2]), __float_as_uint(v[3]), tag));
+  }
+}
+
+template <int BF>
+__device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
+                                          uint8_t* slot, uint8_t* gain, uint32_t* misc, const Next& nx,
+                                          uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
-  constexpr int E = 16 / ESZ;         // elements per 16-byte chunk
+  constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 4, rl = lane & 15;
   const int rows = fr.rows;
   const int H = pl.H, Rmax = pl.Rmax, P = pl.P;
   const int l = tk.layer, p = tk.pos;
+  const uint32_t my_tag = tag_of(epoch, tk.phase);
+  const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
+  const uint32_t res_tag = tag_of(epoch, tk.ph_in1);
 
-  // Operand source, K range, norm and epilogue of this task kind.
+  // Operand source, K range, norm and epilogue of this task kind.  Tagged
+  // buffers hold 2 * ESZ bytes per element.
   const void* xsrc;
-  uint32_t xbytes, ld;  // buffer bytes and row stride (elements)
+  uint32_t xbytes, ld;   // buffer bytes and row length (elements)
+  bool xll = true;       // operand rows are tagged words (all but the frame input)
   int k0 = 0, kt;
-  int in_ssq = -1;      // ssq slot of a normalised input (-1: no norm)
-  int out_ssq = -1;     // ssq slot of a residual output (EPI_PART)
+  int in_ssq = -1;       // ssq slot of a normalised input (-1: no norm)
+  int out_ssq = -1;      // ssq slot of a residual output (EPI_PART)
   int nb = 1;
   Epi epi;
   const void* resid = nullptr;  // residual (EPI_PART)
@@ -254,8 +288,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // Buffers that two positions in flight at once (0 and 1) would share are
   // doubled and picked by position parity.
   const int par = p & 1;
-  const uint32_t hbytes = (uint32_t)Rmax * H * ESZ;
-  const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * pl.d * ESZ;
+  const uint32_t hbytes = (uint32_t)Rmax * H * ESZ * 2;
+  const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * pl.d * ESZ * 2;
   uint8_t* hres = (uint8_t*)pl.hres + (size_t)par * 2 * hbytes;   // [layer parity]
   uint8_t* hmid = (uint8_t*)pl.hmid + (size_t)par * hbytes;
   const uint8_t* layer_in = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
@@ -273,15 +307,15 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       kt = (int)ld / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART; resid = layer_in; out = hmid;
       out_ssq = P + 4 + par; part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; break;
     case T_DOWN:
-      xsrc = (const uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ; ld = pl.I; xbytes = (uint32_t)Rmax * ld * ESZ;
-      kt = pl.I / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART; resid = hmid;
-      out = hres + (size_t)(l & 1) * hbytes; out_ssq = P + 2 * par + (l & 1);
+      xsrc = (const uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ * 2; ld = pl.I;
+      xbytes = (uint32_t)Rmax * ld * ESZ * 2; kt = pl.I / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART;
+      resid = hmid; out = hres + (size_t)(l & 1) * hbytes; out_ssq = P + 2 * par + (l & 1);
       part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; break;
-    default:  // T_INPROJ
-      xsrc = fr.hidden_in; ld = pl.Din; xbytes = (uint32_t)fr.rows * ld * ESZ; kt = pl.Din / tk.nsplit;
+    default:  // T_INPROJ: the frame's input hidden (plain, written before the launch)
+      xsrc = fr.hidden_in; ld = pl.Din; xbytes = (uint32_t)fr.rows * ld * ESZ; xll = false; kt = pl.Din / tk.nsplit;
       k0 = tk.split * kt; epi = EPI_PART; out = pl.xin; out_ssq = 0; part_off = pl.part_in_off; break;
   }
-  const int nck = kt * ESZ / 64;  // 16-byte chunks per lane over the task's K range
+  const int nck = kt * ESZ / 64;  // 16-byte payload chunks per lane over the task's K range
 
   // Waves and row tiles: a wave owns 16 rows; with few rows the waves of a
   // row tile split K and add their results through LDS in a fixed order.
@@ -295,32 +329,45 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const bool wave_live = rt < nrt;
   const bool live = wave_live && row < rows;
   f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);    // [4 waves][2][64 lanes]
-  const uint32_t ssq_bytes = (uint32_t)Rmax * (H / 16) * 4;
+  const uint32_t ssq_bytes = (uint32_t)Rmax * (H / 16) * 8;
+  const bool owner = tk.nsplit == 1 || tk.split == 0;
 
-  // Loads that do not depend on the K loop go out first: the sum-of-squares
-  // partials of a normalised input, the residual of an unsplit o / down tile
-  // and the RoPE angles of a qkv tile.
+  // Operand rows: 4-chunk groups, two in flight.  A tagged chunk is 32 bytes
+  // (two 16-byte loads); a plain chunk 16 bytes.
   const rsrc_t rx = make_rsrc(xsrc, xbytes);
-  const uint32_t xoff = ((uint32_t)row * ld + k0 + q * E) * ESZ + c0 * 64;
-  u32x4 ssv[4];
-  const int nsq = H / 64;  // partials per lane (H/16 partials over 4 lanes), <= 4
-  if (in_ssq >= 0) {
-    const rsrc_t rs = make_rsrc(ssq_slot(pl, in_ssq), ssq_bytes);
+  const uint32_t cstride = xll ? 128 : 64;  // bytes per chunk step (KS elements)
+  const uint32_t xoff = ((uint32_t)row * ld + k0 + q * E) * ESZ * (xll ? 2 : 1) + c0 * cstride;
+  u32x4 xa[8], xb[8];
+  // 16-byte unit u of group g: chunk u / 2, half u % 2
+  auto goff = [&](int g) { return [=](int u) { return xoff + (g * 4 + (u >> 1)) * cstride + (u & 1) * 16; }; };
+  auto load_group = [&](u32x4 (&x)[8], int g) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i * 4 < nsq) ssv[i] = live ? ld16c(rs, (uint32_t)(row * (H / 16) + q * nsq + 4 * i) * 4) : u32x4{0, 0, 0, 0};
-  }
-  const uint32_t eo = (uint32_t)(row * H + 16 * tk.tile + 4 * q) * ESZ;  // this lane's 4 output slots
-  u32x4 rv = {0, 0, 0, 0};
-  if (epi == EPI_PART && tk.nsplit == 1 && resid && live && ks == 0) {
-    const rsrc_t rr = make_rsrc(resid, hbytes);
-    if constexpr (BF) {
-      const u32x2 h = ld8c(rr, eo);
-      rv[0] = h[0]; rv[1] = h[1];
-    } else {
-      rv = ld16c(rr, eo);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t base = xoff + (g * 4 + i) * cstride;
+      // The first attempt may hit the L2, which the other workgroups of this
+      // XCD reading the same rows then share; a stale word fails its tag
+      // check and is reloaded coherently.  Plain rows (the frame input) use
+      // the even units only.
+      x[2 * i] = live ? ld16(rx, base) : u32x4{0, in_tag, 0, in_tag};
+      x[2 * i + 1] = (live && xll) ? ld16(rx, base + 16) : u32x4{0, in_tag, 0, in_tag};
     }
+  };
+  const int ng = ncw / 4;
+  if (wave_live) {
+    load_group(xa, 0);
+    if (ng > 1) load_group(xb, 1);
   }
+  // Sum-of-squares partials of a normalised input (tagged, same writer as the rows).
+  u32x4 ssv[8];
+  const int nsq = H / 64;  // partials per lane (H/16 partials over 4 lanes), <= 16
+  const rsrc_t rs = make_rsrc(in_ssq >= 0 ? ssq_slot(pl, in_ssq) : pl.ssq, ssq_bytes);
+  const uint32_t ss0 = (uint32_t)(row * (H / 16) + q * nsq) * 8;
+  auto sso = [=](int i) { return ss0 + i * 16; };
+  if (in_ssq >= 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ssv[i] = (2 * i < nsq && live) ? ld16(rs, sso(i)) : u32x4{0, in_tag, 0, in_tag};
+  }
+  // RoPE angles of a qkv tile's two rotary pairs per lane.
   float rope_cs[2] = {1.f, 1.f}, rope_sn[2] = {0.f, 0.f};
   if (tk.type == T_QKV) {
     const int d = pl.d, th = d / 16, tpg = (pl.gq + 2) * th, lt = tk.tile % tpg;
@@ -333,17 +380,13 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   }
-
-  // K loop over groups of four chunks: the next group's loads are in flight
-  // while the current one is scaled and multiplied.
-  u32x4 xa[4], xb[4];
-  auto load_group = [&](u32x4 (&x)[4], int g) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = live ? ld16c(rx, xoff + (g * 4 + i) * 64) : u32x4{0, 0, 0, 0};
-  };
-  const int ng = ncw / 4;
-  if (wave_live) load_group(xa, 0);
-  wait_vm();        // this wave's share of the weight tile (and the first group) have landed
+  // Wait for the first group (and the norm partials): the data is its signal.
+  if (xll) {
+    ll_poll<8>(pl, rx, goff(0), xa, in_tag, live);
+    if (ng > 1) ll_poll<8>(pl, rx, goff(1), xb, in_tag, live);
+  }
+  if (in_ssq >= 0) ll_poll<8>(pl, rs, sso, ssv, in_tag, live);
+  wait_vm();        // this wave's share of the weight tile (issued during the previous task) has landed
   __syncthreads();  // every wave's share of the tile is in LDS
   stamp(tr, 2);
 
@@ -351,23 +394,29 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   if (in_ssq >= 0 && wave_live) {
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i * 4 < nsq)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ss += __uint_as_float(ssv[i][e]);
+    for (int i = 0; i < 8; ++i)
+      if (2 * i < nsq) ss += __uint_as_float(ssv[i][0]) + __uint_as_float(ssv[i][2]);
     ss += shfl_xor_f(ss, 16);
     ss += shfl_xor_f(ss, 32);
     rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
   }
   stamp(tr, 3);
+  if (tr) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stamp(tr, 1);
+  }
 
   const bool norm = in_ssq >= 0;
   const bool unit = pl.unit_gains != 0;
-  const uint8_t* gl = (const uint8_t*)misc + kGainLds + c0 * 64;  // gain row staged with the tile
+  const uint8_t* gl = gain + c0 * 64;  // gain row staged with the tile
   const uint8_t* wt = slot + lane * 16 + (size_t)c0 * nb * 1024;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   // a = round(round(x * r) * g) in the activation type, then the MFMAs
-  auto process = [&](u32x4 (&x)[4], int g) {
+  auto process = [&](u32x4 (&xr)[8], int g) {
+    if (xll) ll_poll<8>(pl, rx, goff(g), xr, in_tag, live);
+    u32x4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = xll ? ll_payload(xr[2 * i], xr[2 * i + 1]) : xr[2 * i];
     u32x4 w[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -378,27 +427,27 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const u32x4 gv = *(const u32x4*)(gl + ((g * 4 + i) * KS + q * E) * ESZ);
-        u32x4 o;
+        u32x4 o2;
         if constexpr (BF) {
 #pragma unroll
           for (int w2 = 0; w2 < 4; ++w2) {
             const uint32_t xw = x[i][w2];
             const float t0 = __uint_as_float(xw << 16) * rinv, t1 = __uint_as_float(xw & 0xffff0000u) * rinv;
             if (unit) {
-              o[w2] = pack_bf16(t0, t1);
+              o2[w2] = pack_bf16(t0, t1);
             } else {
               const uint32_t gw = gv[w2];
-              o[w2] = pack_bf16(t0 * __uint_as_float(gw << 16), t1 * __uint_as_float(gw & 0xffff0000u));
+              o2[w2] = pack_bf16(t0 * __uint_as_float(gw << 16), t1 * __uint_as_float(gw & 0xffff0000u));
             }
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float t = __uint_as_float(x[i][e]) * rinv;
-            o[e] = __float_as_uint(unit ? t : t * __uint_as_float(gv[e]));
+            o2[e] = __float_as_uint(unit ? t : t * __uint_as_float(gv[e]));
           }
         }
-        x[i] = live ? o : u32x4{0, 0, 0, 0};
+        x[i] = live ? o2 : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
@@ -414,11 +463,12 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   };
   if (wave_live) {
     for (int g = 0; g < ng; g += 2) {
-      if (g + 1 < ng) load_group(xb, g + 1);
       process(xa, g);
-      if (g + 1 >= ng) break;
+      if (g == 0) stamp(tr, 6);
       if (g + 2 < ng) load_group(xa, g + 2);
+      if (g + 1 >= ng) break;
       process(xb, g + 1);
+      if (g + 3 < ng) load_group(xb, g + 3);
     }
     if (nb == 1) {
 #pragma unroll
@@ -449,6 +499,40 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     }
   }
   const bool epi_wave = wave_live && ks == 0;
+  const uint32_t slots = (uint32_t)(16 * tk.tile + 4 * q);  // this lane's 4 output slots
+
+  // The split-K owner collects its partners' partials and the residual; an
+  // unsplit o / down tile only needs the residual.  All loads go out before
+  // the next task's tile copy, whose completion would otherwise be waited on.
+  u32x4 pv[6], rv[2];
+  const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 8);
+  const rsrc_t rr = make_rsrc(resid ? resid : xsrc, hbytes);
+  const uint32_t pbase = (uint32_t)((tk.tile * tk.nsplit * Rmax + row) * 16 + 4 * q) * 8;
+  const uint32_t pstep = (uint32_t)Rmax * 16 * 8;  // bytes between splits of a tile
+  // unit u of the partners' partials: split 1 + u / 2, half u % 2
+  auto po = [=](int u) { return pbase + (1 + (u >> 1)) * pstep + (u & 1) * 16; };
+  const uint32_t rbase = (uint32_t)(row * H + slots) * ESZ * 2;
+  auto ro = [=](int u) { return rbase + u * 16; };
+  if (epi == EPI_PART && epi_wave) {
+    if (!owner) {
+      if (live) {  // partial of this split, tagged with this phase
+        const uint32_t o = pbase + tk.split * pstep;
+        st16c(rp, o, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag));
+        st16c(rp, o + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        const bool use = 1 + (u >> 1) < tk.nsplit && live;
+        pv[u] = use ? ld16c(rp, po(u)) : u32x4{0, my_tag, 0, my_tag};
+      }
+      rv[0] = (resid && live) ? ld16c(rr, ro(0)) : u32x4{0, res_tag, 0, res_tag};
+      rv[1] = (resid && live && !BF) ? ld16c(rr, ro(1)) : u32x4{0, res_tag, 0, res_tag};
+      ll_poll<6>(pl, rp, po, pv, my_tag, live);
+      ll_poll<2>(pl, rr, ro, rv, res_tag, live && resid);
+    }
+  }
+  nx.issue(pl);  // the next task's tile lands during this epilogue and the next wait
 
   // Lane (q, rl) of an epilogue wave holds output slots 4q .. 4q+3 of row `row`.
   if (epi_wave) {
@@ -457,7 +541,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       const int tpg = (gq + 2) * th;
       const int g = tk.tile / tpg, lt = tk.tile % tpg;
       const uint32_t kvoff = (uint32_t)(((l * Rmax + row) * nkv + g) * P + p) * d;
-      const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ;
+      const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
+      const uint32_t kv_tag = tag_of(epoch, kKvPhase);
       if (live) {
         if (lt < (gq + 1) * th) {
           // q or k head: slots (4q + v) hold rotary pairs 8 tih + 2q + (v >> 1), half v & 1
@@ -469,33 +554,32 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
             const float x1 = acc0[2 * pr], x2 = acc0[2 * pr + 1];
-            const float cs = rope_cs[pr], sn = rope_sn[pr];
-            y[2 * pr] = x1 * cs - x2 * sn;
-            y[2 * pr + 1] = x2 * cs + x1 * sn;
+            y[2 * pr] = x1 * rope_cs[pr] - x2 * rope_sn[pr];
+            y[2 * pr + 1] = x2 * rope_cs[pr] + x1 * rope_sn[pr];
           }
           // dims i0, i0 + 1 (first halves) and i0 + d/2, i0 + d/2 + 1 (second halves)
           rsrc_t r;
-          uint32_t base;
+          uint32_t base, tg;
           if (isq) {
             r = make_rsrc((uint8_t*)pl.qbuf + (size_t)par * qdbytes, qdbytes);
             base = (uint32_t)(row * pl.nq * d + hq * d);
+            tg = my_tag;
           } else {
             r = make_rsrc(pl.kc, kvbytes);
             base = kvoff;
+            tg = kv_tag;
           }
           if constexpr (BF) {
-            st4c(r, (base + i0) * 2, pack_bf16(y[0], y[2]));
-            st4c(r, (base + i0 + d / 2) * 2, pack_bf16(y[1], y[3]));
+            st8c(r, (base + i0) * 4, u32x2{pack_bf16(y[0], y[2]), tg});
+            st8c(r, (base + i0 + d / 2) * 4, u32x2{pack_bf16(y[1], y[3]), tg});
           } else {
-            st8c(r, (base + i0) * 4, u32x2{__float_as_uint(y[0]), __float_as_uint(y[2])});
-            st8c(r, (base + i0 + d / 2) * 4, u32x2{__float_as_uint(y[1]), __float_as_uint(y[3])});
+            st16c(r, (base + i0) * 8, ll_pair(__float_as_uint(y[0]), __float_as_uint(y[2]), tg));
+            st16c(r, (base + i0 + d / 2) * 8, ll_pair(__float_as_uint(y[1]), __float_as_uint(y[3]), tg));
           }
         } else {
           const int tih = lt - (gq + 1) * th;
-          const rsrc_t r = make_rsrc(pl.vc, kvbytes);
-          const uint32_t o = (kvoff + 16 * tih + 4 * q) * ESZ;
-          if constexpr (BF) st8c(r, o, u32x2{pack_bf16(acc0[0], acc0[1]), pack_bf16(acc0[2], acc0[3])});
-          else st16c(r, o, u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
+          const float v4[4] = {acc0[0], acc0[1], acc0[2], acc0[3]};
+          st_act4<BF>(make_rsrc(pl.vc, kvbytes), (kvoff + 16 * tih + 4 * q) * ESZ * 2, v4, kv_tag);
         }
       }
     } else if (epi == EPI_GU) {
@@ -506,19 +590,20 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           const float gv = acc0[v], uv = acc1[v];
           m[v] = (gv / (1.0f + expf(-gv))) * uv;
         }
-        const rsrc_t r = make_rsrc((uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ, (uint32_t)Rmax * pl.I * ESZ);
-        const uint32_t o = (uint32_t)(row * pl.I + 16 * tk.tile + 4 * q) * ESZ;
-        if constexpr (BF) st8c(r, o, u32x2{pack_bf16(m[0], m[1]), pack_bf16(m[2], m[3])});
-        else st16c(r, o, u32x4{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])});
+        const uint32_t mbytes = (uint32_t)Rmax * pl.I * ESZ * 2;
+        st_act4<BF>(make_rsrc((uint8_t*)pl.mbuf + (size_t)par * mbytes, mbytes),
+                    (uint32_t)(row * pl.I + 16 * tk.tile + 4 * q) * ESZ * 2, m, my_tag);
       }
     } else if (epi == EPI_HEAD) {
       const int V = pl.V;
-      const uint32_t n0 = 16 * tk.tile + 4 * q;
+      const uint32_t n0 = slots;
       if (live) {
-        const u32x4 z = {__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])};
-        st16c(make_rsrc(pl.zbuf, (uint32_t)Rmax * V * 4), (uint32_t)(row * V + n0) * 4, z);
+        const rsrc_t rz = make_rsrc(pl.zbuf, (uint32_t)Rmax * V * 8);
+        st16c(rz, (uint32_t)(row * V + n0) * 8, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag));
+        st16c(rz, (uint32_t)(row * V + n0) * 8 + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag));
         if (fr.logits)
-          st16c(make_rsrc(fr.logits, (uint32_t)rows * (P - 1) * V * 4), (uint32_t)((row * (P - 1) + (p - 1)) * V + n0) * 4, z);
+          st16(make_rsrc(fr.logits, (uint32_t)rows * (P - 1) * V * 4), (uint32_t)((row * (P - 1) + (p - 1)) * V + n0) * 4,
+               u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
       }
       // best (value, index) of the tile for this row
       float bv = acc0[0];
@@ -533,85 +618,36 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
       if (live && q == 0)
-        st8c(make_rsrc(pl.cand, (uint32_t)Rmax * pl.n_head_tiles * 8), (uint32_t)(row * pl.n_head_tiles + tk.tile) * 8,
-             u32x2{__float_as_uint(bv), bi});
-    } else if (tk.nsplit == 1) {  // EPI_PART, unsplit: residual add, store, sum of squares
-      float h[4];
+        st16c(make_rsrc(pl.cand, (uint32_t)Rmax * pl.n_head_tiles * 16), (uint32_t)(row * pl.n_head_tiles + tk.tile) * 16,
+              ll_pair(__float_as_uint(bv), bi, my_tag));
+    } else if (owner) {  // EPI_PART: (partials in split order) + residual, store, sum of squares
+      f32x4 s = acc0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(resid ? acc0[e] + chunk_elem<BF>(rv, e) : acc0[e]);
+      for (int sp = 1; sp < 4; ++sp)
+        if (sp < tk.nsplit) {
+          const u32x4 a = pv[2 * sp - 2], b = pv[2 * sp - 1];
+          s[0] = s[0] + __uint_as_float(a[0]); s[1] = s[1] + __uint_as_float(a[2]);
+          s[2] = s[2] + __uint_as_float(b[0]); s[3] = s[3] + __uint_as_float(b[2]);
+        }
+      float h[4];
+      if (resid) {
+        const u32x4 r4 = BF ? u32x4{rv[0][0], rv[0][2], 0, 0} : ll_payload(rv[0], rv[1]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e] + chunk_elem<BF>(r4, e));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e]);
+      }
       const float sq = tile_ssq(h, 16, 4);
       if (live) {
-        const rsrc_t ro = make_rsrc(out, hbytes);
-        if constexpr (BF) st8c(ro, eo, u32x2{pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3])});
-        else st16c(ro, eo, u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]), __float_as_uint(h[3])});
-        if (q == 0) st4c(make_rsrc(ssq_slot(pl, out_ssq), ssq_bytes), (uint32_t)(row * (H / 16) + tk.tile) * 4, __float_as_uint(sq));
-      }
-    } else {  // EPI_PART, split: fp32 partial of this split
-      if (live) {
-        const uint32_t o = (uint32_t)(((tk.tile * tk.nsplit + tk.split) * Rmax + row) * 16 + 4 * q) * 4;
-        st16c(make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4), o,
-              u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
+        st_act4<BF>(make_rsrc(out, hbytes), (uint32_t)(row * H + slots) * ESZ * 2, h, my_tag);
+        if (q == 0)
+          st8c(make_rsrc(ssq_slot(pl, out_ssq), ssq_bytes), (uint32_t)(row * (H / 16) + tk.tile) * 8,
+               u32x2{__float_as_uint(sq), my_tag});
       }
     }
   }
-
-  if (epi != EPI_PART || tk.nsplit == 1) {
-    signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
-    return;
-  }
-
-  // Split-K: the last of the nsplit tasks of this tile to arrive adds the
-  // partials in split order (then the residual) and stores the tile.
-  wait_vm();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(pl.ctr + (size_t)tk.tctr * kCtrStride, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    misc[0] = (old == (uint32_t)tk.nsplit * epoch - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (misc[0] == 0) return;  // uniform across the workgroup
-
-  {
-    const int t = threadIdx.x;  // 64 rows x 4 column quads
-    const int r = t >> 2, c4 = (t & 3) * 4;
-    const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 4);
-    // issue every load (partials and residual) before using any
-    const uint32_t ro_off = (uint32_t)(r * H + 16 * tk.tile + c4) * ESZ;
-    u32x4 pv[4];
-#pragma unroll
-    for (int sp = 0; sp < 4; ++sp)
-      if (sp < tk.nsplit)
-        pv[sp] = r < rows ? ld16c(rp, (uint32_t)(((tk.tile * tk.nsplit + sp) * Rmax + r) * 16 + c4) * 4) : u32x4{0, 0, 0, 0};
-    u32x4 hv = {0, 0, 0, 0};
-    if (resid && r < rows) {
-      const rsrc_t rr = make_rsrc(resid, hbytes);
-      if constexpr (BF) {
-        const u32x2 h = ld8c(rr, ro_off);
-        hv[0] = h[0]; hv[1] = h[1];
-      } else {
-        hv = ld16c(rr, ro_off);
-      }
-    }
-    f32x4 s = {0, 0, 0, 0};
-#pragma unroll
-    for (int sp = 0; sp < 4; ++sp)
-      if (sp < tk.nsplit)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = s[e] + __uint_as_float(pv[sp][e]);
-    float h[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(resid ? s[e] + chunk_elem<BF>(hv, e) : s[e]);
-    const float sq = tile_ssq(h, 1, 4);
-    if (r < rows) {
-      const rsrc_t ro = make_rsrc(out, hbytes);
-      if constexpr (BF) st8c(ro, ro_off, u32x2{pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3])});
-      else st16c(ro, ro_off, u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]), __float_as_uint(h[2]), __float_as_uint(h[3])});
-      if ((t & 3) == 0)
-        st4c(make_rsrc(ssq_slot(pl, out_ssq), ssq_bytes), (uint32_t)(r * (H / 16) + tk.tile) * 4, __float_as_uint(sq));
-    }
-  }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
+  stamp(tr, 5);
 }
 
 // ------------------------------------------------------------------ attention
@@ -620,8 +656,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 // wave's work.  Scores: lane (t, c) takes position t and a quarter c of the
 // head dimension; softmax over t <= p in float; output: lane owns d/64 dims.
 template <int BF>
-__device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent,
-                                          uint64_t* tr) {
+__device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
+                                          const Next& nx, uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d = pl.d, gq = pl.gq, nkv = pl.nkv, P = pl.P, Rmax = pl.Rmax;
@@ -629,48 +665,64 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
   const int ngroups = Rmax / pl.attn_rows;
   const int g = tk.tile / ngroups, rg = tk.tile % ngroups;
   const int npairs = pl.attn_rows * gq;
-  const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * d * ESZ;
+  const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * d * ESZ * 2;
   const rsrc_t rq = make_rsrc((uint8_t*)pl.qbuf + (size_t)(p & 1) * qdbytes, qdbytes);
-  const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ;
+  const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
   const rsrc_t rk = make_rsrc(pl.kc, kvbytes), rv = make_rsrc(pl.vc, kvbytes);
   const rsrc_t ra = make_rsrc((uint8_t*)pl.abuf + (size_t)(p & 1) * qdbytes, qdbytes);
+  const uint32_t q_tag = tag_of(epoch, tk.ph_in0), kv_tag = tag_of(epoch, kKvPhase);
+  const uint32_t my_tag = tag_of(epoch, tk.phase);
   const int t = lane >> 2, c = lane & 3;
   const int dq = d / 4;                  // dims per score lane
-  const int nchunk = dq * ESZ / 16;      // 16-byte chunks per score lane (2, 4 or 8)
+  const int nld = dq * ESZ * 2 / 16;     // 16-byte tagged loads per score lane (4, 8 or 16)
   const int dpl = d / 64;                // output dims per lane (1 or 2)
+  bool issued = false;
   for (int pi = wave; pi < npairs; pi += 4) {
     const int row = rg * pl.attn_rows + pi / gq;
     const int hq = g * gq + pi % gq;
     if (row >= fr.rows) continue;  // wave-uniform
     const uint32_t kvrow = (uint32_t)((l * Rmax + row) * nkv + g) * P;
-    // every load of the pair (Q, K and V for t <= p) is issued before any is used
-    const uint32_t dbase = (uint32_t)(lane * dpl);
-    u32x4 qv[8], kv[8];
-    const uint32_t qo = (uint32_t)(row * pl.nq * d + hq * d + c * dq) * ESZ;
-    const uint32_t ko = (uint32_t)((kvrow + t) * d + c * dq) * ESZ;
+    // Q and K of this lane's quarter
+    constexpr int NQ = BF ? 8 : 16;  // 16-byte tagged loads per score lane at most
+    u32x4 qv[NQ], kv[NQ];
+    const uint32_t q0 = ((uint32_t)(row * pl.nq * d + hq * d + c * dq)) * ESZ * 2;
+    const uint32_t k0 = ((uint32_t)((kvrow + t) * d + c * dq)) * ESZ * 2;
+    auto qo = [=](int i) { return q0 + i * 16; };
+    auto ko = [=](int i) { return k0 + i * 16; };
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < nchunk) {
-        qv[i] = ld16c(rq, qo + i * 16);
-        kv[i] = (t <= p) ? ld16c(rk, ko + i * 16) : u32x4{0, 0, 0, 0};
-      }
-    u32x2 vv[16];  // V[t][dbase .. dbase + dpl) for t = 0 .. 15
+    for (int i = 0; i < NQ; ++i) {
+      const bool use = i < nld;
+      qv[i] = use ? ld16c(rq, qo(i)) : u32x4{0, q_tag, 0, q_tag};
+      kv[i] = (use && t <= p) ? ld16c(rk, ko(i)) : u32x4{0, kv_tag, 0, kv_tag};
+    }
+    // V of this lane's dims for every t <= p: the word holding them (bf16),
+    // or the aligned pair of words (fp32)
+    const uint32_t vrow = (uint32_t)(d * ESZ * 2);
+    const uint32_t v0 = ((uint32_t)(kvrow * d + lane * dpl) * ESZ * 2) & (BF ? ~7u : ~15u);
+    auto vo = [=](int tt) { return v0 + tt * vrow; };
+    u32x2 vw[16];
+    u32x4 vv[BF ? 1 : 16];
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
-      if (tt <= p) {
-        const uint32_t vo = (uint32_t)((kvrow + tt) * d + dbase) * ESZ;
-        if (ESZ * dpl == 8) vv[tt] = ld8c(rv, vo);
-        else if (ESZ * dpl == 4) vv[tt] = u32x2{ld4c(rv, vo), 0u};
-        else vv[tt] = u32x2{ld2c(rv, vo), 0u};
-      }
+      if constexpr (BF) vw[tt] = (tt <= p) ? __builtin_amdgcn_raw_buffer_load_b64(rv, vo(tt), 0, kSC1) : u32x2{0, kv_tag};
+      else vv[tt] = (tt <= p) ? ld16c(rv, vo(tt)) : u32x4{0, kv_tag, 0, kv_tag};
     }
-    // scores
+    ll_poll<NQ>(pl, rq, qo, qv, q_tag, true);
+    ll_poll<NQ>(pl, rk, ko, kv, kv_tag, true);
+    if constexpr (BF) ll_poll1<16>(pl, rv, vo, vw, kv_tag, true);
+    else ll_poll<16>(pl, rv, vo, vv, kv_tag, true);
+    if (!issued) {
+      nx.issue(pl);
+      issued = true;
+    }
     float dot = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < nchunk)
+    for (int i = 0; i < NQ; ++i)
+      if (i < nld) {
+        const u32x4 qp = {qv[i][0], qv[i][2], 0, 0}, kp = {kv[i][0], kv[i][2], 0, 0};
 #pragma unroll
-        for (int e = 0; e < 16 / ESZ; ++e) dot += chunk_elem<BF>(qv[i], e) * chunk_elem<BF>(kv[i], e);
+        for (int e = 0; e < 8 / ESZ; ++e) dot += chunk_elem<BF>(qp, e) * chunk_elem<BF>(kp, e);
+      }
     dot += shfl_xor_f(dot, 1);
     dot += shfl_xor_f(dot, 2);
     const float s = (t <= p) ? dot * pl.attn_scale : -INFINITY;
@@ -684,48 +736,63 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     const float w = e / sum;
     // output: sum over t in ascending order
     float o0 = 0.f, o1 = 0.f;
+    const int wsel = (lane * dpl) & 1;  // fp32, one dim per lane: which word of the pair
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
       const float wt = __shfl(w, tt * 4, 64);
       if (tt <= p) {
         if constexpr (BF) {
+          const uint32_t word = vw[tt][0];
           if (dpl == 2) {
-            o0 += wt * bf2f(vv[tt][0] & 0xffffu);
-            o1 += wt * bf2f(vv[tt][0] >> 16);
+            o0 += wt * bf2f(word & 0xffffu);
+            o1 += wt * bf2f(word >> 16);
           } else {
-            o0 += wt * bf2f(vv[tt][0] & 0xffffu);
+            o0 += wt * bf2f((lane & 1) ? (word >> 16) : (word & 0xffffu));
           }
         } else {
-          o0 += wt * __uint_as_float(vv[tt][0]);
-          if (dpl == 2) o1 += wt * __uint_as_float(vv[tt][1]);
+          if (dpl == 2) {
+            o0 += wt * __uint_as_float(vv[tt][0]);
+            o1 += wt * __uint_as_float(vv[tt][2]);
+          } else {
+            o0 += wt * __uint_as_float(vv[tt][wsel * 2]);
+          }
         }
       }
     }
-    const uint32_t ao = (uint32_t)(row * pl.nq * d + hq * d + dbase) * ESZ;
+    const uint32_t ao = (uint32_t)(row * pl.nq * d + hq * d + lane * dpl);
     if constexpr (BF) {
-      if (dpl == 2) st4c(ra, ao, pack_bf16(o0, o1));
-      else st2c(ra, ao, f2bf(o0));
+      if (dpl == 2) {
+        st8c(ra, ao * 4, u32x2{pack_bf16(o0, o1), my_tag});
+      } else {
+        // two lanes share a word: the even lane writes both dims
+        const float o_nb = __shfl_xor(o0, 1, 64);
+        if ((lane & 1) == 0) st8c(ra, ao * 4, u32x2{pack_bf16(o0, o_nb), my_tag});
+      }
     } else {
-      if (dpl == 2) st8c(ra, ao, u32x2{__float_as_uint(o0), __float_as_uint(o1)});
-      else st4c(ra, ao, __float_as_uint(o0));
+      if (dpl == 2) st16c(ra, ao * 8, ll_pair(__float_as_uint(o0), __float_as_uint(o1), my_tag));
+      else st8c(ra, ao * 8, u32x2{__float_as_uint(o0), my_tag});
     }
   }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
+  if (!issued) nx.issue(pl);
+  stamp(tr, 5);
 }
 
 // ------------------------------------------------------------------ draw + embed
 
 // Writes embedding row `code` of table j as the input of position j + 1 (when
-// there is one) and adds it to the row's fp32 embedding sum.
+// there is one, tagged, with its sum-of-squares partials) and adds it to the
+// row's fp32 embedding sum.  All draws of a row run in one workgroup, so the
+// sum is carried in program order with ordinary loads and stores.
 template <int BF>
-__device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr, int j, int row, int code, bool first) {
+__device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr, int j, int row, int code,
+                                          bool first, uint32_t my_tag) {
   constexpr int ESZ = BF ? 2 : 4;
   const int H = pl.H, V = pl.V;
   const rsrc_t re = make_rsrc(pl.embed, (uint32_t)pl.P * V * H * ESZ);
   const rsrc_t rs = make_rsrc(fr.embsum, (uint32_t)fr.rows * H * 4);
-  const rsrc_t rx = make_rsrc(pl.xin, (uint32_t)pl.P * pl.Rmax * H * ESZ);
+  const uint32_t hbytes = (uint32_t)pl.Rmax * H * ESZ * 2;
+  const rsrc_t rx = make_rsrc((uint8_t*)pl.xin + (size_t)(j + 1) * hbytes, hbytes);
   const uint32_t ebase = (uint32_t)((j * V + code) * H);
-  const uint32_t xbase = (uint32_t)(((j + 1) * pl.Rmax + row) * H);
   const bool feeds = j + 1 < pl.P;  // the row is the input of position j + 1
   // thread t covers elements 4t .. 4t+3: four threads per 16-column tile
   for (int k = threadIdx.x * 4; k < ((H + 1023) / 1024) * 1024; k += kThreads * 4) {
@@ -734,55 +801,71 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
     u32x4 sv = {0, 0, 0, 0};
     if (in) {
       if constexpr (BF) {
-        const u32x2 e = __builtin_amdgcn_raw_buffer_load_b64(re, (ebase + k) * 2, 0, 0);
+        const u32x2 e = ld8(re, (ebase + k) * 2);
         ev[0] = bf2f(e[0] & 0xffffu); ev[1] = bf2f(e[0] >> 16); ev[2] = bf2f(e[1] & 0xffffu); ev[3] = bf2f(e[1] >> 16);
-        if (feeds) st8c(rx, (xbase + k) * 2, e);
       } else {
         const u32x4 e = ld16(re, (ebase + k) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ev[i] = __uint_as_float(e[i]);
-        if (feeds) st16c(rx, (xbase + k) * 4, e);
       }
-      if (!first) sv = ld16c(rs, (uint32_t)(row * H + k) * 4);
+      if (!first) sv = ld16(rs, (uint32_t)(row * H + k) * 4);
+      if (feeds) st_act4<BF>(rx, (uint32_t)(row * H + k) * ESZ * 2, ev, my_tag);
     }
     const float sq = tile_ssq(ev, 1, 4);
     if (in) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(first ? ev[i] : __uint_as_float(sv[i]) + ev[i]);
-      st16c(rs, (uint32_t)(row * H + k) * 4, sv);
+      st16(rs, (uint32_t)(row * H + k) * 4, sv);
       if (feeds && (threadIdx.x & 3) == 0)
-        st4c(make_rsrc(ssq_slot(pl, j + 1), (uint32_t)pl.Rmax * (H / 16) * 4), (uint32_t)(row * (H / 16) + k / 16) * 4,
-             __float_as_uint(sq));
+        st8c(make_rsrc(ssq_slot(pl, j + 1), (uint32_t)pl.Rmax * (H / 16) * 8), (uint32_t)(row * (H / 16) + k / 16) * 8,
+             u32x2{__float_as_uint(sq), my_tag});
     }
   }
 }
 
 template <int BF>
-__device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, bool persistent,
-                                            uint64_t* tr) {
+__device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
+                                            const Next& nx, uint64_t* tr) {
+  nx.issue(pl);
   const int row = (int)tk.tile;
   if (row < fr.rows) {
     int code = fr.code0[row];
     code = code < 0 ? 0 : (code >= pl.V ? pl.V - 1 : code);
-    embed_row<BF>(pl, fr, 0, row, code, true);
+    embed_row<BF>(pl, fr, 0, row, code, true, tag_of(epoch, tk.phase));
   }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
+  stamp(tr, 5);
 }
 
 template <int BF>
-__device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t* misc,
-                                          bool persistent, uint64_t* tr) {
+__device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
+                                          uint32_t* misc, const Next& nx, uint64_t* tr) {
   const int row = (int)tk.tile, p = tk.pos;
+  const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
   if (row < fr.rows) {
     if (threadIdx.x < 64) {
+      // the head tiles' (value, index) candidates of this row, tile order
       const int lane = threadIdx.x;
-      const rsrc_t rc = make_rsrc(pl.cand, (uint32_t)pl.Rmax * pl.n_head_tiles * 8);
+      const rsrc_t rc = make_rsrc(pl.cand, (uint32_t)pl.Rmax * pl.n_head_tiles * 16);
       float bv = -INFINITY;
       uint32_t bi = 0xffffffffu;
-      for (int i = lane; i < pl.n_head_tiles; i += 64) {
-        const u32x2 cv = ld8c(rc, (uint32_t)(row * pl.n_head_tiles + i) * 8);
-        const float v = __uint_as_float(cv[0]);
-        if (beats(v, cv[1], bv, bi)) { bv = v; bi = cv[1]; }
+      for (int i0 = 0; i0 < pl.n_head_tiles; i0 += 64 * 4) {
+        u32x4 cv[4];
+        const uint32_t cbase = (uint32_t)(row * pl.n_head_tiles + i0 + lane) * 16;
+        auto co = [=](int k) { return cbase + k * 64 * 16; };
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + k * 64 + lane;
+          cv[k] = i < pl.n_head_tiles ? ld16c(rc, co(k)) : u32x4{0, in_tag, 0xffffffffu, in_tag};
+        }
+        ll_poll<4>(pl, rc, co, cv, in_tag, true);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = i0 + k * 64 + lane;
+          if (i < pl.n_head_tiles && beats(__uint_as_float(cv[k][0]), cv[k][2], bv, bi)) {
+            bv = __uint_as_float(cv[k][0]);
+            bi = cv[k][2];
+          }
+        }
       }
 #pragma unroll
       for (int m = 1; m <= 32; m <<= 1) {
@@ -792,25 +875,61 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
       }
       if (lane == 0) {
         misc[1] = bi < (uint32_t)pl.V ? bi : 0u;
-        st4c(make_rsrc(fr.codes, (uint32_t)fr.rows * (pl.P - 1) * 4), (uint32_t)(row * (pl.P - 1) + p - 1) * 4, misc[1]);
+        st4(make_rsrc(fr.codes, (uint32_t)fr.rows * (pl.P - 1) * 4), (uint32_t)(row * (pl.P - 1) + p - 1) * 4, misc[1]);
       }
     }
     __syncthreads();
-    embed_row<BF>(pl, fr, p, row, (int)misc[1], false);
+    nx.issue(pl);
+    embed_row<BF>(pl, fr, p, row, (int)misc[1], false, tag_of(epoch, tk.phase));
+  } else {
+    nx.issue(pl);
   }
-  signal_group(pl, tk.sig, tk.sig_slot, persistent, tr);
+  stamp(tr, 5);
 }
 
 // ------------------------------------------------------------------ executors
 
 template <int BF>
-__device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const Task& tk, uint32_t epoch,
-                                         uint8_t* slot, uint32_t* misc, bool persistent, uint64_t* tr) {
+__device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
+                                         uint8_t* slot, uint8_t* gain, uint32_t* misc, const Next& nx, uint64_t* tr) {
   switch (tk.type) {
-    case T_ATTN: attn_task<BF>(pl, fr, tk, persistent, tr); break;
-    case T_EMBED0: embed0_task<BF>(pl, fr, tk, persistent, tr); break;
-    case T_DRAW: draw_task<BF>(pl, fr, tk, misc, persistent, tr); break;
-    default: proj_task<BF>(pl, fr, tk, epoch, slot, misc, persistent, tr); break;
+    case T_ATTN: attn_task<BF>(pl, fr, tk, epoch, nx, tr); break;
+    case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, nx, tr); break;
+    case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, misc, nx, tr); break;
+    default: proj_task<BF>(pl, fr, tk, epoch, slot, gain, misc, nx, tr); break;
+  }
+}
+
+// Clears every tagged buffer; one whole workgroup.
+__device__ __forceinline__ void clear_tagged(const DevPlan& pl) {
+#pragma unroll
+  for (int b = 0; b < kMaxClear; ++b) {
+    if (b >= pl.n_clear) break;
+    const uint64_t words = pl.clear[b].bytes / 8;
+    uint64_t* w = (uint64_t*)pl.clear[b].p;
+    for (uint64_t i = threadIdx.x; i < words; i += kThreads)
+      __hip_atomic_store(w + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wait_vm();
+  __syncthreads();
+}
+
+// Moves the plan to the next frame's epoch.  Run by one whole workgroup once
+// every task of the frame has finished.  When the next epoch would leave the
+// tag space, every tagged buffer is cleared (a few milliseconds, once every
+// four million frames) and the count restarts at 1, so no stale word can carry
+// a tag a later frame expects.  With `defer` the clear is left to
+// clear_pending_kernel, which runs after the frame's K/V have been copied out.
+__device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch, bool defer) {
+  if (epoch + 1 < kEpochWrap) {
+    if (threadIdx.x == 0) __hip_atomic_store(pl.state, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (!defer) clear_tagged(pl);
+  if (threadIdx.x == 0) {
+    if (defer) __hip_atomic_store(pl.state + 96, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(pl.state + 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(pl.state, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -818,40 +937,72 @@ template <int BF>
 __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
-  const uint32_t epoch = ld_ctr(pl.state);
+  const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t b = pl.wg_begin[blockIdx.x], e = pl.wg_begin[blockIdx.x + 1];
+  uint8_t* gains = (uint8_t*)misc + kGainLds;
+  DevTask cur = {};
+  if (b < e) {
+    cur = pl.tasks[b];
+    issue_tile(pl, cur, lds, gains);
+  }
   for (uint32_t i = b; i < e; ++i) {
-    const Task tk = pl.tasks[i];
     uint64_t* tr = pl.trace_on ? pl.trace + (size_t)i * kTraceStamps : nullptr;
     stamp(tr, 0);
-    uint8_t* slot = lds + ((i - b) & 1) * kSlotBytes;
-    issue_tile(pl, tk, slot, (uint8_t*)misc);  // lands while the workgroup waits
-    wait_deps(pl, tk, epoch);
-    stamp(tr, 1);
-    run_task<BF>(pl, fr, tk, epoch, slot, misc, true, tr);
+    const int s = (i - b) & 1;
+    // the next record is fetched now; it is first needed in this task's epilogue
+    const bool more = i + 1 < e;
+    const DevTask nxt = more ? pl.tasks[i + 1] : DevTask{};
+    const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes, gains + (s ^ 1) * 2048};
+    run_task<BF>(pl, fr, cur, epoch, lds + s * kSlotBytes, gains + s * 2048, misc, nx, tr);
+    __syncthreads();  // LDS (tile slot, gains, reductions) of this task is free again
+    stamp(tr, 7);
+    cur = nxt;
   }
   // The last workgroup to finish moves the plan to the next frame.
+  wait_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t old = __hip_atomic_fetch_add(pl.state + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint32_t)pl.n_wg * epoch - 1)
-      __hip_atomic_store(pl.state, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    misc[0] = old == (uint32_t)pl.n_wg * epoch - 1;
   }
+  __syncthreads();
+  if (misc[0]) advance_epoch(pl, epoch, fr.defer_clear);
 }
 
 template <int BF>
-__global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame fr, const Task* tasks) {
+__global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame fr, const DevTask* tasks) {
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
-  const uint32_t epoch = ld_ctr(pl.state);
-  const Task tk = tasks[blockIdx.x];
-  issue_tile(pl, tk, lds, (uint8_t*)misc);
-  run_task<BF>(pl, fr, tk, epoch, lds, misc, false, nullptr);
+  const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const DevTask tk = tasks[blockIdx.x];
+  uint8_t* gains = (uint8_t*)misc + kGainLds;
+  issue_tile(pl, tk, lds, gains);
+  const Next nx = {DevTask{}, false, nullptr, nullptr};
+  run_task<BF>(pl, fr, tk, epoch, lds, gains, misc, nx, nullptr);
 }
 
-__global__ void bump_epoch_kernel(uint32_t* state) {
-  const uint32_t e = ld_ctr(state);
-  __hip_atomic_store(state, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The per-phase executor's last launch of a frame.
+__global__ __launch_bounds__(kThreads, 1) void bump_epoch_kernel(DevPlan pl, int defer) {
+  advance_epoch(pl, __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), defer != 0);
+}
+
+// The clear a wrapping frame deferred (state[96] set), after its K/V copy.
+__global__ __launch_bounds__(kThreads, 1) void clear_pending_kernel(DevPlan pl) {
+  if (__hip_atomic_load(pl.state + 96, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
+  clear_tagged(pl);
+  if (threadIdx.x == 0) __hip_atomic_store(pl.state + 96, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copies the payload of tagged K/V words (bf16 pairs or fp32) out of the
+// plan's cache into the caller's untagged layout: rows [0, rows) of every layer.
+__global__ void unpack_kv_kernel(const uint64_t* src, uint32_t* dst, uint32_t words_per_row, uint32_t rows,
+                                 uint32_t rmax, uint32_t layers) {
+  const uint64_t per_layer = (uint64_t)rows * words_per_row;
+  const uint64_t n = (uint64_t)layers * per_layer;
+  for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
+    const uint64_t l = i / per_layer, rem = i % per_layer;
+    dst[i] = (uint32_t)src[l * rmax * words_per_row + rem];
+  }
 }
 
 }  // namespace cpms
@@ -859,10 +1010,6 @@ __global__ void bump_epoch_kernel(uint32_t* state) {
 // ------------------------------------------------------------------ host-side launchers
 
 namespace cpms {
-
-const void* persistent_kernel_ptr(int bf16) {
-  return bf16 ? (const void*)persistent_kernel<1> : (const void*)persistent_kernel<0>;
-}
 
 hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s) {
   if (pl.bf16)
@@ -872,7 +1019,7 @@ hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const Task* tasks, int n, hipStream_t s) {
+hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const DevTask* tasks, int n, hipStream_t s) {
   if (pl.bf16)
     hipLaunchKernelGGL(phase_kernel<1>, dim3(n), dim3(kThreads), kLdsBytes, s, pl, fr, tasks);
   else
@@ -880,8 +1027,20 @@ hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const Task* tasks
   return hipGetLastError();
 }
 
-hipError_t launch_bump_epoch(uint32_t* state, hipStream_t s) {
-  hipLaunchKernelGGL(bump_epoch_kernel, dim3(1), dim3(1), 0, s, state);
+hipError_t launch_bump_epoch(const DevPlan& pl, int defer_clear, hipStream_t s) {
+  hipLaunchKernelGGL(bump_epoch_kernel, dim3(1), dim3(kThreads), 0, s, pl, defer_clear);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_pending(const DevPlan& pl, hipStream_t s) {
+  hipLaunchKernelGGL(clear_pending_kernel, dim3(1), dim3(kThreads), 0, s, pl);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, uint32_t rows, uint32_t rmax,
+                            uint32_t layers, hipStream_t s) {
+  hipLaunchKernelGGL(unpack_kv_kernel, dim3(256), dim3(256), 0, s, (const uint64_t*)src, (uint32_t*)dst,
+                     words_per_row, rows, rmax, layers);
   return hipGetLastError();
 }
 

@@ -25,10 +25,12 @@
 #include "cp_device.h"
 
 namespace cpms {
-const void* persistent_kernel_ptr(int bf16);
 hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s);
-hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const Task* tasks, int n, hipStream_t s);
-hipError_t launch_bump_epoch(uint32_t* state, hipStream_t s);
+hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const DevTask* tasks, int n, hipStream_t s);
+hipError_t launch_bump_epoch(const DevPlan& pl, int defer_clear, hipStream_t s);
+hipError_t launch_clear_pending(const DevPlan& pl, hipStream_t s);
+hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, uint32_t rows, uint32_t rmax,
+                            uint32_t layers, hipStream_t s);
 hipError_t set_kernel_attributes();
 int occupancy_per_cu(int bf16);
 }  // namespace cpms
@@ -48,7 +50,7 @@ struct cp_plan {
   uint32_t n_ctr = 0;
   int n_phases = 0;
   int max_tasks_wg = 0;
-  Task* d_phase_tasks = nullptr;
+  DevTask* d_phase_tasks = nullptr;
   std::vector<void*> allocs;
   int64_t packed_bytes = 0, scratch_bytes = 0, weight_bytes_frame = 0;
   std::string err;
@@ -106,10 +108,11 @@ struct Builder {
   uint32_t counter() { return next_ctr++; }
 
   // Appends one phase; wg_of maps a task's index in the phase to a workgroup.
+  int next_phase() const { return (int)per_phase.size(); }
   void phase(std::vector<Task> ts, const std::vector<int>& wg_of) {
     const uint32_t ph = (uint32_t)per_phase.size();
     for (size_t i = 0; i < ts.size(); ++i) {
-      ts[i].phase = ph;
+      ts[i].phase = (uint16_t)ph;
       per_wg[wg_of[i] % n_wg].push_back(ts[i]);
     }
     per_phase.push_back(std::move(ts));
@@ -124,12 +127,13 @@ Task make_task(uint8_t type, int l, int p, uint32_t tile) {
   t.tile = tile;
   t.nsplit = 1;
   t.sig = kNone;
-  t.tctr = kNone;
   for (auto& w : t.wait) w = kNone;
   return t;
 }
 
-void add_wait(Task& t, uint32_t g) { t.wait[t.nwait++] = g; }
+void add_wait(Task& t, uint32_t g) {
+  if (t.nwait < (uint32_t)kMaxWaits) t.wait[t.nwait++] = g;
+}
 
 // Spreads n tasks over the workgroups starting at a rotating offset.
 std::vector<int> spread(int n, int n_wg, int& rot) {
@@ -257,21 +261,29 @@ static cp_status build_schedule(cp_plan* P) {
   const int kv_per_osplit = nkv / ns_o;  // kv heads whose attention output one o split reads
   int rot = 0;
 
-  // input projection (split-K) and code-0 embedding: no waits
+  // Every task records the phases whose outputs it reads (ph_in0, ph_in1):
+  // its input words must carry those phases' tags.  The counter groups below
+  // describe the same dependencies for the host validator.
+  // Draws (and the code-0 embedding) of a row always run in one workgroup,
+  // which carries the row's embedding sum in program order.
+  std::vector<int> row_wg(R);
+  for (int r = 0; r < R; ++r) row_wg[r] = r % n_wg;
+
+  // input projection (split-K) and code-0 embedding: no inputs from the frame
   const uint32_t g_inp = B.group(ht);
+  const int ph_inp = B.next_phase();
   {
     std::vector<Task> ts;
-    for (int t = 0; t < ht; ++t) {
-      const uint32_t tc = ns_in > 1 ? B.counter() : kNone;
+    for (int t = 0; t < ht; ++t)
       for (int s = 0; s < ns_in; ++s) {
         Task k = make_task(T_INPROJ, 0, 0, t);
-        k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_in; k.tctr = tc; k.sig = g_inp; k.sig_slot = t;
+        k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_in; k.sig = g_inp; k.sig_slot = t;
         ts.push_back(k);
       }
-    }
     B.phase(ts, split_map(ht, ns_in, n_wg, rot));
   }
   const uint32_t g_emb0 = B.group(R);
+  const int ph_emb0 = B.next_phase();
   {
     std::vector<Task> ts;
     for (int r = 0; r < R; ++r) {
@@ -279,22 +291,26 @@ static cp_status build_schedule(cp_plan* P) {
       k.sig = g_emb0; k.sig_slot = r;
       ts.push_back(k);
     }
-    B.phase(ts, spread(R, n_wg, rot));
+    B.phase(ts, row_wg);
   }
 
   std::vector<std::vector<uint32_t>> g_qkv(Pn * L);  // [p * L + l][g]
   uint32_t g_prev_draw = kNone;
+  int ph_prev_draw = -1;
   for (int p = 0; p < Pn; ++p) {
     uint32_t g_layer_in = (p == 0) ? g_inp : (p == 1 ? g_emb0 : g_prev_draw);
+    int ph_layer_in = (p == 0) ? ph_inp : (p == 1 ? ph_emb0 : ph_prev_draw);
     for (int l = 0; l < L; ++l) {
       // qkv
       std::vector<uint32_t>& gq_groups = g_qkv[p * L + l];
       for (int g = 0; g < nkv; ++g) gq_groups.push_back(B.group(tpg, 4));
+      const int ph_qkv = B.next_phase();
       {
         std::vector<Task> ts;
         for (int t = 0; t < qkv_tiles; ++t) {
           Task k = make_task(T_QKV, l, p, t);
           add_wait(k, g_layer_in);
+          k.ph_in0 = (uint16_t)ph_layer_in;
           k.sig = gq_groups[t / tpg]; k.sig_slot = t % tpg;
           ts.push_back(k);
         }
@@ -303,9 +319,10 @@ static cp_status build_schedule(cp_plan* P) {
       // Position 0 has no head: the residual after its last layer feeds
       // nothing, so only the last layer's qkv (its K/V) is computed there.
       if (p == 0 && l == L - 1) break;
-      // attention, per kv head; it signals the group of the o split that reads it
+      // attention, per kv head; it completes the group of the o split that reads it
       std::vector<uint32_t> g_att(ns_o);
       for (int s = 0; s < ns_o; ++s) g_att[s] = B.group(kv_per_osplit * agroups);
+      const int ph_att = B.next_phase();
       {
         std::vector<Task> ts;
         for (int g = 0; g < nkv; ++g)
@@ -313,85 +330,98 @@ static cp_status build_schedule(cp_plan* P) {
             Task k = make_task(T_ATTN, l, p, g * agroups + rg);
             add_wait(k, gq_groups[g]);
             if (p == 1) add_wait(k, g_qkv[0 * L + l][g]);  // position 0's K/V of this layer
+            k.ph_in0 = (uint16_t)ph_qkv;
             k.sig = g_att[g / kv_per_osplit]; k.sig_slot = (g % kv_per_osplit) * agroups + rg;
             ts.push_back(k);
           }
         B.phase(ts, spread(nkv * agroups, n_wg, rot));
       }
-      // o (split-K over q heads; a split waits only on the kv heads it reads)
+      // o (split-K over q heads; a split reads only the kv heads of its slice)
       const uint32_t g_o = B.group(ht);
+      const int ph_o = B.next_phase();
       {
         std::vector<Task> ts;
-        for (int t = 0; t < ht; ++t) {
-          const uint32_t tc = ns_o > 1 ? B.counter() : kNone;
+        for (int t = 0; t < ht; ++t)
           for (int s = 0; s < ns_o; ++s) {
             Task k = make_task(T_O, l, p, t);
-            k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_o; k.tctr = tc; k.sig = g_o; k.sig_slot = t;
+            k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_o; k.sig = g_o; k.sig_slot = t;
+            k.ph_in0 = (uint16_t)ph_att;
+            k.ph_in1 = (uint16_t)ph_layer_in;
             add_wait(k, g_att[s]);
+            add_wait(k, g_layer_in);  // the residual
             ts.push_back(k);
           }
-        }
         B.phase(ts, split_map(ht, ns_o, n_wg, rot));
       }
       // gate/up
       std::vector<uint32_t> g_gu(ns_d);
       for (int s = 0; s < ns_d; ++s) g_gu[s] = B.group(gu_per_split, 4);
+      const int ph_gu = B.next_phase();
       {
         std::vector<Task> ts;
         for (int t = 0; t < gu_tiles; ++t) {
           Task k = make_task(T_GU, l, p, t);
           add_wait(k, g_o);
+          k.ph_in0 = (uint16_t)ph_o;
           k.sig = g_gu[t / gu_per_split]; k.sig_slot = t % gu_per_split;
           ts.push_back(k);
         }
         B.phase(ts, spread(gu_tiles, n_wg, rot));
       }
-      // down (split-K over the intermediate; a split waits on the gate/up
-      // tiles of its slice)
+      // down (split-K over the intermediate; a split reads the gate/up tiles of its slice)
       const uint32_t g_down = B.group(ht);
+      const int ph_down = B.next_phase();
       {
         std::vector<Task> ts;
-        for (int t = 0; t < ht; ++t) {
-          const uint32_t tc = ns_d > 1 ? B.counter() : kNone;
+        for (int t = 0; t < ht; ++t)
           for (int s = 0; s < ns_d; ++s) {
             Task k = make_task(T_DOWN, l, p, t);
-            k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_d; k.tctr = tc; k.sig = g_down; k.sig_slot = t;
+            k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_d; k.sig = g_down; k.sig_slot = t;
+            k.ph_in0 = (uint16_t)ph_gu;
+            k.ph_in1 = (uint16_t)ph_o;
             add_wait(k, g_gu[s]);
+            add_wait(k, g_o);  // the residual
             ts.push_back(k);
           }
-        }
         B.phase(ts, split_map(ht, ns_d, n_wg, rot));
       }
       g_layer_in = g_down;
+      ph_layer_in = ph_down;
     }
     if (p == 0) continue;
     // head p and draw p
     const uint32_t g_head = B.group(head_tiles);
+    const int ph_head = B.next_phase();
     {
       std::vector<Task> ts;
       for (int t = 0; t < head_tiles; ++t) {
         Task k = make_task(T_HEAD, L - 1, p, t);
         add_wait(k, g_layer_in);
+        k.ph_in0 = (uint16_t)ph_layer_in;
         k.sig = g_head; k.sig_slot = t;
         ts.push_back(k);
       }
       B.phase(ts, spread(head_tiles, n_wg, rot));
     }
     const uint32_t g_draw = B.group(R);
+    const int ph_draw = B.next_phase();
     {
       std::vector<Task> ts;
       for (int r = 0; r < R; ++r) {
         Task k = make_task(T_DRAW, L - 1, p, r);
         add_wait(k, g_head);
+        k.ph_in0 = (uint16_t)ph_head;
         k.sig = g_draw; k.sig_slot = r;
         ts.push_back(k);
       }
-      B.phase(ts, spread(R, n_wg, rot));
+      B.phase(ts, row_wg);
     }
     g_prev_draw = g_draw;
+    ph_prev_draw = ph_draw;
   }
+  if (B.next_phase() > kMaxPhases) return fail(P, CP_ERR_UNSUPPORTED, "too many phases for the tag space");
 
-  P->n_ctr = B.next_ctr;
+  P->n_ctr = B.next_ctr;  // counters of the validator's dependency model (not allocated)
   P->n_phases = (int)B.per_phase.size();
   P->tasks.clear();
   P->wg_begin.assign(1, 0);
@@ -434,14 +464,16 @@ static cp_status check_schedule(cp_plan* P) {
     }
     if (t.w_bytes > (uint32_t)kSlotBytes || t.w_bytes % 1024) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: weight tile too large");
     if ((int64_t)t.w_off + t.w_bytes > P->packed_bytes) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: tile outside blob");
-    if (t.tctr != kNone && t.tctr >= P->n_ctr) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: bad tile counter");
+    if (t.type != T_INPROJ && t.type != T_EMBED0 && t.ph_in0 >= t.phase)
+      return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: input from a later phase");
+    if ((t.type == T_O || t.type == T_DOWN) && t.ph_in1 >= t.phase)
+      return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: residual from a later phase");
   }
   for (size_t g = 0; g < ng; ++g) {
     const CtrGroup& G = P->groups[g];
     if (count[g] != (int64_t)G.nsub * G.per_sub) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: group count mismatch");
     for (int s = 0; s < G.nsub; ++s)
       if (slot_count[g][s] != G.per_sub) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: sub-counter count mismatch");
-    if (G.base + G.nsub > P->n_ctr) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: counter out of range");
   }
   for (const Task& t : P->phase_tasks)
     for (int k = 0; k < t.nwait; ++k) {
@@ -451,6 +483,21 @@ static cp_status check_schedule(cp_plan* P) {
   for (size_t w = 0; w + 1 < P->wg_begin.size(); ++w)
     for (uint32_t i = P->wg_begin[w] + 1; i < P->wg_begin[w + 1]; ++i)
       if (P->tasks[i].phase < P->tasks[i - 1].phase) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: list out of order");
+  // A split-K owner waits for its partners in the same phase: no partner may
+  // sit later in the owner's own list, and a phase with partners must fit the
+  // grid (the per-phase executor runs it as one co-resident launch).
+  for (size_t w = 0; w + 1 < P->wg_begin.size(); ++w)
+    for (uint32_t i = P->wg_begin[w]; i < P->wg_begin[w + 1]; ++i) {
+      const Task& a = P->tasks[i];
+      if (a.nsplit > 1 && a.split == 0)
+        for (uint32_t j = i + 1; j < P->wg_begin[w + 1] && P->tasks[j].phase == a.phase; ++j)
+          if (P->tasks[j].tile == a.tile) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: split partner after its owner");
+    }
+  for (size_t ph = 0; ph + 1 < P->phase_begin.size() && P->cfg.exec == CP_EXEC_PER_PHASE; ++ph) {
+    const Task& f = P->phase_tasks[P->phase_begin[ph]];
+    if (f.nsplit > 1 && (int)(P->phase_begin[ph + 1] - P->phase_begin[ph]) > P->cu_count)
+      return fail(P, CP_ERR_UNSUPPORTED, "schedule: split phase larger than the grid");
+  }
   return CP_OK;
 }
 
@@ -463,8 +510,12 @@ static cp_status fetch(cp_plan* P, const void* dptr, size_t bytes, std::vector<u
   return CP_OK;
 }
 
-static cp_status alloc(cp_plan* P, void** p, size_t bytes) {
+// Device allocation, zero-filled: memory a previous plan freed may still hold
+// tagged words that a frame of this plan would otherwise accept.  Tagged
+// buffers are also recorded for the clear at the epoch wrap.
+static cp_status alloc(cp_plan* P, void** p, size_t bytes, bool tagged = false) {
   if (bytes == 0) bytes = 256;
+  bytes = (bytes + 15) & ~(size_t)15;
   hipError_t e = hipMalloc(p, bytes);
   if (e != hipSuccess) {
     P->err = std::string("hipMalloc: ") + hipGetErrorString(e);
@@ -472,6 +523,11 @@ static cp_status alloc(cp_plan* P, void** p, size_t bytes) {
   }
   P->allocs.push_back(*p);
   P->scratch_bytes += (int64_t)bytes;
+  HIPCHK(P, hipMemset(*p, 0, bytes));
+  if (tagged) {
+    if (P->dp.n_clear >= kMaxClear) return fail(P, CP_ERR_INVALID_ARGUMENT, "too many tagged buffers");
+    P->dp.clear[P->dp.n_clear++] = Span{*p, (uint64_t)bytes};
+  }
   return CP_OK;
 }
 
@@ -629,6 +685,19 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
   return CP_OK;
 }
 
+// Device records of host tasks (fields the kernels read; every value fits).
+static std::vector<DevTask> to_dev(const std::vector<Task>& ts) {
+  std::vector<DevTask> out(ts.size());
+  for (size_t i = 0; i < ts.size(); ++i) {
+    const Task& t = ts[i];
+    DevTask& d = out[i];
+    d.type = t.type; d.split = t.split; d.nsplit = t.nsplit; d.pad0 = 0;
+    d.layer = t.layer; d.pos = t.pos; d.tile = (uint16_t)t.tile; d.phase = t.phase;
+    d.ph_in0 = t.ph_in0; d.ph_in1 = t.ph_in1; d.w_off = t.w_off; d.w_bytes = t.w_bytes;
+  }
+  return out;
+}
+
 static cp_status alloc_scratch(cp_plan* P) {
   const cp_config& c = P->cfg;
   const int L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, d = c.head_dim;
@@ -636,42 +705,40 @@ static cp_status alloc_scratch(cp_plan* P) {
   const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
   DevPlan& dp = P->dp;
   void* p;
-  TRY(alloc(P, &p, (size_t)Pn * R * H * esz)); dp.xin = p;
-  TRY(alloc(P, &p, (size_t)2 * 2 * R * H * esz)); dp.hres = p;     // [parity][layer parity]
-  TRY(alloc(P, &p, (size_t)2 * R * H * esz)); dp.hmid = p;
-  TRY(alloc(P, &p, (size_t)2 * R * nq * d * esz)); dp.qbuf = p;
-  TRY(alloc(P, &p, (size_t)2 * R * nq * d * esz)); dp.abuf = p;
-  TRY(alloc(P, &p, (size_t)2 * R * I * esz)); dp.mbuf = p;
-  TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * esz)); dp.kc = p;
-  TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * esz)); dp.vc = p;
-  const size_t part_one = (size_t)(H / 16) * 4 * R * 16;  // floats per split-K phase buffer
-  TRY(alloc(P, &p, part_one * 5 * 4)); dp.part = (float*)p;          // o[2], down[2], in
+  const size_t e2 = (size_t)esz * 2;  // tagged words: payload + tag per element pair (bf16) or element (fp32)
+  TRY(alloc(P, &p, (size_t)Pn * R * H * e2, true)); dp.xin = p;
+  TRY(alloc(P, &p, (size_t)2 * 2 * R * H * e2, true)); dp.hres = p;     // [parity][layer parity]
+  TRY(alloc(P, &p, (size_t)2 * R * H * e2, true)); dp.hmid = p;
+  TRY(alloc(P, &p, (size_t)2 * R * nq * d * e2, true)); dp.qbuf = p;
+  TRY(alloc(P, &p, (size_t)2 * R * nq * d * e2, true)); dp.abuf = p;
+  TRY(alloc(P, &p, (size_t)2 * R * I * e2, true)); dp.mbuf = p;
+  TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.kc = p;
+  TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.vc = p;
+  const size_t part_one = (size_t)(H / 16) * 4 * R * 16;  // words per split-K phase buffer
+  TRY(alloc(P, &p, part_one * 5 * 8, true)); dp.part = (uint64_t*)p;       // o[2], down[2], in
   dp.part_stride = part_one;
   dp.part_o_off = 0;
   dp.part_d_off = 2 * part_one;
   dp.part_in_off = 4 * part_one;
-  TRY(alloc(P, &p, (size_t)(Pn + 6) * R * (H / 16) * 4)); dp.ssq = (float*)p;
-  TRY(alloc(P, &p, (size_t)R * V * 4)); dp.zbuf = (float*)p;
-  TRY(alloc(P, &p, (size_t)R * (V / 16) * 8)); dp.cand = (uint2*)p;
-  TRY(alloc(P, &p, (size_t)P->n_ctr * kCtrStride * 4)); dp.ctr = (uint32_t*)p;
-  HIPCHK(P, hipMemset(dp.ctr, 0, (size_t)P->n_ctr * kCtrStride * 4));
+  TRY(alloc(P, &p, (size_t)(Pn + 6) * R * (H / 16) * 8, true)); dp.ssq = (uint32_t*)p;
+  TRY(alloc(P, &p, (size_t)R * V * 8, true)); dp.zbuf = (uint64_t*)p;
+  TRY(alloc(P, &p, (size_t)R * (V / 16) * 16, true)); dp.cand = (uint64_t*)p;
   TRY(alloc(P, &p, 128 * 4)); dp.state = (uint32_t*)p;
   std::vector<uint32_t> st(128, 0);
-  st[0] = 1;  // first frame is epoch 1
+  st[0] = 1;  // first frame is epoch 1; zeroed buffers carry tag 0, which no frame expects
   HIPCHK(P, hipMemcpy(dp.state, st.data(), st.size() * 4, hipMemcpyHostToDevice));
-  TRY(alloc(P, &p, P->tasks.size() * sizeof(Task))); dp.tasks = (const Task*)p;
-  HIPCHK(P, hipMemcpy(p, P->tasks.data(), P->tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
+  const std::vector<DevTask> dev_tasks = to_dev(P->tasks), dev_phase = to_dev(P->phase_tasks);
+  TRY(alloc(P, &p, dev_tasks.size() * sizeof(DevTask))); dp.tasks = (const DevTask*)p;
+  HIPCHK(P, hipMemcpy(p, dev_tasks.data(), dev_tasks.size() * sizeof(DevTask), hipMemcpyHostToDevice));
   TRY(alloc(P, &p, P->wg_begin.size() * 4)); dp.wg_begin = (const uint32_t*)p;
   HIPCHK(P, hipMemcpy(p, P->wg_begin.data(), P->wg_begin.size() * 4, hipMemcpyHostToDevice));
-  TRY(alloc(P, &p, P->phase_tasks.size() * sizeof(Task))); P->d_phase_tasks = (Task*)p;
-  HIPCHK(P, hipMemcpy(p, P->phase_tasks.data(), P->phase_tasks.size() * sizeof(Task), hipMemcpyHostToDevice));
+  TRY(alloc(P, &p, dev_phase.size() * sizeof(DevTask))); P->d_phase_tasks = (DevTask*)p;
+  HIPCHK(P, hipMemcpy(p, dev_phase.data(), dev_phase.size() * sizeof(DevTask), hipMemcpyHostToDevice));
   if (c.flags & CP_FLAG_TRACE) {
     TRY(alloc(P, &p, P->tasks.size() * kTraceStamps * 8)); dp.trace = (uint64_t*)p;
     HIPCHK(P, hipMemset(p, 0, P->tasks.size() * kTraceStamps * 8));
     dp.trace_on = 1;
   }
-  TRY(alloc(P, &p, P->groups.size() * sizeof(CtrGroup))); dp.groups = (const CtrGroup*)p;
-  HIPCHK(P, hipMemcpy(p, P->groups.data(), P->groups.size() * sizeof(CtrGroup), hipMemcpyHostToDevice));
   return CP_OK;
 }
 
@@ -824,6 +891,7 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
   DevFrame fr{};
   fr.rows = io->rows;
   fr.sampled = nsamp == 5;
+  fr.defer_clear = (io->k_cache || io->v_cache) ? 1 : 0;
   fr.hidden_in = io->hidden_in;
   fr.code0 = io->code0;
   fr.temperature = io->temperature;
@@ -847,20 +915,14 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
       const uint32_t b = P->phase_begin[ph], n = P->phase_begin[ph + 1] - b;
       e = launch_phase(P->dp, fr, P->d_phase_tasks + b, (int)n, s);
     }
-    if (e == hipSuccess) e = launch_bump_epoch(P->dp.state, s);
+    if (e == hipSuccess) e = launch_bump_epoch(P->dp, fr.defer_clear, s);
   }
   if (e == hipSuccess && (io->k_cache || io->v_cache)) {
     const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
-    const size_t per_row = (size_t)c.n_kv_heads * c.n_positions * c.head_dim * esz;
-    for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
-      const size_t src = (size_t)l * c.max_rows * per_row, dst = (size_t)l * io->rows * per_row;
-      if (io->k_cache)
-        e = hipMemcpyAsync((uint8_t*)io->k_cache + dst, (const uint8_t*)P->dp.kc + src, io->rows * per_row,
-                           hipMemcpyDeviceToDevice, s);
-      if (e == hipSuccess && io->v_cache)
-        e = hipMemcpyAsync((uint8_t*)io->v_cache + dst, (const uint8_t*)P->dp.vc + src, io->rows * per_row,
-                           hipMemcpyDeviceToDevice, s);
-    }
+    const uint32_t wpr = (uint32_t)((size_t)c.n_kv_heads * c.n_positions * c.head_dim * esz / 4);
+    if (io->k_cache) e = launch_unpack_kv(P->dp.kc, io->k_cache, wpr, io->rows, c.max_rows, c.n_layers, s);
+    if (e == hipSuccess && io->v_cache) e = launch_unpack_kv(P->dp.vc, io->v_cache, wpr, io->rows, c.max_rows, c.n_layers, s);
+    if (e == hipSuccess) e = launch_clear_pending(P->dp, s);
   }
   if (e == hipSuccess && io->trace)
     e = hipMemcpyAsync(io->trace, P->dp.trace, P->tasks.size() * kTraceStamps * 8, hipMemcpyDeviceToDevice, s);
@@ -878,6 +940,22 @@ cp_status cp_plan_task_table(const cp_plan* P, int32_t* out, int64_t n_tasks) {
       o[0] = (int32_t)t.phase; o[1] = t.type; o[2] = t.layer; o[3] = t.pos;
       o[4] = (int32_t)t.tile; o[5] = t.split; o[6] = (int32_t)w; o[7] = (int32_t)(i - P->wg_begin[w]);
     }
+  return CP_OK;
+}
+
+cp_status cp_plan_set_epoch(cp_plan* P, uint32_t epoch) {
+  if (!P) return CP_ERR_INVALID_ARGUMENT;
+  if (epoch < 1 || epoch >= kEpochWrap) return fail(P, CP_ERR_INVALID_ARGUMENT, "epoch out of range");
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(P->device);
+  // [0] epoch; [32] the persistent executor's done count, n_wg per finished frame
+  const uint32_t st[2] = {epoch, (uint32_t)P->dp.n_wg * (epoch - 1)};
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(P->dp.state, &st[0], 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(P->dp.state + 32, &st[1], 4, hipMemcpyHostToDevice);
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("set epoch: ") + hipGetErrorString(e));
   return CP_OK;
 }
 

@@ -42,6 +42,7 @@ def test_status_strings_and_null_arguments():
     assert lib.cp_plan_create(C.byref(c), None, 0, C.byref(h)) == 1 and not h.value
     assert lib.cp_plan_destroy(None) == 0
     assert lib.cp_frame_run(None, None, None) == 1
+    assert lib.cp_plan_set_epoch(None, 1) == 1
 
 
 @pytest.mark.parametrize("change,status", [

@@ -146,3 +146,43 @@ def test_l10_hbm_variant(rows):
     inputs = synth.make_inputs(cfg)
     gpu = _gpu_frame(cfg, wdev, inputs, max_rows=64)
     _check(cfg, ow, inputs, gpu, sorted({0, rows - 1}), 0.05)
+
+
+def test_new_plan_on_reused_memory():
+    """A plan created where a destroyed plan's buffers were must not accept
+    the old frame's tagged words: every plan starts at epoch 1, so its
+    buffers are cleared at creation."""
+    cp = _cp()
+    cfg = synth.CONFIGS["tiny_f32"].with_(rows=5, dtype="bf16")
+    w, wdev, ow = _weights(cfg, seed=4)
+    for seed in (11, 12, 13):
+        inputs = synth.make_inputs(cfg, seed=seed)
+        gpu = _gpu_frame(cfg, wdev, inputs, max_rows=5, kv=True)  # creates and destroys a plan
+        _check(cfg, ow, inputs, gpu, range(5), 0.05, kv=True)
+
+
+@pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
+def test_epoch_wrap(exec_mode):
+    """Frames at the last two epochs and the first after the wrap (which
+    clears every tagged buffer) give the same bits as a frame at epoch 1."""
+    cp = _cp()
+    cfg = synth.CONFIGS["tiny_f32"].with_(rows=3, dtype="bf16")
+    w, wdev, ow = _weights(cfg, seed=5)
+    inputs = synth.make_inputs(cfg, seed=5)
+    plan = cp.Plan(cfg, wdev, exec_mode=exec_mode, max_rows=4)
+
+    def frame():
+        io = cp.make_io(cfg, inputs, kv=True)
+        plan.run(io)
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in io.items() if k != "rows"}
+
+    ref = frame()
+    plan.set_epoch(cp.EPOCH_WRAP - 2)
+    for i in range(3):
+        out = frame()
+        for k in ref:
+            assert np.array_equal(ref[k], out[k]), (i, k)
+    plan.device_status()
+    plan.close()
+    _check(cfg, ow, inputs, ref, range(3), 0.05, kv=True)
