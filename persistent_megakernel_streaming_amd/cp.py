@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcpms.so")
+# CPMS_LIBRARY names another build of the same library (same ABI) to load.
+LIB_PATH = os.environ.get("CPMS_LIBRARY") or os.path.join(_PKG, "libcpms.so")
 
 CP_OK = 0
 STATUS = {0: "CP_OK", 1: "CP_ERR_INVALID_ARGUMENT", 2: "CP_ERR_UNSUPPORTED", 3: "CP_ERR_NOT_CORESIDENT",

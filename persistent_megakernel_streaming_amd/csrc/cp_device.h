@@ -24,7 +24,7 @@ constexpr int kTileN = 16;          // output slots per projection tile
 constexpr int kMaxRows = 64;
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kSlotBytes = 64 * 1024;  // one weight-tile slot in LDS (two slots)
-constexpr int kMiscLds = 16384;  // flags, gain row, cross-wave reductions
+constexpr int kMiscLds = 12288;  // flags, cross-wave reductions
 constexpr int kLdsBytes = 2 * kSlotBytes + kMiscLds;
 constexpr int kCtrStride = 32;      // uint32 words between sub-counters (128 B)
 constexpr int kTraceStamps = 8;     // timestamps per task in a traced frame
@@ -92,7 +92,6 @@ struct DevPlan {
   int attn_rows;      // rows per attention task
   int n_head_tiles;   // vocab / 16
   int bf16;           // activation type
-  int unit_gains;     // every RMSNorm gain is exactly 1 (the gain product is skipped)
   float eps;
   float attn_scale;   // 1 / sqrt(head_dim)
   uint32_t spin_limit;
@@ -104,19 +103,20 @@ struct DevPlan {
   uint32_t* state;              // [0] epoch, [32] done counter, [64] error word, [96] clear pending
   // weights (plan-owned copies)
   const uint8_t* wblob;         // packed projection tiles
-  const void* gains;            // [2L + 1][H]: attn_norm[l], mlp_norm[l], final_norm
   const void* embed;            // [P][V][H]
   const float* rope;            // [P][d/2][2]: cos, sin
   // activations and scratch (act = dtype)
-  void* xin;                    // [P][Rmax][H] position inputs
   // Cross-workgroup buffers hold tagged 64-bit words (2 * dtype size bytes
   // per element).  Buffers marked [2] are doubled by position parity:
-  // positions 0 and 1 can be in flight at the same time.
-  void* hres;                   // [2][2][Rmax][H] residual after down, by layer parity
-  void* hmid;                   // [2][Rmax][H] residual after o
-  void* qbuf;                   // [2][Rmax][nq d]
-  void* abuf;                   // [2][Rmax][nq d] attention output
-  void* mbuf;                   // [2][Rmax][I] SwiGLU output
+  // positions 0 and 1 can be in flight at the same time.  Rp = Rmax rounded
+  // up to 16; buffers a projection reads are in the kernels' operand order
+  // (act_off in the kernel source), the others row-major.
+  void* xin;                    // [P][Rp][H] position inputs, operand order
+  void* hres;                   // [2][2][Rp][H] residual after down, by layer parity, operand order
+  void* hmid;                   // [2][Rp][H] residual after o, operand order
+  void* qbuf;                   // [2][Rmax][nq d] rotated q, row-major
+  void* abuf;                   // [2][Rp][nq d] attention output, operand order
+  void* mbuf;                   // [2][Rp][I] SwiGLU output, operand order
   void* kc;                     // [L][Rmax][nkv][P][d]
   void* vc;
   uint64_t* part;               // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16] words

@@ -39,8 +39,7 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kSC1 = 16;  // buffer cache policy bit: coherent at agent scope
 
 // LDS layout of the misc region (after the two weight-tile slots).
-constexpr int kGainLds = 1024;    // RMSNorm gain rows, two slots of 2 KiB
-constexpr int kRedAccLds = 8192;  // cross-wave MFMA accumulators (8 KiB)
+constexpr int kRedAccLds = 1024;  // cross-wave MFMA accumulators (8 KiB)
 
 // ------------------------------------------------------------------ memory helpers
 
@@ -78,6 +77,13 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+// The same, kept as one instruction: the compiler otherwise splits a pack
+// whose halves are used separately into two conversions.
+__device__ __forceinline__ uint32_t pack_bf16_1(float lo, float hi) {
+  uint32_t r;
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 
 // Element e of a 16-byte payload chunk as float.
@@ -129,72 +135,17 @@ struct Spin {
   }
 };
 
-// Polls N 16-byte tagged loads (already issued into v) until every word
-// carries `tag`; stale ones are reloaded from off(i).
-template <int N, typename Off>
-__device__ __forceinline__ void ll_poll(const DevPlan& pl, rsrc_t r, Off off, u32x4 (&v)[N], uint32_t tag,
-                                        bool active) {
-  if (!active) return;
-  Spin sp;
-  while (true) {
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < N; ++i) ok = ok && ll_ok(v[i], tag);
-    if (ok || !sp.next(pl)) break;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      if (!ll_ok(v[i], tag)) v[i] = ld16c(r, off(i));
-  }
-}
-
-// The same for single tagged words (8-byte loads).
-template <int N, typename Off>
-__device__ __forceinline__ void ll_poll1(const DevPlan& pl, rsrc_t r, Off off, u32x2 (&v)[N], uint32_t tag,
-                                         bool active) {
-  if (!active) return;
-  Spin sp;
-  while (true) {
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < N; ++i) ok = ok && v[i][1] == tag;
-    if (ok || !sp.next(pl)) break;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      if (v[i][1] != tag) v[i] = __builtin_amdgcn_raw_buffer_load_b64(r, off(i), 0, kSC1);
-  }
-}
-
 // ------------------------------------------------------------------ weights -> LDS
 
-// Gain row (of the [2L + 1][H] table) a projection task normalises with, or -1.
-__device__ __forceinline__ int gain_row_of(const DevPlan& pl, const DevTask& tk) {
-  switch (tk.type) {
-    case T_QKV: return 2 * tk.layer;
-    case T_GU: return 2 * tk.layer + 1;
-    case T_HEAD: return 2 * pl.L;
-    default: return -1;
-  }
-}
-
-// Direct-to-LDS copies of a task's packed weight tile and, for normalising
-// tasks, its RMSNorm gain row: 1 KiB chunks (64 lanes x 16 B) with
-// global_load_lds_dwordx4, dealt round-robin to the four waves.
-__device__ __forceinline__ void issue_tile(const DevPlan& pl, const DevTask& tk, uint8_t* slot, uint8_t* gain) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// Direct-to-LDS copy of a task's packed weight tile: 1 KiB chunks (64 lanes
+// x 16 B) with global_load_lds_dwordx4, dealt round-robin to the four waves.
+__device__ __forceinline__ void issue_tile(const DevPlan& pl, const DevTask& tk, uint8_t* slot) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const uint32_t nch = tk.w_bytes >> 10;
   const uint8_t* src = pl.wblob + tk.w_off;
   for (uint32_t c = wave; c < nch; c += 4) {
     __builtin_amdgcn_global_load_lds((const void*)(src + c * 1024 + lane * 16),
                                      (void __attribute__((address_space(3)))*)(slot + c * 1024), 16, 0, 0);
-  }
-  const int gr = gain_row_of(pl, tk);
-  if (gr >= 0) {
-    const uint32_t gbytes = (uint32_t)pl.H * (pl.bf16 ? 2 : 4);  // <= 2 KiB
-    const uint8_t* gsrc = (const uint8_t*)pl.gains + (size_t)gr * gbytes;
-    for (uint32_t c = 3 - wave; c < (gbytes + 1023) / 1024; c += 4) {
-      __builtin_amdgcn_global_load_lds((const void*)(gsrc + c * 1024 + lane * 16),
-                                       (void __attribute__((address_space(3)))*)(gain + c * 1024), 16, 0, 0);
-    }
   }
 }
 
@@ -203,9 +154,8 @@ struct Next {
   DevTask tk;  // loaded when the current task starts
   bool valid;
   uint8_t* slot;
-  uint8_t* gain;
   __device__ __forceinline__ void issue(const DevPlan& pl) const {
-    if (valid) issue_tile(pl, tk, slot, gain);
+    if (valid) issue_tile(pl, tk, slot);
   }
 };
 
@@ -244,25 +194,126 @@ __device__ __forceinline__ float tile_ssq(const float (&v)[4], int first, int sp
   return s;
 }
 
-// Stores four activation values as tagged words at byte offset off (element
-// index * ESZ * 2) of r.
-template <int BF>
-__device__ __forceinline__ void st_act4(rsrc_t r, uint32_t off, const float (&v)[4], uint32_t tag) {
-  if constexpr (BF) {
-    st16c(r, off, ll_pair(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), tag));
-  } else {
-    st16c(r, off, ll_pair(__float_as_uint(v[0]), __float_as_uint(v[1]), tag));
-    st16c(r, off + 16, ll_pair(__float_as_uint(v[2]), __float_as_uint(v[3]), tag));
+// Tag check of N tagged 16-byte units: true when every word carries `tag`.
+template <int N>
+__device__ __forceinline__ bool units_ok(const u32x4 (&v)[N], uint32_t tag) {
+  uint32_t d = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) d |= (v[i][1] ^ tag) | (v[i][3] ^ tag);
+  return d == 0;
+}
+// The same for single tagged words (8-byte loads).
+template <int N>
+__device__ __forceinline__ bool units_ok(const u32x2 (&v)[N], uint32_t tag) {
+  uint32_t d = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) d |= v[i][1] ^ tag;
+  return d == 0;
+}
+__device__ __forceinline__ u32x4 ld_coherent(rsrc_t r, uint32_t off, u32x4*) { return ld16c(r, off); }
+__device__ __forceinline__ u32x2 ld_coherent(rsrc_t r, uint32_t off, u32x2*) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSC1);
+}
+
+// A set of tagged units a lane is waiting for: N loads already issued into
+// v, their offsets in r, and the tag they must carry.  Units from `nload` on
+// are fillers that already carry it and are never reloaded.
+template <typename T, int N, typename Off>
+struct Pend {
+  T (&v)[N];
+  rsrc_t r;
+  Off off;
+  uint32_t tag;
+  bool active;
+  int nload;
+  __device__ __forceinline__ bool ok() const { return !active || units_ok(v, tag); }
+  __device__ __forceinline__ void reload() {
+    if (active && !units_ok(v, tag)) {
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (i < nload) v[i] = ld_coherent(r, off(i), (T*)nullptr);
+    }
+  }
+};
+template <typename T, int N, typename Off>
+__device__ __forceinline__ Pend<T, N, Off> pend(T (&v)[N], rsrc_t r, Off off, uint32_t tag, bool active,
+                                                int nload = N) {
+  return Pend<T, N, Off>{v, r, off, tag, active, nload};
+}
+
+// Waits until every set of every lane carries its tag.  When the data is
+// there this is one check per set; otherwise each stale set is reloaded with
+// agent-coherent loads, all sets in the same round trip, and checked again.
+// The loop itself is wave-uniform.
+template <typename... Ps>
+__device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
+  Spin sp;
+  while (__builtin_amdgcn_ballot_w64(!(ps.ok() && ...)) != 0) {
+    if (!sp.next(pl)) break;
+    (ps.reload(), ...);
   }
 }
 
+// Operand-order layout of the activations a projection reads (position
+// inputs, residuals, attention output, SwiGLU output), as tagged words.  For
+// 16-row tile rt, MFMA chunk c (4 E columns) and half u, the 64 lanes'
+// 16-byte units are contiguous: lane (q, rl) of the MFMA B operand finds row
+// rt * 16 + rl, columns c * 4E + q * E + u * E / 2 ... + E / 2 - 1 at
+// ((rt * NC + c) * 2 + u) * 1024 + (q * 16 + rl) * 16, NC = K / (4E).  A wave
+// load instruction then reads 1 KiB in one piece.  Returns the byte offset of
+// the tagged word holding element (row, n) of a K-column buffer.
 template <int BF>
+__device__ __forceinline__ uint32_t act_off(int row, int n, int K) {
+  constexpr int ESZ = BF ? 2 : 4, E = 16 / ESZ, KS = 4 * E, E2 = E / 2;
+  const uint32_t unit = ((uint32_t)((row >> 4) * (K / KS) + n / KS) * 2 + (n % E) / E2) * 1024 +
+                        (uint32_t)(((n % KS) / E) * 16 + (row & 15)) * 16;
+  return unit + (uint32_t)((n % E2) * ESZ / 4) * 8;
+}
+
+// Bytes of one operand-order buffer of `rows` rows (rounded up to 16) and K columns.
+template <int BF>
+__device__ __forceinline__ uint32_t act_bytes(int rows, int K) {
+  return (uint32_t)((rows + 15) & ~15) * K * (BF ? 4 : 8);
+}
+
+// Stores four consecutive columns n .. n+3 (n a multiple of 4) of one row as
+// tagged words in operand order: one 16-byte unit (bf16) or two (fp32).
+template <int BF>
+__device__ __forceinline__ void st_act4(rsrc_t r, int row, int n, int K, const float (&v)[4], uint32_t tag) {
+  if constexpr (BF) {
+    st16c(r, act_off<1>(row, n, K), ll_pair(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), tag));
+  } else {
+    st16c(r, act_off<0>(row, n, K), ll_pair(__float_as_uint(v[0]), __float_as_uint(v[1]), tag));
+    st16c(r, act_off<0>(row, n + 2, K), ll_pair(__float_as_uint(v[2]), __float_as_uint(v[3]), tag));
+  }
+}
+
+// Projection tile: out[row][16 columns] = W_tile . a[row] over the task's K
+// range, for every live row, with MFMA 16x16 tiles (A = the weight tile from
+// LDS, B = 16 rows of activations).  KIND fixes the operand, its RMSNorm and
+// the epilogue at compile time:
+//   T_QKV  : RMSNorm(layer input) -> q (RoPE), k (RoPE), v
+//   T_O    : attention output -> + residual (split-K partials in fixed order)
+//   T_GU   : RMSNorm(residual) -> silu(gate) * up
+//   T_DOWN : SwiGLU output -> + residual (split-K partials in fixed order)
+//   T_HEAD : RMSNorm(last residual) -> logits, per-tile argmax candidate
+//   T_INPROJ: frame input (plain rows) -> position-0 input (split-K partials)
+// RMSNorm: the gain g is folded into the packed weight tile at plan creation
+// (W . (g x / rms(x)) = (W g) . x / rms(x)), so the MFMAs take the residual
+// rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
+template <int BF, int KIND>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint8_t* gain, uint32_t* misc, const Next& nx,
-                                          uint64_t* tr) {
+                                          uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
+  constexpr bool XLL = KIND != T_INPROJ;  // operand rows are tagged words
+  constexpr bool NORM = KIND == T_QKV || KIND == T_GU || KIND == T_HEAD;
+  constexpr int NB = KIND == T_GU ? 2 : 1;  // weight tiles per chunk (gate and up)
+  constexpr bool PART = KIND == T_O || KIND == T_DOWN || KIND == T_INPROJ;
+  constexpr bool RESID = KIND == T_O || KIND == T_DOWN;
+  constexpr int NU = XLL ? 8 : 4;           // 16-byte loads per lane per group of 4 chunks
+  constexpr uint32_t CST = 64;              // plain operand bytes per chunk step
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 4, rl = lane & 15;
   const int rows = fr.rows;
@@ -270,50 +321,35 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const int l = tk.layer, p = tk.pos;
   const uint32_t my_tag = tag_of(epoch, tk.phase);
   const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
-  const uint32_t res_tag = tag_of(epoch, tk.ph_in1);
 
-  // Operand source, K range, norm and epilogue of this task kind.  Tagged
-  // buffers hold 2 * ESZ bytes per element.
-  const void* xsrc;
-  uint32_t xbytes, ld;   // buffer bytes and row length (elements)
-  bool xll = true;       // operand rows are tagged words (all but the frame input)
-  int k0 = 0, kt;
-  int in_ssq = -1;       // ssq slot of a normalised input (-1: no norm)
-  int out_ssq = -1;      // ssq slot of a residual output (EPI_PART)
-  int nb = 1;
-  Epi epi;
-  const void* resid = nullptr;  // residual (EPI_PART)
-  void* out = nullptr;          // output (EPI_PART)
-  uint64_t part_off = 0;
-  // Buffers that two positions in flight at once (0 and 1) would share are
-  // doubled and picked by position parity.
+  // Buffers that positions 0 and 1 (in flight together) would share are
+  // doubled and picked by position parity.  Tagged buffers hold 2 * ESZ
+  // bytes per element.
   const int par = p & 1;
-  const uint32_t hbytes = (uint32_t)Rmax * H * ESZ * 2;
-  const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * pl.d * ESZ * 2;
-  uint8_t* hres = (uint8_t*)pl.hres + (size_t)par * 2 * hbytes;   // [layer parity]
+  const uint32_t hbytes = act_bytes<BF>(Rmax, H);
+  uint8_t* hres = (uint8_t*)pl.hres + (size_t)par * 2 * hbytes;  // [layer parity]
   uint8_t* hmid = (uint8_t*)pl.hmid + (size_t)par * hbytes;
-  const uint8_t* layer_in = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
-  const int layer_in_ssq = (l == 0) ? p : P + 2 * par + ((l - 1) & 1);
-  switch (tk.type) {
-    case T_QKV:
-      xsrc = layer_in; xbytes = hbytes; ld = H; kt = H; in_ssq = layer_in_ssq; epi = EPI_QKV; break;
-    case T_GU:
-      xsrc = hmid; xbytes = hbytes; ld = H; kt = H; in_ssq = P + 4 + par; nb = 2; epi = EPI_GU; break;
-    case T_HEAD:
-      xsrc = hres + (size_t)((pl.L - 1) & 1) * hbytes; xbytes = hbytes; ld = H; kt = H;
-      in_ssq = P + 2 * par + ((pl.L - 1) & 1); epi = EPI_HEAD; break;
-    case T_O:
-      xsrc = (const uint8_t*)pl.abuf + (size_t)par * qdbytes; ld = pl.nq * pl.d; xbytes = qdbytes;
-      kt = (int)ld / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART; resid = layer_in; out = hmid;
-      out_ssq = P + 4 + par; part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; break;
-    case T_DOWN:
-      xsrc = (const uint8_t*)pl.mbuf + (size_t)par * Rmax * pl.I * ESZ * 2; ld = pl.I;
-      xbytes = (uint32_t)Rmax * ld * ESZ * 2; kt = pl.I / tk.nsplit; k0 = tk.split * kt; epi = EPI_PART;
-      resid = hmid; out = hres + (size_t)(l & 1) * hbytes; out_ssq = P + 2 * par + (l & 1);
-      part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; break;
-    default:  // T_INPROJ: the frame's input hidden (plain, written before the launch)
-      xsrc = fr.hidden_in; ld = pl.Din; xbytes = (uint32_t)fr.rows * ld * ESZ; xll = false; kt = pl.Din / tk.nsplit;
-      k0 = tk.split * kt; epi = EPI_PART; out = pl.xin; out_ssq = 0; part_off = pl.part_in_off; break;
+  const uint8_t* xsrc;
+  uint32_t ld;                     // operand row length (elements)
+  int kt = H, k0 = 0, in_ssq = 0;
+  if constexpr (KIND == T_QKV) {
+    xsrc = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
+    in_ssq = (l == 0) ? p : P + 2 * par + ((l - 1) & 1);
+    ld = H;
+  } else if constexpr (KIND == T_GU) {
+    xsrc = hmid; in_ssq = P + 4 + par; ld = H;
+  } else if constexpr (KIND == T_HEAD) {
+    xsrc = hres + (size_t)((pl.L - 1) & 1) * hbytes; in_ssq = P + 2 * par + ((pl.L - 1) & 1); ld = H;
+  } else if constexpr (KIND == T_O) {
+    ld = pl.nq * pl.d; xsrc = (const uint8_t*)pl.abuf + (size_t)par * act_bytes<BF>(Rmax, ld);
+  } else if constexpr (KIND == T_DOWN) {
+    ld = pl.I; xsrc = (const uint8_t*)pl.mbuf + (size_t)par * act_bytes<BF>(Rmax, ld);
+  } else {
+    ld = pl.Din; xsrc = (const uint8_t*)fr.hidden_in;
+  }
+  if constexpr (PART) {
+    kt = (int)ld / tk.nsplit;
+    k0 = tk.split * kt;
   }
   const int nck = kt * ESZ / 64;  // 16-byte payload chunks per lane over the task's K range
 
@@ -324,52 +360,58 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   while (wpr > 1 && nck % (4 * wpr)) wpr >>= 1;        // each wave takes whole groups of 4 chunks
   const int rt = wave / wpr, ks = wave % wpr;
   const int ncw = nck / wpr;                          // chunks this wave handles (a multiple of 4)
+  const int ng = ncw / 4;
   const int c0 = ks * ncw;
   const int row = rt * 16 + rl;
   const bool wave_live = rt < nrt;
   const bool live = wave_live && row < rows;
-  f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);    // [4 waves][2][64 lanes]
-  const uint32_t ssq_bytes = (uint32_t)Rmax * (H / 16) * 8;
-  const bool owner = tk.nsplit == 1 || tk.split == 0;
 
-  // Operand rows: 4-chunk groups, two in flight.  A tagged chunk is 32 bytes
-  // (two 16-byte loads); a plain chunk 16 bytes.
-  const rsrc_t rx = make_rsrc(xsrc, xbytes);
-  const uint32_t cstride = xll ? 128 : 64;  // bytes per chunk step (KS elements)
-  const uint32_t xoff = ((uint32_t)row * ld + k0 + q * E) * ESZ * (xll ? 2 : 1) + c0 * cstride;
-  u32x4 xa[8], xb[8];
-  // 16-byte unit u of group g: chunk u / 2, half u % 2
-  auto goff = [&](int g) { return [=](int u) { return xoff + (g * 4 + (u >> 1)) * cstride + (u & 1) * 16; }; };
-  auto load_group = [&](u32x4 (&x)[8], int g) {
+  // Operand rows.  Tagged operands are in operand order: unit u of chunk c
+  // of this lane is at xoff + c * 2048 + u * 1024.  A lane whose row is past
+  // the frame's rows reads words of no use (left out of every wait; they
+  // only reach that row's MFMA column, which is never stored).  The frame
+  // input is plain row-major; its resource ends at the last row, so rows
+  // past it read zeros.  The first load of a unit may hit the L2, which the
+  // other workgroups of this XCD reading the same rows share; a stale word
+  // fails its tag check and is reloaded coherently.
+  const uint32_t xrow = (uint32_t)ld * ESZ;  // plain input only
+  const rsrc_t rx = XLL ? make_rsrc(xsrc, act_bytes<BF>(Rmax, ld)) : make_rsrc(xsrc, (uint32_t)rows * xrow);
+  const uint32_t xoff = XLL ? ((uint32_t)(rt * (ld / KS) + k0 / KS + c0) * 2) * 1024 + (uint32_t)lane * 16
+                            : (uint32_t)row * xrow + (uint32_t)(k0 + q * E) * ESZ + c0 * CST;
+  auto uoff = [=](int g) {
+    return [=](int u) -> uint32_t {
+      return XLL ? xoff + (g * 4 + (u >> 1)) * 2048 + (u & 1) * 1024 : xoff + (g * 4 + u) * CST;
+    };
+  };
+  // Four groups in flight: xa, xb, xc, xd hold groups g = 0, 1, 2, 3 (mod 4).
+  u32x4 xa[NU], xb[NU], xc[NU], xd[NU];
+  auto load = [&](u32x4 (&x)[NU], int g) {
+    if (g < ng) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t base = xoff + (g * 4 + i) * cstride;
-      // The first attempt may hit the L2, which the other workgroups of this
-      // XCD reading the same rows then share; a stale word fails its tag
-      // check and is reloaded coherently.  Plain rows (the frame input) use
-      // the even units only.
-      x[2 * i] = live ? ld16(rx, base) : u32x4{0, in_tag, 0, in_tag};
-      x[2 * i + 1] = (live && xll) ? ld16(rx, base + 16) : u32x4{0, in_tag, 0, in_tag};
+      for (int u = 0; u < NU; ++u) x[u] = ld16(rx, uoff(g)(u));
     }
   };
-  const int ng = ncw / 4;
   if (wave_live) {
-    load_group(xa, 0);
-    if (ng > 1) load_group(xb, 1);
+    load(xa, 0);
+    load(xb, 1);
+    load(xc, 2);
+    load(xd, 3);
   }
-  // Sum-of-squares partials of a normalised input (tagged, same writer as the rows).
+  // Sum-of-squares partials of a normalised operand (H/16 per row, written
+  // with the rows): lane group q adds H/64 of them.
   u32x4 ssv[8];
-  const int nsq = H / 64;  // partials per lane (H/16 partials over 4 lanes), <= 16
-  const rsrc_t rs = make_rsrc(in_ssq >= 0 ? ssq_slot(pl, in_ssq) : pl.ssq, ssq_bytes);
-  const uint32_t ss0 = (uint32_t)(row * (H / 16) + q * nsq) * 8;
-  auto sso = [=](int i) { return ss0 + i * 16; };
-  if (in_ssq >= 0) {
+  const int nsq = H / 64;
+  const uint32_t ss_row = (uint32_t)(H / 16) * 8;
+  const rsrc_t rs = make_rsrc(ssq_slot(pl, in_ssq), (uint32_t)rows * ss_row);
+  const uint32_t ss0 = (uint32_t)row * ss_row + (uint32_t)(q * nsq) * 8;
+  auto sso = [=](int i) -> uint32_t { return ss0 + i * 16; };
+  if constexpr (NORM) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ssv[i] = (2 * i < nsq && live) ? ld16(rs, sso(i)) : u32x4{0, in_tag, 0, in_tag};
+    for (int i = 0; i < 8; ++i) ssv[i] = (2 * i < nsq) ? ld16(rs, sso(i)) : u32x4{0, in_tag, 0, in_tag};
   }
   // RoPE angles of a qkv tile's two rotary pairs per lane.
   float rope_cs[2] = {1.f, 1.f}, rope_sn[2] = {0.f, 0.f};
-  if (tk.type == T_QKV) {
+  if constexpr (KIND == T_QKV) {
     const int d = pl.d, th = d / 16, tpg = (pl.gq + 2) * th, lt = tk.tile % tpg;
     if (lt < (pl.gq + 1) * th) {
       const int i0 = 8 * (lt % th) + 2 * q;
@@ -380,18 +422,25 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   }
-  // Wait for the first group (and the norm partials): the data is its signal.
-  if (xll) {
-    ll_poll<8>(pl, rx, goff(0), xa, in_tag, live);
-    if (ng > 1) ll_poll<8>(pl, rx, goff(1), xb, in_tag, live);
-  }
-  if (in_ssq >= 0) ll_poll<8>(pl, rs, sso, ssv, in_tag, live);
-  wait_vm();        // this wave's share of the weight tile (issued during the previous task) has landed
-  __syncthreads();  // every wave's share of the tile is in LDS
+  // The data is its own signal: wait for the first two groups and the norm
+  // partials, then for this task's weight tile (issued during the previous
+  // task) to be in LDS.
+  await_all(pl, pend(xa, rx, uoff(0), in_tag, XLL && live), pend(xb, rx, uoff(1), in_tag, XLL && live && ng > 1),
+            pend(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
+  wait_vm();
+  __syncthreads();
   stamp(tr, 2);
+  // The next task's tile copy goes out once this task has issued its last
+  // operand load: a wave's loads retire in order, so a copy issued earlier
+  // would hold up this task's own waits.  A split-K owner still has the
+  // partials to collect and issues it at the end.
+  // (Each wave issues its own share of the copy; a wave without rows to
+  // compute has no operand loads and issues it here.)
+  const bool early = !PART || tk.split != 0;
+  if (early && (ng <= 4 || !wave_live)) nx.issue(pl);
 
   float rinv = 1.f;
-  if (in_ssq >= 0 && wave_live) {
+  if constexpr (NORM) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -401,76 +450,43 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
   }
   stamp(tr, 3);
-  if (tr) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    stamp(tr, 1);
-  }
 
-  const bool norm = in_ssq >= 0;
-  const bool unit = pl.unit_gains != 0;
-  const uint8_t* gl = gain + c0 * 64;  // gain row staged with the tile
-  const uint8_t* wt = slot + lane * 16 + (size_t)c0 * nb * 1024;
+  const uint8_t* wt = slot + lane * 16 + (size_t)c0 * NB * 1024;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  // a = round(round(x * r) * g) in the activation type, then the MFMAs
-  auto process = [&](u32x4 (&xr)[8], int g) {
-    if (xll) ll_poll<8>(pl, rx, goff(g), xr, in_tag, live);
-    u32x4 x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = xll ? ll_payload(xr[2 * i], xr[2 * i + 1]) : xr[2 * i];
-    u32x4 w[8];
+  auto step = [&](u32x4 (&xr)[NU], int g) {
+    if constexpr (XLL) await_all(pl, pend(xr, rx, uoff(g), in_tag, live));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      w[2 * i] = *(const u32x4*)(wt + ((g * 4 + i) * nb) * 1024);
-      if (nb == 2) w[2 * i + 1] = *(const u32x4*)(wt + ((g * 4 + i) * nb + 1) * 1024);
-    }
-    if (norm) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 gv = *(const u32x4*)(gl + ((g * 4 + i) * KS + q * E) * ESZ);
-        u32x4 o2;
-        if constexpr (BF) {
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) {
-            const uint32_t xw = x[i][w2];
-            const float t0 = __uint_as_float(xw << 16) * rinv, t1 = __uint_as_float(xw & 0xffff0000u) * rinv;
-            if (unit) {
-              o2[w2] = pack_bf16(t0, t1);
-            } else {
-              const uint32_t gw = gv[w2];
-              o2[w2] = pack_bf16(t0 * __uint_as_float(gw << 16), t1 * __uint_as_float(gw & 0xffff0000u));
-            }
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float t = __uint_as_float(x[i][e]) * rinv;
-            o2[e] = __float_as_uint(unit ? t : t * __uint_as_float(gv[e]));
-          }
-        }
-        x[i] = live ? o2 : u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (nb == 1) {
-        if (i & 1) acc1 = mma<BF>(w[2 * i], x[i], acc1);
-        else acc0 = mma<BF>(w[2 * i], x[i], acc0);
+      const int c = g * 4 + i;
+      const u32x4 x = XLL ? ll_payload(xr[2 * i], xr[2 * i + 1]) : xr[i];
+      const u32x4 w0 = *(const u32x4*)(wt + c * NB * 1024);
+      if constexpr (NB == 2) {
+        const u32x4 w1 = *(const u32x4*)(wt + (c * 2 + 1) * 1024);
+        acc0 = mma<BF>(w0, x, acc0);
+        acc1 = mma<BF>(w1, x, acc1);
       } else {
-        acc0 = mma<BF>(w[2 * i], x[i], acc0);
-        acc1 = mma<BF>(w[2 * i + 1], x[i], acc1);
+        if (i & 1) acc1 = mma<BF>(w0, x, acc1);
+        else acc0 = mma<BF>(w0, x, acc0);
       }
     }
   };
   if (wave_live) {
-    for (int g = 0; g < ng; g += 2) {
-      process(xa, g);
+    for (int g = 0; g < ng; g += 4) {
+      step(xa, g);
       if (g == 0) stamp(tr, 6);
-      if (g + 2 < ng) load_group(xa, g + 2);
+      load(xa, g + 4);
       if (g + 1 >= ng) break;
-      process(xb, g + 1);
-      if (g + 3 < ng) load_group(xb, g + 3);
+      step(xb, g + 1);
+      load(xb, g + 5);
+      if (g + 2 >= ng) break;
+      step(xc, g + 2);
+      load(xc, g + 6);
+      if (g + 3 >= ng) break;
+      step(xd, g + 3);
+      load(xd, g + 7);
+      if (early && g + 8 >= ng && ng > 4) nx.issue(pl);
     }
-    if (nb == 1) {
+    if constexpr (NB == 1) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + acc1[v];
     }
@@ -478,19 +494,18 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   stamp(tr, 4);
   if (wpr > 1) {
     // K parts of a row tile: (((k0 + k1) + k2) + k3), in the wave of part 0
+    f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);  // [4 waves][2][64 lanes]
     if (wave_live) {
       red_acc[(wave * 2 + 0) * 64 + lane] = acc0;
-      if (nb == 2) red_acc[(wave * 2 + 1) * 64 + lane] = acc1;
+      if constexpr (NB == 2) red_acc[(wave * 2 + 1) * 64 + lane] = acc1;
     }
     __syncthreads();
     if (wave_live && ks == 0) {
-      acc0 = red_acc[(rt * wpr * 2 + 0) * 64 + lane];
-      if (nb == 2) acc1 = red_acc[(rt * wpr * 2 + 1) * 64 + lane];
       for (int k = 1; k < wpr; ++k) {
         const f32x4 a = red_acc[((rt * wpr + k) * 2 + 0) * 64 + lane];
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + a[v];
-        if (nb == 2) {
+        if constexpr (NB == 2) {
           const f32x4 b = red_acc[((rt * wpr + k) * 2 + 1) * 64 + lane];
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc1[v] = acc1[v] + b[v];
@@ -498,52 +513,95 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   }
+  if constexpr (NORM) {  // W (g . x / rms(x)) = (W g) x / rms(x): the gain is in the packed tile
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      acc0[v] = acc0[v] * rinv;
+      if constexpr (NB == 2) acc1[v] = acc1[v] * rinv;
+    }
+  }
   const bool epi_wave = wave_live && ks == 0;
   const uint32_t slots = (uint32_t)(16 * tk.tile + 4 * q);  // this lane's 4 output slots
 
-  // The split-K owner collects its partners' partials and the residual; an
-  // unsplit o / down tile only needs the residual.  All loads go out before
-  // the next task's tile copy, whose completion would otherwise be waited on.
-  u32x4 pv[6], rv[2];
-  const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 8);
-  const rsrc_t rr = make_rsrc(resid ? resid : xsrc, hbytes);
-  const uint32_t pbase = (uint32_t)((tk.tile * tk.nsplit * Rmax + row) * 16 + 4 * q) * 8;
-  const uint32_t pstep = (uint32_t)Rmax * 16 * 8;  // bytes between splits of a tile
-  // unit u of the partners' partials: split 1 + u / 2, half u % 2
-  auto po = [=](int u) { return pbase + (1 + (u >> 1)) * pstep + (u & 1) * 16; };
-  const uint32_t rbase = (uint32_t)(row * H + slots) * ESZ * 2;
-  auto ro = [=](int u) { return rbase + u * 16; };
-  if (epi == EPI_PART && epi_wave) {
-    if (!owner) {
-      if (live) {  // partial of this split, tagged with this phase
+  if constexpr (PART) {
+    // Split-K: the owner (split 0) collects its partners' partials (tagged
+    // with this phase, in split order) and the residual; the next task's
+    // tile copy is issued after these loads so that waiting on them does not
+    // also wait on the copy.
+    const uint32_t res_tag = tag_of(epoch, tk.ph_in1);
+    const bool owner = tk.split == 0;
+    uint64_t part_off;
+    void* out;
+    int out_ssq;
+    const void* resid = nullptr;
+    if constexpr (KIND == T_O) {
+      part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; out = hmid; out_ssq = P + 4 + par;
+      resid = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
+    } else if constexpr (KIND == T_DOWN) {
+      part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; out = hres + (size_t)(l & 1) * hbytes;
+      out_ssq = P + 2 * par + (l & 1); resid = hmid;
+    } else {
+      part_off = pl.part_in_off; out = pl.xin; out_ssq = 0;
+    }
+    const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 8);
+    const uint32_t pbase = (uint32_t)((tk.tile * tk.nsplit * Rmax + row) * 16 + 4 * q) * 8;
+    const uint32_t pstep = (uint32_t)Rmax * 16 * 8;  // bytes between splits of a tile
+    auto po = [=](int u) -> uint32_t { return pbase + (1 + (u >> 1)) * pstep + (u & 1) * 16; };
+    const rsrc_t rr = make_rsrc(resid, hbytes);
+    auto ro = [=](int u) -> uint32_t { return act_off<BF>(row, (int)slots + u * (E / 2), H); };
+    constexpr int NR = BF ? 1 : 2;  // 16-byte loads of the residual's four slots
+    u32x4 pv[6], rv[NR];
+    const int npart = tk.nsplit - 1;
+    if (epi_wave && !owner) {
+      if (live) {
         const uint32_t o = pbase + tk.split * pstep;
         st16c(rp, o, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag));
         st16c(rp, o + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag));
       }
-    } else {
+    } else if (epi_wave) {
 #pragma unroll
-      for (int u = 0; u < 6; ++u) {
-        const bool use = 1 + (u >> 1) < tk.nsplit && live;
-        pv[u] = use ? ld16c(rp, po(u)) : u32x4{0, my_tag, 0, my_tag};
+      for (int u = 0; u < 6; ++u) pv[u] = (u >> 1) < npart ? ld16c(rp, po(u)) : u32x4{0, my_tag, 0, my_tag};
+      if constexpr (RESID) {
+#pragma unroll
+        for (int u = 0; u < NR; ++u) rv[u] = ld16c(rr, ro(u));
       }
-      rv[0] = (resid && live) ? ld16c(rr, ro(0)) : u32x4{0, res_tag, 0, res_tag};
-      rv[1] = (resid && live && !BF) ? ld16c(rr, ro(1)) : u32x4{0, res_tag, 0, res_tag};
-      ll_poll<6>(pl, rp, po, pv, my_tag, live);
-      ll_poll<2>(pl, rr, ro, rv, res_tag, live && resid);
     }
-  }
-  nx.issue(pl);  // the next task's tile lands during this epilogue and the next wait
-
-  // Lane (q, rl) of an epilogue wave holds output slots 4q .. 4q+3 of row `row`.
-  if (epi_wave) {
-    if (epi == EPI_QKV) {
-      const int d = pl.d, th = d / 16, gq = pl.gq, nkv = pl.nkv;
-      const int tpg = (gq + 2) * th;
-      const int g = tk.tile / tpg, lt = tk.tile % tpg;
-      const uint32_t kvoff = (uint32_t)(((l * Rmax + row) * nkv + g) * P + p) * d;
-      const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
-      const uint32_t kv_tag = tag_of(epoch, kKvPhase);
+    if (epi_wave && owner) {
+      await_all(pl, pend(pv, rp, po, my_tag, live && npart > 0, 2 * npart), pend(rv, rr, ro, res_tag, RESID && live));
+      f32x4 s = acc0;
+#pragma unroll
+      for (int sp = 1; sp < 4; ++sp)
+        if (sp <= npart) {
+          const u32x4 a = pv[2 * sp - 2], b = pv[2 * sp - 1];
+          s[0] = s[0] + __uint_as_float(a[0]); s[1] = s[1] + __uint_as_float(a[2]);
+          s[2] = s[2] + __uint_as_float(b[0]); s[3] = s[3] + __uint_as_float(b[2]);
+        }
+      float h[4];
+      if constexpr (RESID) {
+        const u32x4 r4 = BF ? u32x4{rv[0][0], rv[0][2], 0, 0} : ll_payload(rv[0], rv[NR - 1]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e] + chunk_elem<BF>(r4, e));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e]);
+      }
+      const float sq = tile_ssq(h, 16, 4);
       if (live) {
+        st_act4<BF>(make_rsrc(out, hbytes), row, (int)slots, H, h, my_tag);
+        if (q == 0)
+          st8c(make_rsrc(ssq_slot(pl, out_ssq), (uint32_t)Rmax * ss_row), (uint32_t)row * ss_row + tk.tile * 8,
+               u32x2{__float_as_uint(sq), my_tag});
+      }
+    }
+  } else {
+    if (epi_wave && live) {
+      if constexpr (KIND == T_QKV) {
+        const int d = pl.d, th = d / 16, gq = pl.gq, nkv = pl.nkv;
+        const int tpg = (gq + 2) * th;
+        const int g = tk.tile / tpg, lt = tk.tile % tpg;
+        const uint32_t kvoff = (uint32_t)(((l * Rmax + row) * nkv + g) * P + p) * d;
+        const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
+        const uint32_t kv_tag = tag_of(epoch, kKvPhase);
         if (lt < (gq + 1) * th) {
           // q or k head: slots (4q + v) hold rotary pairs 8 tih + 2q + (v >> 1), half v & 1
           const int tih = lt % th;
@@ -558,17 +616,10 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
             y[2 * pr + 1] = x2 * rope_cs[pr] + x1 * rope_sn[pr];
           }
           // dims i0, i0 + 1 (first halves) and i0 + d/2, i0 + d/2 + 1 (second halves)
-          rsrc_t r;
-          uint32_t base, tg;
-          if (isq) {
-            r = make_rsrc((uint8_t*)pl.qbuf + (size_t)par * qdbytes, qdbytes);
-            base = (uint32_t)(row * pl.nq * d + hq * d);
-            tg = my_tag;
-          } else {
-            r = make_rsrc(pl.kc, kvbytes);
-            base = kvoff;
-            tg = kv_tag;
-          }
+          const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * d * ESZ * 2;
+          const rsrc_t r = isq ? make_rsrc((uint8_t*)pl.qbuf + (size_t)par * qdbytes, qdbytes) : make_rsrc(pl.kc, kvbytes);
+          const uint32_t base = isq ? (uint32_t)(row * pl.nq * d + hq * d) : kvoff;
+          const uint32_t tg = isq ? my_tag : kv_tag;
           if constexpr (BF) {
             st8c(r, (base + i0) * 4, u32x2{pack_bf16(y[0], y[2]), tg});
             st8c(r, (base + i0 + d / 2) * 4, u32x2{pack_bf16(y[1], y[3]), tg});
@@ -578,75 +629,58 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           }
         } else {
           const int tih = lt - (gq + 1) * th;
-          const float v4[4] = {acc0[0], acc0[1], acc0[2], acc0[3]};
-          st_act4<BF>(make_rsrc(pl.vc, kvbytes), (kvoff + 16 * tih + 4 * q) * ESZ * 2, v4, kv_tag);
+          const rsrc_t rvc = make_rsrc(pl.vc, kvbytes);
+          const uint32_t vo = (kvoff + 16 * tih + 4 * q) * ESZ * 2;
+          if constexpr (BF) {
+            st16c(rvc, vo, ll_pair(pack_bf16(acc0[0], acc0[1]), pack_bf16(acc0[2], acc0[3]), kv_tag));
+          } else {
+            st16c(rvc, vo, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), kv_tag));
+            st16c(rvc, vo + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), kv_tag));
+          }
         }
-      }
-    } else if (epi == EPI_GU) {
-      if (live) {
+      } else if constexpr (KIND == T_GU) {
         float m[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float gv = acc0[v], uv = acc1[v];
           m[v] = (gv / (1.0f + expf(-gv))) * uv;
         }
-        const uint32_t mbytes = (uint32_t)Rmax * pl.I * ESZ * 2;
-        st_act4<BF>(make_rsrc((uint8_t*)pl.mbuf + (size_t)par * mbytes, mbytes),
-                    (uint32_t)(row * pl.I + 16 * tk.tile + 4 * q) * ESZ * 2, m, my_tag);
+        const uint32_t mbytes = act_bytes<BF>(Rmax, pl.I);
+        st_act4<BF>(make_rsrc((uint8_t*)pl.mbuf + (size_t)par * mbytes, mbytes), row, 16 * tk.tile + 4 * q, pl.I, m,
+                    my_tag);
       }
-    } else if (epi == EPI_HEAD) {
-      const int V = pl.V;
-      const uint32_t n0 = slots;
-      if (live) {
-        const rsrc_t rz = make_rsrc(pl.zbuf, (uint32_t)Rmax * V * 8);
-        st16c(rz, (uint32_t)(row * V + n0) * 8, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag));
-        st16c(rz, (uint32_t)(row * V + n0) * 8 + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag));
-        if (fr.logits)
-          st16(make_rsrc(fr.logits, (uint32_t)rows * (P - 1) * V * 4), (uint32_t)((row * (P - 1) + (p - 1)) * V + n0) * 4,
-               u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
-      }
-      // best (value, index) of the tile for this row
-      float bv = acc0[0];
-      uint32_t bi = n0;
-#pragma unroll
-      for (int v = 1; v < 4; ++v)
-        if (beats(acc0[v], n0 + v, bv, bi)) { bv = acc0[v]; bi = n0 + v; }
-#pragma unroll
-      for (int m = 16; m <= 32; m <<= 1) {
-        const float ov = shfl_xor_f(bv, m);
-        const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
-        if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (live && q == 0)
-        st16c(make_rsrc(pl.cand, (uint32_t)Rmax * pl.n_head_tiles * 16), (uint32_t)(row * pl.n_head_tiles + tk.tile) * 16,
-              ll_pair(__float_as_uint(bv), bi, my_tag));
-    } else if (owner) {  // EPI_PART: (partials in split order) + residual, store, sum of squares
-      f32x4 s = acc0;
-#pragma unroll
-      for (int sp = 1; sp < 4; ++sp)
-        if (sp < tk.nsplit) {
-          const u32x4 a = pv[2 * sp - 2], b = pv[2 * sp - 1];
-          s[0] = s[0] + __uint_as_float(a[0]); s[1] = s[1] + __uint_as_float(a[2]);
-          s[2] = s[2] + __uint_as_float(b[0]); s[3] = s[3] + __uint_as_float(b[2]);
+    }
+    if constexpr (KIND == T_HEAD) {
+      if (epi_wave) {
+        const int V = pl.V;
+        const uint32_t n0 = slots;
+        if (live) {
+          const rsrc_t rz = make_rsrc(pl.zbuf, (uint32_t)Rmax * V * 8);
+          st16c(rz, (uint32_t)(row * V + n0) * 8, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag));
+          st16c(rz, (uint32_t)(row * V + n0) * 8 + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag));
+          if (fr.logits)
+            st16(make_rsrc(fr.logits, (uint32_t)rows * (P - 1) * V * 4), (uint32_t)((row * (P - 1) + (p - 1)) * V + n0) * 4,
+                 u32x4{__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), __float_as_uint(acc0[2]), __float_as_uint(acc0[3])});
         }
-      float h[4];
-      if (resid) {
-        const u32x4 r4 = BF ? u32x4{rv[0][0], rv[0][2], 0, 0} : ll_payload(rv[0], rv[1]);
+        // best (value, index) of the tile for this row
+        float bv = acc0[0];
+        uint32_t bi = n0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e] + chunk_elem<BF>(r4, e));
-      } else {
+        for (int v = 1; v < 4; ++v)
+          if (beats(acc0[v], n0 + v, bv, bi)) { bv = acc0[v]; bi = n0 + v; }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e]);
-      }
-      const float sq = tile_ssq(h, 16, 4);
-      if (live) {
-        st_act4<BF>(make_rsrc(out, hbytes), (uint32_t)(row * H + slots) * ESZ * 2, h, my_tag);
-        if (q == 0)
-          st8c(make_rsrc(ssq_slot(pl, out_ssq), ssq_bytes), (uint32_t)(row * (H / 16) + tk.tile) * 8,
-               u32x2{__float_as_uint(sq), my_tag});
+        for (int m = 16; m <= 32; m <<= 1) {
+          const float ov = shfl_xor_f(bv, m);
+          const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
+          if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        if (live && q == 0)
+          st16c(make_rsrc(pl.cand, (uint32_t)Rmax * pl.n_head_tiles * 16), (uint32_t)(row * pl.n_head_tiles + tk.tile) * 16,
+                ll_pair(__float_as_uint(bv), bi, my_tag));
       }
     }
   }
+  if (!early) nx.issue(pl);  // after the owner's outputs
   stamp(tr, 5);
 }
 
@@ -669,14 +703,14 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
   const rsrc_t rq = make_rsrc((uint8_t*)pl.qbuf + (size_t)(p & 1) * qdbytes, qdbytes);
   const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
   const rsrc_t rk = make_rsrc(pl.kc, kvbytes), rv = make_rsrc(pl.vc, kvbytes);
-  const rsrc_t ra = make_rsrc((uint8_t*)pl.abuf + (size_t)(p & 1) * qdbytes, qdbytes);
+  const uint32_t abytes = act_bytes<BF>(Rmax, pl.nq * d);  // attention output, operand order for o
+  const rsrc_t ra = make_rsrc((uint8_t*)pl.abuf + (size_t)(p & 1) * abytes, abytes);
   const uint32_t q_tag = tag_of(epoch, tk.ph_in0), kv_tag = tag_of(epoch, kKvPhase);
   const uint32_t my_tag = tag_of(epoch, tk.phase);
   const int t = lane >> 2, c = lane & 3;
   const int dq = d / 4;                  // dims per score lane
   const int nld = dq * ESZ * 2 / 16;     // 16-byte tagged loads per score lane (4, 8 or 16)
   const int dpl = d / 64;                // output dims per lane (1 or 2)
-  bool issued = false;
   for (int pi = wave; pi < npairs; pi += 4) {
     const int row = rg * pl.attn_rows + pi / gq;
     const int hq = g * gq + pi % gq;
@@ -707,14 +741,14 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
       if constexpr (BF) vw[tt] = (tt <= p) ? __builtin_amdgcn_raw_buffer_load_b64(rv, vo(tt), 0, kSC1) : u32x2{0, kv_tag};
       else vv[tt] = (tt <= p) ? ld16c(rv, vo(tt)) : u32x4{0, kv_tag, 0, kv_tag};
     }
-    ll_poll<NQ>(pl, rq, qo, qv, q_tag, true);
-    ll_poll<NQ>(pl, rk, ko, kv, kv_tag, true);
-    if constexpr (BF) ll_poll1<16>(pl, rv, vo, vw, kv_tag, true);
-    else ll_poll<16>(pl, rv, vo, vv, kv_tag, true);
-    if (!issued) {
-      nx.issue(pl);
-      issued = true;
-    }
+    // Q and K (this position's from the qkv phase just before, earlier ones
+    // long ready) and V, all in one wait
+    if constexpr (BF)
+      await_all(pl, pend(qv, rq, qo, q_tag, true, nld), pend(kv, rk, ko, kv_tag, t <= p, nld),
+                pend(vw, rv, vo, kv_tag, true, p + 1));
+    else
+      await_all(pl, pend(qv, rq, qo, q_tag, true, nld), pend(kv, rk, ko, kv_tag, t <= p, nld),
+                pend(vv, rv, vo, kv_tag, true, p + 1));
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < NQ; ++i)
@@ -759,21 +793,22 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
         }
       }
     }
-    const uint32_t ao = (uint32_t)(row * pl.nq * d + hq * d + lane * dpl);
+    const int an = hq * d + lane * dpl;  // first output column of this lane
+    const uint32_t ao = act_off<BF>(row, an, pl.nq * d);
     if constexpr (BF) {
       if (dpl == 2) {
-        st8c(ra, ao * 4, u32x2{pack_bf16(o0, o1), my_tag});
+        st8c(ra, ao, u32x2{pack_bf16(o0, o1), my_tag});
       } else {
         // two lanes share a word: the even lane writes both dims
         const float o_nb = __shfl_xor(o0, 1, 64);
-        if ((lane & 1) == 0) st8c(ra, ao * 4, u32x2{pack_bf16(o0, o_nb), my_tag});
+        if ((lane & 1) == 0) st8c(ra, ao, u32x2{pack_bf16(o0, o_nb), my_tag});
       }
     } else {
-      if (dpl == 2) st16c(ra, ao * 8, ll_pair(__float_as_uint(o0), __float_as_uint(o1), my_tag));
-      else st8c(ra, ao * 8, u32x2{__float_as_uint(o0), my_tag});
+      if (dpl == 2) st16c(ra, ao, ll_pair(__float_as_uint(o0), __float_as_uint(o1), my_tag));
+      else st8c(ra, ao, u32x2{__float_as_uint(o0), my_tag});
     }
   }
-  if (!issued) nx.issue(pl);
+  nx.issue(pl);  // after this task's outputs
   stamp(tr, 5);
 }
 
@@ -790,7 +825,7 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
   const int H = pl.H, V = pl.V;
   const rsrc_t re = make_rsrc(pl.embed, (uint32_t)pl.P * V * H * ESZ);
   const rsrc_t rs = make_rsrc(fr.embsum, (uint32_t)fr.rows * H * 4);
-  const uint32_t hbytes = (uint32_t)pl.Rmax * H * ESZ * 2;
+  const uint32_t hbytes = act_bytes<BF>(pl.Rmax, H);
   const rsrc_t rx = make_rsrc((uint8_t*)pl.xin + (size_t)(j + 1) * hbytes, hbytes);
   const uint32_t ebase = (uint32_t)((j * V + code) * H);
   const bool feeds = j + 1 < pl.P;  // the row is the input of position j + 1
@@ -809,7 +844,7 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
         for (int i = 0; i < 4; ++i) ev[i] = __uint_as_float(e[i]);
       }
       if (!first) sv = ld16(rs, (uint32_t)(row * H + k) * 4);
-      if (feeds) st_act4<BF>(rx, (uint32_t)(row * H + k) * ESZ * 2, ev, my_tag);
+      if (feeds) st_act4<BF>(rx, row, k, H, ev, my_tag);
     }
     const float sq = tile_ssq(ev, 1, 4);
     if (in) {
@@ -826,13 +861,13 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
 template <int BF>
 __device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                             const Next& nx, uint64_t* tr) {
-  nx.issue(pl);
   const int row = (int)tk.tile;
   if (row < fr.rows) {
     int code = fr.code0[row];
     code = code < 0 ? 0 : (code >= pl.V ? pl.V - 1 : code);
     embed_row<BF>(pl, fr, 0, row, code, true, tag_of(epoch, tk.phase));
   }
+  nx.issue(pl);
   stamp(tr, 5);
 }
 
@@ -857,7 +892,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
           const int i = i0 + k * 64 + lane;
           cv[k] = i < pl.n_head_tiles ? ld16c(rc, co(k)) : u32x4{0, in_tag, 0xffffffffu, in_tag};
         }
-        ll_poll<4>(pl, rc, co, cv, in_tag, true);
+        await_all(pl, pend(cv, rc, co, in_tag, true, (pl.n_head_tiles - i0 - lane + 63) / 64));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int i = i0 + k * 64 + lane;
@@ -879,11 +914,9 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
     __syncthreads();
-    nx.issue(pl);
     embed_row<BF>(pl, fr, p, row, (int)misc[1], false, tag_of(epoch, tk.phase));
-  } else {
-    nx.issue(pl);
   }
+  nx.issue(pl);
   stamp(tr, 5);
 }
 
@@ -891,12 +924,17 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 
 template <int BF>
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                         uint8_t* slot, uint8_t* gain, uint32_t* misc, const Next& nx, uint64_t* tr) {
+                                         uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
   switch (tk.type) {
     case T_ATTN: attn_task<BF>(pl, fr, tk, epoch, nx, tr); break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, nx, tr); break;
     case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, misc, nx, tr); break;
-    default: proj_task<BF>(pl, fr, tk, epoch, slot, gain, misc, nx, tr); break;
+    case T_QKV: proj_task<BF, T_QKV>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
+    case T_O: proj_task<BF, T_O>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
+    case T_GU: proj_task<BF, T_GU>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
+    case T_DOWN: proj_task<BF, T_DOWN>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
+    case T_HEAD: proj_task<BF, T_HEAD>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
+    default: proj_task<BF, T_INPROJ>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
   }
 }
 
@@ -939,11 +977,10 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t b = pl.wg_begin[blockIdx.x], e = pl.wg_begin[blockIdx.x + 1];
-  uint8_t* gains = (uint8_t*)misc + kGainLds;
   DevTask cur = {};
   if (b < e) {
     cur = pl.tasks[b];
-    issue_tile(pl, cur, lds, gains);
+    issue_tile(pl, cur, lds);
   }
   for (uint32_t i = b; i < e; ++i) {
     uint64_t* tr = pl.trace_on ? pl.trace + (size_t)i * kTraceStamps : nullptr;
@@ -952,9 +989,9 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     // the next record is fetched now; it is first needed in this task's epilogue
     const bool more = i + 1 < e;
     const DevTask nxt = more ? pl.tasks[i + 1] : DevTask{};
-    const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes, gains + (s ^ 1) * 2048};
-    run_task<BF>(pl, fr, cur, epoch, lds + s * kSlotBytes, gains + s * 2048, misc, nx, tr);
-    __syncthreads();  // LDS (tile slot, gains, reductions) of this task is free again
+    const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
+    run_task<BF>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, nx, tr);
+    __syncthreads();  // LDS (tile slot, reductions) of this task is free again
     stamp(tr, 7);
     cur = nxt;
   }
@@ -975,10 +1012,9 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const DevTask tk = tasks[blockIdx.x];
-  uint8_t* gains = (uint8_t*)misc + kGainLds;
-  issue_tile(pl, tk, lds, gains);
-  const Next nx = {DevTask{}, false, nullptr, nullptr};
-  run_task<BF>(pl, fr, tk, epoch, lds, gains, misc, nx, nullptr);
+  issue_tile(pl, tk, lds);
+  const Next nx = {DevTask{}, false, nullptr};
+  run_task<BF>(pl, fr, tk, epoch, lds, misc, nx, nullptr);
 }
 
 // The per-phase executor's last launch of a frame.

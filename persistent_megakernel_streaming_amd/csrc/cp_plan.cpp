@@ -161,13 +161,46 @@ std::vector<int> split_map(int tiles, int nsplit, int n_wg, int& rot) {
 // [k0, k0 + kt).  Output order: chunk step c, row block b, lane, element -- the
 // order in which a wave's 64 lanes read MFMA A fragments (lane l: row l % 16,
 // elements (l / 16) * E .. + E of the step).
-static void pack_tile(std::vector<uint8_t>& blob, const std::vector<const uint8_t*>& rows, int k0, int kt, int esz) {
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+static uint16_t to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Appends rows[*][k0, k0 + kt) in MFMA fragment order: for each K chunk c
+// (4 * E elements), each 16-row block b, each lane (row lane % 16, elements
+// (lane / 16) * E ... + E - 1 of the chunk): 16 bytes.  With `gain`, every
+// element is first multiplied by gain[k] in fp32 and rounded back to the
+// storage type: the RMSNorm gain that precedes the projection, folded in.
+static void pack_tile(std::vector<uint8_t>& blob, const std::vector<const uint8_t*>& rows, int k0, int kt, int esz,
+                      const float* gain = nullptr) {
   const int E = 16 / esz, KS = 4 * E, nb = (int)rows.size() / 16;
   for (int c = 0; c < kt / KS; ++c)
     for (int b = 0; b < nb; ++b)
       for (int lane = 0; lane < 64; ++lane) {
-        const uint8_t* src = rows[16 * b + lane % 16] + (size_t)(k0 + c * KS + (lane / 16) * E) * esz;
-        blob.insert(blob.end(), src, src + 16);
+        const int k = k0 + c * KS + (lane / 16) * E;
+        const uint8_t* src = rows[16 * b + lane % 16] + (size_t)k * esz;
+        if (!gain) {
+          blob.insert(blob.end(), src, src + 16);
+          continue;
+        }
+        uint8_t out[16];
+        for (int e = 0; e < E; ++e) {
+          float f;
+          if (esz == 2) {
+            const uint32_t bits = (uint32_t)((const uint16_t*)src)[e] << 16;
+            std::memcpy(&f, &bits, 4);
+            const uint16_t r = to_bf16(f * gain[k + e]);
+            std::memcpy(out + 2 * e, &r, 2);
+          } else {
+            std::memcpy(&f, src + 4 * e, 4);
+            f *= gain[k + e];
+            std::memcpy(out + 4 * e, &f, 4);
+          }
+        }
+        blob.insert(blob.end(), out, out + 16);
       }
 }
 
@@ -551,6 +584,29 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
   if (!w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->attn_norm || !w->mlp_norm || !w->embed ||
       !w->w_head)
     return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL weight list");
+  // RMSNorm gains, widened to fp32 (exact for bf16): folded into the packed
+  // tiles of the projection each norm feeds (qkv, gate/up, heads).
+  if (!w->final_norm) return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL final_norm");
+  auto gain_f32 = [&](const void* src, std::vector<float>& out) -> cp_status {
+    TRY(fetch(P, src, (size_t)H * esz, m));
+    out.resize(H);
+    for (int i = 0; i < H; ++i) {
+      if (esz == 2) {
+        const uint32_t bits = (uint32_t)((const uint16_t*)m.data())[i] << 16;
+        std::memcpy(&out[i], &bits, 4);
+      } else {
+        std::memcpy(&out[i], m.data() + (size_t)i * 4, 4);
+      }
+    }
+    return CP_OK;
+  };
+  std::vector<std::vector<float>> g_attn(L), g_mlp(L);
+  std::vector<float> g_final;
+  for (int l = 0; l < L; ++l) {
+    TRY(gain_f32(w->attn_norm[l], g_attn[l]));
+    TRY(gain_f32(w->mlp_norm[l], g_mlp[l]));
+  }
+  TRY(gain_f32(w->final_norm, g_final));
   for (int l = 0; l < L; ++l) {
     TRY(fetch(P, w->w_qkv[l], (size_t)(nq + 2 * nkv) * d * H * esz, m));
     for (int t = 0; t < qkv_tiles; ++t) {
@@ -569,7 +625,7 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
         rows[j] = rowp(m, H, r);
       }
       off_qkv[l * qkv_tiles + t] = (uint32_t)blob.size();
-      pack_tile(blob, rows, 0, H, esz);
+      pack_tile(blob, rows, 0, H, esz, g_attn[l].data());
     }
     TRY(fetch(P, w->w_o[l], (size_t)H * qd * esz, m));
     for (int t = 0; t < ht; ++t)
@@ -588,7 +644,7 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
         rows[16 + j] = rowp(m2, H, 16 * t + j);
       }
       off_gu[l * (I / 16) + t] = (uint32_t)blob.size();
-      pack_tile(blob, rows, 0, H, esz);
+      pack_tile(blob, rows, 0, H, esz, g_mlp[l].data());
     }
     TRY(fetch(P, w->w_down[l], (size_t)H * I * esz, m));
     for (int t = 0; t < ht; ++t)
@@ -606,7 +662,7 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
       std::vector<const uint8_t*> rows(16);
       for (int i = 0; i < 16; ++i) rows[i] = rowp(m, H, 16 * t + i);
       off_head[(j - 1) * (V / 16) + t] = (uint32_t)blob.size();
-      pack_tile(blob, rows, 0, H, esz);
+      pack_tile(blob, rows, 0, H, esz, g_final.data());
     }
   }
   TRY(fetch(P, w->w_in, (size_t)H * Din * esz, m));
@@ -640,27 +696,7 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
   P->dp.wblob = (const uint8_t*)dblob;
   P->packed_bytes = (int64_t)blob.size();
 
-  // norm gains [2L + 1][H], embedding tables [P][V][H], RoPE table [P][d/2][2]
-  std::vector<uint8_t> gains((size_t)(2 * L + 1) * H * esz);
-  for (int l = 0; l < L; ++l) {
-    TRY(fetch(P, w->attn_norm[l], (size_t)H * esz, m));
-    std::memcpy(gains.data() + (size_t)(2 * l) * H * esz, m.data(), (size_t)H * esz);
-    TRY(fetch(P, w->mlp_norm[l], (size_t)H * esz, m));
-    std::memcpy(gains.data() + (size_t)(2 * l + 1) * H * esz, m.data(), (size_t)H * esz);
-  }
-  TRY(fetch(P, w->final_norm, (size_t)H * esz, m));
-  std::memcpy(gains.data() + (size_t)(2 * L) * H * esz, m.data(), (size_t)H * esz);
-  // All gains exactly 1: the kernel skips the gain product (x * 1 == x).
-  bool unit = true;
-  for (size_t i = 0; i < gains.size() / esz && unit; ++i) {
-    if (esz == 2) unit = ((const uint16_t*)gains.data())[i] == 0x3f80;
-    else unit = ((const uint32_t*)gains.data())[i] == 0x3f800000u;
-  }
-  P->dp.unit_gains = unit ? 1 : 0;
-  void* dg;
-  TRY(alloc(P, &dg, gains.size()));
-  HIPCHK(P, hipMemcpy(dg, gains.data(), gains.size(), hipMemcpyHostToDevice));
-  P->dp.gains = dg;
+  // embedding tables [P][V][H], RoPE table [P][d/2][2]
   void* de;
   TRY(alloc(P, &de, (size_t)Pn * V * H * esz));
   for (int j = 0; j < Pn; ++j) {
@@ -706,12 +742,15 @@ static cp_status alloc_scratch(cp_plan* P) {
   DevPlan& dp = P->dp;
   void* p;
   const size_t e2 = (size_t)esz * 2;  // tagged words: payload + tag per element pair (bf16) or element (fp32)
-  TRY(alloc(P, &p, (size_t)Pn * R * H * e2, true)); dp.xin = p;
-  TRY(alloc(P, &p, (size_t)2 * 2 * R * H * e2, true)); dp.hres = p;     // [parity][layer parity]
-  TRY(alloc(P, &p, (size_t)2 * R * H * e2, true)); dp.hmid = p;
-  TRY(alloc(P, &p, (size_t)2 * R * nq * d * e2, true)); dp.qbuf = p;
-  TRY(alloc(P, &p, (size_t)2 * R * nq * d * e2, true)); dp.abuf = p;
-  TRY(alloc(P, &p, (size_t)2 * R * I * e2, true)); dp.mbuf = p;
+  // Projection operands (position inputs, residuals, attention and SwiGLU
+  // outputs) are kept in the kernels' operand order, whole 16-row tiles.
+  const size_t Rp = (size_t)((R + 15) / 16) * 16;
+  TRY(alloc(P, &p, (size_t)Pn * Rp * H * e2, true)); dp.xin = p;
+  TRY(alloc(P, &p, (size_t)2 * 2 * Rp * H * e2, true)); dp.hres = p;    // [parity][layer parity]
+  TRY(alloc(P, &p, (size_t)2 * Rp * H * e2, true)); dp.hmid = p;
+  TRY(alloc(P, &p, (size_t)2 * R * nq * d * e2, true)); dp.qbuf = p;     // row-major (attention input)
+  TRY(alloc(P, &p, (size_t)2 * Rp * nq * d * e2, true)); dp.abuf = p;
+  TRY(alloc(P, &p, (size_t)2 * Rp * I * e2, true)); dp.mbuf = p;
   TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.kc = p;
   TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.vc = p;
   const size_t part_one = (size_t)(H / 16) * 4 * R * 16;  // words per split-K phase buffer

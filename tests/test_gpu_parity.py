@@ -108,6 +108,17 @@ def test_full_l5_64_rows_sampled_rows():
     print(f"l5 r64: max logit err {err:.4f}, decided {frac:.2f}")
 
 
+def test_full_l5_40_rows_idle_wave():
+    """40 rows: three row tiles, so one of the four waves has no rows (it
+    still copies its share of every weight tile)."""
+    cfg = synth.CONFIGS["l5_r64"].with_(rows=40)
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg)
+    gpu = _gpu_frame(cfg, wdev, inputs, max_rows=40)
+    err, frac = _check(cfg, ow, inputs, gpu, [0, 39], 0.05)
+    print(f"l5 r40: max logit err {err:.4f}, decided {frac:.2f}")
+
+
 def test_persistent_equals_per_phase_bitwise():
     cfg = synth.CONFIGS["l5_r64"]
     w, wdev, ow = _weights(cfg)
