@@ -54,8 +54,9 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
 
 /* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
  * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a
- * multiple of 256 up to 1024; input_dim, intermediate and vocab multiples of
- * 64; 2 <= n_positions <= 16; 1 <= max_rows <= 64. */
+ * multiple of 256 up to 1024; input_dim and intermediate multiples of 64;
+ * vocab a multiple of 256 up to 4096; 2 <= n_positions <= 16;
+ * 1 <= max_rows <= 64. */
 typedef struct {
   int32_t abi_version;  /* CP_ABI_VERSION */
   int32_t n_layers;
@@ -99,10 +100,18 @@ typedef struct {
   int32_t rows;              /* 1 .. max_rows */
   const void* hidden_in;     /* [rows][input_dim], dtype */
   const int32_t* code0;      /* [rows] code 0 (from outside the loop), each in [0, vocab) */
-  /* Sampling, [rows] each.  All five NULL: greedy for every row.  Some but not
-   * all NULL: CP_ERR_INVALID_ARGUMENT.  Per-row values never fail on the
-   * device: temperature <= 0 is greedy; top_k <= 0 or >= vocab is no top-k
-   * cut; top_p >= 1 is no top-p cut, top_p <= 0 keeps the best token only. */
+  /* Sampling, [rows] each.  All five NULL: greedy for every row (the lowest
+   * index of the largest logit).  Some but not all NULL:
+   * CP_ERR_INVALID_ARGUMENT.  Draw j of a row (j = 1 .. n_positions-1), as
+   * the sampler is defined: y = logits / temperature; keep the top_k largest
+   * y (ties to the lower index); softmax over them; keep the shortest prefix
+   * in rank order whose probability mass reaches top_p (the crossing token
+   * included); the code is the kept i with the largest y_i - log(-log u_i),
+   * u_i = (2m + 1) / 2^24 with m the top 23 bits of word 0 of
+   * Philox4x64-10(counter = (offset + j - 1, i, 0, 0), key = (seed, 0)).
+   * Per-row values never fail on the device: temperature <= 0 is greedy;
+   * top_k <= 0 or >= vocab is no top-k cut; top_p >= 1 is no top-p cut,
+   * top_p <= 0 keeps the best token only. */
   const float* temperature;
   const int32_t* top_k;
   const float* top_p;

@@ -871,12 +871,220 @@ __device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& f
   stamp(tr, 5);
 }
 
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): ten rounds, each two 64 x 64 -> 128-bit products
+// whose halves are mixed with the other two words and the key, then a Weyl
+// step of the key.  Returns word 0 of the output block.
+__device__ __forceinline__ uint64_t philox4x64_w0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                                  uint64_t k1) {
+  constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull, kMul1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kWeyl0 = 0x9E3779B97F4A7C15ull, kWeyl1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kMul0, c0), lo0 = kMul0 * c0;
+    const uint64_t hi1 = __umul64hi(kMul1, c2), lo1 = kMul1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += kWeyl0; k1 += kWeyl1;
+  }
+  return c0;
+}
+
+// Sort key of a scaled logit: larger value first, then lower index.  -0 is
+// taken as +0 so that equal values tie on the index alone.
+__device__ __forceinline__ uint64_t rank_key(float y, uint32_t i) {
+  uint32_t u = __float_as_uint(y == 0.0f ? 0.0f : y);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(~i);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
+
+// Block-wide reductions over the 256 threads through LDS (red: 256 entries).
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + s];
+    __syncthreads();
+  }
+  const double r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// Sampled draw of one row (the row's whole workgroup), in the order the
+// sampler is defined: y = z / T; the top-k largest y (ties to the lower
+// index; k <= 0 or k >= V keeps all); softmax over them; top-p keeps the
+// shortest rank-order prefix whose mass reaches p (the crossing token
+// included; p >= 1 keeps all, p <= 0 the first); then Gumbel-max: the code is
+// the kept i with the largest y_i - log(-log u_i), u_i from Philox4x64-10 with
+// key (seed, 0) and counter (offset + j - 1, i, 0, 0): the top 23 bits m of
+// word 0 give u = (2m + 1) / 2^24.  T <= 0 is a greedy draw on z.
+// z: this thread's V / 256 logits (index threadIdx.x + 256 e).  scratch: LDS,
+// at least Vp * 8 + 2048 bytes, Vp = V rounded up to a power of two.
+__device__ int sampled_code(const DevPlan& pl, const DevFrame& fr, int row, int j, const float* z, int nz,
+                            uint8_t* scratch) {
+  const int V = pl.V;
+  int Vp = 1;
+  while (Vp < V) Vp <<= 1;
+  uint64_t* keys = (uint64_t*)scratch;
+  double* red = (double*)(scratch + (size_t)Vp * 8);
+  const float T = fr.temperature[row];
+  const int tid = threadIdx.x;
+  if (!(T > 0.0f)) {  // greedy on z: the largest value, lowest index
+    uint64_t best = 0;
+    for (int e = 0; e < nz; ++e) {
+      const uint64_t k = rank_key(z[e], (uint32_t)(tid + kThreads * e));
+      best = k > best ? k : best;
+    }
+    keys[tid] = best;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+      if (tid < s && keys[tid + s] > keys[tid]) keys[tid] = keys[tid + s];
+      __syncthreads();
+    }
+    const int code = (int)key_index(keys[0]);
+    __syncthreads();
+    return code;
+  }
+  // keys of y = z / T (IEEE division), padding ranks last
+  for (int e = 0; e < Vp / kThreads; ++e) {
+    const int i = tid + kThreads * e;
+    keys[i] = (i < V) ? rank_key(z[e] / T, (uint32_t)i) : 0ull;
+  }
+  __syncthreads();
+  // bitonic sort, descending
+  for (int k = 2; k <= Vp; k <<= 1)
+    for (int h = k >> 1; h > 0; h >>= 1) {
+      for (int t = tid; t < Vp / 2; t += kThreads) {
+        const int i = 2 * h * (t / h) + (t % h), m = i + h;
+        const uint64_t a = keys[i], b = keys[m];
+        const bool desc = (i & k) == 0;
+        if (desc ? (a < b) : (a > b)) {
+          keys[i] = b;
+          keys[m] = a;
+        }
+      }
+      __syncthreads();
+    }
+  const int tk = fr.top_k[row];
+  const int kk = (tk <= 0 || tk >= V) ? V : tk;
+  const float pp = fr.top_p[row];
+  // this thread's ranks: [r0, r0 + per)
+  const int per = Vp / kThreads, r0 = tid * per;
+  const double ymax = (double)key_value(keys[0]);
+  double wsum = 0.0;
+  for (int e = 0; e < per; ++e)
+    if (r0 + e < kk) wsum += exp((double)key_value(keys[r0 + e]) - ymax);
+  int n_keep = kk;
+  if (pp <= 0.0f) {
+    n_keep = 1;
+  } else if (pp < 1.0f) {
+    // exclusive prefix of the per-thread sums (ranks are contiguous per thread)
+    red[tid] = wsum;
+    __syncthreads();
+    double pre = 0.0, Z = 0.0;
+    for (int t = 0; t < kThreads; ++t) {
+      const double w = red[t];
+      if (t < tid) pre += w;
+      Z += w;
+    }
+    __syncthreads();
+    int first = 0x7fffffff;  // first rank whose cumulative mass reaches p
+    double cum = pre;
+    for (int e = 0; e < per; ++e) {
+      const int t = r0 + e;
+      if (t < kk) {
+        cum += exp((double)key_value(keys[t]) - ymax);
+        if (first == 0x7fffffff && cum / Z >= (double)pp) first = t;
+      }
+    }
+    // block minimum of `first`
+    red[tid] = (double)first;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+      if (tid < s && red[tid + s] < red[tid]) red[tid] = red[tid + s];
+      __syncthreads();
+    }
+    const double fmin = red[0];
+    __syncthreads();
+    if (fmin < (double)kk) n_keep = (int)fmin + 1;
+  }
+  // Gumbel-max over the kept ranks
+  const uint64_t seed = fr.seed[row], ctr = fr.offset[row] + (uint64_t)(j - 1);
+  double best_s = -INFINITY;
+  uint32_t best_i = 0xffffffffu;
+  for (int e = 0; e < per; ++e) {
+    const int t = r0 + e;
+    if (t < n_keep) {
+      const uint64_t key = keys[t];
+      const uint32_t i = key_index(key);
+      const uint64_t m = philox4x64_w0(ctr, (uint64_t)i, 0, 0, seed, 0) >> 41;
+      const double u = (double)(2 * m + 1) * (1.0 / 16777216.0);
+      const double sc = (double)key_value(key) - log(-log(u));
+      if (sc > best_s || (sc == best_s && i < best_i)) {
+        best_s = sc;
+        best_i = i;
+      }
+    }
+  }
+  // block argmax (score, then lower index)
+  __syncthreads();
+  red[tid] = best_s;
+  keys[tid] = best_i;  // the sorted keys are no longer needed
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) {
+      const double os = red[tid + s];
+      const uint64_t oi = keys[tid + s];
+      if (os > red[tid] || (os == red[tid] && oi < keys[tid])) {
+        red[tid] = os;
+        keys[tid] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  const int code = (int)keys[0];
+  __syncthreads();
+  return code;
+}
+
 template <int BF>
 __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint32_t* misc, const Next& nx, uint64_t* tr) {
+                                          uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
   const int row = (int)tk.tile, p = tk.pos;
   const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
-  if (row < fr.rows) {
+  if (row < fr.rows && fr.sampled) {
+    // the row's V logits (tagged words) from the head tiles
+    constexpr int kMaxPer = 16;  // V <= 4096
+    const int nz = pl.V / kThreads;
+    const rsrc_t rz = make_rsrc(pl.zbuf, (uint32_t)pl.Rmax * pl.V * 8);
+    const uint32_t zb = (uint32_t)(row * pl.V + threadIdx.x) * 8;
+    auto zo = [=](int e) -> uint32_t { return zb + e * kThreads * 8; };
+    u32x2 zw[kMaxPer];
+#pragma unroll
+    for (int e = 0; e < kMaxPer; ++e)
+      zw[e] = e < nz ? __builtin_amdgcn_raw_buffer_load_b64(rz, zo(e), 0, kSC1) : u32x2{0, in_tag};
+    await_all(pl, pend(zw, rz, zo, in_tag, true, nz));
+    float z[kMaxPer];
+#pragma unroll
+    for (int e = 0; e < kMaxPer; ++e) z[e] = __uint_as_float(zw[e][0]);
+    int code = sampled_code(pl, fr, row, p, z, nz, slot);
+    code = (code < 0 || code >= pl.V) ? 0 : code;
+    if (threadIdx.x == 0) {
+      st4(make_rsrc(fr.codes, (uint32_t)fr.rows * (pl.P - 1) * 4), (uint32_t)(row * (pl.P - 1) + p - 1) * 4,
+          (uint32_t)code);
+      if (p == pl.P - 1) {  // the frame's draws of this row are done: advance its offset
+        const uint64_t o = fr.offset[row] + (uint64_t)(pl.P - 1);
+        st8c(make_rsrc(fr.offset, (uint32_t)fr.rows * 8), (uint32_t)row * 8, u32x2{(uint32_t)o, (uint32_t)(o >> 32)});
+      }
+    }
+    embed_row<BF>(pl, fr, p, row, code, false, tag_of(epoch, tk.phase));
+  } else if (row < fr.rows) {
     if (threadIdx.x < 64) {
       // the head tiles' (value, index) candidates of this row, tile order
       const int lane = threadIdx.x;
@@ -928,7 +1136,7 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
   switch (tk.type) {
     case T_ATTN: attn_task<BF>(pl, fr, tk, epoch, nx, tr); break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, nx, tr); break;
-    case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, misc, nx, tr); break;
+    case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
     case T_QKV: proj_task<BF, T_QKV>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
     case T_O: proj_task<BF, T_O>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
     case T_GU: proj_task<BF, T_GU>(pl, fr, tk, epoch, slot, misc, nx, tr); break;

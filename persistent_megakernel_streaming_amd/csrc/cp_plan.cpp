@@ -218,6 +218,7 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   if (c->n_q_heads % c->n_kv_heads) { msg = "n_q_heads must be a multiple of n_kv_heads"; return CP_ERR_UNSUPPORTED; }
   if (c->n_positions < 2 || c->n_positions > 16) { msg = "n_positions must be in 2..16"; return CP_ERR_UNSUPPORTED; }
   if (c->max_rows > kMaxRows) { msg = "max_rows must be <= 64"; return CP_ERR_UNSUPPORTED; }
+  if (c->vocab % 256 || c->vocab > 4096) { msg = "vocab must be a multiple of 256, at most 4096"; return CP_ERR_UNSUPPORTED; }
   if (c->hidden % 64 || c->input_dim % 64 || c->intermediate % 64 || c->vocab % 64) {
     msg = "hidden, input_dim, intermediate and vocab must be multiples of 64";
     return CP_ERR_UNSUPPORTED;
@@ -924,7 +925,6 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
   const int nsamp = (io->temperature != nullptr) + (io->top_k != nullptr) + (io->top_p != nullptr) +
                     (io->seed != nullptr) + (io->offset != nullptr);
   if (nsamp != 0 && nsamp != 5) return fail(P, CP_ERR_INVALID_ARGUMENT, "sampling arrays must be all set or all NULL");
-  if (nsamp == 5) return fail(P, CP_ERR_UNSUPPORTED, "sampled draws are not built yet");
   if (io->trace && !(c.flags & CP_FLAG_TRACE)) return fail(P, CP_ERR_INVALID_ARGUMENT, "trace needs CP_FLAG_TRACE");
   if (io->trace && c.exec != CP_EXEC_PERSISTENT) return fail(P, CP_ERR_UNSUPPORTED, "trace needs the persistent executor");
   DevFrame fr{};

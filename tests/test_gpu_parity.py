@@ -197,3 +197,108 @@ def test_epoch_wrap(exec_mode):
     plan.device_status()
     plan.close()
     _check(cfg, ow, inputs, ref, range(3), 0.05, kv=True)
+
+
+def _sampled_decided(margins, dy):
+    """Draws whose code the oracle fixes robustly, given dy, the largest
+    difference between the GPU's and the oracle's scaled logits y = z / T of
+    the draw: a perturbed-score gap over the kept set of at least
+    max(0.1, 2 dy), and a kept set that such differences cannot change --
+    where top-p cut it, the crossing is at least max(1e-3, 2 dy) of
+    probability mass from the threshold on both sides (a shift of dy in every
+    logit moves a probability by a factor of at most e^(2 dy)); where top-k
+    cut it, the k-th and (k+1)-th scaled logits are at least max(0.1, 2 dy)
+    apart."""
+    gap, m_k, m_before, m_at = (margins[..., i] for i in range(4))
+    tol = np.maximum(0.1, 2 * dy)
+    mass_tol = np.maximum(1e-3, 2 * dy)
+    top_p_cut = np.isfinite(m_before)
+    kept_robust = np.where(top_p_cut, (m_before >= mass_tol) & (m_at >= mass_tol), m_k >= tol)
+    return (gap >= tol) & kept_robust
+
+
+def _check_draws_on_gpu_logits(cfg, inputs, gpu, rows):
+    """The GPU's sampler against the oracle's on the GPU's own logits: the same
+    code wherever no boundary is closer than rounding can reach (1e-9)."""
+    from oracle import oracle
+    n, same = 0, 0
+    for r in rows:
+        for j in range(1, cfg.n_positions):
+            z = gpu["logits"][r, j - 1]
+            code, m = oracle.draw(z, inputs["temperature"][r], inputs["top_k"][r], inputs["top_p"][r],
+                                  int(inputs["seed"][r]), int(inputs["offset"][r]) + j - 1)
+            if min(m[0], m[1], m[2], m[3]) < 1e-9:
+                continue
+            n += 1
+            assert gpu["codes"][r, j - 1] == code, (r, j, int(gpu["codes"][r, j - 1]), code, m.tolist())
+            same += 1
+    assert n >= 0.9 * len(rows) * (cfg.n_positions - 1)
+    return n
+
+
+def _check_sampled(cfg, ow, inputs, gpu, rows, logit_tol, min_decided=0.0):
+    from oracle import oracle
+    rows = list(rows)
+    _check_draws_on_gpu_logits(cfg, inputs, gpu, rows)
+    orc = oracle.run_frame(cfg, ow, inputs, forced_codes=gpu["codes"][rows], rows=rows)
+    err = np.abs(gpu["logits"][rows] - orc["logits"]).max()
+    assert err <= logit_tol, f"max |logit diff| {err}"
+    T = np.asarray(inputs["temperature"], np.float32)[rows]
+    dz = np.abs(gpu["logits"][rows] - orc["logits"]).max(axis=2)  # [rows][P-1]
+    dy = np.where(T[:, None] > 0, dz / np.where(T > 0, T, 1)[:, None], dz)
+    decided = _sampled_decided(orc["margins"], dy)
+    assert decided.mean() >= min_decided, f"too few robust draws to test ({decided.mean():.2f})"
+    bad = np.argwhere(decided & (gpu["codes"][rows] != orc["codes"]))
+    assert len(bad) == 0, [(rows[r], j + 1, int(gpu["codes"][rows][r, j]), int(orc["codes"][r, j]),
+                            orc["margins"][r, j].round(4).tolist(), float(dy[r, j])) for r, j in bad[:5]]
+    assert np.array_equal(gpu["embsum"][rows], orc["embsum"]), "embedding sums differ"
+    off_in = np.asarray(inputs["offset"], np.uint64)[rows]
+    assert np.array_equal(gpu["offset"].view(np.uint64)[rows], off_in + np.uint64(cfg.n_positions - 1))
+    assert np.array_equal(orc["offset"], off_in + np.uint64(cfg.n_positions - 1))
+    return err, decided.mean()
+
+
+def _edge_sampling(inputs, V):
+    """Per-row sampler settings at their edges: greedy, no top-k cut, top-k 1,
+    top-k >= vocab, no top-p cut, top-p 0."""
+    t, k, p = inputs["temperature"].copy(), inputs["top_k"].copy(), inputs["top_p"].copy()
+    edits = [("temperature", 0.0), ("top_k", 0), ("top_k", 1), ("top_k", V), ("top_p", 1.0), ("top_p", 0.0),
+             ("temperature", -1.0), ("top_k", -5)]
+    arrs = {"temperature": t, "top_k": k, "top_p": p}
+    for r, (name, v) in enumerate(edits[: len(t) - 1]):
+        arrs[name][r + 1] = v
+    return dict(inputs, temperature=t, top_k=k, top_p=p)
+
+
+@pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
+def test_sampled_tiny_fp32(exec_mode):
+    cfg = synth.CONFIGS["tiny_f32"].with_(rows=8, sampled=True)
+    w, wdev, ow = _weights(cfg, seed=6, gain_jitter=True)
+    inputs = _edge_sampling(synth.make_inputs(cfg, seed=6, sampled=True), cfg.vocab)
+    # sharper distributions (T / 4) so that more draws are robustly decided
+    inputs["temperature"] = np.where(inputs["temperature"] > 0, inputs["temperature"] * np.float32(0.25),
+                                     inputs["temperature"]).astype(np.float32)
+    gpu = _gpu_frame(cfg, wdev, inputs, exec_mode)
+    err, frac = _check_sampled(cfg, ow, inputs, gpu, range(8), 1e-4, min_decided=0.2)
+    print(f"sampled tiny {exec_mode}: max logit err {err:.2e}, robust draws {frac:.2f}")
+
+
+def test_sampled_l5_64_rows():
+    cfg = synth.CONFIGS["l5_r64_sampled"]
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg, sampled=True)
+    gpu = _gpu_frame(cfg, wdev, inputs)
+    err, frac = _check_sampled(cfg, ow, inputs, gpu, [0, 21, 42, 63], 0.05)
+    print(f"sampled l5 r64: max logit err {err:.4f}, robust draws {frac:.2f}")
+
+
+def test_sampled_persistent_equals_per_phase_and_repeats():
+    cfg = synth.CONFIGS["l5_r64_sampled"].with_(rows=9)
+    w, wdev, ow = _weights(cfg)
+    inputs = _edge_sampling(synth.make_inputs(cfg, sampled=True), cfg.vocab)
+    a = _gpu_frame(cfg, wdev, inputs, "persistent", max_rows=16)
+    b = _gpu_frame(cfg, wdev, inputs, "per_phase", max_rows=16)
+    c = _gpu_frame(cfg, wdev, inputs, "persistent", max_rows=16)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+        assert np.array_equal(a[k], c[k]), k
