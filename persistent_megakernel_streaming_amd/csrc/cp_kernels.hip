@@ -903,17 +903,124 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 }
 __device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
 
-// Block-wide reductions over the 256 threads through LDS (red: 256 entries).
-__device__ __forceinline__ double block_sum(double v, double* red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + s];
-    __syncthreads();
+// Bitonic compare-exchange helpers for the sampler's sort (descending keys).
+// `keep_max`: this side of the pair keeps the larger key.
+__device__ __forceinline__ uint64_t cx_pick(uint64_t mine, uint64_t other, bool keep_max) {
+  return keep_max ? (mine > other ? mine : other) : (mine < other ? mine : other);
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sorts the block's Vp = 256 * NE keys descending; thread t holds elements
+// t * NE .. t * NE + NE - 1 in k[], and ends holding ranks in the same places.
+// Strides below NE stay in registers, strides below 64 * NE use wave
+// shuffles, larger strides go through LDS (xch: Vp keys).
+template <int NE>
+__device__ __forceinline__ void block_sort_desc(uint64_t (&k)[NE], int Vp, uint64_t* xch) {
+  const int tid = threadIdx.x;
+  for (int kb = 2; kb <= Vp; kb <<= 1) {
+    for (int h = kb >> 1; h > 0; h >>= 1) {
+      if (h < NE) {
+        // in registers: one compile-time stride per branch, so k[] stays in VGPRs
+#pragma unroll
+        for (int hh = NE / 2; hh >= 1; hh >>= 1) {
+          if (hh == h) {
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+              if ((e & hh) == 0) {
+                const bool desc = ((tid * NE + e) & kb) == 0;
+                const uint64_t a = k[e], b = k[e + hh];
+                const bool swap = desc ? (a < b) : (a > b);
+                k[e] = swap ? b : a;
+                k[e + hh] = swap ? a : b;
+              }
+            }
+          }
+        }
+      } else if (h < 64 * NE) {
+        const int lm = h / NE;  // lane distance
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const int i = tid * NE + e;
+          const bool desc = (i & kb) == 0, low = (tid & lm) == 0;
+          k[e] = cx_pick(k[e], shfl_xor_u64(k[e], lm), desc == low);
+        }
+      } else {
+        const int tm = h / NE;  // thread distance
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < NE; ++e) xch[tid * NE + e] = k[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const int i = tid * NE + e;
+          const bool desc = (i & kb) == 0, low = (tid & tm) == 0;
+          k[e] = cx_pick(k[e], xch[(tid ^ tm) * NE + e], desc == low);
+        }
+      }
+    }
   }
-  const double r = red[0];
+}
+
+// Exclusive prefix sum over the block (thread order) and the block total.
+// red: 8 doubles of LDS.
+__device__ __forceinline__ double block_exscan(double v, double* red, double& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  double before = 0.0;
+  total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    const double t = red[w];
+    if (w < wave) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+// Block minimum of an int.  red: 4 words of LDS.
+__device__ __forceinline__ int block_min_int(int v, uint32_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = min(v, __shfl_xor(v, m, 64));
+  if (lane == 0) red[wave] = (uint32_t)v;
+  __syncthreads();
+  int r = (int)red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = min(r, (int)red[w]);
   __syncthreads();
   return r;
+}
+
+// Block maximum of (score, index): larger score, then lower index.
+__device__ __forceinline__ uint32_t block_argmax(double sc, uint32_t idx, double* red, uint32_t* redi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const double os = __shfl_xor(sc, m, 64);
+    const uint32_t oi = (uint32_t)__shfl_xor((int)idx, m, 64);
+    if (os > sc || (os == sc && oi < idx)) { sc = os; idx = oi; }
+  }
+  if (lane == 0) { red[wave] = sc; redi[wave] = idx; }
+  __syncthreads();
+  double bs = red[0];
+  uint32_t bi = redi[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w)
+    if (red[w] > bs || (red[w] == bs && redi[w] < bi)) { bs = red[w]; bi = redi[w]; }
+  __syncthreads();
+  return bi;
 }
 
 // Sampled draw of one row (the row's whole workgroup), in the order the
@@ -924,133 +1031,115 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 // the kept i with the largest y_i - log(-log u_i), u_i from Philox4x64-10 with
 // key (seed, 0) and counter (offset + j - 1, i, 0, 0): the top 23 bits m of
 // word 0 give u = (2m + 1) / 2^24.  T <= 0 is a greedy draw on z.
-// z: this thread's V / 256 logits (index threadIdx.x + 256 e).  scratch: LDS,
-// at least Vp * 8 + 2048 bytes, Vp = V rounded up to a power of two.
-__device__ int sampled_code(const DevPlan& pl, const DevFrame& fr, int row, int j, const float* z, int nz,
-                            uint8_t* scratch) {
-  const int V = pl.V;
-  int Vp = 1;
-  while (Vp < V) Vp <<= 1;
-  uint64_t* keys = (uint64_t*)scratch;
-  double* red = (double*)(scratch + (size_t)Vp * 8);
-  const float T = fr.temperature[row];
+// z: this thread's NE logits, element index threadIdx.x * NE + e (V = 256 NE).
+// scratch: LDS, V * 8 + 128 bytes.  Kept out of line: it runs once per draw
+// and would otherwise add to the register pressure of every task body.
+template <int NE>
+struct ZRow {
+  float v[NE];
+};
+struct DrawArgs {
+  float T, top_p;
+  int top_k;
+  uint64_t seed, ctr;  // Philox key word 0 and counter word 0 of this draw
+};
+template <int NE>
+__device__ __noinline__ int sampled_code(ZRow<NE> zr, DrawArgs da, uint8_t* scratch) {
+  const int V = kThreads * NE;
+  uint64_t* xch = (uint64_t*)scratch;
+  double* red = (double*)(scratch + (size_t)V * 8);
+  uint32_t* redi = (uint32_t*)(red + 8);
+  const float* z = zr.v;
+  const float T = da.T;
   const int tid = threadIdx.x;
   if (!(T > 0.0f)) {  // greedy on z: the largest value, lowest index
-    uint64_t best = 0;
-    for (int e = 0; e < nz; ++e) {
-      const uint64_t k = rank_key(z[e], (uint32_t)(tid + kThreads * e));
-      best = k > best ? k : best;
-    }
-    keys[tid] = best;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-      if (tid < s && keys[tid + s] > keys[tid]) keys[tid] = keys[tid + s];
-      __syncthreads();
-    }
-    const int code = (int)key_index(keys[0]);
-    __syncthreads();
-    return code;
+    double bs = -INFINITY;
+    uint32_t bi = 0xffffffffu;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      if ((double)z[e] > bs) { bs = (double)z[e]; bi = (uint32_t)(tid * NE + e); }
+    return (int)block_argmax(bs, bi, red, redi);
   }
-  // keys of y = z / T (IEEE division), padding ranks last
-  for (int e = 0; e < Vp / kThreads; ++e) {
-    const int i = tid + kThreads * e;
-    keys[i] = (i < V) ? rank_key(z[e] / T, (uint32_t)i) : 0ull;
-  }
-  __syncthreads();
-  // bitonic sort, descending
-  for (int k = 2; k <= Vp; k <<= 1)
-    for (int h = k >> 1; h > 0; h >>= 1) {
-      for (int t = tid; t < Vp / 2; t += kThreads) {
-        const int i = 2 * h * (t / h) + (t % h), m = i + h;
-        const uint64_t a = keys[i], b = keys[m];
-        const bool desc = (i & k) == 0;
-        if (desc ? (a < b) : (a > b)) {
-          keys[i] = b;
-          keys[m] = a;
-        }
-      }
-      __syncthreads();
-    }
-  const int tk = fr.top_k[row];
+  // keys of y = z / T (IEEE division), sorted descending: rank tid * NE + e
+  uint64_t k[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) k[e] = rank_key(z[e] / T, (uint32_t)(tid * NE + e));
+  block_sort_desc<NE>(k, V, xch);
+  const int tk = da.top_k;
   const int kk = (tk <= 0 || tk >= V) ? V : tk;
-  const float pp = fr.top_p[row];
-  // this thread's ranks: [r0, r0 + per)
-  const int per = Vp / kThreads, r0 = tid * per;
-  const double ymax = (double)key_value(keys[0]);
-  double wsum = 0.0;
-  for (int e = 0; e < per; ++e)
-    if (r0 + e < kk) wsum += exp((double)key_value(keys[r0 + e]) - ymax);
+  const float pp = da.top_p;
+  // ranks to LDS: the Gumbel step deals them round-robin over the block (the
+  // kept ranks are the first few, which one thread would otherwise hold)
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < NE; ++e) xch[tid * NE + e] = k[e];
+  __syncthreads();
   int n_keep = kk;
   if (pp <= 0.0f) {
     n_keep = 1;
-  } else if (pp < 1.0f) {
-    // exclusive prefix of the per-thread sums (ranks are contiguous per thread)
-    red[tid] = wsum;
-    __syncthreads();
-    double pre = 0.0, Z = 0.0;
-    for (int t = 0; t < kThreads; ++t) {
-      const double w = red[t];
-      if (t < tid) pre += w;
-      Z += w;
+  } else if (pp < 1.0f) {  // softmax weights relative to the largest y, fp64
+    const double ymax = (double)key_value(xch[0]);
+    double w[NE], wsum = 0.0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      w[e] = (tid * NE + e < kk) ? exp((double)key_value(k[e]) - ymax) : 0.0;
+      wsum += w[e];
     }
-    __syncthreads();
+    double Z;
+    double cum = block_exscan(wsum, red, Z);
     int first = 0x7fffffff;  // first rank whose cumulative mass reaches p
-    double cum = pre;
-    for (int e = 0; e < per; ++e) {
-      const int t = r0 + e;
-      if (t < kk) {
-        cum += exp((double)key_value(keys[t]) - ymax);
-        if (first == 0x7fffffff && cum / Z >= (double)pp) first = t;
-      }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      cum += w[e];
+      if (first == 0x7fffffff && tid * NE + e < kk && cum / Z >= (double)pp) first = tid * NE + e;
     }
-    // block minimum of `first`
-    red[tid] = (double)first;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-      if (tid < s && red[tid + s] < red[tid]) red[tid] = red[tid + s];
-      __syncthreads();
-    }
-    const double fmin = red[0];
-    __syncthreads();
-    if (fmin < (double)kk) n_keep = (int)fmin + 1;
+    const int fmin = block_min_int(first, redi);
+    if (fmin < kk) n_keep = fmin + 1;
   }
   // Gumbel-max over the kept ranks
-  const uint64_t seed = fr.seed[row], ctr = fr.offset[row] + (uint64_t)(j - 1);
+  const uint64_t seed = da.seed, ctr = da.ctr;
   double best_s = -INFINITY;
   uint32_t best_i = 0xffffffffu;
-  for (int e = 0; e < per; ++e) {
-    const int t = r0 + e;
-    if (t < n_keep) {
-      const uint64_t key = keys[t];
-      const uint32_t i = key_index(key);
-      const uint64_t m = philox4x64_w0(ctr, (uint64_t)i, 0, 0, seed, 0) >> 41;
-      const double u = (double)(2 * m + 1) * (1.0 / 16777216.0);
-      const double sc = (double)key_value(key) - log(-log(u));
-      if (sc > best_s || (sc == best_s && i < best_i)) {
-        best_s = sc;
-        best_i = i;
-      }
-    }
+  for (int r = tid; r < n_keep; r += kThreads) {
+    const uint64_t key = xch[r];
+    const uint32_t i = key_index(key);
+    const uint64_t m = philox4x64_w0(ctr, (uint64_t)i, 0, 0, seed, 0) >> 41;
+    const double u = (double)(2 * m + 1) * (1.0 / 16777216.0);
+    const double sc = (double)key_value(key) - log(-log(u));
+    if (sc > best_s || (sc == best_s && i < best_i)) { best_s = sc; best_i = i; }
   }
-  // block argmax (score, then lower index)
-  __syncthreads();
-  red[tid] = best_s;
-  keys[tid] = best_i;  // the sorted keys are no longer needed
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) {
-      const double os = red[tid + s];
-      const uint64_t oi = keys[tid + s];
-      if (os > red[tid] || (os == red[tid] && oi < keys[tid])) {
-        red[tid] = os;
-        keys[tid] = oi;
-      }
-    }
-    __syncthreads();
+  return (int)block_argmax(best_s, best_i, red, redi);
+}
+
+// The row's V = 256 NE logits (tagged words from the head tiles; thread t
+// takes elements t NE .. t NE + NE - 1) and its sampled code.
+template <int NE>
+__device__ __forceinline__ int sampled_row(const DevPlan& pl, const DevFrame& fr, int row, int j, uint32_t in_tag,
+                                           uint8_t* scratch) {
+  const rsrc_t rz = make_rsrc(pl.zbuf, (uint32_t)pl.Rmax * pl.V * 8);
+  const uint32_t zb = (uint32_t)(row * pl.V + threadIdx.x * NE) * 8;
+  float z[NE];
+  if constexpr (NE == 1) {
+    u32x2 zw[1];
+    auto zo = [=](int) -> uint32_t { return zb; };
+    zw[0] = __builtin_amdgcn_raw_buffer_load_b64(rz, zb, 0, kSC1);
+    await_all(pl, pend(zw, rz, zo, in_tag, true));
+    z[0] = __uint_as_float(zw[0][0]);
+  } else {
+    u32x4 zw[NE / 2];
+    auto zo = [=](int u) -> uint32_t { return zb + u * 16; };
+#pragma unroll
+    for (int u = 0; u < NE / 2; ++u) zw[u] = ld16c(rz, zo(u));
+    await_all(pl, pend(zw, rz, zo, in_tag, true));
+#pragma unroll
+    for (int e = 0; e < NE; ++e) z[e] = __uint_as_float(zw[e >> 1][(e & 1) * 2]);
   }
-  const int code = (int)keys[0];
-  __syncthreads();
-  return code;
+  ZRow<NE> zr;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) zr.v[e] = z[e];
+  const DrawArgs da = {fr.temperature[row], fr.top_p[row], fr.top_k[row], fr.seed[row],
+                       fr.offset[row] + (uint64_t)(j - 1)};
+  return sampled_code<NE>(zr, da, scratch);
 }
 
 template <int BF>
@@ -1059,21 +1148,14 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
   const int row = (int)tk.tile, p = tk.pos;
   const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
   if (row < fr.rows && fr.sampled) {
-    // the row's V logits (tagged words) from the head tiles
-    constexpr int kMaxPer = 16;  // V <= 4096
-    const int nz = pl.V / kThreads;
-    const rsrc_t rz = make_rsrc(pl.zbuf, (uint32_t)pl.Rmax * pl.V * 8);
-    const uint32_t zb = (uint32_t)(row * pl.V + threadIdx.x) * 8;
-    auto zo = [=](int e) -> uint32_t { return zb + e * kThreads * 8; };
-    u32x2 zw[kMaxPer];
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e)
-      zw[e] = e < nz ? __builtin_amdgcn_raw_buffer_load_b64(rz, zo(e), 0, kSC1) : u32x2{0, in_tag};
-    await_all(pl, pend(zw, rz, zo, in_tag, true, nz));
-    float z[kMaxPer];
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e) z[e] = __uint_as_float(zw[e][0]);
-    int code = sampled_code(pl, fr, row, p, z, nz, slot);
+    int code;
+    switch (pl.V) {
+      case 256: code = sampled_row<1>(pl, fr, row, p, in_tag, slot); break;
+      case 512: code = sampled_row<2>(pl, fr, row, p, in_tag, slot); break;
+      case 1024: code = sampled_row<4>(pl, fr, row, p, in_tag, slot); break;
+      case 2048: code = sampled_row<8>(pl, fr, row, p, in_tag, slot); break;
+      default: code = sampled_row<16>(pl, fr, row, p, in_tag, slot); break;
+    }
     code = (code < 0 || code >= pl.V) ? 0 : code;
     if (threadIdx.x == 0) {
       st4(make_rsrc(fr.codes, (uint32_t)fr.rows * (pl.P - 1) * 4), (uint32_t)(row * (pl.P - 1) + p - 1) * 4,
