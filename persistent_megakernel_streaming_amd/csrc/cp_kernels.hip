@@ -371,9 +371,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // the frame's rows reads words of no use (left out of every wait; they
   // only reach that row's MFMA column, which is never stored).  The frame
   // input is plain row-major; its resource ends at the last row, so rows
-  // past it read zeros.  The first load of a unit may hit the L2, which the
-  // other workgroups of this XCD reading the same rows share; a stale word
-  // fails its tag check and is reloaded coherently.
+  // past it read zeros.  Every load of a tagged unit is agent-coherent; a
+  // word that is not yet written fails its tag check and is loaded again.
   const uint32_t xrow = (uint32_t)ld * ESZ;  // plain input only
   const rsrc_t rx = XLL ? make_rsrc(xsrc, act_bytes<BF>(Rmax, ld)) : make_rsrc(xsrc, (uint32_t)rows * xrow);
   const uint32_t xoff = XLL ? ((uint32_t)(rt * (ld / KS) + k0 / KS + c0) * 2) * 1024 + (uint32_t)lane * 16
@@ -388,7 +387,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   auto load = [&](u32x4 (&x)[NU], int g) {
     if (g < ng) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) x[u] = ld16(rx, uoff(g)(u));
+      for (int u = 0; u < NU; ++u) x[u] = XLL ? ld16c(rx, uoff(g)(u)) : ld16(rx, uoff(g)(u));
     }
   };
   if (wave_live) {
@@ -430,14 +429,6 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   wait_vm();
   __syncthreads();
   stamp(tr, 2);
-  // The next task's tile copy goes out once this task has issued its last
-  // operand load: a wave's loads retire in order, so a copy issued earlier
-  // would hold up this task's own waits.  A split-K owner still has the
-  // partials to collect and issues it at the end.
-  // (Each wave issues its own share of the copy; a wave without rows to
-  // compute has no operand loads and issues it here.)
-  const bool early = !PART || tk.split != 0;
-  if (early && (ng <= 4 || !wave_live)) nx.issue(pl);
 
   float rinv = 1.f;
   if constexpr (NORM) {
@@ -484,7 +475,6 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       if (g + 3 >= ng) break;
       step(xd, g + 3);
       load(xd, g + 7);
-      if (early && g + 8 >= ng && ng > 4) nx.issue(pl);
     }
     if constexpr (NB == 1) {
 #pragma unroll
@@ -525,9 +515,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 
   if constexpr (PART) {
     // Split-K: the owner (split 0) collects its partners' partials (tagged
-    // with this phase, in split order) and the residual; the next task's
-    // tile copy is issued after these loads so that waiting on them does not
-    // also wait on the copy.
+    // with this phase, in split order) and the residual.
     const uint32_t res_tag = tag_of(epoch, tk.ph_in1);
     const bool owner = tk.split == 0;
     uint64_t part_off;
@@ -680,7 +668,11 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   }
-  if (!early) nx.issue(pl);  // after the owner's outputs
+  // The next task's tile copy goes out after this task's outputs: a wave's
+  // memory operations retire in order, so a copy issued earlier would hold up
+  // this task's own operand and partial-sum waits, and its burst would meet
+  // the outputs on their way to the consumers.
+  nx.issue(pl);
   stamp(tr, 5);
 }
 
