@@ -47,6 +47,11 @@ constexpr int kMaxPhases = 1023;     // phase ids must stay below kKvPhase
 constexpr uint32_t kEpochWrap = (1u << 22) - 1;
 constexpr int kMaxClear = 16;
 
+// Task flag: the split-K partners of this task's tile and their owner run on
+// workgroups of one XCD, so partials go through that XCD's L2 (plain stores,
+// agent-coherent loads) instead of out to memory and back.
+constexpr uint8_t kTaskLocalPartials = 1;
+
 struct Span {
   void* p;
   uint64_t bytes;  // a multiple of 8
@@ -56,7 +61,7 @@ struct Task {
   uint8_t type;
   uint8_t split;     // split-K index
   uint8_t nsplit;    // split-K ways (1: not split)
-  uint8_t pad0;
+  uint8_t flags;     // kTaskLocalPartials
   uint16_t layer;
   uint16_t pos;
   uint32_t tile;     // projection n-tile, attention (kv head, row group), row
@@ -77,7 +82,7 @@ struct Task {
 // What a workgroup needs to run one task (24 bytes, six scalar registers):
 // the host's Task without the dependency bookkeeping its validator uses.
 struct DevTask {
-  uint8_t type, split, nsplit, pad0;
+  uint8_t type, split, nsplit, flags;
   uint16_t layer, pos;
   uint16_t tile, phase;
   uint16_t ph_in0, ph_in1;

@@ -25,6 +25,8 @@
 // never change during a frame and use ordinary loads and direct-to-LDS copies.
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "cp_device.h"
 
 namespace cpms {
@@ -62,6 +64,13 @@ __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::
 // tr is null when the plan does not trace.
 __device__ __forceinline__ void stamp(uint64_t* tr, int k) {
   if (tr && threadIdx.x == 0) tr[k] = __builtin_amdgcn_s_memrealtime();
+}
+
+// Index of the XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xfu;
 }
 
 // ------------------------------------------------------------------ numerics
@@ -542,9 +551,19 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     const int npart = tk.nsplit - 1;
     if (epi_wave && !owner) {
       if (live) {
+        // With the owner on this XCD the partials stay in its L2 (plain
+        // stores; the owner's agent-coherent loads read the L2); a workgroup
+        // not on the XCD the placement assumed writes through to memory.
         const uint32_t o = pbase + tk.split * pstep;
-        st16c(rp, o, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag));
-        st16c(rp, o + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag));
+        const u32x4 p0 = ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag);
+        const u32x4 p1 = ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag);
+        if ((tk.flags & kTaskLocalPartials) && xcc_id() == (blockIdx.x & 7u)) {
+          st16(rp, o, p0);
+          st16(rp, o + 16, p1);
+        } else {
+          st16c(rp, o, p0);
+          st16c(rp, o + 16, p1);
+        }
       }
     } else if (epi_wave) {
 #pragma unroll
@@ -1277,7 +1296,10 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     stamp(tr, 7);
     cur = nxt;
   }
-  // The last workgroup to finish moves the plan to the next frame.
+  // The last workgroup to finish moves the plan to the next frame.  Before a
+  // wrapping frame's clear, partials held in an XCD's L2 (plain stores) are
+  // written back, so that none lands in memory after the clear.
+  if (epoch + 1 >= kEpochWrap) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   wait_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1368,6 +1390,37 @@ hipError_t set_kernel_attributes() {
   if ((e = hipFuncSetAttribute((const void*)persistent_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
   if ((e = hipFuncSetAttribute((const void*)phase_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
   return hipFuncSetAttribute((const void*)phase_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+}
+
+// Records the XCD of every workgroup of a grid shaped like the persistent
+// one (n_wg workgroups of kThreads threads, kLdsBytes of LDS each).
+__global__ __launch_bounds__(kThreads, 1) void xcd_map_kernel(uint32_t* out) {
+  extern __shared__ __align__(1024) uint8_t lds[];
+  if (threadIdx.x == 0) {
+    lds[0] = 1;
+    out[blockIdx.x] = xcc_id();
+  }
+}
+
+// Whether workgroup i of the persistent grid runs on XCD i % 8, the dealing
+// the split-K placement assumes.
+hipError_t check_xcd_dealing(int n_wg, bool& dealt) {
+  dealt = false;
+  if (n_wg % 8) return hipSuccess;
+  uint32_t* d = nullptr;
+  hipError_t e = hipFuncSetAttribute((const void*)xcd_map_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e == hipSuccess) e = hipMalloc(&d, (size_t)n_wg * 4);
+  if (e != hipSuccess) return e;
+  std::vector<uint32_t> h(n_wg, 0xffffffffu);
+  hipLaunchKernelGGL(xcd_map_kernel, dim3(n_wg), dim3(kThreads), kLdsBytes, 0, d);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpy(h.data(), d, (size_t)n_wg * 4, hipMemcpyDeviceToHost);
+  hipError_t f = hipFree(d);
+  if (e != hipSuccess) return e;
+  if (f != hipSuccess) return f;
+  dealt = true;
+  for (int i = 0; i < n_wg; ++i) dealt = dealt && h[i] == (uint32_t)(i % 8);
+  return hipSuccess;
 }
 
 int occupancy_per_cu(int bf16) {

@@ -33,6 +33,7 @@ hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, 
                             uint32_t layers, hipStream_t s);
 hipError_t set_kernel_attributes();
 int occupancy_per_cu(int bf16);
+hipError_t check_xcd_dealing(int n_wg, bool& dealt);
 }  // namespace cpms
 
 using namespace cpms;
@@ -50,6 +51,7 @@ struct cp_plan {
   uint32_t n_ctr = 0;
   int n_phases = 0;
   int max_tasks_wg = 0;
+  bool xcd_dealing = false;             // persistent workgroup i runs on XCD i % 8 (checked on the device)
   DevTask* d_phase_tasks = nullptr;
   std::vector<void*> allocs;
   int64_t packed_bytes = 0, scratch_bytes = 0, weight_bytes_frame = 0;
@@ -144,15 +146,22 @@ std::vector<int> spread(int n, int n_wg, int& rot) {
 }
 
 // Split-K tasks (tile t, split s): the nsplit partners of a tile share an XCD
-// (workgroups are dealt to XCDs round-robin by id) when the phase fills the grid.
-std::vector<int> split_map(int tiles, int nsplit, int n_wg, int& rot) {
+// (workgroups are dealt to XCDs round-robin by id) when the phase fills the
+// grid; `local` tells whether they do.
+std::vector<int> split_map(int tiles, int nsplit, int n_wg, int& rot, bool& local) {
   std::vector<int> m(tiles * nsplit);
-  if (tiles * nsplit == n_wg && n_wg % 8 == 0 && tiles % 8 == 0) {
+  local = tiles * nsplit == n_wg && n_wg % 8 == 0 && tiles % 8 == 0;
+  if (local) {
     for (int t = 0; t < tiles; ++t)
       for (int s = 0; s < nsplit; ++s) m[t * nsplit + s] = ((t / 8) * nsplit + s) * 8 + (t % 8);
     return m;
   }
   return spread(tiles * nsplit, n_wg, rot);
+}
+
+void mark_local(std::vector<Task>& ts, bool local) {
+  if (local)
+    for (Task& t : ts) t.flags |= kTaskLocalPartials;
 }
 
 }  // namespace
@@ -317,7 +326,10 @@ static cp_status build_schedule(cp_plan* P) {
         k.split = (uint8_t)s; k.nsplit = (uint8_t)ns_in; k.sig = g_inp; k.sig_slot = t;
         ts.push_back(k);
       }
-    B.phase(ts, split_map(ht, ns_in, n_wg, rot));
+    bool local = false;
+    const std::vector<int> m = split_map(ht, ns_in, n_wg, rot, local);
+    mark_local(ts, local);
+    B.phase(ts, m);
   }
   const uint32_t g_emb0 = B.group(R);
   const int ph_emb0 = B.next_phase();
@@ -388,7 +400,10 @@ static cp_status build_schedule(cp_plan* P) {
             add_wait(k, g_layer_in);  // the residual
             ts.push_back(k);
           }
-        B.phase(ts, split_map(ht, ns_o, n_wg, rot));
+        bool local = false;
+        const std::vector<int> m = split_map(ht, ns_o, n_wg, rot, local);
+        mark_local(ts, local);
+        B.phase(ts, m);
       }
       // gate/up
       std::vector<uint32_t> g_gu(ns_d);
@@ -420,7 +435,10 @@ static cp_status build_schedule(cp_plan* P) {
             add_wait(k, g_o);  // the residual
             ts.push_back(k);
           }
-        B.phase(ts, split_map(ht, ns_d, n_wg, rot));
+        bool local = false;
+        const std::vector<int> m = split_map(ht, ns_d, n_wg, rot, local);
+        mark_local(ts, local);
+        B.phase(ts, m);
       }
       g_layer_in = g_down;
       ph_layer_in = ph_down;
@@ -726,12 +744,15 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
 }
 
 // Device records of host tasks (fields the kernels read; every value fits).
-static std::vector<DevTask> to_dev(const std::vector<Task>& ts) {
+// Device task records; `local` keeps kTaskLocalPartials (persistent grid on
+// a device whose workgroup-to-XCD dealing was checked), else it is cleared.
+static std::vector<DevTask> to_dev(const std::vector<Task>& ts, bool local) {
   std::vector<DevTask> out(ts.size());
   for (size_t i = 0; i < ts.size(); ++i) {
     const Task& t = ts[i];
     DevTask& d = out[i];
-    d.type = t.type; d.split = t.split; d.nsplit = t.nsplit; d.pad0 = 0;
+    d.type = t.type; d.split = t.split; d.nsplit = t.nsplit;
+    d.flags = local ? t.flags : (uint8_t)(t.flags & ~kTaskLocalPartials);
     d.layer = t.layer; d.pos = t.pos; d.tile = (uint16_t)t.tile; d.phase = t.phase;
     d.ph_in0 = t.ph_in0; d.ph_in1 = t.ph_in1; d.w_off = t.w_off; d.w_bytes = t.w_bytes;
   }
@@ -770,7 +791,7 @@ static cp_status alloc_scratch(cp_plan* P) {
   std::vector<uint32_t> st(128, 0);
   st[0] = 1;  // first frame is epoch 1; zeroed buffers carry tag 0, which no frame expects
   HIPCHK(P, hipMemcpy(dp.state, st.data(), st.size() * 4, hipMemcpyHostToDevice));
-  const std::vector<DevTask> dev_tasks = to_dev(P->tasks), dev_phase = to_dev(P->phase_tasks);
+  const std::vector<DevTask> dev_tasks = to_dev(P->tasks, P->xcd_dealing), dev_phase = to_dev(P->phase_tasks, false);
   TRY(alloc(P, &p, dev_tasks.size() * sizeof(DevTask))); dp.tasks = (const DevTask*)p;
   HIPCHK(P, hipMemcpy(p, dev_tasks.data(), dev_tasks.size() * sizeof(DevTask), hipMemcpyHostToDevice));
   TRY(alloc(P, &p, P->wg_begin.size() * 4)); dp.wg_begin = (const uint32_t*)p;
@@ -844,6 +865,7 @@ static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights*
   dp.bf16 = bf; dp.eps = cfg->rms_eps; dp.attn_scale = (float)(1.0 / std::sqrt((double)cfg->head_dim));
   dp.spin_limit = 1u << 22;
   dp.n_wg = P->cu_count;
+  HIPCHK(P, check_xcd_dealing(dp.n_wg, P->xcd_dealing));
   TRY(build_schedule(P));
   TRY(pack_weights(P, w));
   TRY(check_schedule(P));
