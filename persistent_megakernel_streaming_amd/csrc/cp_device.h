@@ -25,7 +25,8 @@ constexpr int kMaxRows = 64;
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kSlotBytes = 64 * 1024;  // one weight-tile slot in LDS (two slots)
 constexpr int kMiscLds = 12288;  // flags, cross-wave reductions
-constexpr int kLdsBytes = 2 * kSlotBytes + kMiscLds;
+constexpr int kTaskLds = 19968;  // the persistent workgroup's task records (832 of them)
+constexpr int kLdsBytes = 2 * kSlotBytes + kMiscLds + kTaskLds;  // 162816 of the CU's 163840
 constexpr int kCtrStride = 32;      // uint32 words between sub-counters (128 B)
 constexpr int kTraceStamps = 8;     // timestamps per task in a traced frame
 
@@ -51,6 +52,9 @@ constexpr int kMaxClear = 16;
 // workgroups of one XCD, so partials go through that XCD's L2 (plain stores,
 // agent-coherent loads) instead of out to memory and back.
 constexpr uint8_t kTaskLocalPartials = 1;
+// Task flag (qkv): the attention tasks that read this tile's q, k and v run on
+// this workgroup's XCD, so the stores stay in its L2.
+constexpr uint8_t kTaskLocalQkv = 2;
 
 struct Span {
   void* p;
@@ -61,7 +65,7 @@ struct Task {
   uint8_t type;
   uint8_t split;     // split-K index
   uint8_t nsplit;    // split-K ways (1: not split)
-  uint8_t flags;     // kTaskLocalPartials
+  uint8_t flags;     // kTaskLocalPartials, kTaskLocalQkv
   uint16_t layer;
   uint16_t pos;
   uint32_t tile;     // projection n-tile, attention (kv head, row group), row
@@ -102,6 +106,7 @@ struct DevPlan {
   uint32_t spin_limit;
   int n_wg;
   int n_tasks;
+  int tasks_in_lds;             // every workgroup's list fits kTaskLds: the executor copies it to LDS
   // task lists
   const DevTask* tasks;         // all tasks, grouped by workgroup
   const uint32_t* wg_begin;     // [n_wg + 1]

@@ -73,6 +73,20 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return v & 0xfu;
 }
 
+// Whether this workgroup runs on the XCD the schedule dealt it to (i % 8).
+__device__ __forceinline__ bool on_dealt_xcd() { return xcc_id() == (blockIdx.x & 7u); }
+
+// Tagged-word stores that stay in this XCD's L2 (`local`: every reader runs
+// on this XCD and loads agent-coherently) or write through to memory.
+__device__ __forceinline__ void st8x(rsrc_t r, uint32_t off, u32x2 v, bool local) {
+  if (local) __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  else st8c(r, off, v);
+}
+__device__ __forceinline__ void st16x(rsrc_t r, uint32_t off, u32x4 v, bool local) {
+  if (local) st16(r, off, v);
+  else st16c(r, off, v);
+}
+
 // ------------------------------------------------------------------ numerics
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
@@ -557,7 +571,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         const uint32_t o = pbase + tk.split * pstep;
         const u32x4 p0 = ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag);
         const u32x4 p1 = ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag);
-        if ((tk.flags & kTaskLocalPartials) && xcc_id() == (blockIdx.x & 7u)) {
+        if ((tk.flags & kTaskLocalPartials) && on_dealt_xcd()) {
           st16(rp, o, p0);
           st16(rp, o + 16, p1);
         } else {
@@ -609,6 +623,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         const uint32_t kvoff = (uint32_t)(((l * Rmax + row) * nkv + g) * P + p) * d;
         const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
         const uint32_t kv_tag = tag_of(epoch, kKvPhase);
+        // q, k and v stay in this XCD's L2 when the attention of kv group g runs here
+        const bool lqkv = (tk.flags & kTaskLocalQkv) && on_dealt_xcd();
         if (lt < (gq + 1) * th) {
           // q or k head: slots (4q + v) hold rotary pairs 8 tih + 2q + (v >> 1), half v & 1
           const int tih = lt % th;
@@ -628,21 +644,21 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           const uint32_t base = isq ? (uint32_t)(row * pl.nq * d + hq * d) : kvoff;
           const uint32_t tg = isq ? my_tag : kv_tag;
           if constexpr (BF) {
-            st8c(r, (base + i0) * 4, u32x2{pack_bf16(y[0], y[2]), tg});
-            st8c(r, (base + i0 + d / 2) * 4, u32x2{pack_bf16(y[1], y[3]), tg});
+            st8x(r, (base + i0) * 4, u32x2{pack_bf16(y[0], y[2]), tg}, lqkv);
+            st8x(r, (base + i0 + d / 2) * 4, u32x2{pack_bf16(y[1], y[3]), tg}, lqkv);
           } else {
-            st16c(r, (base + i0) * 8, ll_pair(__float_as_uint(y[0]), __float_as_uint(y[2]), tg));
-            st16c(r, (base + i0 + d / 2) * 8, ll_pair(__float_as_uint(y[1]), __float_as_uint(y[3]), tg));
+            st16x(r, (base + i0) * 8, ll_pair(__float_as_uint(y[0]), __float_as_uint(y[2]), tg), lqkv);
+            st16x(r, (base + i0 + d / 2) * 8, ll_pair(__float_as_uint(y[1]), __float_as_uint(y[3]), tg), lqkv);
           }
         } else {
           const int tih = lt - (gq + 1) * th;
           const rsrc_t rvc = make_rsrc(pl.vc, kvbytes);
           const uint32_t vo = (kvoff + 16 * tih + 4 * q) * ESZ * 2;
           if constexpr (BF) {
-            st16c(rvc, vo, ll_pair(pack_bf16(acc0[0], acc0[1]), pack_bf16(acc0[2], acc0[3]), kv_tag));
+            st16x(rvc, vo, ll_pair(pack_bf16(acc0[0], acc0[1]), pack_bf16(acc0[2], acc0[3]), kv_tag), lqkv);
           } else {
-            st16c(rvc, vo, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), kv_tag));
-            st16c(rvc, vo + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), kv_tag));
+            st16x(rvc, vo, ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), kv_tag), lqkv);
+            st16x(rvc, vo + 16, ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), kv_tag), lqkv);
           }
         }
       } else if constexpr (KIND == T_GU) {
@@ -1272,24 +1288,45 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
   }
 }
 
-template <int BF>
+template <int BF, bool TL>
 __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t b = pl.wg_begin[blockIdx.x], e = pl.wg_begin[blockIdx.x + 1];
+  // With TL the workgroup's task records are copied to LDS once: reading a
+  // record from memory between tasks would make the wave wait for every
+  // memory operation still in flight, the previous task's stores and the
+  // next tile's copy included.  (TL needs every list to fit kTaskLds.)
+  constexpr uint32_t kWords = sizeof(DevTask) / 4;
+  uint32_t* tw = (uint32_t*)(lds + 2 * kSlotBytes + kMiscLds);
+  if constexpr (TL) {
+    const rsrc_t rt = make_rsrc((void*)pl.tasks, (uint32_t)pl.n_tasks * (uint32_t)sizeof(DevTask));
+    for (uint32_t w = threadIdx.x; w < (e - b) * kWords; w += kThreads)
+      tw[w] = __builtin_amdgcn_raw_buffer_load_b32(rt, (b * kWords + w) * 4, 0, 0);
+    wait_vm();
+    __syncthreads();
+  }
+  auto task_at = [&](uint32_t i) -> DevTask {
+    if constexpr (TL) {
+      DevTask t;
+      __builtin_memcpy(&t, tw + (i - b) * kWords, sizeof(DevTask));
+      return t;
+    } else {
+      return pl.tasks[i];
+    }
+  };
   DevTask cur = {};
   if (b < e) {
-    cur = pl.tasks[b];
+    cur = task_at(b);
     issue_tile(pl, cur, lds);
   }
   for (uint32_t i = b; i < e; ++i) {
     uint64_t* tr = pl.trace_on ? pl.trace + (size_t)i * kTraceStamps : nullptr;
     stamp(tr, 0);
     const int s = (i - b) & 1;
-    // the next record is fetched now; it is first needed in this task's epilogue
     const bool more = i + 1 < e;
-    const DevTask nxt = more ? pl.tasks[i + 1] : DevTask{};
+    const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
     run_task<BF>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, nx, tr);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
@@ -1352,10 +1389,11 @@ __global__ void unpack_kv_kernel(const uint64_t* src, uint32_t* dst, uint32_t wo
 namespace cpms {
 
 hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s) {
-  if (pl.bf16)
-    hipLaunchKernelGGL(persistent_kernel<1>, dim3(pl.n_wg), dim3(kThreads), kLdsBytes, s, pl, fr);
-  else
-    hipLaunchKernelGGL(persistent_kernel<0>, dim3(pl.n_wg), dim3(kThreads), kLdsBytes, s, pl, fr);
+  const dim3 g(pl.n_wg), t(kThreads);
+  if (pl.bf16 && pl.tasks_in_lds) hipLaunchKernelGGL((persistent_kernel<1, true>), g, t, kLdsBytes, s, pl, fr);
+  else if (pl.bf16) hipLaunchKernelGGL((persistent_kernel<1, false>), g, t, kLdsBytes, s, pl, fr);
+  else if (pl.tasks_in_lds) hipLaunchKernelGGL((persistent_kernel<0, true>), g, t, kLdsBytes, s, pl, fr);
+  else hipLaunchKernelGGL((persistent_kernel<0, false>), g, t, kLdsBytes, s, pl, fr);
   return hipGetLastError();
 }
 
@@ -1386,8 +1424,10 @@ hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, 
 
 hipError_t set_kernel_attributes() {
   hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<0, true>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<0, false>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
   if ((e = hipFuncSetAttribute((const void*)phase_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
   return hipFuncSetAttribute((const void*)phase_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
 }
@@ -1425,7 +1465,7 @@ hipError_t check_xcd_dealing(int n_wg, bool& dealt) {
 
 int occupancy_per_cu(int bf16) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bf16 ? persistent_kernel<1> : persistent_kernel<0>, kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bf16 ? persistent_kernel<1, true> : persistent_kernel<0, true>, kThreads,
                                                    kLdsBytes) != hipSuccess)
     return -1;
   return n;

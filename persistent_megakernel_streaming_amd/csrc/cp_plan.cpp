@@ -159,9 +159,24 @@ std::vector<int> split_map(int tiles, int nsplit, int n_wg, int& rot, bool& loca
   return spread(tiles * nsplit, n_wg, rot);
 }
 
-void mark_local(std::vector<Task>& ts, bool local) {
+void mark_local(std::vector<Task>& ts, bool local, uint8_t flag = kTaskLocalPartials) {
   if (local)
-    for (Task& t : ts) t.flags |= kTaskLocalPartials;
+    for (Task& t : ts) t.flags |= flag;
+}
+
+// Tasks dealt to the workgroups of given XCDs (workgroup i runs on XCD i % 8):
+// task k goes to XCD xcd[k], to that XCD's workgroups in turn from a rotating
+// start.  Needs n_wg % 8 == 0.
+std::vector<int> xcd_deal(const std::vector<int>& xcd, int n_wg, int& rot) {
+  std::vector<int> m(xcd.size());
+  int rank[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int per = n_wg / 8, start = (rot / 8) % per;
+  for (size_t k = 0; k < xcd.size(); ++k) {
+    const int x = xcd[k] % 8;
+    m[k] = ((start + rank[x]++) % per) * 8 + x;
+  }
+  rot = (rot + (int)xcd.size()) % n_wg;
+  return m;
 }
 
 }  // namespace
@@ -363,7 +378,15 @@ static cp_status build_schedule(cp_plan* P) {
           k.sig = gq_groups[t / tpg]; k.sig_slot = t % tpg;
           ts.push_back(k);
         }
-        B.phase(ts, spread(qkv_tiles, n_wg, rot));
+        // kv group g's tiles on XCD g % 8, where its attention tasks run
+        if (n_wg % 8 == 0) {
+          std::vector<int> x(qkv_tiles);
+          for (int t = 0; t < qkv_tiles; ++t) x[t] = t / tpg;
+          mark_local(ts, true, kTaskLocalQkv);
+          B.phase(ts, xcd_deal(x, n_wg, rot));
+        } else {
+          B.phase(ts, spread(qkv_tiles, n_wg, rot));
+        }
       }
       // Position 0 has no head: the residual after its last layer feeds
       // nothing, so only the last layer's qkv (its K/V) is computed there.
@@ -383,7 +406,13 @@ static cp_status build_schedule(cp_plan* P) {
             k.sig = g_att[g / kv_per_osplit]; k.sig_slot = (g % kv_per_osplit) * agroups + rg;
             ts.push_back(k);
           }
-        B.phase(ts, spread(nkv * agroups, n_wg, rot));
+        if (n_wg % 8 == 0) {
+          std::vector<int> x(nkv * agroups);
+          for (int i = 0; i < nkv * agroups; ++i) x[i] = i / agroups;
+          B.phase(ts, xcd_deal(x, n_wg, rot));
+        } else {
+          B.phase(ts, spread(nkv * agroups, n_wg, rot));
+        }
       }
       // o (split-K over q heads; a split reads only the kv heads of its slice)
       const uint32_t g_o = B.group(ht);
@@ -744,15 +773,15 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
 }
 
 // Device records of host tasks (fields the kernels read; every value fits).
-// Device task records; `local` keeps kTaskLocalPartials (persistent grid on
-// a device whose workgroup-to-XCD dealing was checked), else it is cleared.
+// Device task records; `local` keeps the XCD-local flags (persistent grid on
+// a device whose workgroup-to-XCD dealing was checked), else they are cleared.
 static std::vector<DevTask> to_dev(const std::vector<Task>& ts, bool local) {
   std::vector<DevTask> out(ts.size());
   for (size_t i = 0; i < ts.size(); ++i) {
     const Task& t = ts[i];
     DevTask& d = out[i];
     d.type = t.type; d.split = t.split; d.nsplit = t.nsplit;
-    d.flags = local ? t.flags : (uint8_t)(t.flags & ~kTaskLocalPartials);
+    d.flags = local ? t.flags : (uint8_t)(t.flags & ~(kTaskLocalPartials | kTaskLocalQkv));
     d.layer = t.layer; d.pos = t.pos; d.tile = (uint16_t)t.tile; d.phase = t.phase;
     d.ph_in0 = t.ph_in0; d.ph_in1 = t.ph_in1; d.w_off = t.w_off; d.w_bytes = t.w_bytes;
   }
@@ -870,6 +899,7 @@ static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights*
   TRY(pack_weights(P, w));
   TRY(check_schedule(P));
   dp.n_tasks = (int)P->tasks.size();
+  dp.tasks_in_lds = (int64_t)P->max_tasks_wg * (int64_t)sizeof(DevTask) <= kTaskLds;
   TRY(alloc_scratch(P));
   HIPCHK(P, hipDeviceSynchronize());
   return CP_OK;
