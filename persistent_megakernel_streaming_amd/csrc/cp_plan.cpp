@@ -582,6 +582,39 @@ static cp_status check_schedule(cp_plan* P) {
     if (f.nsplit > 1 && (int)(P->phase_begin[ph + 1] - P->phase_begin[ph]) > P->cu_count)
       return fail(P, CP_ERR_UNSUPPORTED, "schedule: split phase larger than the grid");
   }
+  // XCD-local hand-offs (workgroup w runs on XCD w % 8): the partners of a
+  // kTaskLocalPartials tile share its owner's XCD, and the qkv tiles marked
+  // kTaskLocalQkv share the XCD of every attention task reading them (same
+  // layer, position, kv group).  A broken placement would make a reader spin
+  // on words that never leave another XCD's L2.
+  {
+    const int nkv = P->cfg.n_kv_heads, tpg = (P->cfg.n_q_heads / nkv + 2) * P->cfg.head_dim / 16;
+    const int agroups = P->cfg.max_rows / std::max(1, P->dp.attn_rows);
+    std::vector<int> owner_xcd(P->n_phases * 4096, -1), qkv_xcd(P->n_phases * 64, -1);
+    for (size_t w = 0; w + 1 < P->wg_begin.size(); ++w)
+      for (uint32_t i = P->wg_begin[w]; i < P->wg_begin[w + 1]; ++i) {
+        const Task& t = P->tasks[i];
+        const int x = (int)(w % 8);
+        if ((t.flags & kTaskLocalPartials) && t.split == 0 && t.tile < 4096) owner_xcd[t.phase * 4096 + t.tile] = x;
+        if ((t.flags & kTaskLocalQkv) && (int)(t.tile / tpg) < 64) {
+          int& q = qkv_xcd[t.phase * 64 + t.tile / tpg];
+          if (q >= 0 && q != x) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: a kv group's qkv tiles span XCDs");
+          q = x;
+        }
+      }
+    for (size_t w = 0; w + 1 < P->wg_begin.size(); ++w)
+      for (uint32_t i = P->wg_begin[w]; i < P->wg_begin[w + 1]; ++i) {
+        const Task& t = P->tasks[i];
+        const int x = (int)(w % 8);
+        if ((t.flags & kTaskLocalPartials) && t.split != 0 && t.tile < 4096 && owner_xcd[t.phase * 4096 + t.tile] != x)
+          return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: split partner off its owner's XCD");
+        if (t.type == T_ATTN) {
+          const int g = (int)t.tile / agroups;
+          const int q = g < 64 ? qkv_xcd[t.ph_in0 * 64 + g] : -1;
+          if (q >= 0 && q != x) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: attention off its kv group's XCD");
+        }
+      }
+  }
   return CP_OK;
 }
 
