@@ -150,10 +150,13 @@ std::vector<int> spread(int n, int n_wg, int& rot) {
 // grid; `local` tells whether they do.
 std::vector<int> split_map(int tiles, int nsplit, int n_wg, int& rot, bool& local) {
   std::vector<int> m(tiles * nsplit);
-  local = tiles * nsplit == n_wg && n_wg % 8 == 0 && tiles % 8 == 0;
+  local = tiles * nsplit <= n_wg && n_wg % 8 == 0 && tiles % 8 == 0;
   if (local) {
+    // a rotating start in whole groups of 8 keeps tile t on XCD t % 8
+    const int base = (rot / 8) * 8;
     for (int t = 0; t < tiles; ++t)
-      for (int s = 0; s < nsplit; ++s) m[t * nsplit + s] = ((t / 8) * nsplit + s) * 8 + (t % 8);
+      for (int s = 0; s < nsplit; ++s) m[t * nsplit + s] = (base + ((t / 8) * nsplit + s) * 8 + (t % 8)) % n_wg;
+    rot = (rot + tiles * nsplit) % n_wg;
     return m;
   }
   return spread(tiles * nsplit, n_wg, rot);
@@ -265,12 +268,13 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   return CP_OK;
 }
 
-// Split-K ways for o, down and the input projection.  With at most 16 rows a
-// frame is latency-bound: unsplit tiles (down in halves, to fit an LDS slot)
-// save the partial-sum hand-off.  With more rows the activation bytes each
-// workgroup reads dominate, and four ways cut them by four.  A choice must
-// keep the weight tile within one LDS slot, each wave's K share within 32
-// chunks, and every o split on whole kv heads.
+// Split-K ways for o, down and the input projection: four where the shapes
+// allow.  The partners of a tile share the owner's XCD and hand over their
+// partials through its L2 (about 0.5 us), so splitting pays at every row
+// count: it cuts the activation bytes each workgroup streams by four (at 1
+// row, 2.75 -> 2.41 ms per frame against unsplit o and halved down).  A
+// choice must keep the weight tile within one LDS slot, each wave's K share
+// within 32 chunks, and every o split on whole kv heads.
 static cp_status choose_splits(cp_plan* P) {
   const cp_config& c = P->cfg;
   const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
@@ -283,8 +287,7 @@ static cp_status choose_splits(cp_plan* P) {
     const int nck = kt * esz / 64;
     return kt * esz * 64 % 64 == 0 && nck % 4 == 0 && 16 * kt * esz <= kSlotBytes && nck / wpr_min <= 32;
   };
-  const int order_lo[3] = {1, 2, 4}, order_hi[3] = {4, 2, 1};
-  const int* order = R <= 16 ? order_lo : order_hi;
+  const int order[3] = {4, 2, 1};
   int ns_o = 0, ns_d = 0, ns_in = 0;
   for (int i = 0; i < 3 && !ns_o; ++i) {
     const int ns = order[i];
