@@ -324,7 +324,7 @@ __device__ __forceinline__ void st_act4(rsrc_t r, int row, int n, int K, const f
 // RMSNorm: the gain g is folded into the packed weight tile at plan creation
 // (W . (g x / rms(x)) = (W g) . x / rms(x)), so the MFMAs take the residual
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
-template <int BF, int KIND>
+template <int BF, int KIND, bool ONE = false>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                           uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
@@ -337,6 +337,11 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   constexpr bool RESID = KIND == T_O || KIND == T_DOWN;
   constexpr int NU = XLL ? 8 : 4;           // 16-byte loads per lane per group of 4 chunks
   constexpr uint32_t CST = 64;              // plain operand bytes per chunk step
+  // ONE: a frame of one row.  Only row 0 of the operand tile is loaded, its
+  // 16-byte units packed densely over the lanes (one load instruction per 8
+  // chunks instead of two per chunk), and handed to the MFMA lanes with
+  // ds_bpermute; the norm partials of the row come in one load as well.
+  static_assert(!ONE || XLL, "one-row operands are tagged");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 4, rl = lane & 15;
   const int rows = fr.rows;
@@ -413,21 +418,42 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       for (int u = 0; u < NU; ++u) x[u] = XLL ? ld16c(rx, uoff(g)(u)) : ld16(rx, uoff(g)(u));
     }
   };
+  // ONE: piece P = (c * 2 + u) * 4 + q' (chunk c of this wave, unit u, lane
+  // group q') is loaded by lane P % 64 of instruction P / 64; lanes past the
+  // last piece load a duplicate.
+  constexpr int NJ1 = 4;  // at most 32 chunks per wave
+  u32x4 xo[NJ1];
+  const int npc = 8 * ncw, nj1 = (npc + 63) / 64;
+  const uint32_t xbase1 = ((uint32_t)(k0 / KS + c0) * 2) * 1024;
+  auto oo = [=](int j) -> uint32_t {
+    const int P = (j * 64 + lane) % npc;
+    return xbase1 + (uint32_t)((P >> 3) * 2048 + ((P >> 2) & 1) * 1024 + (P & 3) * 256);
+  };
   if (wave_live) {
-    load(xa, 0);
-    load(xb, 1);
-    load(xc, 2);
-    load(xd, 3);
+    if constexpr (ONE) {
+#pragma unroll
+      for (int j = 0; j < NJ1; ++j) xo[j] = j < nj1 ? ld16c(rx, oo(j)) : u32x4{0, in_tag, 0, in_tag};
+    } else {
+      load(xa, 0);
+      load(xb, 1);
+      load(xc, 2);
+      load(xd, 3);
+    }
   }
   // Sum-of-squares partials of a normalised operand (H/16 per row, written
-  // with the rows): lane group q adds H/64 of them.
+  // with the rows): lane group q adds H/64 of them (ONE: lane i of the wave
+  // loads partials 2i, 2i + 1 of row 0).
   u32x4 ssv[8];
   const int nsq = H / 64;
   const uint32_t ss_row = (uint32_t)(H / 16) * 8;
   const rsrc_t rs = make_rsrc(ssq_slot(pl, in_ssq), (uint32_t)rows * ss_row);
   const uint32_t ss0 = (uint32_t)row * ss_row + (uint32_t)(q * nsq) * 8;
-  auto sso = [=](int i) -> uint32_t { return ss0 + i * 16; };
-  if constexpr (NORM) {
+  auto sso = [=](int i) -> uint32_t { return ONE ? (uint32_t)(lane % (H / 32)) * 16 : ss0 + i * 16; };
+  if constexpr (NORM && ONE) {
+    ssv[0] = ld16(rs, sso(0));
+#pragma unroll
+    for (int i = 1; i < 8; ++i) ssv[i] = u32x4{0, in_tag, 0, in_tag};
+  } else if constexpr (NORM) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) ssv[i] = (2 * i < nsq) ? ld16(rs, sso(i)) : u32x4{0, in_tag, 0, in_tag};
   }
@@ -447,14 +473,22 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // The data is its own signal: wait for the first two groups and the norm
   // partials, then for this task's weight tile (issued during the previous
   // task) to be in LDS.
-  await_all(pl, pend(xa, rx, uoff(0), in_tag, XLL && live), pend(xb, rx, uoff(1), in_tag, XLL && live && ng > 1),
-            pend(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
+  if constexpr (ONE)
+    await_all(pl, pend(xo, rx, oo, in_tag, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live, 1));
+  else
+    await_all(pl, pend(xa, rx, uoff(0), in_tag, XLL && live), pend(xb, rx, uoff(1), in_tag, XLL && live && ng > 1),
+              pend(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
   wait_vm();
   __syncthreads();
   stamp(tr, 2);
 
   float rinv = 1.f;
-  if constexpr (NORM) {
+  if constexpr (NORM && ONE) {
+    float ss = lane < H / 32 ? __uint_as_float(ssv[0][0]) + __uint_as_float(ssv[0][2]) : 0.f;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) ss += shfl_xor_f(ss, m);
+    rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
+  } else if constexpr (NORM) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -484,7 +518,37 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   };
-  if (wave_live) {
+  if (wave_live && ONE) {
+    // chunk c of instruction j = c / 8: units 0 and 1 of lane group q sit in
+    // lanes (c % 8) * 8 + q and + 4 (every MFMA column gets row 0)
+#pragma unroll
+    for (int j = 0; j < NJ1; ++j) {
+#pragma unroll
+      for (int ci = 0; ci < 8; ++ci) {
+        const int c = j * 8 + ci;
+        if (c < ncw) {
+          const int a0 = (ci * 8 + q) * 4, a1 = (ci * 8 + 4 + q) * 4;
+          const u32x4 x = {(uint32_t)__builtin_amdgcn_ds_bpermute(a0, (int)xo[j][0]),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(a0, (int)xo[j][2]),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(a1, (int)xo[j][0]),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(a1, (int)xo[j][2])};
+          const u32x4 w0 = *(const u32x4*)(wt + c * NB * 1024);
+          if constexpr (NB == 2) {
+            const u32x4 w1 = *(const u32x4*)(wt + (c * 2 + 1) * 1024);
+            acc0 = mma<BF>(w0, x, acc0);
+            acc1 = mma<BF>(w1, x, acc1);
+          } else {
+            if (c & 1) acc1 = mma<BF>(w0, x, acc1);
+            else acc0 = mma<BF>(w0, x, acc0);
+          }
+        }
+      }
+    }
+    if constexpr (NB == 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + acc1[v];
+    }
+  } else if (wave_live) {
     for (int g = 0; g < ng; g += 4) {
       step(xa, g);
       if (g == 0) stamp(tr, 6);
@@ -1239,18 +1303,22 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 
 // ------------------------------------------------------------------ executors
 
-template <int BF>
+// ONE: the executor was launched for a one-row frame (the densely loaded
+// operand path; a separate kernel, so the many-row code is left as it is).
+template <int BF, bool ONE>
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                          uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
   switch (tk.type) {
     case T_ATTN: attn_task<BF>(pl, fr, tk, epoch, nx, tr); break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, nx, tr); break;
     case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
-    case T_QKV: proj_task<BF, T_QKV>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
-    case T_O: proj_task<BF, T_O>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
-    case T_GU: proj_task<BF, T_GU>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
-    case T_DOWN: proj_task<BF, T_DOWN>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
-    case T_HEAD: proj_task<BF, T_HEAD>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
+#define CP_PROJ(K) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, nx, tr);
+    case T_QKV: CP_PROJ(T_QKV) break;
+    case T_O: CP_PROJ(T_O) break;
+    case T_GU: CP_PROJ(T_GU) break;
+    case T_DOWN: CP_PROJ(T_DOWN) break;
+    case T_HEAD: CP_PROJ(T_HEAD) break;
+#undef CP_PROJ
     default: proj_task<BF, T_INPROJ>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
   }
 }
@@ -1288,7 +1356,7 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
   }
 }
 
-template <int BF, bool TL>
+template <int BF, bool TL, bool ONE>
 __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
@@ -1328,7 +1396,7 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     const bool more = i + 1 < e;
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
-    run_task<BF>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, nx, tr);
+    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, nx, tr);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
     stamp(tr, 7);
     cur = nxt;
@@ -1347,7 +1415,7 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
   if (misc[0]) advance_epoch(pl, epoch, fr.defer_clear);
 }
 
-template <int BF>
+template <int BF, bool ONE>
 __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame fr, const DevTask* tasks) {
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
@@ -1355,7 +1423,7 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   const DevTask tk = tasks[blockIdx.x];
   issue_tile(pl, tk, lds);
   const Next nx = {DevTask{}, false, nullptr};
-  run_task<BF>(pl, fr, tk, epoch, lds, misc, nx, nullptr);
+  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nx, nullptr);
 }
 
 // The per-phase executor's last launch of a frame.
@@ -1388,21 +1456,36 @@ __global__ void unpack_kv_kernel(const uint64_t* src, uint32_t* dst, uint32_t wo
 
 namespace cpms {
 
+// Executor variants: activation type, task list in LDS (persistent), and a
+// one-row frame (its own code path; task lists that do not fit LDS keep the
+// general path).
+#define CP_PERSISTENT_VARIANTS(X) \
+  X(1, true, true) X(1, true, false) X(1, false, false) X(0, true, true) X(0, true, false) X(0, false, false)
+#define CP_PHASE_VARIANTS(X) X(1, true) X(1, false) X(0, true) X(0, false)
+
 hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s) {
   const dim3 g(pl.n_wg), t(kThreads);
-  if (pl.bf16 && pl.tasks_in_lds) hipLaunchKernelGGL((persistent_kernel<1, true>), g, t, kLdsBytes, s, pl, fr);
-  else if (pl.bf16) hipLaunchKernelGGL((persistent_kernel<1, false>), g, t, kLdsBytes, s, pl, fr);
-  else if (pl.tasks_in_lds) hipLaunchKernelGGL((persistent_kernel<0, true>), g, t, kLdsBytes, s, pl, fr);
-  else hipLaunchKernelGGL((persistent_kernel<0, false>), g, t, kLdsBytes, s, pl, fr);
-  return hipGetLastError();
+  const bool one = fr.rows == 1 && pl.tasks_in_lds;
+#define X(B, T, O)                                                                      \
+  if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O) {                        \
+    hipLaunchKernelGGL((persistent_kernel<B, T, O>), g, t, kLdsBytes, s, pl, fr);       \
+    return hipGetLastError();                                                          \
+  }
+  CP_PERSISTENT_VARIANTS(X)
+#undef X
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const DevTask* tasks, int n, hipStream_t s) {
-  if (pl.bf16)
-    hipLaunchKernelGGL(phase_kernel<1>, dim3(n), dim3(kThreads), kLdsBytes, s, pl, fr, tasks);
-  else
-    hipLaunchKernelGGL(phase_kernel<0>, dim3(n), dim3(kThreads), kLdsBytes, s, pl, fr, tasks);
-  return hipGetLastError();
+  const bool one = fr.rows == 1;
+#define X(B, O)                                                                            \
+  if (pl.bf16 == B && one == O) {                                                          \
+    hipLaunchKernelGGL((phase_kernel<B, O>), dim3(n), dim3(kThreads), kLdsBytes, s, pl, fr, tasks); \
+    return hipGetLastError();                                                             \
+  }
+  CP_PHASE_VARIANTS(X)
+#undef X
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bump_epoch(const DevPlan& pl, int defer_clear, hipStream_t s) {
@@ -1424,12 +1507,18 @@ hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, 
 
 hipError_t set_kernel_attributes() {
   hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<0, true>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<0, false>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
-  if ((e = hipFuncSetAttribute((const void*)phase_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) return e;
-  return hipFuncSetAttribute((const void*)phase_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+#define X(B, T, O)                                                                                          \
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<B, T, O>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                               kLdsBytes)))                                                                   \
+    return e;
+  CP_PERSISTENT_VARIANTS(X)
+#undef X
+#define X(B, O)                                                                                                \
+  if ((e = hipFuncSetAttribute((const void*)phase_kernel<B, O>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes))) \
+    return e;
+  CP_PHASE_VARIANTS(X)
+#undef X
+  return hipSuccess;
 }
 
 // Records the XCD of every workgroup of a grid shaped like the persistent
@@ -1465,7 +1554,7 @@ hipError_t check_xcd_dealing(int n_wg, bool& dealt) {
 
 int occupancy_per_cu(int bf16) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bf16 ? persistent_kernel<1, true> : persistent_kernel<0, true>, kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bf16 ? persistent_kernel<1, true, false> : persistent_kernel<0, true, false>, kThreads,
                                                    kLdsBytes) != hipSuccess)
     return -1;
   return n;
