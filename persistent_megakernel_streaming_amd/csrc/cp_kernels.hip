@@ -326,7 +326,7 @@ __device__ __forceinline__ void st_act4(rsrc_t r, int row, int n, int K, const f
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
 template <int BF, int KIND, bool ONE = false>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
+                                          uint8_t* slot, uint32_t* misc, uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
@@ -767,11 +767,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   }
-  // The next task's tile copy goes out after this task's outputs: a wave's
-  // memory operations retire in order, so a copy issued earlier would hold up
-  // this task's own operand and partial-sum waits, and its burst would meet
-  // the outputs on their way to the consumers.
-  nx.issue(pl);
+
   stamp(tr, 5);
 }
 
@@ -782,7 +778,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 // head dimension; softmax over t <= p in float; output: lane owns d/64 dims.
 template <int BF>
 __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          const Next& nx, uint64_t* tr) {
+                                          uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d = pl.d, gq = pl.gq, nkv = pl.nkv, P = pl.P, Rmax = pl.Rmax;
@@ -899,7 +895,6 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
       else st8c(ra, ao, u32x2{__float_as_uint(o0), my_tag});
     }
   }
-  nx.issue(pl);  // after this task's outputs
   stamp(tr, 5);
 }
 
@@ -951,14 +946,13 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
 
 template <int BF>
 __device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                            const Next& nx, uint64_t* tr) {
+                                            uint64_t* tr) {
   const int row = (int)tk.tile;
   if (row < fr.rows) {
     int code = fr.code0[row];
     code = code < 0 ? 0 : (code >= pl.V ? pl.V - 1 : code);
     embed_row<BF>(pl, fr, 0, row, code, true, tag_of(epoch, tk.phase));
   }
-  nx.issue(pl);
   stamp(tr, 5);
 }
 
@@ -1235,7 +1229,7 @@ __device__ __forceinline__ int sampled_row(const DevPlan& pl, const DevFrame& fr
 
 template <int BF>
 __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
+                                          uint8_t* slot, uint32_t* misc, uint64_t* tr) {
   const int row = (int)tk.tile, p = tk.pos;
   const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
   if (row < fr.rows && fr.sampled) {
@@ -1297,7 +1291,6 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
     __syncthreads();
     embed_row<BF>(pl, fr, p, row, (int)misc[1], false, tag_of(epoch, tk.phase));
   }
-  nx.issue(pl);
   stamp(tr, 5);
 }
 
@@ -1307,19 +1300,19 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 // operand path; a separate kernel, so the many-row code is left as it is).
 template <int BF, bool ONE>
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                         uint8_t* slot, uint32_t* misc, const Next& nx, uint64_t* tr) {
+                                         uint8_t* slot, uint32_t* misc, uint64_t* tr) {
   switch (tk.type) {
-    case T_ATTN: attn_task<BF>(pl, fr, tk, epoch, nx, tr); break;
-    case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, nx, tr); break;
-    case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
-#define CP_PROJ(K) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, nx, tr);
+    case T_ATTN: attn_task<BF>(pl, fr, tk, epoch, tr); break;
+    case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
+    case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, slot, misc, tr); break;
+#define CP_PROJ(K) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr);
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
     case T_GU: CP_PROJ(T_GU) break;
     case T_DOWN: CP_PROJ(T_DOWN) break;
     case T_HEAD: CP_PROJ(T_HEAD) break;
 #undef CP_PROJ
-    default: proj_task<BF, T_INPROJ>(pl, fr, tk, epoch, slot, misc, nx, tr); break;
+    default: proj_task<BF, T_INPROJ>(pl, fr, tk, epoch, slot, misc, tr); break;
   }
 }
 
@@ -1396,8 +1389,14 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     const bool more = i + 1 < e;
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
-    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, nx, tr);
+    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
+    // The next task's tile copy goes out once every wave has issued this
+    // task's outputs: the CU's waves share one memory instruction queue and
+    // each wave's operations retire in order, so a copy issued earlier would
+    // hold up this task's operand and partial-sum waits and delay its stores
+    // on their way to the consumers.
+    nx.issue(pl);
     stamp(tr, 7);
     cur = nxt;
   }
@@ -1422,8 +1421,7 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const DevTask tk = tasks[blockIdx.x];
   issue_tile(pl, tk, lds);
-  const Next nx = {DevTask{}, false, nullptr};
-  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nx, nullptr);
+  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr);
 }
 
 // The per-phase executor's last launch of a frame.
