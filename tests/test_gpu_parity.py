@@ -129,6 +129,21 @@ def test_persistent_equals_per_phase_bitwise():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_one_row_frame_on_64_row_plan():
+    """A one-row frame runs the one-row kernels (row 0 of each operand tile
+    loaded densely and handed out with ds_bpermute) on a plan built for 64
+    rows; the two executors agree bitwise, and the oracle agrees."""
+    cfg = synth.CONFIGS["l5_r64"]
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg, rows=1)
+    a = _gpu_frame(cfg, wdev, inputs, "persistent", max_rows=64, kv=True)
+    b = _gpu_frame(cfg, wdev, inputs, "per_phase", max_rows=64, kv=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    err, frac = _check(cfg, ow, inputs, a, [0], 0.05, kv=True)
+    print(f"l5 r1 of 64: max logit err {err:.4f}, decided {frac:.2f}")
+
+
 def test_ten_runs_bitwise_identical():
     cp = _cp()
     cfg = synth.CONFIGS["l5_r64"]
