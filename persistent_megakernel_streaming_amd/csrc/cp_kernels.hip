@@ -524,9 +524,11 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
     for (int j = 0; j < NJ1; ++j) {
 #pragma unroll
-      for (int ci = 0; ci < 8; ++ci) {
-        const int c = j * 8 + ci;
-        if (c < ncw) {
+      for (int h = 0; h < 2; ++h) {
+        if (j * 8 + h * 4 >= ncw) break;  // ncw is a multiple of 4: whole blocks of 4 chunks
+#pragma unroll
+        for (int cj = 0; cj < 4; ++cj) {
+          const int ci = h * 4 + cj, c = j * 8 + ci;
           const int a0 = (ci * 8 + q) * 4, a1 = (ci * 8 + 4 + q) * 4;
           const u32x4 x = {(uint32_t)__builtin_amdgcn_ds_bpermute(a0, (int)xo[j][0]),
                            (uint32_t)__builtin_amdgcn_ds_bpermute(a0, (int)xo[j][2]),
