@@ -825,10 +825,19 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     auto vo = [=](int tt) { return v0 + tt * vrow; };
     u32x2 vw[16];
     u32x4 vv[BF ? 1 : 16];
+    // (every position is loaded, so the loads issue without branches; those
+    // past p take the expected tag, stay out of the wait and are masked below)
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
-      if constexpr (BF) vw[tt] = (tt <= p) ? __builtin_amdgcn_raw_buffer_load_b64(rv, vo(tt), 0, kSC1) : u32x2{0, kv_tag};
-      else vv[tt] = (tt <= p) ? ld16c(rv, vo(tt)) : u32x4{0, kv_tag, 0, kv_tag};
+      const uint32_t o = vo(min(tt, P - 1));
+      if constexpr (BF) {
+        vw[tt] = __builtin_amdgcn_raw_buffer_load_b64(rv, o, 0, kSC1);
+        vw[tt][1] = tt <= p ? vw[tt][1] : kv_tag;
+      } else {
+        vv[tt] = ld16c(rv, o);
+        vv[tt][1] = tt <= p ? vv[tt][1] : kv_tag;
+        vv[tt][3] = tt <= p ? vv[tt][3] : kv_tag;
+      }
     }
     // Q and K (this position's from the qkv phase just before, earlier ones
     // long ready) and V, all in one wait
@@ -858,28 +867,37 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     for (int k = 4; k <= 32; k <<= 1) sum += shfl_xor_f(sum, k);
     const float w = e / sum;
     // output: sum over t in ascending order
+    // (positions past p add an exact 0: weight and value both selected to 0)
     float o0 = 0.f, o1 = 0.f;
     const int wsel = (lane * dpl) & 1;  // fp32, one dim per lane: which word of the pair
+    float wv[16];
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      const float wt = __shfl(w, tt * 4, 64);
-      if (tt <= p) {
+    for (int tt = 0; tt < 16; ++tt) wv[tt] = __shfl(w, tt * 4, 64);
+    if (dpl == 2) {
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        const bool on = tt <= p;
+        const float wt = on ? wv[tt] : 0.f;
+        float v0, v1;
         if constexpr (BF) {
-          const uint32_t word = vw[tt][0];
-          if (dpl == 2) {
-            o0 += wt * bf2f(word & 0xffffu);
-            o1 += wt * bf2f(word >> 16);
-          } else {
-            o0 += wt * bf2f((lane & 1) ? (word >> 16) : (word & 0xffffu));
-          }
+          v0 = bf2f(vw[tt][0] & 0xffffu);
+          v1 = bf2f(vw[tt][0] >> 16);
         } else {
-          if (dpl == 2) {
-            o0 += wt * __uint_as_float(vv[tt][0]);
-            o1 += wt * __uint_as_float(vv[tt][2]);
-          } else {
-            o0 += wt * __uint_as_float(vv[tt][wsel * 2]);
-          }
+          v0 = __uint_as_float(vv[tt][0]);
+          v1 = __uint_as_float(vv[tt][2]);
         }
+        o0 += wt * (on ? v0 : 0.f);
+        o1 += wt * (on ? v1 : 0.f);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        const bool on = tt <= p;
+        const float wt = on ? wv[tt] : 0.f;
+        float v0;
+        if constexpr (BF) v0 = bf2f((lane & 1) ? (vw[tt][0] >> 16) : (vw[tt][0] & 0xffffu));
+        else v0 = __uint_as_float(vv[tt][wsel * 2]);
+        o0 += wt * (on ? v0 : 0.f);
       }
     }
     const int an = hq * d + lane * dpl;  // first output column of this lane
