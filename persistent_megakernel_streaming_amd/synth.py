@@ -109,6 +109,8 @@ CONFIGS: dict[str, DepthLoopConfig] = {
     "l10_r1": DepthLoopConfig(name="l10_r1", rows=1, **{**_FULL, "n_layers": 10}),
     "l10_r16": DepthLoopConfig(name="l10_r16", rows=16, **{**_FULL, "n_layers": 10}),
     "l10_r64": DepthLoopConfig(name="l10_r64", rows=64, **{**_FULL, "n_layers": 10}),
+    # Input projection from a 2048-wide hidden (a larger text model) to 1024.
+    "l5_in2048_r8": DepthLoopConfig(name="l5_in2048_r8", rows=8, **{**_FULL, "input_dim": 2048}),
 }
 
 

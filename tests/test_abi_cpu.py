@@ -59,7 +59,7 @@ def test_unsupported_shapes_are_refused_on_the_host(change, status):
     assert cp.lib().cp_last_create_error()
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "l5_r1", "l5_r64", "l10_r64"])
+@pytest.mark.parametrize("name", ["tiny_f32", "l5_r1", "l5_r64", "l10_r64", "l5_in2048_r8"])
 @pytest.mark.parametrize("cus", [256, 64, 7])
 def test_schedule_invariants(name, cus):
     cp = _cp()

@@ -90,6 +90,27 @@ def test_tiny_bf16_ragged(exec_mode):
     _check(cfg, ow, inputs, gpu, range(5), 0.05, kv=True)
 
 
+@pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
+def test_tiny_wide_input(exec_mode):
+    """Input projection from a hidden twice the model width (fp32, exact bar)."""
+    cfg = synth.CONFIGS["tiny_f32"].with_(rows=2, input_dim=512)
+    w, wdev, ow = _weights(cfg, seed=3, gain_jitter=True)
+    inputs = synth.make_inputs(cfg, seed=3)
+    gpu = _gpu_frame(cfg, wdev, inputs, exec_mode)
+    _check(cfg, ow, inputs, gpu, range(2), 1e-4)
+
+
+@pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
+def test_full_l5_input_2048(exec_mode):
+    """2048 -> 1024 input projection in front of the 5-layer depth loop, all 8 rows."""
+    cfg = synth.CONFIGS["l5_in2048_r8"]
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg)
+    gpu = _gpu_frame(cfg, wdev, inputs, exec_mode)
+    err, frac = _check(cfg, ow, inputs, gpu, range(cfg.rows), 0.05)
+    print(f"l5 input 2048 {exec_mode}: max logit err {err:.4f}, decided {frac:.2f}")
+
+
 def test_full_l5_one_row():
     cfg = synth.CONFIGS["l5_r1"]
     w, wdev, ow = _weights(cfg)
