@@ -18,6 +18,8 @@ LIB_PATH = os.environ.get("CPMS_LIBRARY") or os.path.join(_PKG, "libcpms.so")
 CP_OK = 0
 STATUS = {0: "CP_OK", 1: "CP_ERR_INVALID_ARGUMENT", 2: "CP_ERR_UNSUPPORTED", 3: "CP_ERR_NOT_CORESIDENT",
           4: "CP_ERR_OUT_OF_MEMORY", 5: "CP_ERR_HIP", 6: "CP_ERR_DEVICE_TIMEOUT"}
+(CP_ERR_INVALID_ARGUMENT, CP_ERR_UNSUPPORTED, CP_ERR_NOT_CORESIDENT, CP_ERR_OUT_OF_MEMORY, CP_ERR_HIP,
+ CP_ERR_DEVICE_TIMEOUT) = range(1, 7)
 CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
 CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1

@@ -195,6 +195,33 @@ def test_l10_hbm_variant(rows):
     _check(cfg, ow, inputs, gpu, sorted({0, rows - 1}), 0.05)
 
 
+def test_frame_refusals_leave_the_plan_usable():
+    """Frames the host refuses (rows out of range, some sampler arrays
+    missing, a trace buffer without the trace flag) enqueue nothing; the next
+    valid frame on the same plan is correct."""
+    cp = _cp()
+    cfg = synth.CONFIGS["tiny_f32"].with_(rows=2, sampled=True)
+    w, wdev, ow = _weights(cfg, seed=4)
+    inputs = synth.make_inputs(cfg, seed=4)
+    plan = cp.Plan(cfg, wdev, max_rows=4)
+    io = cp.make_io(cfg, inputs)
+    codes0 = io["codes"].clone()
+    bad = [dict(io, rows=0), dict(io, rows=5), dict(io, top_p=None),
+           dict(io, trace=torch.zeros(64, dtype=torch.int64, device="cuda"))]
+    for b in bad:
+        with pytest.raises(cp.CpError) as e:
+            plan.run(b)
+        assert e.value.status == cp.CP_ERR_INVALID_ARGUMENT and str(e.value)
+    torch.cuda.synchronize()
+    assert torch.equal(io["codes"], codes0), "a refused frame wrote outputs"
+    plan.run(io)
+    torch.cuda.synchronize()
+    plan.device_status()
+    gpu = {k: v.cpu().numpy() for k, v in io.items() if k != "rows"}
+    plan.close()
+    _check_sampled(cfg, ow, inputs, gpu, range(2), 1e-4)
+
+
 def test_new_plan_on_reused_memory():
     """A plan created where a destroyed plan's buffers were must not accept
     the old frame's tagged words: every plan starts at epoch 1, so its
