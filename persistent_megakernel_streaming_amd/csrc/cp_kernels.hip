@@ -217,20 +217,23 @@ __device__ __forceinline__ float tile_ssq(const float (&v)[4], int first, int sp
   return s;
 }
 
-// Tag check of N tagged 16-byte units: true when every word carries `tag`.
+// Tag check of the first n of N tagged 16-byte units: true when every word
+// carries `tag`.
 template <int N>
-__device__ __forceinline__ bool units_ok(const u32x4 (&v)[N], uint32_t tag) {
+__device__ __forceinline__ bool units_ok(const u32x4 (&v)[N], uint32_t tag, int n = N) {
   uint32_t d = 0;
 #pragma unroll
-  for (int i = 0; i < N; ++i) d |= (v[i][1] ^ tag) | (v[i][3] ^ tag);
+  for (int i = 0; i < N; ++i)
+    if (i < n) d |= (v[i][1] ^ tag) | (v[i][3] ^ tag);
   return d == 0;
 }
 // The same for single tagged words (8-byte loads).
 template <int N>
-__device__ __forceinline__ bool units_ok(const u32x2 (&v)[N], uint32_t tag) {
+__device__ __forceinline__ bool units_ok(const u32x2 (&v)[N], uint32_t tag, int n = N) {
   uint32_t d = 0;
 #pragma unroll
-  for (int i = 0; i < N; ++i) d |= v[i][1] ^ tag;
+  for (int i = 0; i < N; ++i)
+    if (i < n) d |= v[i][1] ^ tag;
   return d == 0;
 }
 __device__ __forceinline__ u32x4 ld_coherent(rsrc_t r, uint32_t off, u32x4*) { return ld16c(r, off); }
@@ -240,7 +243,7 @@ __device__ __forceinline__ u32x2 ld_coherent(rsrc_t r, uint32_t off, u32x2*) {
 
 // A set of tagged units a lane is waiting for: N loads already issued into
 // v, their offsets in r, and the tag they must carry.  Units from `nload` on
-// are fillers that already carry it and are never reloaded.
+// are neither checked nor reloaded (they may hold anything).
 template <typename T, int N, typename Off>
 struct Pend {
   T (&v)[N];
@@ -249,9 +252,9 @@ struct Pend {
   uint32_t tag;
   bool active;
   int nload;
-  __device__ __forceinline__ bool ok() const { return !active || units_ok(v, tag); }
+  __device__ __forceinline__ bool ok() const { return !active || units_ok(v, tag, nload); }
   __device__ __forceinline__ void reload() {
-    if (active && !units_ok(v, tag)) {
+    if (active && !units_ok(v, tag, nload)) {
 #pragma unroll
       for (int i = 0; i < N; ++i)
         if (i < nload) v[i] = ld_coherent(r, off(i), (T*)nullptr);
@@ -812,11 +815,14 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     const uint32_t k0 = ((uint32_t)((kvrow + t) * d + c * dq)) * ESZ * 2;
     auto qo = [=](int i) { return q0 + i * 16; };
     auto ko = [=](int i) { return k0 + i * 16; };
+    // (loads without branches: units past nld repeat the last one and
+    // positions past p read position p; neither is part of the wait)
+    const uint32_t kclamp = (uint32_t)(min(t, p) - t) * (uint32_t)(d * ESZ * 2);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-      const bool use = i < nld;
-      qv[i] = use ? ld16c(rq, qo(i)) : u32x4{0, q_tag, 0, q_tag};
-      kv[i] = (use && t <= p) ? ld16c(rk, ko(i)) : u32x4{0, kv_tag, 0, kv_tag};
+      const int iu = i < nld ? i : nld - 1;
+      qv[i] = ld16c(rq, qo(iu));
+      kv[i] = ld16c(rk, ko(iu) + kclamp);
     }
     // V of this lane's dims for every t <= p: the word holding them (bf16),
     // or the aligned pair of words (fp32)
@@ -826,18 +832,12 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     u32x2 vw[16];
     u32x4 vv[BF ? 1 : 16];
     // (every position is loaded, so the loads issue without branches; those
-    // past p take the expected tag, stay out of the wait and are masked below)
+    // past p stay out of the wait and are masked below)
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
       const uint32_t o = vo(min(tt, P - 1));
-      if constexpr (BF) {
-        vw[tt] = __builtin_amdgcn_raw_buffer_load_b64(rv, o, 0, kSC1);
-        vw[tt][1] = tt <= p ? vw[tt][1] : kv_tag;
-      } else {
-        vv[tt] = ld16c(rv, o);
-        vv[tt][1] = tt <= p ? vv[tt][1] : kv_tag;
-        vv[tt][3] = tt <= p ? vv[tt][3] : kv_tag;
-      }
+      if constexpr (BF) vw[tt] = __builtin_amdgcn_raw_buffer_load_b64(rv, o, 0, kSC1);
+      else vv[tt] = ld16c(rv, o);
     }
     // Q and K (this position's from the qkv phase just before, earlier ones
     // long ready) and V, all in one wait
