@@ -124,6 +124,18 @@ __device__ __forceinline__ float act_val(float f) {
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+// Value of v in lane `src` (a constant), for every lane: a scalar read, not
+// an LDS round trip.
+__device__ __forceinline__ float lane_f(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+// v from the lane whose index differs in bit 0 (1) or bit 1 (2), by DPP quad
+// permutation.
+template <int M>
+__device__ __forceinline__ float quad_xor_f(float v) {
+  static_assert(M == 1 || M == 2, "quad permutation");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), M == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false));
+}
 
 // (value, index) that wins an argmax: larger value, then lower index.
 __device__ __forceinline__ bool beats(float v, uint32_t i, float bv, uint32_t bi) {
@@ -855,16 +867,17 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
         for (int e = 0; e < 8 / ESZ; ++e) dot += chunk_elem<BF>(qp, e) * chunk_elem<BF>(kp, e);
       }
-    dot += shfl_xor_f(dot, 1);
-    dot += shfl_xor_f(dot, 2);
+    dot += quad_xor_f<1>(dot);
+    dot += quad_xor_f<2>(dot);
     const float s = (t <= p) ? dot * pl.attn_scale : -INFINITY;
-    float m = s;
+    // max and sum over the 16 positions (lanes 4t hold position t's values)
+    float m = lane_f(s, 0);
 #pragma unroll
-    for (int k = 4; k <= 32; k <<= 1) m = fmaxf(m, shfl_xor_f(m, k));
+    for (int tt = 1; tt < 16; ++tt) m = fmaxf(m, lane_f(s, tt * 4));
     const float e = (t <= p) ? expf(s - m) : 0.f;
-    float sum = e;
+    float sum = lane_f(e, 0);
 #pragma unroll
-    for (int k = 4; k <= 32; k <<= 1) sum += shfl_xor_f(sum, k);
+    for (int tt = 1; tt < 16; ++tt) sum += lane_f(e, tt * 4);
     const float w = e / sum;
     // output: sum over t in ascending order
     // (positions past p add an exact 0: weight and value both selected to 0)
@@ -872,7 +885,7 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     const int wsel = (lane * dpl) & 1;  // fp32, one dim per lane: which word of the pair
     float wv[16];
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) wv[tt] = __shfl(w, tt * 4, 64);
+    for (int tt = 0; tt < 16; ++tt) wv[tt] = lane_f(w, tt * 4);
     if (dpl == 2) {
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
