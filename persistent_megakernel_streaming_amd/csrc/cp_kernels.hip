@@ -793,12 +793,13 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 // One kv head g for a group of rows: every (row, q head of g) pair is one
 // wave's work.  Scores: lane (t, c) takes position t and a quarter c of the
 // head dimension; softmax over t <= p in float; output: lane owns d/64 dims.
-template <int BF>
+template <int BF, int D>
 __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                           uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int d = pl.d, gq = pl.gq, nkv = pl.nkv, P = pl.P, Rmax = pl.Rmax;
+  constexpr int d = D;  // head dim (64 or 128; the plan refuses others)
+  const int gq = pl.gq, nkv = pl.nkv, P = pl.P, Rmax = pl.Rmax;
   const int l = tk.layer, p = tk.pos;
   const int ngroups = Rmax / pl.attn_rows;
   const int g = tk.tile / ngroups, rg = tk.tile % ngroups;
@@ -812,9 +813,9 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
   const uint32_t q_tag = tag_of(epoch, tk.ph_in0), kv_tag = tag_of(epoch, kKvPhase);
   const uint32_t my_tag = tag_of(epoch, tk.phase);
   const int t = lane >> 2, c = lane & 3;
-  const int dq = d / 4;                  // dims per score lane
-  const int nld = dq * ESZ * 2 / 16;     // 16-byte tagged loads per score lane (4, 8 or 16)
-  const int dpl = d / 64;                // output dims per lane (1 or 2)
+  constexpr int dq = d / 4;              // dims per score lane
+  constexpr int nld = dq * ESZ * 2 / 16; // 16-byte tagged loads per score lane (4, 8 or 16)
+  constexpr int dpl = d / 64;            // output dims per lane (1 or 2)
   for (int pi = wave; pi < npairs; pi += 4) {
     const int row = rg * pl.attn_rows + pi / gq;
     const int hq = g * gq + pi % gq;
@@ -1335,7 +1336,10 @@ template <int BF, bool ONE>
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                          uint8_t* slot, uint32_t* misc, uint64_t* tr) {
   switch (tk.type) {
-    case T_ATTN: attn_task<BF>(pl, fr, tk, epoch, tr); break;
+    case T_ATTN:
+      if (pl.d == 128) attn_task<BF, 128>(pl, fr, tk, epoch, tr);
+      else attn_task<BF, 64>(pl, fr, tk, epoch, tr);
+      break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, slot, misc, tr); break;
 #define CP_PROJ(K) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr);
