@@ -447,7 +447,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   if (wave_live) {
     if constexpr (ONE) {
 #pragma unroll
-      for (int j = 0; j < NJ1; ++j) xo[j] = j < nj1 ? ld16c(rx, oo(j)) : u32x4{0, in_tag, 0, in_tag};
+      for (int j = 0; j < NJ1; ++j) xo[j] = ld16c(rx, oo(j < nj1 ? j : nj1 - 1));  // (past nj1: not waited for)
     } else {
       load(xa, 0);
       load(xb, 1);
