@@ -449,10 +449,17 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
       for (int j = 0; j < NJ1; ++j) xo[j] = ld16c(rx, oo(j < nj1 ? j : nj1 - 1));  // (past nj1: not waited for)
     } else {
-      load(xa, 0);
-      load(xb, 1);
-      load(xc, 2);
-      load(xd, 3);
+      // (the first four groups without branches; past the last group,
+      // the last one is read again and never waited for)
+      auto load0 = [&](u32x4 (&x)[NU], int g) {
+        const int gg = g < ng ? g : ng - 1;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) x[u] = XLL ? ld16c(rx, uoff(gg)(u)) : ld16(rx, uoff(gg)(u));
+      };
+      load0(xa, 0);
+      load0(xb, 1);
+      load0(xc, 2);
+      load0(xd, 3);
     }
   }
   // Sum-of-squares partials of a normalised operand (H/16 per row, written
