@@ -477,19 +477,18 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     for (int i = 1; i < 8; ++i) ssv[i] = u32x4{0, in_tag, 0, in_tag};
   } else if constexpr (NORM) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ssv[i] = (2 * i < nsq) ? ld16(rs, sso(i)) : u32x4{0, in_tag, 0, in_tag};
+    for (int i = 0; i < 8; ++i) ssv[i] = ld16(rs, sso(2 * i < nsq ? i : nsq / 2 - 1));  // (past nsq: not waited for)
   }
   // RoPE angles of a qkv tile's two rotary pairs per lane.
   float rope_cs[2] = {1.f, 1.f}, rope_sn[2] = {0.f, 0.f};
   if constexpr (KIND == T_QKV) {
     const int d = pl.d, th = d / 16, tpg = (pl.gq + 2) * th, lt = tk.tile % tpg;
-    if (lt < (pl.gq + 1) * th) {
-      const int i0 = 8 * (lt % th) + 2 * q;
+    // (loaded for v tiles too, which do not use them: no branch between loads)
+    const int i0 = 8 * (lt % th) + 2 * q;
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        rope_cs[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2];
-        rope_sn[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2 + 1];
-      }
+    for (int pr = 0; pr < 2; ++pr) {
+      rope_cs[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2];
+      rope_sn[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2 + 1];
     }
   }
   // The data is its own signal: wait for the first two groups and the norm
@@ -668,8 +667,10 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         }
       }
     } else if (epi_wave) {
+      // (splits past the last partner reread the last one, or read beyond the
+      // tile's partials when there is no partner; never waited for)
 #pragma unroll
-      for (int u = 0; u < 6; ++u) pv[u] = (u >> 1) < npart ? ld16c(rp, po(u)) : u32x4{0, my_tag, 0, my_tag};
+      for (int u = 0; u < 6; ++u) pv[u] = ld16c(rp, po((u >> 1) < npart ? u : 2 * npart - 2 + (u & 1)));
       if constexpr (RESID) {
 #pragma unroll
         for (int u = 0; u < NR; ++u) rv[u] = ld16c(rr, ro(u));
