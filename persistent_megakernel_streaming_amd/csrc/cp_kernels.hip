@@ -124,6 +124,40 @@ __device__ __forceinline__ float act_val(float f) {
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+// v from lane (lane ^ M) for M = 16, 32: the gfx950 row swaps (rows of 16
+// lanes trade places with their neighbours, or halves of the wave).
+template <int M>
+__device__ __forceinline__ uint32_t swap_xor_u(uint32_t v) {
+  static_assert(M == 16 || M == 32, "row swap distance");
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+// v from another lane by a DPP pattern CTRL that pairs lanes within rows:
+// quad permutations 0xB1 (lane ^ 1) and 0x4E (lane ^ 2), half-row mirror
+// 0x141 (lanes i and 7 - i of each 8), row mirror 0x140 (i and 15 - i).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+// Applies f(value from a partner lane) over a tree that reaches all 64
+// lanes: quads, half rows, rows by DPP, then the two row swaps.  With an
+// exchange that is commutative and associative every lane ends with the same
+// result.
+template <typename F>
+__device__ __forceinline__ void wave_tree(F&& f) {
+  f([](uint32_t v) { return dpp_u<0xB1>(v); });
+  f([](uint32_t v) { return dpp_u<0x4E>(v); });
+  f([](uint32_t v) { return dpp_u<0x141>(v); });
+  f([](uint32_t v) { return dpp_u<0x140>(v); });
+  f([](uint32_t v) { return swap_xor_u<16>(v); });
+  f([](uint32_t v) { return swap_xor_u<32>(v); });
+}
+
 // Value of v in lane `src` (a constant), for every lane: a scalar read, not
 // an LDS round trip.
 __device__ __forceinline__ float lane_f(float v, int src) {
@@ -506,8 +540,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   float rinv = 1.f;
   if constexpr (NORM && ONE) {
     float ss = lane < H / 32 ? __uint_as_float(ssv[0][0]) + __uint_as_float(ssv[0][2]) : 0.f;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) ss += shfl_xor_f(ss, m);
+    wave_tree([&](auto other) { ss += __uint_as_float(other(__float_as_uint(ss))); });
     rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
   } else if constexpr (NORM) {
     float ss = 0.f;
@@ -960,20 +993,24 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
   // thread t covers elements 4t .. 4t+3: four threads per 16-column tile
   for (int k = threadIdx.x * 4; k < ((H + 1023) / 1024) * 1024; k += kThreads * 4) {
     const bool in = k < H;
-    float ev[4] = {0.f, 0.f, 0.f, 0.f};
-    u32x4 sv = {0, 0, 0, 0};
-    if (in) {
-      if constexpr (BF) {
-        const u32x2 e = ld8(re, (ebase + k) * 2);
-        ev[0] = bf2f(e[0] & 0xffffu); ev[1] = bf2f(e[0] >> 16); ev[2] = bf2f(e[1] & 0xffffu); ev[3] = bf2f(e[1] >> 16);
-      } else {
-        const u32x4 e = ld16(re, (ebase + k) * 4);
+    // (both loads without branches, so they go out together; past H the
+    // last four elements are read again and not used)
+    const int kc = in ? k : H - 4;
+    float ev[4];
+    if constexpr (BF) {
+      const u32x2 e = ld8(re, (ebase + kc) * 2);
+      ev[0] = bf2f(e[0] & 0xffffu); ev[1] = bf2f(e[0] >> 16); ev[2] = bf2f(e[1] & 0xffffu); ev[3] = bf2f(e[1] >> 16);
+    } else {
+      const u32x4 e = ld16(re, (ebase + kc) * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ev[i] = __uint_as_float(e[i]);
-      }
-      if (!first) sv = ld16(rs, (uint32_t)(row * H + k) * 4);
-      if (feeds) st_act4<BF>(rx, row, k, H, ev, my_tag);
+      for (int i = 0; i < 4; ++i) ev[i] = __uint_as_float(e[i]);
     }
+    u32x4 sv = ld16(rs, (uint32_t)(row * H + kc) * 4);  // (not used by the first embedding)
+    if (!in) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ev[i] = 0.f;
+    }
+    if (in && feeds) st_act4<BF>(rx, row, k, H, ev, my_tag);
     const float sq = tile_ssq(ev, 1, 4);
     if (in) {
 #pragma unroll
@@ -1319,12 +1356,11 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
           }
         }
       }
-#pragma unroll
-      for (int m = 1; m <= 32; m <<= 1) {
-        const float ov = shfl_xor_f(bv, m);
-        const uint32_t oi = (uint32_t)__shfl_xor((int)bi, m, 64);
+      wave_tree([&](auto other) {
+        const float ov = __uint_as_float(other(__float_as_uint(bv)));
+        const uint32_t oi = other(bi);
         if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
+      });
       if (lane == 0) {
         misc[1] = bi < (uint32_t)pl.V ? bi : 0u;
         st4(make_rsrc(fr.codes, (uint32_t)fr.rows * (pl.P - 1) * 4), (uint32_t)(row * (pl.P - 1) + p - 1) * 4, misc[1]);
