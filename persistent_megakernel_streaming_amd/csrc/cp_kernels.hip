@@ -298,7 +298,9 @@ struct Pend {
   uint32_t tag;
   bool active;
   int nload;
-  __device__ __forceinline__ bool ok() const { return !active || units_ok(v, tag, nload); }
+  // (both sides always evaluated: the tag check then reads every unit on
+  // every path, so the compiler knows the loads are complete after a wait)
+  __device__ __forceinline__ bool ok() const { return !active | units_ok(v, tag, nload); }
   __device__ __forceinline__ void reload() {
     if (active && !units_ok(v, tag, nload)) {
 #pragma unroll
@@ -605,19 +607,22 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + acc1[v];
     }
   } else if (wave_live) {
+    // Blocks of four groups: the four are in flight together and consumed in
+    // order, then the next four go out together.  (Refilling each set right
+    // after its use made the compiler wait for every outstanding load at
+    // each group, one round trip per group.)
     for (int g = 0; g < ng; g += 4) {
       step(xa, g);
       if (g == 0) stamp(tr, 6);
-      load(xa, g + 4);
-      if (g + 1 >= ng) break;
-      step(xb, g + 1);
-      load(xb, g + 5);
-      if (g + 2 >= ng) break;
-      step(xc, g + 2);
-      load(xc, g + 6);
-      if (g + 3 >= ng) break;
-      step(xd, g + 3);
-      load(xd, g + 7);
+      if (g + 1 < ng) step(xb, g + 1);
+      if (g + 2 < ng) step(xc, g + 2);
+      if (g + 3 < ng) step(xd, g + 3);
+      if (g + 4 < ng) {
+        load(xa, g + 4);
+        load(xb, g + 5);
+        load(xc, g + 6);
+        load(xd, g + 7);
+      }
     }
     if constexpr (NB == 1) {
 #pragma unroll
