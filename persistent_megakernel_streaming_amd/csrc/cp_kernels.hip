@@ -1158,6 +1158,60 @@ __device__ __forceinline__ double block_exscan(double v, double* red, double& to
   return before + x - v;
 }
 
+// The kk largest of the block's keys (kk < 256 NE), sorted descending into
+// xch[0 .. kk) and into ranks tid * NE + e < kk of k.  The kk-th largest key
+// is found a byte at a time from the top, with exact counts per byte value
+// (it stops as soon as a whole byte class is kept); the kept keys are then
+// ranked by counting the larger ones (keys are distinct: they carry the
+// index).  tmp: kk keys, hist: 260 words, red: as block_exscan.
+template <int NE>
+__device__ __forceinline__ void block_topk_desc(uint64_t (&k)[NE], int kk, uint64_t* xch, uint64_t* tmp,
+                                                uint32_t* hist, double* red) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0, pmask = 0;
+  uint32_t remaining = (uint32_t)kk;
+  for (int b = 7; b >= 0; --b) {
+    hist[tid] = 0;  // one bin per thread
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      if ((k[e] & pmask) == prefix) atomicAdd(&hist[(uint32_t)(k[e] >> (8 * b)) & 255u], 1u);
+    __syncthreads();
+    // thread t takes bin 255 - t: thread order is descending key order
+    const uint32_t c = hist[255 - tid];
+    double total;
+    const uint32_t before = (uint32_t)block_exscan((double)c, red, total);
+    if (before < remaining && remaining <= before + c) {
+      hist[256] = 255u - (uint32_t)tid;
+      hist[257] = before;
+      hist[258] = c;
+    }
+    __syncthreads();
+    const uint32_t bin = hist[256], nbefore = hist[257], nclass = hist[258];
+    __syncthreads();
+    prefix |= (uint64_t)bin << (8 * b);
+    pmask |= 0xFFull << (8 * b);
+    remaining -= nbefore;
+    if (remaining == nclass) break;  // the whole class is kept
+  }
+  // exactly kk keys are >= prefix
+  if (tid == 0) hist[259] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+    if (k[e] >= prefix) tmp[atomicAdd(&hist[259], 1u)] = k[e];
+  __syncthreads();
+  if (tid < kk) {
+    const uint64_t key = tmp[tid];
+    int r = 0;
+    for (int j = 0; j < kk; ++j) r += tmp[j] > key ? 1 : 0;
+    xch[r] = key;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < NE; ++e) k[e] = tid * NE + e < kk ? xch[tid * NE + e] : 0ull;
+}
+
 // Block minimum of an int.  red: 4 words of LDS.
 __device__ __forceinline__ int block_min_int(int v, uint32_t* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1233,9 +1287,16 @@ __device__ __noinline__ int sampled_code(ZRow<NE> zr, DrawArgs da, uint8_t* scra
   uint64_t k[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) k[e] = rank_key(z[e] / T, (uint32_t)(tid * NE + e));
-  block_sort_desc<NE>(k, V, xch);
   const int tk = da.top_k;
   const int kk = (tk <= 0 || tk >= V) ? V : tk;
+  if (kk < kThreads) {
+    // only the top kk ranks matter: select them instead of sorting all V
+    uint64_t* tmp = (uint64_t*)(scratch + (size_t)V * 8 + 128);
+    uint32_t* hist = (uint32_t*)(scratch + (size_t)V * 8 + 128 + kThreads * 8);
+    block_topk_desc<NE>(k, kk, xch, tmp, hist, red);
+  } else {
+    block_sort_desc<NE>(k, V, xch);
+  }
   const float pp = da.top_p;
   // ranks to LDS: the Gumbel step deals them round-robin over the block (the
   // kept ranks are the first few, which one thread would otherwise hold)
