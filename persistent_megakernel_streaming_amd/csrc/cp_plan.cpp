@@ -82,13 +82,6 @@ cp_status fail(cp_plan* p, cp_status s, const std::string& msg) {
   return s;
 }
 
-uint16_t f32_to_bf16(float f) {
-  uint32_t u;
-  std::memcpy(&u, &f, 4);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
 // ---------------------------------------------------------------- planning
 
 struct Builder {
@@ -184,11 +177,8 @@ std::vector<int> xcd_deal(const std::vector<int>& xcd, int n_wg, int& rot) {
 
 }  // namespace
 
-// Repacks one projection tile: rows[16 * nb] source rows (host), K range
-// [k0, k0 + kt).  Output order: chunk step c, row block b, lane, element -- the
-// order in which a wave's 64 lanes read MFMA A fragments (lane l: row l % 16,
-// elements (l / 16) * E .. + E of the step).
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16 bits, round to nearest even (finite inputs: products of
+// finite weights and gains).
 static uint16_t to_bf16(float f) {
   uint32_t u;
   std::memcpy(&u, &f, 4);
@@ -563,7 +553,7 @@ static cp_status check_schedule(cp_plan* P) {
       if (slot_count[g][s] != G.per_sub) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: sub-counter count mismatch");
   }
   for (const Task& t : P->phase_tasks)
-    for (int k = 0; k < t.nwait; ++k) {
+    for (uint32_t k = 0; k < t.nwait; ++k) {
       if (t.wait[k] >= ng) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: bad wait group");
       if (last_sig[t.wait[k]] >= (int)t.phase) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: wait on a later phase");
     }
