@@ -355,6 +355,24 @@ def test_sampled_l5_64_rows():
     print(f"sampled l5 r64: max logit err {err:.4f}, robust draws {frac:.2f}")
 
 
+@pytest.mark.parametrize("name,top_ks", [
+    ("tiny_f32", [255, 256, 254, 2]),           # 255 = the largest cut below V that is selected, 256 = V
+    ("l5_r64_sampled", [255, 256, 2047, 64]),   # below / at the 256-key selection limit, V - 1
+])
+def test_sampled_top_k_around_selection_limit(name, top_ks):
+    """Top-k cuts of fewer than 256 keys are selected a byte at a time, larger
+    ones sorted in full: draws on both sides of the limit against the oracle,
+    with top-p off so that top-k alone sets the kept set."""
+    cfg = synth.CONFIGS[name].with_(rows=4, sampled=True)
+    w, wdev, ow = _weights(cfg, seed=7)
+    inputs = synth.make_inputs(cfg, seed=7, sampled=True)
+    inputs["top_k"] = np.array(top_ks, dtype=np.int32)
+    inputs["top_p"] = np.ones(4, dtype=np.float32)
+    gpu = _gpu_frame(cfg, wdev, inputs)
+    err, frac = _check_sampled(cfg, ow, inputs, gpu, range(4), 1e-4 if cfg.dtype == "f32" else 0.05)
+    print(f"top-k {top_ks} {name}: max logit err {err:.2e}, robust draws {frac:.2f}")
+
+
 def test_sampled_persistent_equals_per_phase_and_repeats():
     cfg = synth.CONFIGS["l5_r64_sampled"].with_(rows=9)
     w, wdev, ow = _weights(cfg)
