@@ -287,10 +287,137 @@ __device__ __forceinline__ u32x2 ld_coherent(rsrc_t r, uint32_t off, u32x2*) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSC1);
 }
 
+// Reloads of tagged units while polling, as one asm block: all loads, then a
+// wait for them.  Hidden from the compiler's own wait bookkeeping, they do
+// not make it treat the polled registers as the newest loads in flight (it
+// would then drain every load issued after them wherever they are read).
+// The block starts with five wait states: the compiler does not guard inline
+// asm against the hazard of a vector-memory instruction reading SGPRs (here
+// the buffer resource) that a VALU instruction (v_readlane) has just written.
+__device__ __forceinline__ void asm_reload(u32x4 (&v)[1], rsrc_t r, const uint32_t (&o)[1]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx4 %0, %1, %2, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0])
+               : "v"(o[0]), "s"(r)
+               : "memory");
+}
+
+__device__ __forceinline__ void asm_reload(u32x4 (&v)[2], rsrc_t r, const uint32_t (&o)[2]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx4 %0, %2, %4, 0 offen sc1\n"
+               "buffer_load_dwordx4 %1, %3, %4, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1])
+               : "v"(o[0]), "v"(o[1]), "s"(r)
+               : "memory");
+}
+
+__device__ __forceinline__ void asm_reload(u32x4 (&v)[4], rsrc_t r, const uint32_t (&o)[4]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx4 %0, %4, %8, 0 offen sc1\n"
+               "buffer_load_dwordx4 %1, %5, %8, 0 offen sc1\n"
+               "buffer_load_dwordx4 %2, %6, %8, 0 offen sc1\n"
+               "buffer_load_dwordx4 %3, %7, %8, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])
+               : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "s"(r)
+               : "memory");
+}
+
+__device__ __forceinline__ void asm_reload(u32x4 (&v)[6], rsrc_t r, const uint32_t (&o)[6]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx4 %0, %6, %12, 0 offen sc1\n"
+               "buffer_load_dwordx4 %1, %7, %12, 0 offen sc1\n"
+               "buffer_load_dwordx4 %2, %8, %12, 0 offen sc1\n"
+               "buffer_load_dwordx4 %3, %9, %12, 0 offen sc1\n"
+               "buffer_load_dwordx4 %4, %10, %12, 0 offen sc1\n"
+               "buffer_load_dwordx4 %5, %11, %12, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5])
+               : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "v"(o[5]), "s"(r)
+               : "memory");
+}
+
+__device__ __forceinline__ void asm_reload(u32x4 (&v)[8], rsrc_t r, const uint32_t (&o)[8]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx4 %0, %8, %16, 0 offen sc1\n"
+               "buffer_load_dwordx4 %1, %9, %16, 0 offen sc1\n"
+               "buffer_load_dwordx4 %2, %10, %16, 0 offen sc1\n"
+               "buffer_load_dwordx4 %3, %11, %16, 0 offen sc1\n"
+               "buffer_load_dwordx4 %4, %12, %16, 0 offen sc1\n"
+               "buffer_load_dwordx4 %5, %13, %16, 0 offen sc1\n"
+               "buffer_load_dwordx4 %6, %14, %16, 0 offen sc1\n"
+               "buffer_load_dwordx4 %7, %15, %16, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+               : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "v"(o[5]), "v"(o[6]), "v"(o[7]), "s"(r)
+               : "memory");
+}
+
+__device__ __forceinline__ void asm_reload(u32x4 (&v)[16], rsrc_t r, const uint32_t (&o)[16]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx4 %0, %16, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %1, %17, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %2, %18, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %3, %19, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %4, %20, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %5, %21, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %6, %22, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %7, %23, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %8, %24, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %9, %25, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %10, %26, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %11, %27, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %12, %28, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %13, %29, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %14, %30, %32, 0 offen sc1\n"
+               "buffer_load_dwordx4 %15, %31, %32, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+               : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "v"(o[5]), "v"(o[6]), "v"(o[7]), "v"(o[8]), "v"(o[9]), "v"(o[10]), "v"(o[11]), "v"(o[12]), "v"(o[13]), "v"(o[14]), "v"(o[15]), "s"(r)
+               : "memory");
+}
+
+__device__ __forceinline__ void asm_reload(u32x2 (&v)[1], rsrc_t r, const uint32_t (&o)[1]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx2 %0, %1, %2, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0])
+               : "v"(o[0]), "s"(r)
+               : "memory");
+}
+
+__device__ __forceinline__ void asm_reload(u32x2 (&v)[16], rsrc_t r, const uint32_t (&o)[16]) {
+  asm volatile("s_nop 4\n"
+               "buffer_load_dwordx2 %0, %16, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %1, %17, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %2, %18, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %3, %19, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %4, %20, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %5, %21, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %6, %22, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %7, %23, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %8, %24, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %9, %25, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %10, %26, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %11, %27, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %12, %28, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %13, %29, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %14, %30, %32, 0 offen sc1\n"
+               "buffer_load_dwordx2 %15, %31, %32, 0 offen sc1\n"
+               "s_waitcnt vmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+               : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "v"(o[5]), "v"(o[6]), "v"(o[7]), "v"(o[8]), "v"(o[9]), "v"(o[10]), "v"(o[11]), "v"(o[12]), "v"(o[13]), "v"(o[14]), "v"(o[15]), "s"(r)
+               : "memory");
+}
+
 // A set of tagged units a lane is waiting for: N loads already issued into
 // v, their offsets in r, and the tag they must carry.  Units from `nload` on
-// are neither checked nor reloaded (they may hold anything).
-template <typename T, int N, typename Off>
+// are neither checked nor reloaded (they may hold anything).  ASM: reloads
+// through asm_reload (every unit, those past nload being rereads nobody
+// checks).
+template <typename T, int N, typename Off, bool ASM>
 struct Pend {
   T (&v)[N];
   rsrc_t r;
@@ -303,16 +430,23 @@ struct Pend {
   __device__ __forceinline__ bool ok() const { return !active | units_ok(v, tag, nload); }
   __device__ __forceinline__ void reload() {
     if (active && !units_ok(v, tag, nload)) {
+      if constexpr (ASM) {
+        uint32_t o[N];
 #pragma unroll
-      for (int i = 0; i < N; ++i)
-        if (i < nload) v[i] = ld_coherent(r, off(i), (T*)nullptr);
+        for (int i = 0; i < N; ++i) o[i] = off(i);
+        asm_reload(v, r, o);
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+          if (i < nload) v[i] = ld_coherent(r, off(i), (T*)nullptr);
+      }
     }
   }
 };
-template <typename T, int N, typename Off>
-__device__ __forceinline__ Pend<T, N, Off> pend(T (&v)[N], rsrc_t r, Off off, uint32_t tag, bool active,
-                                                int nload = N) {
-  return Pend<T, N, Off>{v, r, off, tag, active, nload};
+template <bool ASM = false, typename T, int N, typename Off>
+__device__ __forceinline__ Pend<T, N, Off, ASM> pend(T (&v)[N], rsrc_t r, Off off, uint32_t tag, bool active,
+                                                     int nload = N) {
+  return Pend<T, N, Off, ASM>{v, r, off, tag, active, nload};
 }
 
 // Waits until every set of every lane carries its tag.  When the data is
@@ -375,7 +509,7 @@ __device__ __forceinline__ void st_act4(rsrc_t r, int row, int n, int K, const f
 // RMSNorm: the gain g is folded into the packed weight tile at plan creation
 // (W . (g x / rms(x)) = (W g) . x / rms(x)), so the MFMAs take the residual
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
-template <int BF, int KIND, bool ONE = false>
+template <int BF, int KIND, bool ONE = false, bool ASM = !ONE>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                           uint8_t* slot, uint32_t* misc, uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
@@ -533,8 +667,9 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   if constexpr (ONE)
     await_all(pl, pend(xo, rx, oo, in_tag, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live, 1));
   else
-    await_all(pl, pend(xa, rx, uoff(0), in_tag, XLL && live), pend(xb, rx, uoff(1), in_tag, XLL && live && ng > 1),
-              pend(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
+    await_all(pl, pend<ASM>(xa, rx, uoff(0), in_tag, XLL && live),
+              pend<ASM>(xb, rx, uoff(1), in_tag, XLL && live && ng > 1),
+              pend<ASM>(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
   wait_vm();
   __syncthreads();
   stamp(tr, 2);
@@ -558,7 +693,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const uint8_t* wt = slot + lane * 16 + (size_t)c0 * NB * 1024;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   auto step = [&](u32x4 (&xr)[NU], int g) {
-    if constexpr (XLL) await_all(pl, pend(xr, rx, uoff(g), in_tag, live));
+    if constexpr (XLL) await_all(pl, pend<ASM>(xr, rx, uoff(g), in_tag, live));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = g * 4 + i;
@@ -715,7 +850,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
     if (epi_wave && owner) {
-      await_all(pl, pend(pv, rp, po, my_tag, live && npart > 0, 2 * npart), pend(rv, rr, ro, res_tag, RESID && live));
+      await_all(pl, pend<ASM>(pv, rp, po, my_tag, live && npart > 0, 2 * npart),
+                pend<ASM>(rv, rr, ro, res_tag, RESID && live));
       f32x4 s = acc0;
 #pragma unroll
       for (int sp = 1; sp < 4; ++sp)
@@ -839,7 +975,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 // One kv head g for a group of rows: every (row, q head of g) pair is one
 // wave's work.  Scores: lane (t, c) takes position t and a quarter c of the
 // head dimension; softmax over t <= p in float; output: lane owns d/64 dims.
-template <int BF, int D>
+template <int BF, int D, bool ASM>
 __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                           uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;
@@ -901,11 +1037,11 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     // Q and K (this position's from the qkv phase just before, earlier ones
     // long ready) and V, all in one wait
     if constexpr (BF)
-      await_all(pl, pend(qv, rq, qo, q_tag, true, nld), pend(kv, rk, ko, kv_tag, t <= p, nld),
-                pend(vw, rv, vo, kv_tag, true, p + 1));
+      await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, kv_tag, t <= p, nld),
+                pend<ASM>(vw, rv, vo, kv_tag, true, p + 1));
     else
-      await_all(pl, pend(qv, rq, qo, q_tag, true, nld), pend(kv, rk, ko, kv_tag, t <= p, nld),
-                pend(vv, rv, vo, kv_tag, true, p + 1));
+      await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, kv_tag, t <= p, nld),
+                pend<ASM>(vv, rv, vo, kv_tag, true, p + 1));
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < NQ; ++i)
@@ -1372,7 +1508,7 @@ __device__ __forceinline__ int sampled_row(const DevPlan& pl, const DevFrame& fr
   return sampled_code<NE>(zr, da, scratch);
 }
 
-template <int BF>
+template <int BF, bool ASM>
 __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                           uint8_t* slot, uint32_t* misc, uint64_t* tr) {
   const int row = (int)tk.tile, p = tk.pos;
@@ -1412,7 +1548,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
           const int i = i0 + k * 64 + lane;
           cv[k] = i < pl.n_head_tiles ? ld16c(rc, co(k)) : u32x4{0, in_tag, 0xffffffffu, in_tag};
         }
-        await_all(pl, pend(cv, rc, co, in_tag, true, (pl.n_head_tiles - i0 - lane + 63) / 64));
+        await_all(pl, pend<ASM>(cv, rc, co, in_tag, true, (pl.n_head_tiles - i0 - lane + 63) / 64));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int i = i0 + k * 64 + lane;
@@ -1447,11 +1583,11 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
                                          uint8_t* slot, uint32_t* misc, uint64_t* tr) {
   switch (tk.type) {
     case T_ATTN:
-      if (pl.d == 128) attn_task<BF, 128>(pl, fr, tk, epoch, tr);
-      else attn_task<BF, 64>(pl, fr, tk, epoch, tr);
+      if (pl.d == 128) attn_task<BF, 128, !ONE>(pl, fr, tk, epoch, tr);
+      else attn_task<BF, 64, !ONE>(pl, fr, tk, epoch, tr);
       break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
-    case T_DRAW: draw_task<BF>(pl, fr, tk, epoch, slot, misc, tr); break;
+    case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
 #define CP_PROJ(K) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr);
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
@@ -1459,7 +1595,7 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
     case T_DOWN: CP_PROJ(T_DOWN) break;
     case T_HEAD: CP_PROJ(T_HEAD) break;
 #undef CP_PROJ
-    default: proj_task<BF, T_INPROJ>(pl, fr, tk, epoch, slot, misc, tr); break;
+    default: proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
   }
 }
 
