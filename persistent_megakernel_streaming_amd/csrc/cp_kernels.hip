@@ -742,22 +742,18 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + acc1[v];
     }
   } else if (wave_live) {
-    // Blocks of four groups: the four are in flight together and consumed in
-    // order, then the next four go out together.  (Refilling each set right
-    // after its use made the compiler wait for every outstanding load at
-    // each group, one round trip per group.)
+    // Each set is refilled with the group four ahead right after its use, so
+    // three or four groups are always on their way.  The compiler's waits are
+    // in issue order: a set's wait then covers only the loads issued before
+    // it (its polling reloads are in asm; compiler-issued reloads made every
+    // set look like the newest loads and drained all of them at each group).
     for (int g = 0; g < ng; g += 4) {
       step(xa, g);
       if (g == 0) stamp(tr, 6);
-      if (g + 1 < ng) step(xb, g + 1);
-      if (g + 2 < ng) step(xc, g + 2);
-      if (g + 3 < ng) step(xd, g + 3);
-      if (g + 4 < ng) {
-        load(xa, g + 4);
-        load(xb, g + 5);
-        load(xc, g + 6);
-        load(xd, g + 7);
-      }
+      load(xa, g + 4);
+      if (g + 1 < ng) { step(xb, g + 1); load(xb, g + 5); }
+      if (g + 2 < ng) { step(xc, g + 2); load(xc, g + 6); }
+      if (g + 3 < ng) { step(xd, g + 3); load(xd, g + 7); }
     }
     if constexpr (NB == 1) {
 #pragma unroll
