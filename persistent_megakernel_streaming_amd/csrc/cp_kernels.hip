@@ -59,6 +59,11 @@ __device__ __forceinline__ void st16(rsrc_t r, uint32_t off, u32x4 v) { __builti
 __device__ __forceinline__ void st4(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0); }
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Returns once the load that wrote x has completed, and with it (a wave's
+// vector-memory operations complete in issue order) every vector-memory
+// operation the wave issued before it: the compiler must make x valid for the
+// asm, and the asm keeps later memory operations after it.
+__device__ __forceinline__ void wait_for(const u32x4& x) { asm volatile("" ::"v"(x) : "memory"); }
 
 // Trace stamp k of the current task (100 MHz constant clock), thread 0 only.
 // tr is null when the plan does not trace.
@@ -661,16 +666,20 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       rope_sn[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2 + 1];
     }
   }
-  // The data is its own signal: wait for the first two groups and the norm
+  // The data is its own signal: wait for the first group and the norm
   // partials, then for this task's weight tile (issued during the previous
-  // task) to be in LDS.
+  // task) to be in LDS.  With tagged operands the tile's copy is older than
+  // every load of group 0 (the executor issues it before it dispatches the
+  // task, and a task's loads are its own code, behind that dispatch), so
+  // group 0 having arrived covers this wave's part of it and the later groups
+  // stay in flight; otherwise, and on one-row frames, every load is waited
+  // for.
   if constexpr (ONE)
     await_all(pl, pend(xo, rx, oo, in_tag, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live, 1));
   else
-    await_all(pl, pend<ASM>(xa, rx, uoff(0), in_tag, XLL && live),
-              pend<ASM>(xb, rx, uoff(1), in_tag, XLL && live && ng > 1),
-              pend<ASM>(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
-  wait_vm();
+    await_all(pl, pend<ASM>(xa, rx, uoff(0), in_tag, XLL && live), pend<ASM>(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
+  if constexpr (XLL && !ONE) wait_for(xa[0]);
+  else wait_vm();
   __syncthreads();
   stamp(tr, 2);
 
