@@ -186,6 +186,30 @@ def test_ten_runs_bitwise_identical():
     plan.close()
 
 
+@pytest.mark.parametrize("rows", [1, 64])
+def test_back_to_back_frames_bitwise_identical(rows):
+    """Forty frames launched back to back on one stream, no host sync between
+    them, each into its own buffers: every one equals the first bit for bit.
+    A frame whose tasks read a weight tile, an operand or a partial before it
+    is complete would differ at some point under this load."""
+    cp = _cp()
+    cfg = synth.CONFIGS["l5_r64"].with_(rows=rows)
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg)
+    plan = cp.Plan(cfg, wdev, exec_mode="persistent", max_rows=64)
+    ios = [cp.make_io(cfg, inputs, kv=True) for _ in range(40)]
+    torch.cuda.synchronize()
+    for io in ios:
+        plan.run(io)
+    torch.cuda.synchronize()
+    plan.device_status()
+    ref = {k: v.cpu().numpy() for k, v in ios[0].items() if k != "rows"}
+    for i, io in enumerate(ios[1:], 1):
+        for k in ref:
+            assert np.array_equal(ref[k], io[k].cpu().numpy()), (i, k)
+    plan.close()
+
+
 @pytest.mark.parametrize("rows", [1, 16])
 def test_l10_hbm_variant(rows):
     cfg = synth.CONFIGS["l10_r16"].with_(rows=rows)
