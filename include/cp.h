@@ -7,14 +7,22 @@
  * every position after the first, and n_positions code embeddings whose sum is
  * returned with the codes.  This is the frame of the mstar pull request
  * "Qwen3-TTS: Run the 1.7B Depth Loop as One Persistent Kernel on Hopper"
- * (#1183), section "How it works"; the outputs are the ones its section
- * "Testing" compares (codes, embedding sums, KV cache, logits).
+ * (#1183), section "How it works" (first bullet: the phases of a frame); the
+ * outputs are the ones its section "Testing" compares (codes, embedding sums,
+ * KV cache, logits).
  *
  * Two executors compute bitwise-identical frames from the same task bodies:
  *   CP_EXEC_PERSISTENT  one launch of one workgroup per compute unit that walks
- *                       a static per-workgroup task list and hands data between
- *                       phases through counters in device memory;
- *   CP_EXEC_PER_PHASE   one launch per phase (the unfused comparison).
+ *                       a static per-workgroup task list (section "How it
+ *                       works", first and second bullets).  Workgroups hand
+ *                       data to each other through tagged words in device
+ *                       memory: every value one workgroup writes for another is
+ *                       stored next to a 32-bit tag (epoch * 1024 + the
+ *                       writer's phase), and the reader reloads the words until
+ *                       every tag is the one it expects.  There are no
+ *                       counters and no fences: the data is its own signal.
+ *   CP_EXEC_PER_PHASE   one launch per phase (the unfused comparison, the
+ *                       "loop" of section "Where the depth loop's time goes").
  *
  * Conventions for every call:
  *   - every call returns a cp_status; no exception or abort crosses the ABI;
@@ -23,7 +31,11 @@
  *   - sizes are element counts unless a name says bytes;
  *   - matrices are row-major [out][in], the layout of nn.Linear;
  *   - the activation type of a plan (dtype) is also the storage type of its
- *     weights, input hidden and KV outputs: IEEE fp32, or bf16 as 16-bit words.
+ *     weights, input hidden and KV outputs: IEEE fp32, or bf16 as 16-bit words;
+ *   - a call refused on the host (CP_ERR_INVALID_ARGUMENT, CP_ERR_UNSUPPORTED)
+ *     enqueues nothing, so the caller can run its own per-launch loop instead
+ *     (section "How it works", opening paragraphs: a step the kernel cannot
+ *     take runs the loop, and startup logs why).
  */
 #ifndef CP_H
 #define CP_H
@@ -50,13 +62,15 @@ typedef enum { CP_DTYPE_F32 = 0, CP_DTYPE_BF16 = 1 } cp_dtype;
 typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
 
 /* Plan flags. */
-#define CP_FLAG_TRACE 0x1u /* record per-task timestamps (persistent executor) */
+#define CP_FLAG_TRACE 0x1u /* record eight timestamps per task (persistent executor; see cp_frame_io.trace) */
 
 /* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
  * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a
  * multiple of 256 up to 1024; input_dim and intermediate multiples of 64;
  * vocab 256, 512, 1024, 2048 or 4096; 2 <= n_positions <= 16;
- * 1 <= max_rows <= 64. */
+ * 1 <= max_rows <= 64 (a step of more rows is refused and runs the loop:
+ * section "How it works", opening paragraphs; the 128-row frame is listed
+ * under "What's left in the frame, open"). */
 typedef struct {
   int32_t abi_version;  /* CP_ABI_VERSION */
   int32_t n_layers;
@@ -76,8 +90,10 @@ typedef struct {
   uint32_t flags;       /* CP_FLAG_* */
 } cp_config;
 
-/* Weights, read only inside cp_plan_create: the plan copies and repacks them,
- * so the caller may free them afterwards.  Single matrices are device
+/* Weights of the code predictor (section "Cost": hidden 1024, 16 q and 8 kv
+ * heads of 128, intermediate 3072, 5 layers for the 1.7B model; other shapes
+ * within the limits above are accepted).  Read only inside cp_plan_create:
+ * the plan copies and repacks them, so the caller may free them afterwards.  Single matrices are device
  * pointers; per-layer, per-table and per-head lists are HOST arrays of device
  * pointers. */
 typedef struct {
@@ -94,14 +110,17 @@ typedef struct {
   const void* const* w_head;      /* (n_positions - 1) x [vocab][hidden]; entry j-1 is head j */
 } cp_weights;
 
-/* One frame's inputs and outputs: all device pointers, borrowed until the
- * frame's stream work completes. */
+/* One frame's inputs and outputs (section "Testing": codes and embedding
+ * sums, the KV cache and logits are what a frame is checked on): all device
+ * pointers, borrowed until the frame's stream work completes. */
 typedef struct {
   int32_t rows;              /* 1 .. max_rows */
   const void* hidden_in;     /* [rows][input_dim], dtype */
   const int32_t* code0;      /* [rows] code 0 (from outside the loop), each in [0, vocab) */
-  /* Sampling, [rows] each.  All five NULL: greedy for every row (the lowest
-   * index of the largest logit).  Some but not all NULL:
+  /* Sampling, [rows] each (section "How it works", sampler bullet: a kernel
+   * that draws in place reads each row's temperature, top-k, top-p, seed and
+   * offset, and moves the offsets as that many single draws would).  All
+   * five NULL: greedy for every row (the lowest index of the largest logit).  Some but not all NULL:
    * CP_ERR_INVALID_ARGUMENT.  Draw j of a row (j = 1 .. n_positions-1), as
    * the sampler is defined: y = logits / temperature; keep the top_k largest
    * y (ties to the lower index); softmax over them; keep the shortest prefix
@@ -124,9 +143,18 @@ typedef struct {
   void* v_cache;             /* optional out, same layout */
   uint64_t* trace;           /* optional out, cp_plan_info.trace_words words (needs CP_FLAG_TRACE and the
                                 persistent executor): per task, in the order of cp_plan_task_table, eight
-                                100 MHz timestamps -- task start, dependencies met, operands landed,
-                                normalised, K loop done, epilogue issued, stores complete, signalled
-                                (stamps a task kind does not pass through are left as they were) */
+                                timestamps of the device's 100 MHz constant clock, written by the task's
+                                workgroup:
+                                  0 task start, 1 dispatched (next task's record read),
+                                  2 dependencies met (projections: first operand group, norm partials and
+                                    weight tile in place; attention: Q, K, V of its first pair; draw: the
+                                    head's logits or candidates),
+                                  3 first operand group consumed, 4 K loop done (projections),
+                                  5 outputs issued, 6 end-of-task barrier passed, 7 next tile copy issued.
+                                Stamps a task kind does not pass through (2-4 for the code-0 embedding,
+                                3-4 for attention and draws) hold no value of the frame.  The timestamps
+                                follow the eight-per-task split of section "Where the depth loop's time
+                                goes" ("Inside a task"). */
 } cp_frame_io;
 
 typedef struct {
@@ -145,32 +173,49 @@ typedef struct {
 typedef struct cp_plan cp_plan; /* opaque, owned by the library */
 
 /* Validates cfg, checks that the persistent grid is co-resident on
- * hip_device (CP_ERR_NOT_CORESIDENT otherwise), repacks the weights, builds
- * the per-workgroup task lists and allocates all scratch.  On success *out
- * owns the plan; on failure *out is NULL. */
+ * hip_device (CP_ERR_NOT_CORESIDENT otherwise: the workgroups wait on each
+ * other, so all of them must be resident at once -- section "How it works",
+ * last bullet), repacks the weights, builds the static per-workgroup task
+ * lists (section "How it works", first bullet) and allocates all scratch.
+ * On success *out owns the plan; on failure *out is NULL and
+ * cp_last_create_error() says why.  Allocates device memory (hipMalloc);
+ * synchronises the device. */
 cp_status cp_plan_create(const cp_config* cfg, const cp_weights* w, int hip_device, cp_plan** out);
 
 /* Enqueues one frame on hip_stream (a hipStream_t; NULL = default stream) and
  * returns without waiting.  Checks io on the host first and enqueues nothing
- * on an error.  The call allocates nothing and never synchronises, so it may
- * be captured into a HIP graph.  Frames of one plan must be stream-ordered:
- * the persistent executor holds every compute unit while it runs, and two of
- * its frames in flight at once on one device could wait on each other. */
+ * on an error (CP_ERR_INVALID_ARGUMENT: rows outside 1..max_rows, a required
+ * pointer NULL, some but not all sampling arrays, a trace buffer without
+ * CP_FLAG_TRACE).  The call allocates nothing and never synchronises, so it
+ * may be captured into a HIP graph and replayed (section "Testing": a
+ * captured frame replays what it ran).  Frames of one plan must be
+ * stream-ordered: the persistent executor holds every compute unit while it
+ * runs (section "Cost": the frame holds every SM), and two of its frames in
+ * flight at once on one device could wait on each other; a device-side wait
+ * that gives up is reported by cp_plan_device_status. */
 cp_status cp_frame_run(cp_plan* plan, const cp_frame_io* io, void* hip_stream);
 
-/* Writes 8 int32 per task, in trace order: phase index, task type (1 input
+/* The static task list as a table (host memory `out`, 8 int32 per task), for
+ * decoding traces and for tests of the schedule.  Writes, in trace order: phase index, task type (1 input
  * projection, 2 code-0 embedding, 3 qkv, 4 attention, 5 o, 6 gate/up, 7 down,
  * 8 head, 9 draw), layer, position, tile, split-K index, workgroup, index in
  * the workgroup's list.  n_tasks must equal cp_plan_info.n_tasks. */
 cp_status cp_plan_task_table(const cp_plan* plan, int32_t* out, int64_t n_tasks);
 
-/* Frees everything the plan owns.  NULL is accepted. */
+/* Frees everything the plan owns (device memory and the host object).  NULL
+ * is accepted.  The plan's frames must have completed. */
 cp_status cp_plan_destroy(cp_plan* plan);
 
+/* Fills *info (host memory) with the plan's sizes; touches no device. */
 cp_status cp_plan_query(const cp_plan* plan, cp_plan_info* info);
 
 /* Synchronises the plan's device and reports CP_ERR_DEVICE_TIMEOUT if a
- * device-side wait gave up since the plan was created, else CP_OK. */
+ * device-side wait gave up since the plan was created, else CP_OK.  Every
+ * wait is bounded (a poll count, see cp_plan_set_spin_limit), so a broken
+ * schedule or two frames waiting on each other end the kernel with this
+ * error instead of hanging the device (handbook chapter "The gaps between
+ * kernels: PDL and megakernels", section "Megakernels": deadlock is the
+ * price of cross-block waits).  The error stays set for the plan's life. */
 cp_status cp_plan_device_status(cp_plan* plan);
 
 /* Frame epochs.  Every word one workgroup hands to another carries the epoch
@@ -183,6 +228,15 @@ cp_status cp_plan_device_status(cp_plan* plan);
  * CP_ERR_INVALID_ARGUMENT for an epoch outside that range. */
 cp_status cp_plan_set_epoch(cp_plan* plan, uint32_t epoch);
 
+/* Bounds every device-side wait of the plan's later frames to `polls`
+ * reloads of stale data (0 restores the default of 4194304, several seconds
+ * of polling).  A wait that runs out raises the plan's error word; every
+ * later wait of that frame then gives up at once and the kernel ends
+ * normally, with CP_ERR_DEVICE_TIMEOUT from cp_plan_device_status and the
+ * frame's outputs undefined.  For tests of the time-out path: a small bound
+ * forces it without any wait having to hang.  Touches no device. */
+cp_status cp_plan_set_spin_limit(cp_plan* plan, uint32_t polls);
+
 const char* cp_status_string(cp_status s);
 
 /* Text of the last error recorded on the plan ("" if none). */
@@ -193,9 +247,11 @@ const char* cp_plan_last_error(const cp_plan* plan);
 const char* cp_last_create_error(void);
 
 /* Builds the per-workgroup task lists cfg would get on a device of cu_count
- * compute units and checks their invariants, touching no device: every wait
- * points to a counter group that only earlier phases signal; every counter
- * receives exactly its per-frame count; every workgroup's list is in phase
+ * compute units and checks their invariants, touching no device (section
+ * "Testing": the task lists are checked on the host): every task waits only
+ * on dependency groups (the outputs of one phase, or of one kv head's tiles)
+ * that earlier phases complete; every group is completed exactly once per
+ * frame by the tasks that make it; every workgroup's list is in phase
  * order.  On success fills n_phases, n_tasks, n_workgroups and
  * max_tasks_per_workgroup of info (other fields zero).  For tests and
  * planning tools; cp_plan_create runs the same checks. */

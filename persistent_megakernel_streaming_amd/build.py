@@ -6,6 +6,7 @@ Run as ``python -m persistent_megakernel_streaming_amd.build`` or call
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -24,6 +25,35 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-ffp-con
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 
 
+# A vector-memory instruction that reads SGPRs a VALU instruction (such as
+# v_readlane, which restores spilled buffer resources) has just written needs
+# five wait states.  The compiler inserts them before its own instructions but
+# not before inline asm, so every asm block that issues a vector-memory
+# instruction must begin with "s_nop 4" (or longer) itself.
+_ASM_RE = re.compile(r'asm\s+volatile\s*\(((?:\s*"(?:[^"\\]|\\.)*")+)')
+_VMEM_RE = re.compile(r'\b(buffer|global|flat|scratch)_(load|store|atomic)')
+
+
+def check_asm_guards(path: str) -> int:
+    """Raises if an inline-asm block of `path` issues a vector-memory
+    instruction without starting with s_nop 4 or longer; returns the number
+    of such blocks checked."""
+    text = open(path).read()
+    n = 0
+    for m in _ASM_RE.finditer(text):
+        body = "".join(re.findall(r'"((?:[^"\\]|\\.)*)"', m.group(1))).replace("\\n", "\n")
+        if not _VMEM_RE.search(body):
+            continue
+        n += 1
+        first = body.strip().split("\n")[0].strip()
+        g = re.fullmatch(r"s_nop\s+(\d+)", first)
+        if not g or int(g.group(1)) < 4:
+            line = text.count("\n", 0, m.start()) + 1
+            raise RuntimeError(f"{path}:{line}: inline asm with a vector-memory instruction must start with "
+                               f"'s_nop 4' (found {first!r})")
+    return n
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -34,6 +64,7 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     """Compiles every HIP source and links libcpms.so next to the package."""
+    check_asm_guards(os.path.join(CSRC, "cp_kernels.hip"))
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)

@@ -12,8 +12,7 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# CPMS_LIBRARY names another build of the same library (same ABI) to load.
-LIB_PATH = os.environ.get("CPMS_LIBRARY") or os.path.join(_PKG, "libcpms.so")
+LIB_PATH = os.path.join(_PKG, "libcpms.so")
 
 CP_OK = 0
 STATUS = {0: "CP_OK", 1: "CP_ERR_INVALID_ARGUMENT", 2: "CP_ERR_UNSUPPORTED", 3: "CP_ERR_NOT_CORESIDENT",
@@ -79,8 +78,9 @@ def load_library():
     lib.cp_schedule_check.argtypes = [C.POINTER(Config), C.c_int, C.POINTER(PlanInfo)]
     lib.cp_plan_task_table.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
     lib.cp_plan_set_epoch.argtypes = [C.c_void_p, C.c_uint32]
+    lib.cp_plan_set_spin_limit.argtypes = [C.c_void_p, C.c_uint32]
     for f in ("cp_plan_create", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
-              "cp_schedule_check", "cp_plan_task_table", "cp_plan_set_epoch"):
+              "cp_schedule_check", "cp_plan_task_table", "cp_plan_set_epoch", "cp_plan_set_spin_limit"):
         getattr(lib, f).restype = C.c_int
     return lib
 
@@ -194,6 +194,11 @@ class Plan:
     def set_epoch(self, epoch: int):
         """Makes the next frame run as ``epoch`` (exercises the epoch wrap)."""
         self._check(_lib.cp_plan_set_epoch(self._h, int(epoch)))
+
+    def set_spin_limit(self, polls: int):
+        """Bounds every device-side wait of later frames to ``polls`` reloads
+        (0: the default); exercises the time-out path."""
+        self._check(_lib.cp_plan_set_spin_limit(self._h, int(polls)))
 
     def device_status(self):
         self._check(_lib.cp_plan_device_status(self._h))

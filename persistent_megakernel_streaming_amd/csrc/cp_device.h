@@ -47,6 +47,8 @@ constexpr int kMaxPhases = 1023;     // phase ids must stay below kKvPhase
 // the count restarts at 1 (epoch 0 is the tag of cleared memory).
 constexpr uint32_t kEpochWrap = (1u << 22) - 1;
 constexpr int kMaxClear = 16;
+// Reloads of stale data a device-side wait makes before it gives up.
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 
 // Task flag: the split-K partners of this task's tile and their owner run on
 // workgroups of one XCD, so partials go through that XCD's L2 (plain stores,

@@ -672,13 +672,14 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // every load of group 0 (the executor issues it before it dispatches the
   // task, and a task's loads are its own code, behind that dispatch), so
   // group 0 having arrived covers this wave's part of it and the later groups
-  // stay in flight; otherwise, and on one-row frames, every load is waited
-  // for.
+  // stay in flight.  A wave with no live rows issued no operand loads but
+  // still copied its share of the tile, and waits for every load; so do
+  // one-row frames and untagged operands.  (wave_live is wave-uniform.)
   if constexpr (ONE)
     await_all(pl, pend(xo, rx, oo, in_tag, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live, 1));
   else
     await_all(pl, pend<ASM>(xa, rx, uoff(0), in_tag, XLL && live), pend<ASM>(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
-  if constexpr (XLL && !ONE) wait_for(xa[0]);
+  if (XLL && !ONE && wave_live) wait_for(xa[0]);
   else wait_vm();
   __syncthreads();
   stamp(tr, 2);
@@ -697,7 +698,6 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     ss += shfl_xor_f(ss, 32);
     rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
   }
-  stamp(tr, 3);
 
   const uint8_t* wt = slot + lane * 16 + (size_t)c0 * NB * 1024;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
@@ -758,7 +758,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     // set look like the newest loads and drained all of them at each group).
     for (int g = 0; g < ng; g += 4) {
       step(xa, g);
-      if (g == 0) stamp(tr, 6);
+      if (g == 0) stamp(tr, 3);
       load(xa, g + 4);
       if (g + 1 < ng) { step(xb, g + 1); load(xb, g + 5); }
       if (g + 2 < ng) { step(xc, g + 2); load(xc, g + 6); }
@@ -1047,6 +1047,7 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     else
       await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, kv_tag, t <= p, nld),
                 pend<ASM>(vv, rv, vo, kv_tag, true, p + 1));
+    if (pi < 4) stamp(tr, 2);
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < NQ; ++i)
@@ -1486,7 +1487,7 @@ __device__ __noinline__ int sampled_code(ZRow<NE> zr, DrawArgs da, uint8_t* scra
 // takes elements t NE .. t NE + NE - 1) and its sampled code.
 template <int NE>
 __device__ __forceinline__ int sampled_row(const DevPlan& pl, const DevFrame& fr, int row, int j, uint32_t in_tag,
-                                           uint8_t* scratch) {
+                                           uint8_t* scratch, uint64_t* tr) {
   const rsrc_t rz = make_rsrc(pl.zbuf, (uint32_t)pl.Rmax * pl.V * 8);
   const uint32_t zb = (uint32_t)(row * pl.V + threadIdx.x * NE) * 8;
   float z[NE];
@@ -1495,6 +1496,7 @@ __device__ __forceinline__ int sampled_row(const DevPlan& pl, const DevFrame& fr
     auto zo = [=](int) -> uint32_t { return zb; };
     zw[0] = __builtin_amdgcn_raw_buffer_load_b64(rz, zb, 0, kSC1);
     await_all(pl, pend(zw, rz, zo, in_tag, true));
+    stamp(tr, 2);
     z[0] = __uint_as_float(zw[0][0]);
   } else {
     u32x4 zw[NE / 2];
@@ -1502,6 +1504,7 @@ __device__ __forceinline__ int sampled_row(const DevPlan& pl, const DevFrame& fr
 #pragma unroll
     for (int u = 0; u < NE / 2; ++u) zw[u] = ld16c(rz, zo(u));
     await_all(pl, pend(zw, rz, zo, in_tag, true));
+    stamp(tr, 2);
 #pragma unroll
     for (int e = 0; e < NE; ++e) z[e] = __uint_as_float(zw[e >> 1][(e & 1) * 2]);
   }
@@ -1521,11 +1524,11 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
   if (row < fr.rows && fr.sampled) {
     int code;
     switch (pl.V) {
-      case 256: code = sampled_row<1>(pl, fr, row, p, in_tag, slot); break;
-      case 512: code = sampled_row<2>(pl, fr, row, p, in_tag, slot); break;
-      case 1024: code = sampled_row<4>(pl, fr, row, p, in_tag, slot); break;
-      case 2048: code = sampled_row<8>(pl, fr, row, p, in_tag, slot); break;
-      default: code = sampled_row<16>(pl, fr, row, p, in_tag, slot); break;
+      case 256: code = sampled_row<1>(pl, fr, row, p, in_tag, slot, tr); break;
+      case 512: code = sampled_row<2>(pl, fr, row, p, in_tag, slot, tr); break;
+      case 1024: code = sampled_row<4>(pl, fr, row, p, in_tag, slot, tr); break;
+      case 2048: code = sampled_row<8>(pl, fr, row, p, in_tag, slot, tr); break;
+      default: code = sampled_row<16>(pl, fr, row, p, in_tag, slot, tr); break;
     }
     code = (code < 0 || code >= pl.V) ? 0 : code;
     if (threadIdx.x == 0) {
@@ -1554,6 +1557,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
           cv[k] = i < pl.n_head_tiles ? ld16c(rc, co(k)) : u32x4{0, in_tag, 0xffffffffu, in_tag};
         }
         await_all(pl, pend<ASM>(cv, rc, co, in_tag, true, (pl.n_head_tiles - i0 - lane + 63) / 64));
+        if (i0 == 0) stamp(tr, 2);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int i = i0 + k * 64 + lane;
@@ -1677,8 +1681,10 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     const bool more = i + 1 < e;
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
+    stamp(tr, 1);
     run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
+    stamp(tr, 6);
     // The next task's tile copy goes out once every wave has issued this
     // task's outputs: the CU's waves share one memory instruction queue and
     // each wave's operations retire in order, so a copy issued earlier would

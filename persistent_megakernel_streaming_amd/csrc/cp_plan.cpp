@@ -918,7 +918,7 @@ static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights*
   dp.nkv = cfg->n_kv_heads; dp.d = cfg->head_dim; dp.I = cfg->intermediate; dp.P = cfg->n_positions;
   dp.V = cfg->vocab; dp.Rmax = cfg->max_rows; dp.gq = dp.nq / dp.nkv; dp.n_head_tiles = dp.V / 16;
   dp.bf16 = bf; dp.eps = cfg->rms_eps; dp.attn_scale = (float)(1.0 / std::sqrt((double)cfg->head_dim));
-  dp.spin_limit = 1u << 22;
+  dp.spin_limit = kDefaultSpinLimit;
   dp.n_wg = P->cu_count;
   HIPCHK(P, check_xcd_dealing(dp.n_wg, P->xcd_dealing));
   TRY(build_schedule(P));
@@ -1076,6 +1076,12 @@ cp_status cp_plan_set_epoch(cp_plan* P, uint32_t epoch) {
   if (e == hipSuccess) e = hipMemcpy(P->dp.state + 32, &st[1], 4, hipMemcpyHostToDevice);
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("set epoch: ") + hipGetErrorString(e));
+  return CP_OK;
+}
+
+cp_status cp_plan_set_spin_limit(cp_plan* P, uint32_t polls) {
+  if (!P) return CP_ERR_INVALID_ARGUMENT;
+  P->dp.spin_limit = polls ? polls : kDefaultSpinLimit;
   return CP_OK;
 }
 

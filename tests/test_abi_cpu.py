@@ -71,3 +71,22 @@ def test_schedule_invariants(name, cus):
     assert info.n_phases == 5 * L * P + 2 * P - 4
     assert info.n_workgroups == cus
     assert info.max_tasks_per_workgroup * cus >= info.n_tasks
+
+
+def test_inline_asm_vector_memory_blocks_start_with_the_guard(tmp_path):
+    """Every inline-asm block that issues a vector-memory instruction starts
+    with five wait states (the build refuses the source otherwise): the
+    compiler does not guard asm against reading SGPRs a VALU instruction has
+    just written, and an unguarded block faulted the GPU."""
+    from persistent_megakernel_streaming_amd import build
+    src = os.path.join(ROOT, "persistent_megakernel_streaming_amd", "csrc", "cp_kernels.hip")
+    assert build.check_asm_guards(src) >= 8
+    bad = tmp_path / "bad.hip"
+    bad.write_text('asm volatile("s_nop 4\\n"\n "s_waitcnt vmcnt(0)" ::: "memory");\n'
+                   'asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen sc1\\n"\n'
+                   '             "s_waitcnt vmcnt(0)" : "+v"(v) : "v"(o), "s"(r) : "memory");\n')
+    with pytest.raises(RuntimeError, match="bad.hip:3"):
+        build.check_asm_guards(str(bad))
+    bad.write_text('asm volatile("s_nop 1\\nglobal_store_dword %0, %1, off" :: "v"(a), "v"(b));\n')
+    with pytest.raises(RuntimeError):
+        build.check_asm_guards(str(bad))

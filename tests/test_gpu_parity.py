@@ -8,7 +8,8 @@ GPU's codes, then
   * every code whose oracle top-1/top-2 logit gap is >= 0.1 equals the oracle's;
   * the fp32 embedding sums are bitwise equal;
   * K/V agree within 2% of the largest |K/V|.
-Full-size configurations check a sample of rows (rows are independent).
+Every row of every frame is checked (one oracle frame of 64 rows takes a
+few seconds on the host cores).
 """
 import numpy as np
 import pytest
@@ -53,7 +54,11 @@ def _kv_f32(cfg, a):
     return synth.bf16_bits_to_f32(a.view(np.uint16)) if cfg.dtype == "bf16" else a
 
 
-def _check(cfg, ow, inputs, gpu, rows, logit_tol, kv=False):
+def _check(cfg, ow, inputs, gpu, rows, logit_tol, kv=False, min_decided=None):
+    """min_decided: the smallest fraction of draws whose oracle top-1/top-2
+    gap is >= 0.1 (so that the code comparison is not vacuous); by default
+    0.3 for frames of at least 60 draws (synthetic logits have a standard
+    deviation near 0.64, and about half of the gaps reach 0.1)."""
     from oracle import oracle
     rows = list(rows)
     forced = gpu["codes"][rows]
@@ -61,6 +66,9 @@ def _check(cfg, ow, inputs, gpu, rows, logit_tol, kv=False):
     err = np.abs(gpu["logits"][rows] - orc["logits"]).max()
     assert err <= logit_tol, f"max |logit diff| {err}"
     decided = orc["margins"][..., 0] >= 0.1
+    if min_decided is None:
+        min_decided = 0.3 if decided.size >= 60 else 0.0
+    assert decided.mean() >= min_decided, f"only {decided.mean():.2f} of the draws are decided"
     assert np.array_equal(gpu["codes"][rows][decided], orc["codes"][decided]), "decided code differs"
     assert np.array_equal(gpu["embsum"][rows], orc["embsum"]), "embedding sums differ"
     if kv:
@@ -120,12 +128,12 @@ def test_full_l5_one_row():
     print(f"l5 r1: max logit err {err:.4f}, decided {frac:.2f}")
 
 
-def test_full_l5_64_rows_sampled_rows():
+def test_full_l5_64_rows_all_rows():
     cfg = synth.CONFIGS["l5_r64"]
     w, wdev, ow = _weights(cfg)
     inputs = synth.make_inputs(cfg)
     gpu = _gpu_frame(cfg, wdev, inputs, kv=True)
-    err, frac = _check(cfg, ow, inputs, gpu, [0, 21, 42, 63], 0.05, kv=True)
+    err, frac = _check(cfg, ow, inputs, gpu, range(64), 0.05, kv=True)
     print(f"l5 r64: max logit err {err:.4f}, decided {frac:.2f}")
 
 
@@ -136,8 +144,22 @@ def test_full_l5_40_rows_idle_wave():
     w, wdev, ow = _weights(cfg)
     inputs = synth.make_inputs(cfg)
     gpu = _gpu_frame(cfg, wdev, inputs, max_rows=40)
-    err, frac = _check(cfg, ow, inputs, gpu, [0, 39], 0.05)
+    err, frac = _check(cfg, ow, inputs, gpu, range(40), 0.05)
     print(f"l5 r40: max logit err {err:.4f}, decided {frac:.2f}")
+
+
+@pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
+def test_full_l5_gain_jitter(exec_mode):
+    """Full-size bf16 with RMSNorm gains 1 + N(0, 0.1): the plan folds each
+    gain into the next projection's packed bf16 weights and scales the fp32
+    result by 1 / rms, while the oracle rounds bf(h r g); both round once, at
+    different points, and must stay within the logit bar."""
+    cfg = synth.CONFIGS["l5_r64"].with_(rows=8)
+    w, wdev, ow = _weights(cfg, seed=21, gain_jitter=True)
+    inputs = synth.make_inputs(cfg, seed=21)
+    gpu = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=8, kv=True)
+    err, frac = _check(cfg, ow, inputs, gpu, range(8), 0.05, kv=True)
+    print(f"l5 gain jitter {exec_mode}: max logit err {err:.4f}, decided {frac:.2f}")
 
 
 def test_persistent_equals_per_phase_bitwise():
@@ -186,12 +208,14 @@ def test_ten_runs_bitwise_identical():
     plan.close()
 
 
-@pytest.mark.parametrize("rows", [1, 64])
+@pytest.mark.parametrize("rows", [1, 8, 40, 64])
 def test_back_to_back_frames_bitwise_identical(rows):
     """Forty frames launched back to back on one stream, no host sync between
     them, each into its own buffers: every one equals the first bit for bit.
     A frame whose tasks read a weight tile, an operand or a partial before it
-    is complete would differ at some point under this load."""
+    is complete would differ at some point under this load.  At 8 and 40
+    rows some waves of a projection task have no rows and only copy their
+    share of the weight tile."""
     cp = _cp()
     cfg = synth.CONFIGS["l5_r64"].with_(rows=rows)
     w, wdev, ow = _weights(cfg)
@@ -210,13 +234,16 @@ def test_back_to_back_frames_bitwise_identical(rows):
     plan.close()
 
 
-@pytest.mark.parametrize("rows", [1, 16])
+@pytest.mark.parametrize("rows", [1, 16, 64])
 def test_l10_hbm_variant(rows):
+    """The 10-layer variant (314 MB of layer weights, more than the Infinity
+    Cache holds) at the row counts the benchmark times, every row."""
     cfg = synth.CONFIGS["l10_r16"].with_(rows=rows)
     w, wdev, ow = _weights(cfg)
     inputs = synth.make_inputs(cfg)
     gpu = _gpu_frame(cfg, wdev, inputs, max_rows=64)
-    _check(cfg, ow, inputs, gpu, sorted({0, rows - 1}), 0.05)
+    err, frac = _check(cfg, ow, inputs, gpu, range(rows), 0.05)
+    print(f"l10 r{rows}: max logit err {err:.4f}, decided {frac:.2f}")
 
 
 def test_frame_refusals_leave_the_plan_usable():
@@ -286,22 +313,27 @@ def test_epoch_wrap(exec_mode):
     _check(cfg, ow, inputs, ref, range(3), 0.05, kv=True)
 
 
-def _sampled_decided(margins, dy):
-    """Draws whose code the oracle fixes robustly, given dy, the largest
-    difference between the GPU's and the oracle's scaled logits y = z / T of
-    the draw: a perturbed-score gap over the kept set of at least
-    max(0.1, 2 dy), and a kept set that such differences cannot change --
-    where top-p cut it, the crossing is at least max(1e-3, 2 dy) of
-    probability mass from the threshold on both sides (a shift of dy in every
-    logit moves a probability by a factor of at most e^(2 dy)); where top-k
-    cut it, the k-th and (k+1)-th scaled logits are at least max(0.1, 2 dy)
-    apart."""
-    gap, m_k, m_before, m_at = (margins[..., i] for i in range(4))
-    tol = np.maximum(0.1, 2 * dy)
-    mass_tol = np.maximum(1e-3, 2 * dy)
-    top_p_cut = np.isfinite(m_before)
-    kept_robust = np.where(top_p_cut, (m_before >= mass_tol) & (m_at >= mass_tol), m_k >= tol)
-    return (gap >= tol) & kept_robust
+def _sampled_robust(cfg, inputs, rows, orc, gpu_logits, dy):
+    """Draws whose code the oracle fixes whatever the logit error of at most
+    dy (per scaled logit y = z / T) does: the oracle's kept set is the same
+    from the oracle's logits and from the GPU's, and the oracle's
+    perturbed-score winner leads the runner-up by more than 2 dy (both sides
+    add the same Gumbel noise, so each score moves by at most dy).  Greedy
+    rows (T <= 0): a top-1/top-2 gap of at least 0.1."""
+    from oracle import oracle
+    R, J = orc["codes"].shape
+    robust = np.zeros((R, J), bool)
+    for ri, r in enumerate(rows):
+        T, k, p = inputs["temperature"][r], inputs["top_k"][r], inputs["top_p"][r]
+        for j in range(J):
+            m = orc["margins"][ri, j]
+            if not T > 0:
+                robust[ri, j] = m[0] >= 0.1
+                continue
+            ko = oracle.kept_set(orc["logits"][ri, j], T, k, p)
+            kg = oracle.kept_set(gpu_logits[ri, j], T, k, p)
+            robust[ri, j] = np.array_equal(ko, kg) and m[0] > 2 * dy[ri, j] + 1e-9
+    return robust
 
 
 def _check_draws_on_gpu_logits(cfg, inputs, gpu, rows):
@@ -323,7 +355,7 @@ def _check_draws_on_gpu_logits(cfg, inputs, gpu, rows):
     return n
 
 
-def _check_sampled(cfg, ow, inputs, gpu, rows, logit_tol, min_decided=0.0):
+def _check_sampled(cfg, ow, inputs, gpu, rows, logit_tol, min_robust=0.0):
     from oracle import oracle
     rows = list(rows)
     _check_draws_on_gpu_logits(cfg, inputs, gpu, rows)
@@ -333,16 +365,16 @@ def _check_sampled(cfg, ow, inputs, gpu, rows, logit_tol, min_decided=0.0):
     T = np.asarray(inputs["temperature"], np.float32)[rows]
     dz = np.abs(gpu["logits"][rows] - orc["logits"]).max(axis=2)  # [rows][P-1]
     dy = np.where(T[:, None] > 0, dz / np.where(T > 0, T, 1)[:, None], dz)
-    decided = _sampled_decided(orc["margins"], dy)
-    assert decided.mean() >= min_decided, f"too few robust draws to test ({decided.mean():.2f})"
-    bad = np.argwhere(decided & (gpu["codes"][rows] != orc["codes"]))
+    robust = _sampled_robust(cfg, inputs, rows, orc, gpu["logits"][rows], dy)
+    assert robust.mean() >= min_robust, f"too few robust draws to test ({robust.mean():.2f})"
+    bad = np.argwhere(robust & (gpu["codes"][rows] != orc["codes"]))
     assert len(bad) == 0, [(rows[r], j + 1, int(gpu["codes"][rows][r, j]), int(orc["codes"][r, j]),
                             orc["margins"][r, j].round(4).tolist(), float(dy[r, j])) for r, j in bad[:5]]
     assert np.array_equal(gpu["embsum"][rows], orc["embsum"]), "embedding sums differ"
     off_in = np.asarray(inputs["offset"], np.uint64)[rows]
     assert np.array_equal(gpu["offset"].view(np.uint64)[rows], off_in + np.uint64(cfg.n_positions - 1))
     assert np.array_equal(orc["offset"], off_in + np.uint64(cfg.n_positions - 1))
-    return err, decided.mean()
+    return err, robust.mean()
 
 
 def _edge_sampling(inputs, V):
@@ -366,7 +398,7 @@ def test_sampled_tiny_fp32(exec_mode):
     inputs["temperature"] = np.where(inputs["temperature"] > 0, inputs["temperature"] * np.float32(0.25),
                                      inputs["temperature"]).astype(np.float32)
     gpu = _gpu_frame(cfg, wdev, inputs, exec_mode)
-    err, frac = _check_sampled(cfg, ow, inputs, gpu, range(8), 1e-4, min_decided=0.2)
+    err, frac = _check_sampled(cfg, ow, inputs, gpu, range(8), 1e-4, min_robust=0.2)
     print(f"sampled tiny {exec_mode}: max logit err {err:.2e}, robust draws {frac:.2f}")
 
 
@@ -375,7 +407,7 @@ def test_sampled_l5_64_rows():
     w, wdev, ow = _weights(cfg)
     inputs = synth.make_inputs(cfg, sampled=True)
     gpu = _gpu_frame(cfg, wdev, inputs)
-    err, frac = _check_sampled(cfg, ow, inputs, gpu, [0, 21, 42, 63], 0.05)
+    err, frac = _check_sampled(cfg, ow, inputs, gpu, range(64), 0.05, min_robust=0.5)
     print(f"sampled l5 r64: max logit err {err:.4f}, robust draws {frac:.2f}")
 
 
@@ -407,3 +439,101 @@ def test_sampled_persistent_equals_per_phase_and_repeats():
     for k in a:
         assert np.array_equal(a[k], b[k]), k
         assert np.array_equal(a[k], c[k]), k
+
+
+@pytest.mark.parametrize("rows", [1, 64])
+def test_traced_frame_equals_untraced_and_stamps_rise(rows):
+    """A frame with per-task timestamps computes the same bits as one
+    without; every task's stamps rise, and each workgroup's tasks follow
+    each other (section "Where the depth loop's time goes": eight timestamps
+    per task)."""
+    cp = _cp()
+    from persistent_megakernel_streaming_amd import trace
+    cfg = synth.CONFIGS["l5_r64"].with_(rows=rows)
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg)
+    ref = _gpu_frame(cfg, wdev, inputs, max_rows=64, kv=True)
+    plan = cp.Plan(cfg, wdev, exec_mode="persistent", max_rows=64, flags=cp.CP_FLAG_TRACE)
+    info = plan.info()
+    io = cp.make_io(cfg, inputs, kv=True)
+    io["trace"] = torch.zeros(info.trace_words, dtype=torch.int64, device="cuda")
+    plan.run(io)
+    torch.cuda.synchronize()
+    plan.device_status()
+    table = plan.task_table()
+    out = {k: v.cpu().numpy() for k, v in io.items() if k not in ("rows", "trace")}
+    words = io["trace"].cpu().numpy().view(np.uint64)
+    plan.close()
+    for k in ref:
+        assert np.array_equal(ref[k], out[k]), k
+    us = trace.decode(words, table)
+    assert not np.isnan(us[:, [trace.S_START, trace.S_DISPATCH, trace.S_OUT, trace.S_BARRIER,
+                               trace.S_ISSUE]]).any()
+    proj = np.isin(table[:, 1], trace.PROJ)
+    assert not np.isnan(us[proj][:, [trace.S_DEPS, trace.S_GROUP0, trace.S_KLOOP]]).any()
+    assert trace.check_monotone(us, table) == []
+    s = trace.summary(us, table)
+    print(f"\n{rows} rows, traced:\n" + trace.markdown(s))
+
+
+@pytest.mark.parametrize("sampled", [False, True])
+def test_graph_captured_persistent_frame_replays(sampled):
+    """A persistent frame captured into a HIP graph replays what it ran
+    (section "Testing"): five replays, with eager work and host syncs
+    between them, each bitwise equal to an eager frame on the same inputs.
+    Sampled frames advance their offsets in place, so each replay starts
+    from restored offsets."""
+    cp = _cp()
+    name = "l5_r64_sampled" if sampled else "l5_r64"
+    cfg = synth.CONFIGS[name].with_(rows=13)
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg, sampled=sampled)
+    plan = cp.Plan(cfg, wdev, exec_mode="persistent", max_rows=16)
+    eager = cp.make_io(cfg, inputs, kv=True)
+    plan.run(eager)
+    torch.cuda.synchronize()
+    ref = {k: v.cpu().numpy() for k, v in eager.items() if k != "rows"}
+    io = cp.make_io(cfg, inputs, kv=True)
+    off0 = io["offset"].clone() if sampled else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(io)
+    torch.cuda.synchronize()
+    for i in range(5):
+        for k in ("codes", "embsum", "logits", "k_cache", "v_cache"):
+            io[k].fill_(-7)
+        if sampled:
+            io["offset"].copy_(off0)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for k in ref:
+            assert np.array_equal(ref[k], io[k].cpu().numpy()), (i, k)
+    plan.device_status()
+    del g
+    plan.close()
+
+
+def test_device_timeout_is_reported_and_the_kernel_ends():
+    """A wait bounded to one reload gives up, raises the plan's error word and
+    the rest of the frame's waits give up at once: the kernel ends normally
+    and cp_plan_device_status reports CP_ERR_DEVICE_TIMEOUT.  The bound is set
+    from the host; no wait is made to hang."""
+    cp = _cp()
+    cfg = synth.CONFIGS["tiny_f32"].with_(rows=4, dtype="bf16")
+    w, wdev, ow = _weights(cfg, seed=9)
+    inputs = synth.make_inputs(cfg, seed=9)
+    plan = cp.Plan(cfg, wdev, exec_mode="persistent", max_rows=4)
+    plan.set_spin_limit(1)
+    io = cp.make_io(cfg, inputs)
+    plan.run(io)
+    torch.cuda.synchronize()
+    with pytest.raises(cp.CpError) as e:
+        plan.device_status()
+    assert e.value.status == cp.CP_ERR_DEVICE_TIMEOUT
+    plan.close()
+    # a new plan on the same device is unaffected
+    gpu = _gpu_frame(cfg, wdev, inputs, max_rows=4)
+    _check(cfg, ow, inputs, gpu, range(4), 0.05)
