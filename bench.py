@@ -7,14 +7,19 @@ synthetic N(0, 0.02) weights and N(0, 1) input hidden).  A "step" is one
 frame: one cp_frame_run over all rows with inputs already resident in device
 memory, timed with HIP events on the stream the frames run on.
 
-The line also carries the 1-row latency, the sampled 64-row frame, the
-10-layer variant, the per-phase executor (one launch per phase, eager and
-HIP-graph replay), the weight-read roofline of the persistent kernel, the
-HBM traffic measured by counters (from the committed profile summary, when it
-was taken on the current kernel source) and the CPU oracle timed on the host
-cores.
+The line also carries the 1-row latency, per-frame p50 / p99, cold frames
+(the Infinity Cache scrubbed by a 512 MiB read before each), the sampled
+64-row frame, the 10-layer variant, the per-phase executor (one launch per
+phase, eager and HIP-graph replay), the weight-read roofline of the
+persistent kernel against the 8 TB/s spec and against a measured floor (a
+plain HIP read kernel over a working set of the layer weights' size), the
+empty-chain hand-off floor, the traffic measured by counters (from the
+committed profile summary, when it was taken on the current kernel source)
+and the CPU oracle timed on the host cores.  The pages' H200 figures are
+listed as context only; there is no baseline for this metric on MI355X.
 
-``--calibrate-copy`` instead runs a plain device copy of known size, for
+``--trace DIR`` instead writes traced 64- and 1-row frames (decoded split and
+raw stamps); ``--calibrate-copy`` runs a plain device copy of known size, for
 scaling the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
@@ -87,19 +92,70 @@ def _time_frames(plan, io, steps, warmup, repeats, graph=False):
     return statistics.median(out), min(out), max(out)
 
 
-def _cpu_baseline(cfg, w, inputs, min_seconds=10.0, max_frames=6):
-    """The oracle on the host cores: whole 64-row frames until about
-    `min_seconds` of CPU work (at most `max_frames`)."""
+def _per_frame_us(plan, io, n, scrub=None):
+    """µs of each of n frames, each bracketed by its own events (p50/p99).
+    With `scrub` (a device buffer), a plain read of it runs before every
+    frame, outside the events, to evict the weights from the Infinity Cache
+    (cold frames)."""
+    import torch
+    from persistent_megakernel_streaming_amd import cp
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for _ in range(3):
+        plan.run(io)
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        if scrub is not None:
+            cp.stream_read(scrub, sink)
+        e0.record(stream)
+        plan.run(io)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    plan.device_status()
+    return np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_threads():
+    """Host threads the oracle may use: OMP_NUM_THREADS where set (the host's
+    share of cores), else every core."""
+    n = os.environ.get("OMP_NUM_THREADS")
+    return max(1, int(n)) if n and n.isdigit() else (os.cpu_count() or 1)
+
+
+def _cpu_baseline(cfg, w, inputs, min_seconds=10.0, max_frames=4):
+    """The oracle as it stands on the host cores: whole frames of the timed
+    workload with every host thread until about `min_seconds` of work (at
+    most `max_frames`), and one-row frames on one thread for the
+    single-thread figure."""
     from oracle import oracle
     ow = oracle.OracleWeights(cfg, w)
-    threads = min(os.cpu_count() or 1, 16)
+    threads = _cpu_threads()
     n, t0 = 0, time.perf_counter()
     while n < max_frames and (n == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.run_frame(cfg, ow, inputs, n_threads=threads)
         n += 1
     dt = time.perf_counter() - t0
+    n1, t1 = 0, time.perf_counter()
+    while n1 < 3 and (n1 == 0 or time.perf_counter() - t1 < 5.0):
+        oracle.run_frame(cfg, ow, inputs, n_threads=1, rows=[0])
+        n1 += 1
+    dt1 = time.perf_counter() - t1
     return {"value": n / dt, "unit": "frames/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} whole {cfg.rows}-row frames ({dt:.1f} s)"}
+            "sample": f"{n} whole {cfg.rows}-row frames ({dt:.1f} s) on {threads} threads",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "one_thread_us_per_frame_1row": dt1 / n1 * 1e6,
+            "one_thread_sample": f"{n1} one-row frames ({dt1:.1f} s) on 1 thread"}
 
 
 def _stored_traffic():
@@ -118,25 +174,52 @@ def _stored_traffic():
     return d.get("hbm_bytes_per_launch")
 
 
-def _measured_read_floor(nbytes, reps=20):
-    """Best streaming-read rate of a plain device read over a working set of
-    `nbytes` (a sum over a bf16 tensor that size), GB/s."""
+def _measured_read_rate(nbytes, reps=20):
+    """Best rate of cp_stream_read (a plain HIP read kernel, 16-byte loads)
+    over a working set of `nbytes`, read back to back `reps` times: GB/s."""
     import torch
+    from persistent_megakernel_streaming_amd import cp
     x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     for _ in range(3):
-        x.sum(dtype=torch.float32)
+        cp.stream_read(x, sink)
     torch.cuda.synchronize()
     best = float("inf")
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        x.sum(dtype=torch.float32)
+        cp.stream_read(x, sink)
         e1.record()
         torch.cuda.synchronize()
         best = min(best, e0.elapsed_time(e1) * 1e-3)
     del x
     torch.cuda.empty_cache()
     return nbytes / best / 1e9
+
+
+def _chain_us_per_phase(n_phases, launches=20):
+    """µs per phase of an empty chain of tagged-word hand-offs over 256 one-wave
+    workgroups: (all-to-all, XCD-local) best of `launches`."""
+    import torch
+    from persistent_megakernel_streaming_amd import cp
+    out = []
+    for local in (0, 1):
+        slots = torch.zeros(2 * 256 * 4, dtype=torch.int32, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        base, best = 0, float("inf")
+        for i in range(launches + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            cp.chain_run(slots, 256, n_phases, base, local, err)
+            e1.record()
+            torch.cuda.synchronize()
+            base += n_phases
+            if i >= 2:
+                best = min(best, e0.elapsed_time(e1) * 1e3)
+        if int(err.item()) != 0:
+            raise RuntimeError("an empty-chain wait gave up")
+        out.append(best / n_phases)
+    return out
 
 
 def calibrate_copy():
@@ -149,6 +232,33 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "launches": 5}), flush=True)
 
 
+def _trace_frames(out_dir, wdev, steps=3):
+    """Traced frames of the 5-layer loop at 64 and 1 rows: the decoded split
+    (markdown) and the raw stamps and task table, written to out_dir."""
+    import torch
+    from persistent_megakernel_streaming_amd import cp, synth, trace
+    os.makedirs(out_dir, exist_ok=True)
+    res = {}
+    for rows in (64, 1):
+        cfg = synth.CONFIGS["l5_r64"].with_(rows=rows)
+        plan = cp.Plan(cfg, wdev, exec_mode="persistent", max_rows=rows, flags=cp.CP_FLAG_TRACE)
+        io = cp.make_io(cfg, synth.make_inputs(cfg), logits=False)
+        io["trace"] = torch.zeros(plan.info().trace_words, dtype=torch.int64, device="cuda")
+        for _ in range(steps):
+            plan.run(io)
+        torch.cuda.synchronize()
+        plan.device_status()
+        table = plan.task_table()
+        words = io["trace"].cpu().numpy().view(np.uint64)
+        np.savez(os.path.join(out_dir, f"trace_l5_r{rows}.npz"), words=words, table=table)
+        s = trace.summary(trace.decode(words, table), table)
+        with open(os.path.join(out_dir, f"trace_l5_r{rows}.md"), "w") as f:
+            f.write(trace.markdown(s) + "\n")
+        res[rows] = s
+        plan.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,7 +266,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of p64,p1,s64,pp64,pp1,l10,floor (default all)")
+    ap.add_argument("--only", default="",
+                    help="comma list of p64,p1,s64,pp64,pp1,l10,floor,chain,cold,pct (default all)")
+    ap.add_argument("--trace", default="", help="write traced 64- and 1-row frames to this directory and exit")
     ap.add_argument("--calibrate-copy", action="store_true", help="run a plain copy of known size and exit")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -170,19 +282,34 @@ def main():
     import torch
     from persistent_megakernel_streaming_amd import cp, synth
 
-    only = set(args.only.split(",")) if args.only else {"p64", "p1", "s64", "pp64", "pp1", "l10", "floor"}
+    everything = {"p64", "p1", "s64", "pp64", "pp1", "l10", "floor", "chain", "cold", "pct"}
+    only = set(args.only.split(",")) if args.only else everything
     steps, warm, reps = args.steps, args.warmup, args.repeats
     cfg64 = synth.CONFIGS["l5_r64"]
     w = synth.make_weights(cfg64)
     wdev = cp.upload_weights(cfg64, w)
-    res = {}
+    if args.trace:
+        res = _trace_frames(args.trace, wdev)
+        print(json.dumps({str(k): {kk: v[kk] for kk in ("frame_us", "handoff_us", "body_us")}
+                          for k, v in res.items()}), flush=True)
+        return
+    res, extra = {}, {}
     plan = cp.Plan(cfg64, wdev, exec_mode="persistent", max_rows=64)
     info = plan.info()
     wbytes = info.weight_bytes_per_frame
     phases = info.n_phases
+    io64 = cp.make_io(cfg64, synth.make_inputs(cfg64), logits=False)
     if "p64" in only:
-        io64 = cp.make_io(cfg64, synth.make_inputs(cfg64), logits=False)
         res["persistent_us_64"] = _time_frames(plan, io64, steps, warm, reps)
+    if "pct" in only:
+        t = _per_frame_us(plan, io64, 200)
+        extra["per_frame_us_64rows"] = {"p50": float(np.percentile(t, 50)), "p99": float(np.percentile(t, 99)),
+                                        "frames": len(t)}
+    scrub = None
+    if "cold" in only:
+        scrub = torch.ones(256 * 1024 * 1024, dtype=torch.int16, device="cuda")  # 512 MiB
+        t = _per_frame_us(plan, io64, 20, scrub=scrub)
+        extra["cold_us_64rows"] = float(np.median(t))
     plan.close()
     if "s64" in only:
         cs = synth.CONFIGS["l5_r64_sampled"]
@@ -195,6 +322,10 @@ def main():
         plan1 = cp.Plan(cfg1, wdev, exec_mode="persistent", max_rows=1)
         io1 = cp.make_io(cfg1, synth.make_inputs(cfg1), logits=False)
         res["persistent_us_1"] = _time_frames(plan1, io1, steps, warm, reps)
+        if "pct" in only:
+            t = _per_frame_us(plan1, io1, 200)
+            extra["per_frame_us_1row"] = {"p50": float(np.percentile(t, 50)), "p99": float(np.percentile(t, 99)),
+                                          "frames": len(t)}
         plan1.close()
     for tag, c, mr in (("pp64", cfg64, 64), ("pp1", cfg1, 1)):
         if tag in only:
@@ -206,6 +337,7 @@ def main():
             pp.close()
     del wdev
     torch.cuda.empty_cache()
+    l10_bytes = None
     if "l10" in only:
         cfg10 = synth.CONFIGS["l10_r64"]
         w10 = cp.upload_weights(cfg10, synth.make_weights(cfg10))
@@ -214,12 +346,25 @@ def main():
             pl = cp.Plan(c, w10, exec_mode="persistent", max_rows=rows)
             io = cp.make_io(c, synth.make_inputs(c), logits=False)
             res[f"l10_persistent_us_{rows}"] = _time_frames(pl, io, max(20, steps // 4), warm, 3)
-            if rows == 1:
-                res["l10_weight_bytes"] = pl.info().weight_bytes_per_frame
+            l10_bytes = pl.info().weight_bytes_per_frame
+            if rows == 64 and scrub is not None:
+                extra["l10_cold_us_64rows"] = float(np.median(_per_frame_us(pl, io, 20, scrub=scrub)))
             pl.close()
         del w10
         torch.cuda.empty_cache()
-    floor_gbps = _measured_read_floor(157 * 1024 * 1024) if "floor" in only else None
+    del scrub
+    floor = None
+    if "floor" in only:
+        g157 = _measured_read_rate(157 * 1000 * 1000)
+        g314 = _measured_read_rate(314 * 1000 * 1000)
+        floor = {"read_GBps_157MB": g157, "read_GBps_314MB": g314,
+                 "measured_floor_us_5layers": wbytes / (g157 * 1e3),
+                 "measured_floor_us_10layers": (l10_bytes / (g314 * 1e3)) if l10_bytes else None,
+                 "kernel": "cp_stream_read (plain HIP read, 16-byte loads, 4096 x 256 threads)"}
+    if "chain" in only:
+        a2a, loc = _chain_us_per_phase(phases)
+        extra["empty_chain"] = {"us_per_phase_all_to_all": a2a, "us_per_phase_xcd_local": loc,
+                                "phases": phases, "chain_bound_us_all_to_all": a2a * phases}
 
     us64 = res["persistent_us_64"][0] if "persistent_us_64" in res else None
     us1 = res["persistent_us_1"][0] if "persistent_us_1" in res else None
@@ -234,7 +379,7 @@ def main():
         "ms_per_step": us64 / 1e3 if us64 else None,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": (H200_US_64ROWS / us64) if us64 else None,
+        "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "depth loop, 5 layers bf16, hidden 1024, 16x128 q / 8 kv heads, SwiGLU 3072, "
@@ -245,14 +390,20 @@ def main():
         "weight_floor_us_at_8TBps": floor_us,
         "x_floor_64rows": (us64 / floor_us) if us64 else None,
         "x_floor_1row": (us1 / floor_us) if us1 else None,
-        "measured_read_GBps_157MB": floor_gbps,
+        "gap_to_2x_floor_us_64rows": (us64 - 2 * floor_us) if us64 else None,
+        "h200_context_us": {"persistent_1row": 2127.0, "persistent_64rows": H200_US_64ROWS,
+                            "frame_in_59row_step": 2220.0, "floor_at_4.8TBps": 537.8},
+        "measured_floor": floor,
         "detail_us_median_min_max": res,
         "repeats": reps,
     }
+    out.update(extra)
     if us64:
         achieved = wbytes / (us64 * 1e-6) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBPS, "traffic": _stored_traffic()}
+                           "frac": achieved / HBM_PEAK_GBPS, "traffic": _stored_traffic(),
+                           "traffic_counts": "FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated: bytes between "
+                                             "the L2s and the memory side (Infinity Cache or HBM)"}
     if us1:
         a1 = wbytes / (us1 * 1e-6) / 1e9
         out["roofline_1row"] = {"bound": "hbm", "achieved": a1, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

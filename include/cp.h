@@ -257,6 +257,34 @@ const char* cp_last_create_error(void);
  * planning tools; cp_plan_create runs the same checks. */
 cp_status cp_schedule_check(const cp_config* cfg, int cu_count, cp_plan_info* info);
 
+/* ---------------------------------------------------------------- measurement
+ * Two floors the pull request prices a frame against (section "Where the
+ * depth loop's time goes"): the weight-read floor (bullet "The floor") and the
+ * fixed latency of each dependent phase (bullet "Phases"). */
+
+/* Enqueues one read of the device buffer [buf, buf + bytes) with 16-byte
+ * loads and nothing else (bytes a positive multiple of 16, else
+ * CP_ERR_INVALID_ARGUMENT).  bytes divided by the launch's time is the
+ * streaming-read rate of a working set of that size.  sink: one device uint32
+ * the kernel may write (to keep its loads).  Allocates nothing; does not
+ * synchronise. */
+cp_status cp_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* hip_stream);
+
+/* Enqueues a chain of n_phases phases with no work in them on n_workgroups
+ * one-wave workgroups (1..256): in phase k every workgroup stores the tag
+ * tag_base + k + 1 into its slot and waits until the slots of the workgroups
+ * it depends on carry it -- all of them, or with xcd_local the ones whose
+ * index is congruent to its own modulo 8 (the workgroups the persistent
+ * executor places on one XCD; n_workgroups then a multiple of 8).  The time
+ * of the launch divided by n_phases is the per-phase cost of the persistent
+ * executor's tagged-word hand-off.  slots: device memory of 2 * n_workgroups
+ * * 16 bytes, zero before the first launch; tags must grow from launch to
+ * launch (tag_base of the next launch >= this tag_base + n_phases, at most
+ * 2^32 - 1 in all).  error_word: a device uint32 set to 1 if a wait gave up
+ * (every wait is bounded).  Allocates nothing; does not synchronise. */
+cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t tag_base, int xcd_local,
+                       uint32_t* error_word, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-ffp-con
                 "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-Wno-unused-command-line-argument"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+DEVICE_SOURCES = ["cp_kernels.hip", "cp_measure.hip"]
 
 
 # A vector-memory instruction that reads SGPRs a VALU instruction (such as
@@ -64,16 +65,18 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     """Compiles every HIP source and links libcpms.so next to the package."""
-    check_asm_guards(os.path.join(CSRC, "cp_kernels.hip"))
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
-    kobj = os.path.join(tmpdir, "cp_kernels.o")
-    pobj = os.path.join(tmpdir, "cp_plan.o")
-    _run([HIPCC, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, "cp_kernels.hip"), "-o", kobj])
-    _run([HIPCC, *HOST_FLAGS, *inc, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "cp_plan.cpp"), "-o", pobj])
+    objs = []
+    for name in DEVICE_SOURCES:
+        check_asm_guards(os.path.join(CSRC, name))
+        objs.append(os.path.join(tmpdir, name.replace(".hip", ".o")))
+        _run([HIPCC, *DEVICE_FLAGS, *inc, "-c", os.path.join(CSRC, name), "-o", objs[-1]])
+    objs.append(os.path.join(tmpdir, "cp_plan.o"))
+    _run([HIPCC, *HOST_FLAGS, *inc, "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "cp_plan.cpp"), "-o", objs[-1]])
     tmp = LIB + f".tmp{os.getpid()}"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", kobj, pobj, "-o", tmp])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

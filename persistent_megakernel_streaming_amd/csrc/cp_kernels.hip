@@ -745,6 +745,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           }
         }
       }
+      if (j == 0) stamp(tr, 3);
     }
     if constexpr (NB == 1) {
 #pragma unroll

@@ -34,6 +34,9 @@ hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, 
 hipError_t set_kernel_attributes();
 int occupancy_per_cu(int bf16);
 hipError_t check_xcd_dealing(int n_wg, bool& dealt);
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_chain(uint32_t* slots, int n_wg, int n_phases, uint32_t base, int local, uint32_t* err,
+                        hipStream_t s);
 }  // namespace cpms
 
 using namespace cpms;
@@ -1097,6 +1100,21 @@ cp_status cp_plan_device_status(cp_plan* P) {
   if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("device status: ") + hipGetErrorString(e));
   if (st[64]) return fail(P, CP_ERR_DEVICE_TIMEOUT, "a device-side wait gave up");
   return CP_OK;
+}
+
+cp_status cp_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16) return CP_ERR_INVALID_ARGUMENT;
+  return launch_stream_read(buf, bytes, sink, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_ERR_HIP;
+}
+
+cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t tag_base, int xcd_local,
+                       uint32_t* error_word, void* stream) {
+  if (!slots || !error_word || n_workgroups < 1 || n_workgroups > 256 || n_phases < 1 ||
+      (xcd_local && n_workgroups % 8) || (uint64_t)tag_base + (uint64_t)n_phases > 0xffffffffull)
+    return CP_ERR_INVALID_ARGUMENT;
+  return launch_chain(slots, n_workgroups, n_phases, tag_base, xcd_local, error_word, (hipStream_t)stream) == hipSuccess
+             ? CP_OK
+             : CP_ERR_HIP;
 }
 
 }  // extern "C"
