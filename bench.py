@@ -197,28 +197,35 @@ def _measured_read_rate(nbytes, reps=20):
     return nbytes / best / 1e9
 
 
-def _chain_us_per_phase(n_phases, launches=20):
-    """µs per phase of an empty chain of tagged-word hand-offs over 256 one-wave
-    workgroups: (all-to-all, XCD-local) best of `launches`."""
+CHAIN_VARIANTS = [  # (name, xcd_local, cp_chain_run variant)
+    ("all_to_all_sc1_sc1", 0, 0), ("all_to_all_sys_sys", 0, 4),
+    ("xcd_local_sc1_sc1", 1, 0), ("xcd_local_plain_sc1", 1, 1), ("xcd_local_plain_sc0", 1, 2),
+    ("xcd_local_plain_sys", 1, 3)]
+
+
+def _chain_us_per_phase(n_phases, launches=10):
+    """µs per phase of empty chains of tagged-word hand-offs over 256 one-wave
+    workgroups, for each store / load cache policy and scope: best of
+    `launches`; None where a wait gave up (stores its readers never saw)."""
     import torch
     from persistent_megakernel_streaming_amd import cp
-    out = []
-    for local in (0, 1):
+    out = {}
+    for name, local, variant in CHAIN_VARIANTS:
         slots = torch.zeros(2 * 256 * 4, dtype=torch.int32, device="cuda")
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
         base, best = 0, float("inf")
         for i in range(launches + 2):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            cp.chain_run(slots, 256, n_phases, base, local, err)
+            cp.chain_run(slots, 256, n_phases, base, local, err, variant=variant)
             e1.record()
             torch.cuda.synchronize()
             base += n_phases
+            if int(err.item()) != 0:
+                break
             if i >= 2:
                 best = min(best, e0.elapsed_time(e1) * 1e3)
-        if int(err.item()) != 0:
-            raise RuntimeError("an empty-chain wait gave up")
-        out.append(best / n_phases)
+        out[name] = None if int(err.item()) != 0 else best / n_phases
     return out
 
 
@@ -362,9 +369,10 @@ def main():
                  "measured_floor_us_10layers": (l10_bytes / (g314 * 1e3)) if l10_bytes else None,
                  "kernel": "cp_stream_read (plain HIP read, 16-byte loads, 4096 x 256 threads)"}
     if "chain" in only:
-        a2a, loc = _chain_us_per_phase(phases)
-        extra["empty_chain"] = {"us_per_phase_all_to_all": a2a, "us_per_phase_xcd_local": loc,
-                                "phases": phases, "chain_bound_us_all_to_all": a2a * phases}
+        ch = _chain_us_per_phase(phases)
+        a2a = ch["all_to_all_sc1_sc1"]
+        extra["empty_chain"] = {"us_per_phase": ch, "phases": phases,
+                                "chain_bound_us_all_to_all": a2a * phases if a2a else None}
 
     us64 = res["persistent_us_64"][0] if "persistent_us_64" in res else None
     us1 = res["persistent_us_1"][0] if "persistent_us_1" in res else None

@@ -276,13 +276,20 @@ cp_status cp_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* 
  * it depends on carry it -- all of them, or with xcd_local the ones whose
  * index is congruent to its own modulo 8 (the workgroups the persistent
  * executor places on one XCD; n_workgroups then a multiple of 8).  The time
- * of the launch divided by n_phases is the per-phase cost of the persistent
- * executor's tagged-word hand-off.  slots: device memory of 2 * n_workgroups
- * * 16 bytes, zero before the first launch; tags must grow from launch to
- * launch (tag_base of the next launch >= this tag_base + n_phases, at most
- * 2^32 - 1 in all).  error_word: a device uint32 set to 1 if a wait gave up
- * (every wait is bounded).  Allocates nothing; does not synchronise. */
-cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t tag_base, int xcd_local,
+ * of the launch divided by n_phases is the per-phase cost of a tagged-word
+ * hand-off.  variant picks the stores' and loads' cache policy:
+ *   0  agent-coherent stores and loads (the executor's cross-XCD hand-off);
+ *   1  plain stores, agent-coherent loads (its XCD-local hand-off);
+ *   2  plain stores, workgroup-coherent loads;
+ *   3  plain stores, system-coherent loads;
+ *   4  system-coherent stores and loads;
+ * variants 1-3 need xcd_local (plain stores stay in the writer's XCD).
+ * slots: device memory of 2 * n_workgroups * 16 bytes, zero before the first
+ * launch; tags must grow from launch to launch (tag_base of the next launch
+ * >= this tag_base + n_phases, at most 2^32 - 1 in all).  error_word: a
+ * device uint32 set to 1 if a wait gave up (every wait is bounded, about
+ * 65536 polls).  Allocates nothing; does not synchronise. */
+cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t tag_base, int xcd_local, int variant,
                        uint32_t* error_word, void* hip_stream);
 
 #ifdef __cplusplus

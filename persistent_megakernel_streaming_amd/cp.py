@@ -80,7 +80,7 @@ def load_library():
     lib.cp_plan_set_epoch.argtypes = [C.c_void_p, C.c_uint32]
     lib.cp_plan_set_spin_limit.argtypes = [C.c_void_p, C.c_uint32]
     lib.cp_stream_read.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]
-    lib.cp_chain_run.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_int, C.c_void_p, C.c_void_p]
+    lib.cp_chain_run.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     for f in ("cp_plan_create", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
               "cp_schedule_check", "cp_plan_task_table", "cp_plan_set_epoch", "cp_plan_set_spin_limit",
               "cp_stream_read", "cp_chain_run"):
@@ -129,10 +129,11 @@ def stream_read(buf, sink, stream=None):
         raise CpError(st, "cp_stream_read")
 
 
-def chain_run(slots, n_workgroups, n_phases, tag_base, xcd_local, error_word, stream=None):
+def chain_run(slots, n_workgroups, n_phases, tag_base, xcd_local, error_word, variant=0, stream=None):
     """Enqueues an empty chain of tagged-word hand-offs (cp_chain_run)."""
     st = _lib.cp_chain_run(C.c_void_p(slots.data_ptr()), int(n_workgroups), int(n_phases), int(tag_base),
-                           int(bool(xcd_local)), C.c_void_p(error_word.data_ptr()), C.c_void_p(_stream(stream)))
+                           int(bool(xcd_local)), int(variant), C.c_void_p(error_word.data_ptr()),
+                           C.c_void_p(_stream(stream)))
     if st != CP_OK:
         raise CpError(st, "cp_chain_run")
 

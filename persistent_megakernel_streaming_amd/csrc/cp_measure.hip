@@ -23,7 +23,6 @@ namespace cpms {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t v4u;
-constexpr int kAgentCoherent = 16;  // buffer cache-policy bit sc1
 
 __device__ __forceinline__ uint32_t fold(const v4u& a) { return a[0] ^ a[1] ^ a[2] ^ a[3]; }
 
@@ -43,14 +42,15 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const v4u* __restrict_
 }
 
 // One wave per workgroup.  Phase k (tag = base + k + 1): lane 0 stores the tag
-// into slot [k & 1][w] (16 bytes, agent-coherent); then the wave reloads the
-// slots of the workgroups it waits for (all of them, or with `local` the ones
-// whose index is congruent to w modulo 8, the workgroups the persistent
-// executor deals to w's XCD) until each carries the tag.  A slot of parity k & 1
-// is written again only in phase k + 2, which no workgroup enters before every
-// workgroup it waits for has finished waiting in phase k + 1, hence in phase k.
-// A wait that runs past spin_limit reloads sets *err and ends the workgroup's
-// chain; the others then run out of polls too.
+// into slot [k & 1][w] (16 bytes, cache policy SP); then the wave reloads (cache
+// policy LP) the slots of the workgroups it waits for -- all of them, or with
+// `local` the ones whose index is congruent to w modulo 8, the workgroups the
+// persistent executor deals to w's XCD -- until each carries the tag.  A slot of
+// parity k & 1 is written again only in phase k + 2, which no workgroup enters
+// before every workgroup it waits for has finished waiting in phase k + 1,
+// hence in phase k.  A wait that runs past spin_limit reloads sets *err and
+// ends the workgroup's chain; the others then run out of polls too.
+template <int SP, int LP>
 __global__ __launch_bounds__(64) void chain_kernel(uint32_t* slots, uint32_t n_wg, uint32_t n_phases, uint32_t base,
                                                    uint32_t local, uint32_t spin_limit, uint32_t* err) {
   const uint32_t w = blockIdx.x, lane = threadIdx.x;
@@ -66,14 +66,13 @@ __global__ __launch_bounds__(64) void chain_kernel(uint32_t* slots, uint32_t n_w
   }
   for (uint32_t k = 0; k < n_phases; ++k) {
     const uint32_t tag = base + k + 1, par = k & 1;
-    if (lane == 0)
-      __builtin_amdgcn_raw_buffer_store_b128(v4u{tag, tag, tag, tag}, r, (par * n_wg + w) * 16, 0, kAgentCoherent);
+    if (lane == 0) __builtin_amdgcn_raw_buffer_store_b128(v4u{tag, tag, tag, tag}, r, (par * n_wg + w) * 16, 0, SP);
     uint32_t n = 0;
     while (true) {
       uint32_t bad = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (par * n_wg + who[i]) * 16, 0, kAgentCoherent);
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (par * n_wg + who[i]) * 16, 0, LP);
         bad |= (i < nw) ? (v[0] ^ tag) : 0u;
       }
       if (__builtin_amdgcn_ballot_w64(bad != 0) == 0) break;
@@ -81,8 +80,8 @@ __global__ __launch_bounds__(64) void chain_kernel(uint32_t* slots, uint32_t n_w
         if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
       }
-      // every 4096 polls: has another workgroup given up already?
-      if ((n & 4095u) == 0 &&
+      // every 1024 polls: has another workgroup given up already?
+      if ((n & 1023u) == 0 &&
           __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)))
         return;
       __builtin_amdgcn_s_sleep(1);
@@ -97,10 +96,22 @@ hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, h
   return hipGetLastError();
 }
 
-hipError_t launch_chain(uint32_t* slots, int n_wg, int n_phases, uint32_t base, int local, uint32_t* err,
+// Cache-policy bits of buffer instructions (gfx950): sc0 = 1, sc1 = 16.
+hipError_t launch_chain(uint32_t* slots, int n_wg, int n_phases, uint32_t base, int local, int variant, uint32_t* err,
                         hipStream_t s) {
-  hipLaunchKernelGGL(chain_kernel, dim3(n_wg), dim3(64), 0, s, slots, (uint32_t)n_wg, (uint32_t)n_phases, base,
-                     (uint32_t)(local != 0), kDefaultSpinLimit, err);
+  // at most ~65 ms of polling per wait: a variant whose stores the readers
+  // cannot see ends with *err set instead of running for seconds
+  constexpr uint32_t kChainSpin = 1u << 16;
+  const dim3 g(n_wg), t(64);
+  const uint32_t nw = (uint32_t)n_wg, np = (uint32_t)n_phases, lo = local != 0;
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((chain_kernel<16, 16>), g, t, 0, s, slots, nw, np, base, lo, kChainSpin, err); break;
+    case 1: hipLaunchKernelGGL((chain_kernel<0, 16>), g, t, 0, s, slots, nw, np, base, lo, kChainSpin, err); break;
+    case 2: hipLaunchKernelGGL((chain_kernel<0, 1>), g, t, 0, s, slots, nw, np, base, lo, kChainSpin, err); break;
+    case 3: hipLaunchKernelGGL((chain_kernel<0, 17>), g, t, 0, s, slots, nw, np, base, lo, kChainSpin, err); break;
+    case 4: hipLaunchKernelGGL((chain_kernel<17, 17>), g, t, 0, s, slots, nw, np, base, lo, kChainSpin, err); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

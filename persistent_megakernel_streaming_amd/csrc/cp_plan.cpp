@@ -35,7 +35,7 @@ hipError_t set_kernel_attributes();
 int occupancy_per_cu(int bf16);
 hipError_t check_xcd_dealing(int n_wg, bool& dealt);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
-hipError_t launch_chain(uint32_t* slots, int n_wg, int n_phases, uint32_t base, int local, uint32_t* err,
+hipError_t launch_chain(uint32_t* slots, int n_wg, int n_phases, uint32_t base, int local, int variant, uint32_t* err,
                         hipStream_t s);
 }  // namespace cpms
 
@@ -1107,12 +1107,14 @@ cp_status cp_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* 
   return launch_stream_read(buf, bytes, sink, (hipStream_t)stream) == hipSuccess ? CP_OK : CP_ERR_HIP;
 }
 
-cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t tag_base, int xcd_local,
+cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t tag_base, int xcd_local, int variant,
                        uint32_t* error_word, void* stream) {
   if (!slots || !error_word || n_workgroups < 1 || n_workgroups > 256 || n_phases < 1 ||
-      (xcd_local && n_workgroups % 8) || (uint64_t)tag_base + (uint64_t)n_phases > 0xffffffffull)
+      (xcd_local && n_workgroups % 8) || (uint64_t)tag_base + (uint64_t)n_phases > 0xffffffffull || variant < 0 ||
+      variant > 4 || (variant >= 1 && variant <= 3 && !xcd_local))
     return CP_ERR_INVALID_ARGUMENT;
-  return launch_chain(slots, n_workgroups, n_phases, tag_base, xcd_local, error_word, (hipStream_t)stream) == hipSuccess
+  return launch_chain(slots, n_workgroups, n_phases, tag_base, xcd_local, variant, error_word, (hipStream_t)stream) ==
+                 hipSuccess
              ? CP_OK
              : CP_ERR_HIP;
 }
