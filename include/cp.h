@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 1
+#define CP_ABI_VERSION 2
 
 typedef enum {
   CP_OK = 0,
@@ -168,6 +168,9 @@ typedef struct {
   int64_t trace_words;            /* uint64 words a traced frame writes */
   int32_t cu_count;
   int32_t max_tasks_per_workgroup;
+  int64_t const_bytes;            /* device bytes of the plan's constants (repacked weights, embedding tables,
+                                     RoPE table, each rounded up to 256): the weight arena cp_plan_create_static
+                                     needs; cp_schedule_check reports it too */
 } cp_plan_info;
 
 typedef struct cp_plan cp_plan; /* opaque, owned by the library */
@@ -181,6 +184,26 @@ typedef struct cp_plan cp_plan; /* opaque, owned by the library */
  * cp_last_create_error() says why.  Allocates device memory (hipMalloc);
  * synchronises the device. */
 cp_status cp_plan_create(const cp_config* cfg, const cp_weights* w, int hip_device, cp_plan** out);
+
+/* For callers that cannot allocate device memory (code that forbids
+ * hipMalloc: serving loops or harnesses that own the device's memory).  The
+ * same plan as cp_plan_create, with no device allocation: the repacked
+ * weights and tables are written into weight_arena (caller-owned device
+ * memory on hip_device of at least cp_plan_info.const_bytes bytes, as
+ * cp_schedule_check reports for cfg, else CP_ERR_INVALID_ARGUMENT; it must
+ * outlive the plan), and every scratch buffer of the plan is carved from an
+ * array of 96 MiB the library holds on each device it runs on until the
+ * process ends (a plan that needs more -- the 5-layer bf16 loop at 64 rows
+ * needs about 66 MiB, the 10-layer one at 64 rows more -- is refused with
+ * CP_ERR_OUT_OF_MEMORY and a message giving both sizes).  The array is
+ * zeroed with a kernel at creation.  All static plans of a device share that
+ * one array, so only one may live per device at a time: a second
+ * cp_plan_create_static on a device whose static plan has not been destroyed
+ * is refused (CP_ERR_INVALID_ARGUMENT).  Its frames behave as those of
+ * cp_plan_create's plans (same kernels, same results); cp_plan_destroy frees
+ * only the host object.  Synchronises the device. */
+cp_status cp_plan_create_static(const cp_config* cfg, const cp_weights* w, int hip_device, void* weight_arena,
+                                uint64_t arena_bytes, cp_plan** out);
 
 /* Enqueues one frame on hip_stream (a hipStream_t; NULL = default stream) and
  * returns without waiting.  Checks io on the host first and enqueues nothing

@@ -23,7 +23,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-ffp-con
                 "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-Wno-unused-command-line-argument"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
-DEVICE_SOURCES = ["cp_kernels.hip", "cp_measure.hip"]
+DEVICE_SOURCES = ["cp_kernels.hip", "cp_measure.hip", "cp_static.hip"]
 
 
 # A vector-memory instruction that reads SGPRs a VALU instruction (such as

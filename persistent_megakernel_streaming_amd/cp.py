@@ -22,7 +22,7 @@ STATUS = {0: "CP_OK", 1: "CP_ERR_INVALID_ARGUMENT", 2: "CP_ERR_UNSUPPORTED", 3: 
 CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
 CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 EPOCH_WRAP = (1 << 22) - 1  # epochs run 1 .. EPOCH_WRAP - 1
 
 _VP = C.c_void_p
@@ -52,7 +52,7 @@ class PlanInfo(C.Structure):
     _fields_ = [("n_phases", C.c_int32), ("n_tasks", C.c_int32), ("n_workgroups", C.c_int32),
                 ("lds_bytes", C.c_int32), ("weight_bytes_per_frame", C.c_int64),
                 ("packed_weight_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("trace_words", C.c_int64),
-                ("cu_count", C.c_int32), ("max_tasks_per_workgroup", C.c_int32)]
+                ("cu_count", C.c_int32), ("max_tasks_per_workgroup", C.c_int32), ("const_bytes", C.c_int64)]
 
 
 class CpError(RuntimeError):
@@ -66,6 +66,8 @@ def load_library():
         raise ImportError(f"{LIB_PATH} is not built; run persistent_megakernel_streaming_amd.build")
     lib = C.CDLL(LIB_PATH)
     lib.cp_plan_create.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.c_int, C.POINTER(C.c_void_p)]
+    lib.cp_plan_create_static.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.c_int, C.c_void_p, C.c_uint64,
+                                          C.POINTER(C.c_void_p)]
     lib.cp_frame_run.argtypes = [C.c_void_p, C.POINTER(FrameIO), C.c_void_p]
     lib.cp_plan_destroy.argtypes = [C.c_void_p]
     lib.cp_plan_query.argtypes = [C.c_void_p, C.POINTER(PlanInfo)]
@@ -81,7 +83,7 @@ def load_library():
     lib.cp_plan_set_spin_limit.argtypes = [C.c_void_p, C.c_uint32]
     lib.cp_stream_read.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]
     lib.cp_chain_run.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
-    for f in ("cp_plan_create", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
+    for f in ("cp_plan_create", "cp_plan_create_static", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
               "cp_schedule_check", "cp_plan_task_table", "cp_plan_set_epoch", "cp_plan_set_spin_limit",
               "cp_stream_read", "cp_chain_run"):
         getattr(lib, f).restype = C.c_int
@@ -157,7 +159,11 @@ def upload_weights(cfg, w: dict, device="cuda"):
 class Plan:
     """A cp_plan.  ``weights``: device tensors keyed as synth.make_weights names them."""
 
-    def __init__(self, cfg, weights: dict, exec_mode="persistent", max_rows=None, device=0, flags=0):
+    def __init__(self, cfg, weights: dict, exec_mode="persistent", max_rows=None, device=0, flags=0,
+                 weight_arena=None):
+        """``weight_arena``: a device tensor of at least ``const_bytes``
+        bytes makes a static plan (cp_plan_create_static: no device
+        allocation; its scratch lives in the library's per-device array)."""
         self.cfg = cfg
         self._c = make_config(cfg, max_rows=max_rows, exec_mode=exec_mode, flags=flags)
         L, P = cfg.n_layers, cfg.n_positions
@@ -181,7 +187,12 @@ class Plan:
             keep.append(a)
         self._w = Weights(w_in=weights["w_in"].data_ptr(), final_norm=weights["final_norm"].data_ptr(), **fields)
         h = C.c_void_p()
-        st = _lib.cp_plan_create(C.byref(self._c), C.byref(self._w), int(device), C.byref(h))
+        if weight_arena is None:
+            st = _lib.cp_plan_create(C.byref(self._c), C.byref(self._w), int(device), C.byref(h))
+        else:
+            st = _lib.cp_plan_create_static(C.byref(self._c), C.byref(self._w), int(device),
+                                            C.c_void_p(weight_arena.data_ptr()),
+                                            weight_arena.numel() * weight_arena.element_size(), C.byref(h))
         if st != CP_OK:
             raise CpError(st, _lib.cp_last_create_error().decode())
         self._h = h

@@ -49,6 +49,9 @@ constexpr uint32_t kEpochWrap = (1u << 22) - 1;
 constexpr int kMaxClear = 16;
 // Reloads of stale data a device-side wait makes before it gives up.
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+// Device bytes the library holds on each device for the scratch of a plan
+// made by cp_plan_create_static.
+constexpr size_t kStaticScratchBytes = (size_t)96 << 20;
 
 // Task flag: the split-K partners of this task's tile and their owner run on
 // workgroups of one XCD, so partials go through that XCD's L2 (plain stores,

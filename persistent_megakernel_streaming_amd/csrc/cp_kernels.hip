@@ -1825,19 +1825,20 @@ __global__ __launch_bounds__(kThreads, 1) void xcd_map_kernel(uint32_t* out) {
 }
 
 // Whether workgroup i of the persistent grid runs on XCD i % 8, the dealing
-// the split-K placement assumes.
-hipError_t check_xcd_dealing(int n_wg, bool& dealt) {
+// the split-K placement assumes.  buf: n_wg words of device memory to record
+// into, or null to allocate (and free) them here.
+hipError_t check_xcd_dealing(int n_wg, bool& dealt, uint32_t* buf) {
   dealt = false;
   if (n_wg % 8) return hipSuccess;
-  uint32_t* d = nullptr;
+  uint32_t* d = buf;
   hipError_t e = hipFuncSetAttribute((const void*)xcd_map_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (e == hipSuccess) e = hipMalloc(&d, (size_t)n_wg * 4);
+  if (e == hipSuccess && !buf) e = hipMalloc(&d, (size_t)n_wg * 4);
   if (e != hipSuccess) return e;
   std::vector<uint32_t> h(n_wg, 0xffffffffu);
   hipLaunchKernelGGL(xcd_map_kernel, dim3(n_wg), dim3(kThreads), kLdsBytes, 0, d);
   e = hipGetLastError();
   if (e == hipSuccess) e = hipMemcpy(h.data(), d, (size_t)n_wg * 4, hipMemcpyDeviceToHost);
-  hipError_t f = hipFree(d);
+  const hipError_t f = buf ? hipSuccess : hipFree(d);
   if (e != hipSuccess) return e;
   if (f != hipSuccess) return f;
   dealt = true;

@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -33,7 +34,9 @@ hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, 
                             uint32_t layers, hipStream_t s);
 hipError_t set_kernel_attributes();
 int occupancy_per_cu(int bf16);
-hipError_t check_xcd_dealing(int n_wg, bool& dealt);
+hipError_t check_xcd_dealing(int n_wg, bool& dealt, uint32_t* buf);
+hipError_t static_scratch(int device, void** ptr, size_t* bytes);
+hipError_t launch_fill_zero(void* p, size_t bytes);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_chain(uint32_t* slots, int n_wg, int n_phases, uint32_t base, int local, int variant, uint32_t* err,
                         hipStream_t s);
@@ -59,7 +62,20 @@ struct cp_plan {
   std::vector<void*> allocs;
   int64_t packed_bytes = 0, scratch_bytes = 0, weight_bytes_frame = 0;
   std::string err;
+  // A plan made by cp_plan_create_static allocates nothing: its scratch is
+  // carved from the library's static array on its device, its constants
+  // (repacked weights, tables) from the caller's arena.  While `measuring`,
+  // alloc() only adds up sizes.
+  bool is_static = false, measuring = false;
+  uint8_t* st_base = nullptr;
+  size_t st_cap = 0, st_used = 0;
+  uint8_t* arena = nullptr;
+  size_t arena_cap = 0, arena_used = 0;
 };
+
+// The live static plan of each device (at most one: they share the array).
+static std::mutex g_static_mu;
+static const cp_plan* g_static_owner[64];
 
 static thread_local std::string g_create_err;
 
@@ -623,25 +639,66 @@ static cp_status fetch(cp_plan* P, const void* dptr, size_t bytes, std::vector<u
   return CP_OK;
 }
 
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 // Device allocation, zero-filled: memory a previous plan freed may still hold
 // tagged words that a frame of this plan would otherwise accept.  Tagged
-// buffers are also recorded for the clear at the epoch wrap.
+// buffers are also recorded for the clear at the epoch wrap.  A static plan
+// carves it from the library's array and zeroes it with a kernel.
 static cp_status alloc(cp_plan* P, void** p, size_t bytes, bool tagged = false) {
   if (bytes == 0) bytes = 256;
   bytes = (bytes + 15) & ~(size_t)15;
-  hipError_t e = hipMalloc(p, bytes);
-  if (e != hipSuccess) {
-    P->err = std::string("hipMalloc: ") + hipGetErrorString(e);
-    return CP_ERR_OUT_OF_MEMORY;
+  if (P->is_static) {
+    const size_t off = round256(P->st_used);
+    P->st_used = off + bytes;
+    *p = P->st_base + off;  // (while measuring: a placeholder, never dereferenced)
+    if (!P->measuring) {
+      if (P->st_used > P->st_cap) return fail(P, CP_ERR_OUT_OF_MEMORY, "static scratch overflow");
+      HIPCHK(P, launch_fill_zero(*p, bytes));
+    }
+  } else {
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+      P->err = std::string("hipMalloc: ") + hipGetErrorString(e);
+      return CP_ERR_OUT_OF_MEMORY;
+    }
+    P->allocs.push_back(*p);
+    HIPCHK(P, hipMemset(*p, 0, bytes));
   }
-  P->allocs.push_back(*p);
   P->scratch_bytes += (int64_t)bytes;
-  HIPCHK(P, hipMemset(*p, 0, bytes));
   if (tagged) {
     if (P->dp.n_clear >= kMaxClear) return fail(P, CP_ERR_INVALID_ARGUMENT, "too many tagged buffers");
     P->dp.clear[P->dp.n_clear++] = Span{*p, (uint64_t)bytes};
   }
   return CP_OK;
+}
+
+// Copies host data into plan memory (skipped while a static plan measures).
+static cp_status upload(cp_plan* P, void* dst, const void* src, size_t bytes) {
+  if (P->measuring) return CP_OK;
+  HIPCHK(P, hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice));
+  return CP_OK;
+}
+
+// Device memory for the plan's constants (repacked weights, embedding
+// tables, RoPE table): the caller's arena for a static plan, else alloc().
+static cp_status alloc_const(cp_plan* P, void** p, size_t bytes) {
+  if (!P->is_static) return alloc(P, p, bytes);
+  const size_t off = round256(P->arena_used);
+  if (off + bytes > P->arena_cap)
+    return fail(P, CP_ERR_INVALID_ARGUMENT, "weight arena too small: needs cp_plan_info.const_bytes (cp_schedule_check)");
+  *p = P->arena + off;
+  P->arena_used = off + bytes;
+  return CP_OK;
+}
+
+// Device bytes of a plan's constants, each of the three rounded up to 256.
+static int64_t const_bytes(const cp_config& c) {
+  const int64_t esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
+  const int64_t L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, d = c.head_dim;
+  const int64_t I = c.intermediate, Pn = c.n_positions, V = c.vocab, Din = c.input_dim;
+  const int64_t blob = esz * (L * ((nq + 2 * nkv) * d * H + H * nq * d + 3 * I * H) + (Pn - 1) * V * H + H * Din);
+  return (int64_t)(round256((size_t)blob) + round256((size_t)(Pn * V * H * esz)) + round256((size_t)(Pn * d * 4)));
 }
 
 
@@ -771,14 +828,17 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
   for (Task& t : P->phase_tasks) attach(t);
 
   void* dblob;
-  TRY(alloc(P, &dblob, blob.size()));
+  if (blob.size() != (size_t)esz * ((size_t)L * ((nq + 2 * nkv) * d * H + H * qd + 3 * I * H) + (size_t)(Pn - 1) * V * H +
+                                    (size_t)H * Din))
+    return fail(P, CP_ERR_INVALID_ARGUMENT, "internal: packed weight size");
+  TRY(alloc_const(P, &dblob, blob.size()));
   HIPCHK(P, hipMemcpy(dblob, blob.data(), blob.size(), hipMemcpyHostToDevice));
   P->dp.wblob = (const uint8_t*)dblob;
   P->packed_bytes = (int64_t)blob.size();
 
   // embedding tables [P][V][H], RoPE table [P][d/2][2]
   void* de;
-  TRY(alloc(P, &de, (size_t)Pn * V * H * esz));
+  TRY(alloc_const(P, &de, (size_t)Pn * V * H * esz));
   for (int j = 0; j < Pn; ++j) {
     if (!w->embed[j]) return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL embedding table");
     HIPCHK(P, hipMemcpy((uint8_t*)de + (size_t)j * V * H * esz, w->embed[j], (size_t)V * H * esz, hipMemcpyDeviceToDevice));
@@ -792,7 +852,7 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
       rope[((size_t)p * (d / 2) + i) * 2 + 1] = (float)std::sin(ang);
     }
   void* dr;
-  TRY(alloc(P, &dr, rope.size() * 4));
+  TRY(alloc_const(P, &dr, rope.size() * 4));
   HIPCHK(P, hipMemcpy(dr, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
   P->dp.rope = (const float*)dr;
   int64_t wb = (int64_t)esz * ((int64_t)Pn * L * ((nq + 2 * nkv) * d * H + (int64_t)H * qd + 3LL * I * H) +
@@ -848,17 +908,16 @@ static cp_status alloc_scratch(cp_plan* P) {
   TRY(alloc(P, &p, 128 * 4)); dp.state = (uint32_t*)p;
   std::vector<uint32_t> st(128, 0);
   st[0] = 1;  // first frame is epoch 1; zeroed buffers carry tag 0, which no frame expects
-  HIPCHK(P, hipMemcpy(dp.state, st.data(), st.size() * 4, hipMemcpyHostToDevice));
+  TRY(upload(P, dp.state, st.data(), st.size() * 4));
   const std::vector<DevTask> dev_tasks = to_dev(P->tasks, P->xcd_dealing), dev_phase = to_dev(P->phase_tasks, false);
   TRY(alloc(P, &p, dev_tasks.size() * sizeof(DevTask))); dp.tasks = (const DevTask*)p;
-  HIPCHK(P, hipMemcpy(p, dev_tasks.data(), dev_tasks.size() * sizeof(DevTask), hipMemcpyHostToDevice));
+  TRY(upload(P, p, dev_tasks.data(), dev_tasks.size() * sizeof(DevTask)));
   TRY(alloc(P, &p, P->wg_begin.size() * 4)); dp.wg_begin = (const uint32_t*)p;
-  HIPCHK(P, hipMemcpy(p, P->wg_begin.data(), P->wg_begin.size() * 4, hipMemcpyHostToDevice));
+  TRY(upload(P, p, P->wg_begin.data(), P->wg_begin.size() * 4));
   TRY(alloc(P, &p, dev_phase.size() * sizeof(DevTask))); P->d_phase_tasks = (DevTask*)p;
-  HIPCHK(P, hipMemcpy(p, dev_phase.data(), dev_phase.size() * sizeof(DevTask), hipMemcpyHostToDevice));
+  TRY(upload(P, p, dev_phase.data(), dev_phase.size() * sizeof(DevTask)));
   if (c.flags & CP_FLAG_TRACE) {
-    TRY(alloc(P, &p, P->tasks.size() * kTraceStamps * 8)); dp.trace = (uint64_t*)p;
-    HIPCHK(P, hipMemset(p, 0, P->tasks.size() * kTraceStamps * 8));
+    TRY(alloc(P, &p, P->tasks.size() * kTraceStamps * 8)); dp.trace = (uint64_t*)p;  // zeroed by alloc
     dp.trace_on = 1;
   }
   return CP_OK;
@@ -886,6 +945,11 @@ const char* cp_last_create_error(void) { return g_create_err.c_str(); }
 
 cp_status cp_plan_destroy(cp_plan* plan) {
   if (!plan) return CP_OK;
+  if (plan->is_static) {
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (plan->device >= 0 && plan->device < 64 && g_static_owner[plan->device] == plan)
+      g_static_owner[plan->device] = nullptr;
+  }
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(plan->device);
@@ -896,6 +960,7 @@ cp_status cp_plan_destroy(cp_plan* plan) {
 }
 
 static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights* w, int dev) {
+  // (a static plan arrives with is_static and its arena set)
   std::string msg;
   cp_status s = validate(cfg, msg);
   if (s != CP_OK) return fail(P, s, msg);
@@ -923,11 +988,37 @@ static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights*
   dp.bf16 = bf; dp.eps = cfg->rms_eps; dp.attn_scale = (float)(1.0 / std::sqrt((double)cfg->head_dim));
   dp.spin_limit = kDefaultSpinLimit;
   dp.n_wg = P->cu_count;
-  HIPCHK(P, check_xcd_dealing(dp.n_wg, P->xcd_dealing));
+  if (P->is_static) {
+    void* base = nullptr;
+    HIPCHK(P, static_scratch(dev, &base, &P->st_cap));
+    P->st_base = (uint8_t*)base;
+    if ((size_t)dp.n_wg * 4 > P->st_cap) return fail(P, CP_ERR_OUT_OF_MEMORY, "static scratch too small");
+  }
+  // (a static plan records the dealing into its scratch array, which is
+  // zeroed again when its buffers are carved)
+  HIPCHK(P, check_xcd_dealing(dp.n_wg, P->xcd_dealing, P->is_static ? (uint32_t*)P->st_base : nullptr));
   TRY(build_schedule(P));
+  dp.n_tasks = (int)P->tasks.size();
+  if (P->is_static) {
+    // the scratch this plan needs, before anything is written
+    if ((int64_t)P->arena_cap < const_bytes(*cfg))
+      return fail(P, CP_ERR_INVALID_ARGUMENT,
+                  "weight arena of " + std::to_string(P->arena_cap) + " bytes; the plan's constants need " +
+                      std::to_string(const_bytes(*cfg)) + " (cp_plan_info.const_bytes)");
+    P->measuring = true;
+    TRY(alloc_scratch(P));
+    P->measuring = false;
+    if (P->st_used > P->st_cap)
+      return fail(P, CP_ERR_OUT_OF_MEMORY,
+                  "the plan's scratch needs " + std::to_string(P->st_used) + " bytes, more than the " +
+                      std::to_string(P->st_cap) + " bytes the library holds per device for static plans; "
+                      "use cp_plan_create, or fewer rows or layers");
+    P->st_used = 0;
+    P->scratch_bytes = 0;
+    dp.n_clear = 0;
+  }
   TRY(pack_weights(P, w));
   TRY(check_schedule(P));
-  dp.n_tasks = (int)P->tasks.size();
   dp.tasks_in_lds = (int64_t)P->max_tasks_wg * (int64_t)sizeof(DevTask) <= kTaskLds;
   TRY(alloc_scratch(P));
   HIPCHK(P, hipDeviceSynchronize());
@@ -952,6 +1043,43 @@ cp_status cp_plan_create(const cp_config* cfg, const cp_weights* w, int hip_devi
     cp_plan_destroy(P);
     return s;
   }
+  *out = P;
+  return CP_OK;
+}
+
+cp_status cp_plan_create_static(const cp_config* cfg, const cp_weights* w, int hip_device, void* weight_arena,
+                                uint64_t arena_bytes, cp_plan** out) {
+  if (!out) return CP_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  g_create_err.clear();
+  if (!cfg || !w || !weight_arena) {
+    g_create_err = "NULL config, weights or weight arena";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  if (hip_device < 0 || hip_device >= 64) {
+    g_create_err = "no such device";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (g_static_owner[hip_device]) {
+    g_create_err = "a static plan already lives on this device (they share its scratch array): destroy it first";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  cp_plan* P = new cp_plan();
+  P->is_static = true;
+  P->arena = (uint8_t*)weight_arena;
+  P->arena_cap = (size_t)arena_bytes;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  cp_status s = create_impl(P, cfg, w, hip_device);
+  (void)hipSetDevice(prev);
+  if (s != CP_OK) {
+    g_create_err = P->err;
+    P->is_static = false;  // not the owner: destroy must not touch the slot
+    cp_plan_destroy(P);
+    return s;
+  }
+  g_static_owner[hip_device] = P;
   *out = P;
   return CP_OK;
 }
@@ -982,6 +1110,7 @@ cp_status cp_schedule_check(const cp_config* cfg, int cu_count, cp_plan_info* in
   info->n_tasks = (int32_t)P.tasks.size();
   info->n_workgroups = cu_count;
   info->max_tasks_per_workgroup = P.max_tasks_wg;
+  info->const_bytes = const_bytes(*cfg);
   return CP_OK;
 }
 
@@ -997,6 +1126,7 @@ cp_status cp_plan_query(const cp_plan* P, cp_plan_info* info) {
   info->trace_words = (P->cfg.flags & CP_FLAG_TRACE) ? (int64_t)P->tasks.size() * kTraceStamps : 0;
   info->cu_count = P->cu_count;
   info->max_tasks_per_workgroup = P->max_tasks_wg;
+  info->const_bytes = const_bytes(P->cfg);
   return CP_OK;
 }
 
