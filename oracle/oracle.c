@@ -21,8 +21,11 @@
  * Pins (in the test suite): the transformer stack against an fp64 Llama
  * forward from the transformers library; Philox against numpy's Philox;
  * the draw against brute force and the Gumbel-max sampling law; the
- * embedding sum, the offsets, the causal structure and the bf16 rounding
- * points against their definitions.
+ * embedding sum, the offsets and the causal structure against their
+ * definitions; the bf16 rounding points stage by stage (every recorded stage
+ * recomputed from the one before it with numpy and torch's bf16 rounding, a
+ * planted frame worked out by hand, and mutants with one rounding removed,
+ * moved or added, each of which must fail).
  */
 #include "oracle.h"
 
@@ -227,6 +230,24 @@ static void rmsnorm(const orc_cfg *c, const float *h, const float *g, float *out
   }
 }
 
+int32_t orc_stage_width(const orc_cfg *c) {
+  int32_t wd = c->hidden;
+  const int32_t qkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+  if (qkv > wd) wd = qkv;
+  if (c->intermediate > wd) wd = c->intermediate;
+  return wd;
+}
+
+/* Copies n values of each row's stage s at (p, l) into fr->stages. */
+static void record(const orc_cfg *c, orc_frame *fr, int p, int l, int s, const float *src, int stride, int n) {
+  if (!fr->stages) return;
+  const size_t W = (size_t)orc_stage_width(c);
+  for (int r = 0; r < fr->rows; ++r) {
+    float *dst = fr->stages + ((((size_t)r * c->n_positions + p) * c->n_layers + l) * ORC_STAGES + s) * W;
+    memcpy(dst, src + (size_t)r * stride, sizeof(float) * n);
+  }
+}
+
 int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
   if (!c || !w || !fr) return -1;
   const int L = c->n_layers, H = c->hidden, Din = c->input_dim, nq = c->n_q_heads,
@@ -300,13 +321,16 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
       const float *wu = w->w_up + (size_t)l * I * H;
       const float *wd = w->w_down + (size_t)l * H * I;
       float *kl = kc + (size_t)l * kv_stride_l, *vl = vc + (size_t)l * kv_stride_l;
+      record(c, fr, p, l, ORC_ST_H_IN, h, H, H);
 
       /* qkv: a = RMSNorm(h) * g_attn; [q|k|v] = W_qkv . a (float). */
       for (int r = 0; r < R; ++r) rmsnorm(c, h + (size_t)r * H, w->attn_norm + (size_t)l * H, a + (size_t)r * H);
+      record(c, fr, p, l, ORC_ST_A, a, H, H);
 #pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
       for (int r = 0; r < R; ++r)
         for (int n = 0; n < QKV; ++n)
           qkv[(size_t)r * QKV + n] = (float)dot(wqkv + (size_t)n * H, a + (size_t)r * H, H);
+      record(c, fr, p, l, ORC_ST_QKV_RAW, qkv, QKV, QKV);
 
       /* RoPE at position p on every q and k head (pairs i, i + d/2), then the
          stored Q, K, V. */
@@ -329,6 +353,7 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
           memcpy(vl + o, row + qd + (size_t)(nkv + g) * d, sizeof(float) * d);
         }
       }
+      record(c, fr, p, l, ORC_ST_QKV, qkv, QKV, QKV);
 
       /* Attention: q head hq reads kv head hq / (nq / nkv); causal over t <= p;
          scale 1 / sqrt(d); softmax in double; output stored. */
@@ -359,6 +384,7 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
           if (sp != s) free(sp);
           if (ep != e) free(ep);
         }
+      record(c, fr, p, l, ORC_ST_ATT, att, qd, qd);
 
       /* o projection and residual: h = store(h + W_o . attn). */
 #pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
@@ -368,10 +394,12 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
           a[(size_t)r * H + n] = store_act(c, v); /* a used as scratch for the new h */
         }
       memcpy(h, a, sizeof(float) * (size_t)R * H);
+      record(c, fr, p, l, ORC_ST_H_MID, h, H, H);
 
       /* gate/up: a2 = RMSNorm(h) * g_mlp; m = store(silu(W_gate . a2) * (W_up . a2)),
          silu(x) = x / (1 + exp(-x)). */
       for (int r = 0; r < R; ++r) rmsnorm(c, h + (size_t)r * H, w->mlp_norm + (size_t)l * H, a + (size_t)r * H);
+      record(c, fr, p, l, ORC_ST_A2, a, H, H);
 #pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
       for (int r = 0; r < R; ++r)
         for (int n = 0; n < I; ++n) {
@@ -382,6 +410,9 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
           up[(size_t)r * I + n] = uv;
           mm[(size_t)r * I + n] = store_act(c, sl * (double)uv);
         }
+      record(c, fr, p, l, ORC_ST_GATE, gt, I, I);
+      record(c, fr, p, l, ORC_ST_UP, up, I, I);
+      record(c, fr, p, l, ORC_ST_M, mm, I, I);
 
       /* down projection and residual: h = store(h + W_down . m). */
 #pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
@@ -391,6 +422,7 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
           a[(size_t)r * H + n] = store_act(c, v);
         }
       memcpy(h, a, sizeof(float) * (size_t)R * H);
+      record(c, fr, p, l, ORC_ST_H_OUT, h, H, H);
     }
 
     if (fr->pos_hidden)
@@ -402,6 +434,9 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
     const int j = p;
     const float *wh = w->w_head + (size_t)(j - 1) * V * H;
     for (int r = 0; r < R; ++r) rmsnorm(c, h + (size_t)r * H, w->final_norm, a + (size_t)r * H);
+    if (fr->final_normed)
+      for (int r = 0; r < R; ++r)
+        memcpy(fr->final_normed + ((size_t)r * (P - 1) + (j - 1)) * H, a + (size_t)r * H, sizeof(float) * H);
 #pragma omp parallel for collapse(2) schedule(static) num_threads(nt)
     for (int r = 0; r < R; ++r)
       for (int n = 0; n < V; ++n) z[(size_t)r * V + n] = (float)dot(wh + (size_t)n * H, a + (size_t)r * H, H);

@@ -77,7 +77,32 @@ typedef struct {
   uint64_t *offset_out;         /* NULL or [rows] */
   double *margins;              /* NULL or [rows][P-1][4], see orc_draw */
   int32_t n_threads;            /* <= 0: library default */
+  /* NULL or [rows][P][L][ORC_STAGES][orc_stage_width(cfg)]: every stage's
+     values for each row, position and layer, as stored (for the tests that
+     pin where rounding happens).  Stage s holds ORC_STAGE_LEN(s) leading
+     values of its slot. */
+  float *stages;
+  float *final_normed;          /* NULL or [rows][P-1][hidden]: the final-norm output before head j */
 } orc_frame;
+
+/* Stages recorded per (row, position, layer). */
+enum {
+  ORC_ST_H_IN = 0,   /* the layer's input residual row [hidden] */
+  ORC_ST_A,          /* attention RMSNorm output [hidden] */
+  ORC_ST_QKV_RAW,    /* W_qkv . a as float, before RoPE [(nq + 2 nkv) d] */
+  ORC_ST_QKV,        /* q, k, v after RoPE, as stored [(nq + 2 nkv) d] */
+  ORC_ST_ATT,        /* attention output as stored [nq d] */
+  ORC_ST_H_MID,      /* residual after o, as stored [hidden] */
+  ORC_ST_A2,         /* MLP RMSNorm output [hidden] */
+  ORC_ST_GATE,       /* W_gate . a2 as float [inter] */
+  ORC_ST_UP,         /* W_up . a2 as float [inter] */
+  ORC_ST_M,          /* SwiGLU output as stored [inter] */
+  ORC_ST_H_OUT,      /* residual after down, as stored [hidden] */
+  ORC_STAGES
+};
+
+/* Floats per stage slot: the largest of hidden, (nq + 2 nkv) d and inter. */
+int32_t orc_stage_width(const orc_cfg *cfg);
 
 /* Runs one frame.  Returns 0 on success, a negative value for invalid input. */
 int orc_frame_run(const orc_cfg *cfg, const orc_weights *w, orc_frame *fr);

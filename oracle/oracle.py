@@ -32,6 +32,25 @@ def build(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def load(path: str):
+    """A ctypes handle on an oracle library at `path` (the built one, or a
+    copy compiled from altered source by a test that plants a mistake)."""
+    l = C.CDLL(path)
+    l.orc_frame_run.argtypes = [C.POINTER(_Cfg), C.POINTER(_Weights), C.POINTER(_Frame)]
+    l.orc_frame_run.restype = C.c_int
+    l.orc_philox4x64.argtypes = [_UP, _UP, _UP]
+    l.orc_philox4x64.restype = None
+    l.orc_draw.argtypes = [_FP, C.c_int32, C.c_float, C.c_int32, C.c_float, C.c_uint64, C.c_uint64, _DP]
+    l.orc_draw.restype = C.c_int32
+    l.orc_kept_set.argtypes = [_FP, C.c_int32, C.c_float, C.c_int32, C.c_float, _IP]
+    l.orc_kept_set.restype = C.c_int32
+    l.orc_round_bf16.argtypes = [C.c_float]
+    l.orc_round_bf16.restype = C.c_float
+    l.orc_stage_width.argtypes = [C.POINTER(_Cfg)]
+    l.orc_stage_width.restype = C.c_int32
+    return l
+
+
 class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "hidden", "input_dim", "n_q_heads",
                                           "n_kv_heads", "head_dim", "intermediate",
@@ -55,26 +74,18 @@ class _Frame(C.Structure):
                 ("temperature", _FP), ("top_k", _IP), ("top_p", _FP), ("seed", _UP),
                 ("offset_in", _UP), ("forced_codes", _IP), ("codes", _IP), ("embsum", _FP),
                 ("logits", _FP), ("k_cache", _FP), ("v_cache", _FP), ("pos_hidden", _FP),
-                ("offset_out", _UP), ("margins", _DP), ("n_threads", C.c_int32)]
+                ("offset_out", _UP), ("margins", _DP), ("n_threads", C.c_int32), ("stages", _FP),
+                ("final_normed", _FP)]
+
+# Stages recorded per (row, position, layer) with keep_stages (oracle.h, ORC_ST_*).
+STAGES = ("h_in", "a", "qkv_raw", "qkv", "att", "h_mid", "a2", "gate", "up", "m", "h_out")
 
 
 def lib():
     global _lib
     with _lock:
         if _lib is None:
-            l = C.CDLL(build())
-            l.orc_frame_run.argtypes = [C.POINTER(_Cfg), C.POINTER(_Weights), C.POINTER(_Frame)]
-            l.orc_frame_run.restype = C.c_int
-            l.orc_philox4x64.argtypes = [_UP, _UP, _UP]
-            l.orc_philox4x64.restype = None
-            l.orc_draw.argtypes = [_FP, C.c_int32, C.c_float, C.c_int32, C.c_float, C.c_uint64,
-                                   C.c_uint64, _DP]
-            l.orc_draw.restype = C.c_int32
-            l.orc_kept_set.argtypes = [_FP, C.c_int32, C.c_float, C.c_int32, C.c_float, _IP]
-            l.orc_kept_set.restype = C.c_int32
-            l.orc_round_bf16.argtypes = [C.c_float]
-            l.orc_round_bf16.restype = C.c_float
-            _lib = l
+            _lib = load(build())
     return _lib
 
 
@@ -129,7 +140,8 @@ def _cfg(cfg):
 
 
 def run_frame(cfg, weights, inputs: dict, forced_codes=None, keep_kv: bool = False,
-              keep_hidden: bool = False, n_threads: int = 0, rows=None) -> dict:
+              keep_hidden: bool = False, n_threads: int = 0, rows=None, keep_stages: bool = False,
+              library=None) -> dict:
     """One oracle frame.
 
     ``weights``: an ``OracleWeights`` or a dict of stored weights.  ``inputs``:
@@ -137,8 +149,10 @@ def run_frame(cfg, weights, inputs: dict, forced_codes=None, keep_kv: bool = Fal
     when sampling, temperature/top_k/top_p/seed/offset).  ``rows`` optionally
     selects a subset of the input rows (rows are independent).  Returns
     codes [R][P-1], embsum [R][H], logits [R][P-1][V], margins [R][P-1][4],
-    offset [R] and, on request, k/v caches [L][R][P][nkv][d] and the residual
-    stream after the last layer [R][P][H].
+    offset [R] and, on request, k/v caches [L][R][P][nkv][d], the residual
+    stream after the last layer [R][P][H], and (keep_stages) every stage's
+    stored values [R][P][L][len(STAGES)][width] with the final-norm outputs
+    [R][P-1][H].  ``library``: another oracle library handle (``load``).
     """
     if not isinstance(weights, OracleWeights):
         weights = OracleWeights(cfg, weights)
@@ -160,6 +174,11 @@ def run_frame(cfg, weights, inputs: dict, forced_codes=None, keep_kv: bool = Fal
         out["v_cache"] = np.zeros(kv_shape, np.float32)
     if keep_hidden:
         out["pos_hidden"] = np.zeros((R, P, H), np.float32)
+    lb = lib() if library is None else library
+    if keep_stages:
+        wd = lb.orc_stage_width(C.byref(_cfg(cfg)))
+        out["stages"] = np.zeros((R, P, cfg.n_layers, len(STAGES), wd), np.float32)
+        out["final_normed"] = np.zeros((R, P - 1, H), np.float32)
     samp = {}
     if "temperature" in inputs:
         samp = {k: np.ascontiguousarray(np.asarray(inputs[k])[sel]) for k in
@@ -178,10 +197,11 @@ def run_frame(cfg, weights, inputs: dict, forced_codes=None, keep_kv: bool = Fal
                 logits=_ptr(out["logits"], _FP), k_cache=_ptr(out.get("k_cache"), _FP),
                 v_cache=_ptr(out.get("v_cache"), _FP), pos_hidden=_ptr(out.get("pos_hidden"), _FP),
                 offset_out=_ptr(out["offset"], _UP), margins=_ptr(out["margins"], _DP),
-                n_threads=int(n_threads))
+                n_threads=int(n_threads), stages=_ptr(out.get("stages"), _FP),
+                final_normed=_ptr(out.get("final_normed"), _FP))
         # keep numpy buffers alive for the duration of the call
     keep = (hid, code0, samp, fc, weights)
-    rc = lib().orc_frame_run(C.byref(_cfg(cfg)), C.byref(weights.c), C.byref(fr))
+    rc = lb.orc_frame_run(C.byref(_cfg(cfg)), C.byref(weights.c), C.byref(fr))
     del keep
     if rc != 0:
         raise ValueError(f"oracle rejected the frame (code {rc})")
