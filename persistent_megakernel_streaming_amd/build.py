@@ -31,27 +31,42 @@ DEVICE_SOURCES = ["cp_kernels.hip", "cp_measure.hip", "cp_static.hip"]
 # five wait states.  The compiler inserts them before its own instructions but
 # not before inline asm, so every asm block that issues a vector-memory
 # instruction must begin with "s_nop 4" (or longer) itself.
-_ASM_RE = re.compile(r'asm\s+volatile\s*\(((?:\s*"(?:[^"\\]|\\.)*")+)')
+#
+# A load written in inline asm writes its output registers some time after it
+# issues, while the compiler takes the asm's outputs as written at once: an
+# output that shares registers with an input (an address) could be
+# overwritten while a later instruction of the block still reads it.  Every
+# output of an asm block that loads must therefore be early-clobber ("=&") or
+# read-write ("+").
+_ASM_RE = re.compile(r'asm\s+volatile\s*\(((?:\s*"(?:[^"\\]|\\.)*")+)\s*(:[^;]*)?\);')
 _VMEM_RE = re.compile(r'\b(buffer|global|flat|scratch)_(load|store|atomic)')
+_LOAD_RE = re.compile(r'\b((buffer|global|flat|scratch|s)_load|ds_read)')
 
 
 def check_asm_guards(path: str) -> int:
-    """Raises if an inline-asm block of `path` issues a vector-memory
-    instruction without starting with s_nop 4 or longer; returns the number
-    of such blocks checked."""
+    """Raises if an inline-asm block of `path` issues a vector- or scalar-memory
+    instruction without starting with s_nop 4 or longer, or loads (LDS reads
+    included) into an output that is neither early-clobber nor read-write;
+    returns the number of blocks with a memory instruction."""
     text = open(path).read()
     n = 0
     for m in _ASM_RE.finditer(text):
         body = "".join(re.findall(r'"((?:[^"\\]|\\.)*)"', m.group(1))).replace("\\n", "\n")
-        if not _VMEM_RE.search(body):
+        if not (_VMEM_RE.search(body) or _LOAD_RE.search(body)):
             continue
         n += 1
+        line = text.count("\n", 0, m.start()) + 1
         first = body.strip().split("\n")[0].strip()
         g = re.fullmatch(r"s_nop\s+(\d+)", first)
-        if not g or int(g.group(1)) < 4:
-            line = text.count("\n", 0, m.start()) + 1
-            raise RuntimeError(f"{path}:{line}: inline asm with a vector-memory instruction must start with "
+        if (_VMEM_RE.search(body) or re.search(r"\bs_load", body)) and (not g or int(g.group(1)) < 4):
+            raise RuntimeError(f"{path}:{line}: inline asm with a memory instruction must start with "
                                f"'s_nop 4' (found {first!r})")
+        if _LOAD_RE.search(body):
+            outs = (m.group(2) or ":").split(":")[1]
+            for c in re.findall(r'"([^"]*)"\s*\(', outs):
+                if not (c.startswith("=&") or c.startswith("+")):
+                    raise RuntimeError(f"{path}:{line}: inline asm that loads needs early-clobber ('=&') or "
+                                       f"read-write ('+') outputs (found {c!r})")
     return n
 
 

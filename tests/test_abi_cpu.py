@@ -90,3 +90,11 @@ def test_inline_asm_vector_memory_blocks_start_with_the_guard(tmp_path):
     bad.write_text('asm volatile("s_nop 1\\nglobal_store_dword %0, %1, off" :: "v"(a), "v"(b));\n')
     with pytest.raises(RuntimeError):
         build.check_asm_guards(str(bad))
+    # a load's outputs must not be able to share the address's registers
+    bad.write_text('asm volatile("s_nop 4\\ns_load_dwordx4 %0, %2, 0x0\\ns_load_dwordx2 %1, %2, 0x10"\n'
+                   '             : "=s"(a), "=&s"(b) : "s"(t));\n')
+    with pytest.raises(RuntimeError, match="early-clobber"):
+        build.check_asm_guards(str(bad))
+    bad.write_text('asm volatile("s_nop 4\\ns_load_dwordx4 %0, %2, 0x0\\ns_load_dwordx2 %1, %2, 0x10"\n'
+                   '             : "=&s"(a), "=&s"(b) : "s"(t));\n')
+    assert build.check_asm_guards(str(bad)) == 1
