@@ -15,12 +15,20 @@
  *   CP_EXEC_PERSISTENT  one launch of one workgroup per compute unit that walks
  *                       a static per-workgroup task list (section "How it
  *                       works", first and second bullets).  Workgroups hand
- *                       data to each other through tagged words in device
- *                       memory: every value one workgroup writes for another is
- *                       stored next to a 32-bit tag (epoch * 1024 + the
- *                       writer's phase), and the reader reloads the words until
- *                       every tag is the one it expects.  There are no
- *                       counters and no fences: the data is its own signal.
+ *                       data to each other through device memory, where the
+ *                       data is its own ready signal.  The activations a
+ *                       projection streams (position inputs, residuals,
+ *                       attention and SwiGLU outputs) live in buffers with a
+ *                       plane per layer and position, written once per
+ *                       frame; until then an element holds a sentinel (all
+ *                       bits set, a NaN no producer stores), and the reader
+ *                       reloads until none is left.  After the frame every
+ *                       workgroup meets at one counter and refills its share
+ *                       of those buffers with the sentinel.  Every other value
+ *                       (q, K/V, split-K and norm partials, logits) is stored
+ *                       next to a 32-bit tag (epoch * 1024 + the writer's
+ *                       phase), and the reader reloads the words until every
+ *                       tag is the one it expects.  No fence is on the path.
  *   CP_EXEC_PER_PHASE   one launch per phase (the unfused comparison, the
  *                       "loop" of section "Where the depth loop's time goes").
  *
@@ -192,11 +200,11 @@ cp_status cp_plan_create(const cp_config* cfg, const cp_weights* w, int hip_devi
  * memory on hip_device of at least cp_plan_info.const_bytes bytes, as
  * cp_schedule_check reports for cfg, else CP_ERR_INVALID_ARGUMENT; it must
  * outlive the plan), and every scratch buffer of the plan is carved from an
- * array of 96 MiB the library holds on each device it runs on until the
+ * array of 160 MiB the library holds on each device it runs on until the
  * process ends (a plan that needs more -- the 5-layer bf16 loop at 64 rows
- * needs about 66 MiB, the 10-layer one at 64 rows more -- is refused with
- * CP_ERR_OUT_OF_MEMORY and a message giving both sizes).  The array is
- * zeroed with a kernel at creation.  All static plans of a device share that
+ * needs about 130 MiB, the 10-layer one at 64 rows more -- is refused with
+ * CP_ERR_OUT_OF_MEMORY and a message giving both sizes).  The plan's part of
+ * the array is initialised with a kernel at creation.  All static plans of a device share that
  * one array, so only one may live per device at a time: a second
  * cp_plan_create_static on a device whose static plan has not been destroyed
  * is refused (CP_ERR_INVALID_ARGUMENT).  Its frames behave as those of
@@ -241,9 +249,9 @@ cp_status cp_plan_query(const cp_plan* plan, cp_plan_info* info);
  * price of cross-block waits).  The error stays set for the plan's life. */
 cp_status cp_plan_device_status(cp_plan* plan);
 
-/* Frame epochs.  Every word one workgroup hands to another carries the epoch
- * of the frame that wrote it, so a reader can tell this frame's data from
- * anything older.  Epochs count 1, 2, ... per frame (cp_frame_run) and wrap
+/* Frame epochs.  Every tagged word one workgroup hands to another carries
+ * the epoch of the frame that wrote it, so a reader can tell this frame's
+ * data from anything older.  Epochs count 1, 2, ... per frame (cp_frame_run) and wrap
  * after 4194302 frames: the frame that reaches the limit also clears every
  * tagged buffer, and the next frame is epoch 1 again.  cp_plan_set_epoch makes
  * the plan's next frame run as `epoch` (1 <= epoch <= 4194302), so that the

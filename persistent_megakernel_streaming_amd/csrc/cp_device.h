@@ -51,7 +51,7 @@ constexpr int kMaxClear = 16;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
 // Device bytes the library holds on each device for the scratch of a plan
 // made by cp_plan_create_static.
-constexpr size_t kStaticScratchBytes = (size_t)96 << 20;
+constexpr size_t kStaticScratchBytes = (size_t)160 << 20;
 
 // Task flag: the split-K partners of this task's tile and their owner run on
 // workgroups of one XCD, so partials go through that XCD's L2 (plain stores,
@@ -115,23 +115,30 @@ struct DevPlan {
   // task lists
   const DevTask* tasks;         // all tasks, grouped by workgroup
   const uint32_t* wg_begin;     // [n_wg + 1]
-  uint32_t* state;              // [0] epoch, [32] done counter, [64] error word, [96] clear pending
+  uint32_t* state;              // [0] epoch, [64] error word, [96] clear pending,
+                                // [128 + 32 (epoch & 1)] frame-end arrivals of the persistent executor
   // weights (plan-owned copies)
   const uint8_t* wblob;         // packed projection tiles
   const void* embed;            // [P][V][H]
   const float* rope;            // [P][d/2][2]: cos, sin
   // activations and scratch (act = dtype)
-  // Cross-workgroup buffers hold tagged 64-bit words (2 * dtype size bytes
-  // per element).  Buffers marked [2] are doubled by position parity:
-  // positions 0 and 1 can be in flight at the same time.  Rp = Rmax rounded
-  // up to 16; buffers a projection reads are in the kernels' operand order
-  // (act_off in the kernel source), the others row-major.
-  void* xin;                    // [P][Rp][H] position inputs, operand order
-  void* hres;                   // [2][2][Rp][H] residual after down, by layer parity, operand order
-  void* hmid;                   // [2][Rp][H] residual after o, operand order
-  void* qbuf;                   // [2][Rmax][nq d] rotated q, row-major
-  void* abuf;                   // [2][Rp][nq d] attention output, operand order
-  void* mbuf;                   // [2][Rp][I] SwiGLU output, operand order
+  // The buffers a projection reads (position inputs, residuals, attention
+  // and SwiGLU outputs) hold plain activations in the kernels' operand order
+  // (sop_off in the kernel source), one plane per layer and position, so
+  // that no element is written twice in a frame; an element not yet written
+  // holds the sentinel (all bits set), and the whole region is refilled with
+  // it at the end of every frame.  Rp = Rmax rounded up to 16.  The other
+  // cross-workgroup buffers hold tagged 64-bit words (2 * dtype size bytes
+  // per element); those marked [2] are doubled by position parity:
+  // positions 0 and 1 can be in flight at the same time.
+  void* xin;                    // [P][Rp][H] position inputs
+  void* hres;                   // [L][P][Rp][H] residual after down
+  void* hmid;                   // [L][P][Rp][H] residual after o
+  void* abuf;                   // [L][P][Rp][nq d] attention output
+  void* mbuf;                   // [L][P][Rp][I] SwiGLU output
+  void* opbuf;                  // the region holding the five above
+  uint64_t opbuf_bytes;
+  void* qbuf;                   // [2][Rmax][nq d] rotated q, row-major, tagged
   void* kc;                     // [L][Rmax][nkv][P][d]
   void* vc;
   uint64_t* part;               // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16] words

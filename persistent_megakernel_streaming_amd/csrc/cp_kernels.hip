@@ -14,15 +14,23 @@
 //
 // Hand-off between workgroups.  MI355X has eight XCDs, each with its own L2,
 // and a 256-workgroup counter barrier with agent-scope acquire/release costs
-// several microseconds there.  Instead, every value one workgroup writes and
-// another reads is stored as 64-bit words {payload, tag}: the payload is two
-// bf16 (or one fp32) and the tag is epoch * 1024 + the writer's phase index.
-// Words are written with agent-coherent (sc1) stores whose 8-byte words are
-// single-copy atomic, and read with agent-coherent loads; a reader whose words
-// do not yet carry the tag it expects reloads them.  The data is its own ready
-// signal: there are no counters, no store-completion waits and no cache
-// write-back or invalidate on the path.  Weights, norms and embedding tables
-// never change during a frame and use ordinary loads and direct-to-LDS copies.
+// several microseconds there.  Instead the data is its own ready signal, in
+// one of two forms:
+//   * the activations a projection streams (position inputs, residuals,
+//     attention and SwiGLU outputs) are plain values in buffers where every
+//     element is written at most once per frame and holds a sentinel (all
+//     bits set, a NaN no producer stores) until then; a reader reloads a unit
+//     until none of its elements is the sentinel, and the region is refilled
+//     with the sentinel at the end of every frame;
+//   * everything else (q, K/V, split-K partials, norm partials, logits) is
+//     stored as 64-bit words {payload, tag}: the payload is two bf16 (or one
+//     fp32) and the tag is epoch * 1024 + the writer's phase index, and a
+//     reader reloads until every word carries the tag it expects.
+// Values are written with agent-coherent (sc1) stores and read with
+// agent-coherent loads; there are no counters, no store-completion waits and
+// no cache write-back or invalidate on the path.  Weights, norms and
+// embedding tables never change during a frame and use ordinary loads and
+// direct-to-LDS copies.
 #include <hip/hip_runtime.h>
 
 #include <vector>
@@ -55,6 +63,8 @@ __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) { return __builtin
 __device__ __forceinline__ u32x2 ld8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0); }
 __device__ __forceinline__ void st16c(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSC1); }
 __device__ __forceinline__ void st8c(rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kSC1); }
+__device__ __forceinline__ void st4c(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kSC1); }
+__device__ __forceinline__ u32x2 ld8c(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSC1); }
 __device__ __forceinline__ void st16(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0); }
 __device__ __forceinline__ void st4(rsrc_t r, uint32_t off, uint32_t v) { __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0); }
 
@@ -188,11 +198,67 @@ __device__ __forceinline__ uint32_t tag_of(uint32_t epoch, uint32_t phase) { ret
 // A 16-byte load holds two tagged words: [payload, tag, payload, tag].
 __device__ __forceinline__ bool ll_ok(const u32x4& v, uint32_t tag) { return v[1] == tag && v[3] == tag; }
 
-// Payload of a 32-byte (four-word) chunk: 16 bytes of activations.
-__device__ __forceinline__ u32x4 ll_payload(const u32x4& a, const u32x4& b) { return u32x4{a[0], a[2], b[0], b[2]}; }
-
 // Tagged pair of payload words for a 16-byte store.
 __device__ __forceinline__ u32x4 ll_pair(uint32_t p0, uint32_t p1, uint32_t tag) { return u32x4{p0, tag, p1, tag}; }
+
+// ------------------------------------------------------------------ sentinel operands
+
+// Operand buffers hold plain values; an element not yet written this frame
+// holds the sentinel, all bits set.  As an unsigned 16-bit (bf16) or 32-bit
+// (fp32) number the sentinel is the largest there is, so the maximum over a
+// unit's elements tells whether one is still missing (v_pk_max_u16 takes two
+// bf16 at a time).  Producers never store it: a value whose bits are all set
+// (a NaN) is stored with its sign bit cleared (still a NaN).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int BF>
+__device__ __forceinline__ uint32_t sop_max(uint32_t m, uint32_t w) {
+  if constexpr (BF)
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m), __builtin_bit_cast(u16x2, w)));
+  else
+    return m > w ? m : w;
+}
+// No sentinel among the elements whose maximum is m.
+template <int BF>
+__device__ __forceinline__ bool sop_clear(uint32_t m) {
+  if constexpr (BF) return (m & 0xffffu) != 0xffffu && (m >> 16) != 0xffffu;
+  else return m != 0xffffffffu;
+}
+// The stored form of a packed bf16 pair or an fp32 value: never the sentinel.
+template <int BF>
+__device__ __forceinline__ uint32_t sop_canon(uint32_t w) {
+  if constexpr (BF) return w ^ (((w & 0xffffu) == 0xffffu) ? 0x8000u : 0u) ^ (((w >> 16) == 0xffffu) ? 0x80000000u : 0u);
+  else return w == 0xffffffffu ? 0x7fffffffu : w;
+}
+
+// Operand order of a buffer of K columns: for 16-row tile rt, MFMA chunk c
+// (4 E columns) and lane (q, rl) of the MFMA B operand, the 16-byte unit of
+// row rt * 16 + rl, columns c * 4E + q * E ... + E - 1 lies at
+// (rt * NC + c) * 1024 + (q * 16 + rl) * 16, NC = K / (4E): one wave load
+// instruction reads 1 KiB in one piece, one MFMA operand per lane.  Returns
+// the byte offset of element (row, n).
+template <int BF>
+__device__ __forceinline__ uint32_t sop_off(int row, int n, int K) {
+  constexpr int ESZ = BF ? 2 : 4, E = 16 / ESZ, KS = 4 * E;
+  return (uint32_t)((row >> 4) * (K / KS) + n / KS) * 1024 + (uint32_t)(((n % KS) / E) * 16 + (row & 15)) * 16 +
+         (uint32_t)(n % E) * ESZ;
+}
+// Bytes of one plane of `rows` rows (rounded up to 16) and K columns.
+template <int BF>
+__device__ __forceinline__ uint32_t sop_bytes(int rows, int K) {
+  return (uint32_t)((rows + 15) & ~15) * K * (BF ? 2 : 4);
+}
+// Stores four consecutive columns n .. n+3 (n a multiple of 4) of one row:
+// 8 bytes (bf16) or one 16-byte unit (fp32), contiguous in operand order.
+template <int BF>
+__device__ __forceinline__ void st_sop4(rsrc_t r, int row, int n, int K, const float (&v)[4]) {
+  if constexpr (BF) {
+    st8c(r, sop_off<1>(row, n, K), u32x2{sop_canon<1>(pack_bf16(v[0], v[1])), sop_canon<1>(pack_bf16(v[2], v[3]))});
+  } else {
+    st16c(r, sop_off<0>(row, n, K),
+          u32x4{sop_canon<0>(__float_as_uint(v[0])), sop_canon<0>(__float_as_uint(v[1])),
+                sop_canon<0>(__float_as_uint(v[2])), sop_canon<0>(__float_as_uint(v[3]))});
+  }
+}
 
 // Gives up a wait after spin_limit polls and raises the error word, so a
 // broken schedule ends the kernel instead of hanging it.
@@ -417,12 +483,32 @@ __device__ __forceinline__ void asm_reload(u32x2 (&v)[16], rsrc_t r, const uint3
                : "memory");
 }
 
-// A set of tagged units a lane is waiting for: N loads already issued into
-// v, their offsets in r, and the tag they must carry.  Units from `nload` on
-// are neither checked nor reloaded (they may hold anything).  ASM: reloads
-// through asm_reload (every unit, those past nload being rereads nobody
-// checks).
-template <typename T, int N, typename Off, bool ASM>
+// Sentinel check of the first n of N operand units (16 or 8 bytes each).
+template <int BF, int N>
+__device__ __forceinline__ bool sop_units_ok(const u32x4 (&v)[N], int n = N) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    uint32_t mi = sop_max<BF>(sop_max<BF>(v[i][0], v[i][1]), sop_max<BF>(v[i][2], v[i][3]));
+    m = (i < n) ? sop_max<BF>(m, mi) : m;
+  }
+  return sop_clear<BF>(m);
+}
+template <int BF, int N>
+__device__ __forceinline__ bool sop_units_ok(const u32x2 (&v)[N], int n = N) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = (i < n) ? sop_max<BF>(m, sop_max<BF>(v[i][0], v[i][1])) : m;
+  return sop_clear<BF>(m);
+}
+
+// A set of units a lane is waiting for: N loads already issued into v, their
+// offsets in r, and what makes them current -- CK = 0: the tag they must
+// carry; CK = 1 (bf16) or 2 (fp32): no sentinel left among their elements.
+// Units from `nload` on are neither checked nor reloaded (they may hold
+// anything).  ASM: reloads through asm_reload (every unit, those past nload
+// being rereads nobody checks).
+template <typename T, int N, typename Off, bool ASM, int CK = 0>
 struct Pend {
   T (&v)[N];
   rsrc_t r;
@@ -430,11 +516,15 @@ struct Pend {
   uint32_t tag;
   bool active;
   int nload;
-  // (both sides always evaluated: the tag check then reads every unit on
-  // every path, so the compiler knows the loads are complete after a wait)
-  __device__ __forceinline__ bool ok() const { return !active | units_ok(v, tag, nload); }
+  __device__ __forceinline__ bool current() const {
+    if constexpr (CK == 0) return units_ok(v, tag, nload);
+    else return sop_units_ok<CK == 1>(v, nload);
+  }
+  // (both sides always evaluated: the check then reads every unit on every
+  // path, so the compiler knows the loads are complete after a wait)
+  __device__ __forceinline__ bool ok() const { return !active | current(); }
   __device__ __forceinline__ void reload() {
-    if (active && !units_ok(v, tag, nload)) {
+    if (active && !current()) {
       if constexpr (ASM) {
         uint32_t o[N];
 #pragma unroll
@@ -453,6 +543,12 @@ __device__ __forceinline__ Pend<T, N, Off, ASM> pend(T (&v)[N], rsrc_t r, Off of
                                                      int nload = N) {
   return Pend<T, N, Off, ASM>{v, r, off, tag, active, nload};
 }
+// A set of operand units (sentinel check, activation type BF).
+template <int BF, bool ASM = false, typename T, int N, typename Off>
+__device__ __forceinline__ Pend<T, N, Off, ASM, BF ? 1 : 2> spend(T (&v)[N], rsrc_t r, Off off, bool active,
+                                                                 int nload = N) {
+  return Pend<T, N, Off, ASM, BF ? 1 : 2>{v, r, off, 0u, active, nload};
+}
 
 // Waits until every set of every lane carries its tag.  When the data is
 // there this is one check per set; otherwise each stale set is reloaded with
@@ -464,40 +560,6 @@ __device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
   while (__builtin_amdgcn_ballot_w64(!(ps.ok() && ...)) != 0) {
     if (!sp.next(pl)) break;
     (ps.reload(), ...);
-  }
-}
-
-// Operand-order layout of the activations a projection reads (position
-// inputs, residuals, attention output, SwiGLU output), as tagged words.  For
-// 16-row tile rt, MFMA chunk c (4 E columns) and half u, the 64 lanes'
-// 16-byte units are contiguous: lane (q, rl) of the MFMA B operand finds row
-// rt * 16 + rl, columns c * 4E + q * E + u * E / 2 ... + E / 2 - 1 at
-// ((rt * NC + c) * 2 + u) * 1024 + (q * 16 + rl) * 16, NC = K / (4E).  A wave
-// load instruction then reads 1 KiB in one piece.  Returns the byte offset of
-// the tagged word holding element (row, n) of a K-column buffer.
-template <int BF>
-__device__ __forceinline__ uint32_t act_off(int row, int n, int K) {
-  constexpr int ESZ = BF ? 2 : 4, E = 16 / ESZ, KS = 4 * E, E2 = E / 2;
-  const uint32_t unit = ((uint32_t)((row >> 4) * (K / KS) + n / KS) * 2 + (n % E) / E2) * 1024 +
-                        (uint32_t)(((n % KS) / E) * 16 + (row & 15)) * 16;
-  return unit + (uint32_t)((n % E2) * ESZ / 4) * 8;
-}
-
-// Bytes of one operand-order buffer of `rows` rows (rounded up to 16) and K columns.
-template <int BF>
-__device__ __forceinline__ uint32_t act_bytes(int rows, int K) {
-  return (uint32_t)((rows + 15) & ~15) * K * (BF ? 4 : 8);
-}
-
-// Stores four consecutive columns n .. n+3 (n a multiple of 4) of one row as
-// tagged words in operand order: one 16-byte unit (bf16) or two (fp32).
-template <int BF>
-__device__ __forceinline__ void st_act4(rsrc_t r, int row, int n, int K, const float (&v)[4], uint32_t tag) {
-  if constexpr (BF) {
-    st16c(r, act_off<1>(row, n, K), ll_pair(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), tag));
-  } else {
-    st16c(r, act_off<0>(row, n, K), ll_pair(__float_as_uint(v[0]), __float_as_uint(v[1]), tag));
-    st16c(r, act_off<0>(row, n + 2, K), ll_pair(__float_as_uint(v[2]), __float_as_uint(v[3]), tag));
   }
 }
 
@@ -525,11 +587,11 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   constexpr int NB = KIND == T_GU ? 2 : 1;  // weight tiles per chunk (gate and up)
   constexpr bool PART = KIND == T_O || KIND == T_DOWN || KIND == T_INPROJ;
   constexpr bool RESID = KIND == T_O || KIND == T_DOWN;
-  constexpr int NU = XLL ? 8 : 4;           // 16-byte loads per lane per group of 4 chunks
-  constexpr uint32_t CST = 64;              // plain operand bytes per chunk step
+  constexpr int NU = 4;                     // 16-byte loads per lane per group of 4 chunks
+  constexpr uint32_t CST = 64;              // frame-input bytes per chunk step
   // ONE: a frame of one row.  Only row 0 of the operand tile is loaded, its
-  // 16-byte units packed densely over the lanes (one load instruction per 8
-  // chunks instead of two per chunk), and handed to the MFMA lanes with
+  // 16-byte units packed densely over the lanes (one load instruction per 16
+  // chunks instead of one per chunk), and handed to the MFMA lanes with
   // ds_bpermute; the norm partials of the row come in one load as well.
   static_assert(!ONE || XLL, "one-row operands are tagged");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -540,28 +602,30 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const uint32_t my_tag = tag_of(epoch, tk.phase);
   const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
 
-  // Buffers that positions 0 and 1 (in flight together) would share are
-  // doubled and picked by position parity.  Tagged buffers hold 2 * ESZ
-  // bytes per element.
+  // Operand buffers have a plane per layer and position; the tagged norm
+  // partials and split-K partials that positions 0 and 1 (in flight
+  // together) would share are doubled and picked by position parity.
   const int par = p & 1;
-  const uint32_t hbytes = act_bytes<BF>(Rmax, H);
-  uint8_t* hres = (uint8_t*)pl.hres + (size_t)par * 2 * hbytes;  // [layer parity]
-  uint8_t* hmid = (uint8_t*)pl.hmid + (size_t)par * hbytes;
+  const uint32_t hbytes = sop_bytes<BF>(Rmax, H);
+  auto plane = [&](int ll, int pp) -> size_t { return (size_t)(ll * P + pp); };
+  uint8_t* const xin = (uint8_t*)pl.xin;
+  uint8_t* const hres = (uint8_t*)pl.hres;
+  uint8_t* const hmid = (uint8_t*)pl.hmid;
   const uint8_t* xsrc;
   uint32_t ld;                     // operand row length (elements)
   int kt = H, k0 = 0, in_ssq = 0;
   if constexpr (KIND == T_QKV) {
-    xsrc = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
+    xsrc = (l == 0) ? xin + (size_t)p * hbytes : hres + plane(l - 1, p) * hbytes;
     in_ssq = (l == 0) ? p : P + 2 * par + ((l - 1) & 1);
     ld = H;
   } else if constexpr (KIND == T_GU) {
-    xsrc = hmid; in_ssq = P + 4 + par; ld = H;
+    xsrc = hmid + plane(l, p) * hbytes; in_ssq = P + 4 + par; ld = H;
   } else if constexpr (KIND == T_HEAD) {
-    xsrc = hres + (size_t)((pl.L - 1) & 1) * hbytes; in_ssq = P + 2 * par + ((pl.L - 1) & 1); ld = H;
+    xsrc = hres + plane(pl.L - 1, p) * hbytes; in_ssq = P + 2 * par + ((pl.L - 1) & 1); ld = H;
   } else if constexpr (KIND == T_O) {
-    ld = pl.nq * pl.d; xsrc = (const uint8_t*)pl.abuf + (size_t)par * act_bytes<BF>(Rmax, ld);
+    ld = pl.nq * pl.d; xsrc = (const uint8_t*)pl.abuf + plane(l, p) * sop_bytes<BF>(Rmax, ld);
   } else if constexpr (KIND == T_DOWN) {
-    ld = pl.I; xsrc = (const uint8_t*)pl.mbuf + (size_t)par * act_bytes<BF>(Rmax, ld);
+    ld = pl.I; xsrc = (const uint8_t*)pl.mbuf + plane(l, p) * sop_bytes<BF>(Rmax, ld);
   } else {
     ld = pl.Din; xsrc = (const uint8_t*)fr.hidden_in;
   }
@@ -584,21 +648,19 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const bool wave_live = rt < nrt;
   const bool live = wave_live && row < rows;
 
-  // Operand rows.  Tagged operands are in operand order: unit u of chunk c
-  // of this lane is at xoff + c * 2048 + u * 1024.  A lane whose row is past
-  // the frame's rows reads words of no use (left out of every wait; they
-  // only reach that row's MFMA column, which is never stored).  The frame
-  // input is plain row-major; its resource ends at the last row, so rows
-  // past it read zeros.  Every load of a tagged unit is agent-coherent; a
-  // word that is not yet written fails its tag check and is loaded again.
-  const uint32_t xrow = (uint32_t)ld * ESZ;  // plain input only
-  const rsrc_t rx = XLL ? make_rsrc(xsrc, act_bytes<BF>(Rmax, ld)) : make_rsrc(xsrc, (uint32_t)rows * xrow);
-  const uint32_t xoff = XLL ? ((uint32_t)(rt * (ld / KS) + k0 / KS + c0) * 2) * 1024 + (uint32_t)lane * 16
+  // Operand rows.  Operand buffers are in operand order: the unit of chunk
+  // c of this lane is at xoff + c * 1024.  A lane whose row is past the
+  // frame's rows reads values of no use (left out of every wait; they only
+  // reach that row's MFMA column, which is never stored).  The frame input is
+  // plain row-major; its resource ends at the last row, so rows past it read
+  // zeros.  Every load of an operand unit is agent-coherent; a unit that still
+  // holds a sentinel is loaded again.
+  const uint32_t xrow = (uint32_t)ld * ESZ;  // frame input only
+  const rsrc_t rx = XLL ? make_rsrc(xsrc, sop_bytes<BF>(Rmax, ld)) : make_rsrc(xsrc, (uint32_t)rows * xrow);
+  const uint32_t xoff = XLL ? (uint32_t)(rt * (ld / KS) + k0 / KS + c0) * 1024 + (uint32_t)lane * 16
                             : (uint32_t)row * xrow + (uint32_t)(k0 + q * E) * ESZ + c0 * CST;
   auto uoff = [=](int g) {
-    return [=](int u) -> uint32_t {
-      return XLL ? xoff + (g * 4 + (u >> 1)) * 2048 + (u & 1) * 1024 : xoff + (g * 4 + u) * CST;
-    };
+    return [=](int u) -> uint32_t { return xoff + (uint32_t)(g * 4 + u) * (XLL ? 1024u : CST); };
   };
   // Four groups in flight: xa, xb, xc, xd hold groups g = 0, 1, 2, 3 (mod 4).
   u32x4 xa[NU], xb[NU], xc[NU], xd[NU];
@@ -608,16 +670,16 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       for (int u = 0; u < NU; ++u) x[u] = XLL ? ld16c(rx, uoff(g)(u)) : ld16(rx, uoff(g)(u));
     }
   };
-  // ONE: piece P = (c * 2 + u) * 4 + q' (chunk c of this wave, unit u, lane
-  // group q') is loaded by lane P % 64 of instruction P / 64; lanes past the
-  // last piece load a duplicate.
-  constexpr int NJ1 = 4;  // at most 32 chunks per wave
+  // ONE: piece P = c * 4 + q' (chunk c of this wave, lane group q') is
+  // loaded by lane P % 64 of instruction P / 64; lanes past the last piece
+  // load a duplicate.
+  constexpr int NJ1 = 2;  // at most 32 chunks per wave
   u32x4 xo[NJ1];
-  const int npc = 8 * ncw, nj1 = (npc + 63) / 64;
-  const uint32_t xbase1 = ((uint32_t)(k0 / KS + c0) * 2) * 1024;
+  const int npc = 4 * ncw, nj1 = (npc + 63) / 64;
+  const uint32_t xbase1 = (uint32_t)(k0 / KS + c0) * 1024;
   auto oo = [=](int j) -> uint32_t {
     const int P = (j * 64 + lane) % npc;
-    return xbase1 + (uint32_t)((P >> 3) * 2048 + ((P >> 2) & 1) * 1024 + (P & 3) * 256);
+    return xbase1 + (uint32_t)((P >> 2) * 1024 + (P & 3) * 256);
   };
   if (wave_live) {
     if constexpr (ONE) {
@@ -676,9 +738,9 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // still copied its share of the tile, and waits for every load; so do
   // one-row frames and untagged operands.  (wave_live is wave-uniform.)
   if constexpr (ONE)
-    await_all(pl, pend(xo, rx, oo, in_tag, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live, 1));
+    await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live, 1));
   else
-    await_all(pl, pend<ASM>(xa, rx, uoff(0), in_tag, XLL && live), pend<ASM>(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
+    await_all(pl, spend<BF, ASM>(xa, rx, uoff(0), XLL && live), pend<ASM>(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
   if (XLL && !ONE && wave_live) wait_for(xa[0]);
   else wait_vm();
   __syncthreads();
@@ -702,11 +764,11 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const uint8_t* wt = slot + lane * 16 + (size_t)c0 * NB * 1024;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   auto step = [&](u32x4 (&xr)[NU], int g) {
-    if constexpr (XLL) await_all(pl, pend<ASM>(xr, rx, uoff(g), in_tag, live));
+    if constexpr (XLL) await_all(pl, spend<BF, ASM>(xr, rx, uoff(g), live));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = g * 4 + i;
-      const u32x4 x = XLL ? ll_payload(xr[2 * i], xr[2 * i + 1]) : xr[i];
+      const u32x4 x = xr[i];
       const u32x4 w0 = *(const u32x4*)(wt + c * NB * 1024);
       if constexpr (NB == 2) {
         const u32x4 w1 = *(const u32x4*)(wt + (c * 2 + 1) * 1024);
@@ -719,21 +781,21 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     }
   };
   if (wave_live && ONE) {
-    // chunk c of instruction j = c / 8: units 0 and 1 of lane group q sit in
-    // lanes (c % 8) * 8 + q and + 4 (every MFMA column gets row 0)
+    // chunk c of instruction j = c / 16: the unit of lane group q sits in
+    // lane (c % 16) * 4 + q (every MFMA column gets row 0)
 #pragma unroll
     for (int j = 0; j < NJ1; ++j) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (j * 8 + h * 4 >= ncw) break;  // ncw is a multiple of 4: whole blocks of 4 chunks
+      for (int h = 0; h < 4; ++h) {
+        if (j * 16 + h * 4 >= ncw) break;  // ncw is a multiple of 4: whole blocks of 4 chunks
 #pragma unroll
         for (int cj = 0; cj < 4; ++cj) {
-          const int ci = h * 4 + cj, c = j * 8 + ci;
-          const int a0 = (ci * 8 + q) * 4, a1 = (ci * 8 + 4 + q) * 4;
-          const u32x4 x = {(uint32_t)__builtin_amdgcn_ds_bpermute(a0, (int)xo[j][0]),
-                           (uint32_t)__builtin_amdgcn_ds_bpermute(a0, (int)xo[j][2]),
-                           (uint32_t)__builtin_amdgcn_ds_bpermute(a1, (int)xo[j][0]),
-                           (uint32_t)__builtin_amdgcn_ds_bpermute(a1, (int)xo[j][2])};
+          const int ci = h * 4 + cj, c = j * 16 + ci;
+          const int a = (ci * 4 + q) * 4;
+          const u32x4 x = {(uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)xo[j][0]),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)xo[j][1]),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)xo[j][2]),
+                           (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)xo[j][3])};
           const u32x4 w0 = *(const u32x4*)(wt + c * NB * 1024);
           if constexpr (NB == 2) {
             const u32x4 w1 = *(const u32x4*)(wt + (c * 2 + 1) * 1024);
@@ -805,29 +867,31 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   if constexpr (PART) {
     // Split-K: the owner (split 0) collects its partners' partials (tagged
     // with this phase, in split order) and the residual.
-    const uint32_t res_tag = tag_of(epoch, tk.ph_in1);
     const bool owner = tk.split == 0;
     uint64_t part_off;
     void* out;
     int out_ssq;
     const void* resid = nullptr;
     if constexpr (KIND == T_O) {
-      part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; out = hmid; out_ssq = P + 4 + par;
-      resid = (l == 0) ? (const uint8_t*)pl.xin + (size_t)p * hbytes : hres + (size_t)((l - 1) & 1) * hbytes;
+      part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; out = hmid + plane(l, p) * hbytes;
+      out_ssq = P + 4 + par;
+      resid = (l == 0) ? xin + (size_t)p * hbytes : hres + plane(l - 1, p) * hbytes;
     } else if constexpr (KIND == T_DOWN) {
-      part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; out = hres + (size_t)(l & 1) * hbytes;
-      out_ssq = P + 2 * par + (l & 1); resid = hmid;
+      part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; out = hres + plane(l, p) * hbytes;
+      out_ssq = P + 2 * par + (l & 1); resid = hmid + plane(l, p) * hbytes;
     } else {
-      part_off = pl.part_in_off; out = pl.xin; out_ssq = 0;
+      part_off = pl.part_in_off; out = xin; out_ssq = 0;
     }
     const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 8);
     const uint32_t pbase = (uint32_t)((tk.tile * tk.nsplit * Rmax + row) * 16 + 4 * q) * 8;
     const uint32_t pstep = (uint32_t)Rmax * 16 * 8;  // bytes between splits of a tile
     auto po = [=](int u) -> uint32_t { return pbase + (1 + (u >> 1)) * pstep + (u & 1) * 16; };
     const rsrc_t rr = make_rsrc(resid, hbytes);
-    auto ro = [=](int u) -> uint32_t { return act_off<BF>(row, (int)slots + u * (E / 2), H); };
-    constexpr int NR = BF ? 1 : 2;  // 16-byte loads of the residual's four slots
-    u32x4 pv[6], rv[NR];
+    auto ro = [=](int) -> uint32_t { return sop_off<BF>(row, (int)slots, H); };
+    // the residual's four slots: 8 bytes (bf16) or one 16-byte unit (fp32)
+    u32x4 pv[6];
+    u32x2 rw[1];
+    u32x4 rq[1];
     const int npart = tk.nsplit - 1;
     if (epi_wave && !owner) {
       if (live) {
@@ -851,13 +915,17 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
       for (int u = 0; u < 6; ++u) pv[u] = ld16c(rp, po((u >> 1) < npart ? u : 2 * npart - 2 + (u & 1)));
       if constexpr (RESID) {
-#pragma unroll
-        for (int u = 0; u < NR; ++u) rv[u] = ld16c(rr, ro(u));
+        if constexpr (BF) rw[0] = ld8c(rr, ro(0));
+        else rq[0] = ld16c(rr, ro(0));
       }
     }
     if (epi_wave && owner) {
-      await_all(pl, pend<ASM>(pv, rp, po, my_tag, live && npart > 0, 2 * npart),
-                pend<ASM>(rv, rr, ro, res_tag, RESID && live));
+      if constexpr (BF)
+        await_all(pl, pend<ASM>(pv, rp, po, my_tag, live && npart > 0, 2 * npart),
+                  spend<BF, ASM>(rw, rr, ro, RESID && live));
+      else
+        await_all(pl, pend<ASM>(pv, rp, po, my_tag, live && npart > 0, 2 * npart),
+                  spend<BF, ASM>(rq, rr, ro, RESID && live));
       f32x4 s = acc0;
 #pragma unroll
       for (int sp = 1; sp < 4; ++sp)
@@ -868,7 +936,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         }
       float h[4];
       if constexpr (RESID) {
-        const u32x4 r4 = BF ? u32x4{rv[0][0], rv[0][2], 0, 0} : ll_payload(rv[0], rv[NR - 1]);
+        const u32x4 r4 = BF ? u32x4{rw[0][0], rw[0][1], 0, 0} : rq[0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e] + chunk_elem<BF>(r4, e));
       } else {
@@ -877,7 +945,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
       const float sq = tile_ssq(h, 16, 4);
       if (live) {
-        st_act4<BF>(make_rsrc(out, hbytes), row, (int)slots, H, h, my_tag);
+        st_sop4<BF>(make_rsrc(out, hbytes), row, (int)slots, H, h);
         if (q == 0)
           st8c(make_rsrc(ssq_slot(pl, out_ssq), (uint32_t)Rmax * ss_row), (uint32_t)row * ss_row + tk.tile * 8,
                u32x2{__float_as_uint(sq), my_tag});
@@ -937,9 +1005,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           const float gv = acc0[v], uv = acc1[v];
           m[v] = (gv / (1.0f + expf(-gv))) * uv;
         }
-        const uint32_t mbytes = act_bytes<BF>(Rmax, pl.I);
-        st_act4<BF>(make_rsrc((uint8_t*)pl.mbuf + (size_t)par * mbytes, mbytes), row, 16 * tk.tile + 4 * q, pl.I, m,
-                    my_tag);
+        const uint32_t mbytes = sop_bytes<BF>(Rmax, pl.I);
+        st_sop4<BF>(make_rsrc((uint8_t*)pl.mbuf + plane(l, p) * mbytes, mbytes), row, 16 * tk.tile + 4 * q, pl.I, m);
       }
     }
     if constexpr (KIND == T_HEAD) {
@@ -996,8 +1063,8 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
   const rsrc_t rq = make_rsrc((uint8_t*)pl.qbuf + (size_t)(p & 1) * qdbytes, qdbytes);
   const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
   const rsrc_t rk = make_rsrc(pl.kc, kvbytes), rv = make_rsrc(pl.vc, kvbytes);
-  const uint32_t abytes = act_bytes<BF>(Rmax, pl.nq * d);  // attention output, operand order for o
-  const rsrc_t ra = make_rsrc((uint8_t*)pl.abuf + (size_t)(p & 1) * abytes, abytes);
+  const uint32_t abytes = sop_bytes<BF>(Rmax, pl.nq * d);  // attention output, operand order for o
+  const rsrc_t ra = make_rsrc((uint8_t*)pl.abuf + (size_t)(l * P + p) * abytes, abytes);
   const uint32_t q_tag = tag_of(epoch, tk.ph_in0), kv_tag = tag_of(epoch, kKvPhase);
   const uint32_t my_tag = tag_of(epoch, tk.phase);
   const int t = lane >> 2, c = lane & 3;
@@ -1104,18 +1171,18 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
     const int an = hq * d + lane * dpl;  // first output column of this lane
-    const uint32_t ao = act_off<BF>(row, an, pl.nq * d);
+    const uint32_t ao = sop_off<BF>(row, an, pl.nq * d);
     if constexpr (BF) {
       if (dpl == 2) {
-        st8c(ra, ao, u32x2{pack_bf16(o0, o1), my_tag});
+        st4c(ra, ao, sop_canon<1>(pack_bf16(o0, o1)));
       } else {
-        // two lanes share a word: the even lane writes both dims
+        // two lanes share a dword: the even lane writes both dims
         const float o_nb = __shfl_xor(o0, 1, 64);
-        if ((lane & 1) == 0) st8c(ra, ao, u32x2{pack_bf16(o0, o_nb), my_tag});
+        if ((lane & 1) == 0) st4c(ra, ao, sop_canon<1>(pack_bf16(o0, o_nb)));
       }
     } else {
-      if (dpl == 2) st16c(ra, ao, ll_pair(__float_as_uint(o0), __float_as_uint(o1), my_tag));
-      else st8c(ra, ao, u32x2{__float_as_uint(o0), my_tag});
+      if (dpl == 2) st8c(ra, ao, u32x2{sop_canon<0>(__float_as_uint(o0)), sop_canon<0>(__float_as_uint(o1))});
+      else st4c(ra, ao, sop_canon<0>(__float_as_uint(o0)));
     }
   }
   stamp(tr, 5);
@@ -1134,7 +1201,7 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
   const int H = pl.H, V = pl.V;
   const rsrc_t re = make_rsrc(pl.embed, (uint32_t)pl.P * V * H * ESZ);
   const rsrc_t rs = make_rsrc(fr.embsum, (uint32_t)fr.rows * H * 4);
-  const uint32_t hbytes = act_bytes<BF>(pl.Rmax, H);
+  const uint32_t hbytes = sop_bytes<BF>(pl.Rmax, H);
   const rsrc_t rx = make_rsrc((uint8_t*)pl.xin + (size_t)(j + 1) * hbytes, hbytes);
   const uint32_t ebase = (uint32_t)((j * V + code) * H);
   const bool feeds = j + 1 < pl.P;  // the row is the input of position j + 1
@@ -1158,7 +1225,7 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
       for (int i = 0; i < 4; ++i) ev[i] = 0.f;
     }
-    if (in && feeds) st_act4<BF>(rx, row, k, H, ev, my_tag);
+    if (in && feeds) st_sop4<BF>(rx, row, k, H, ev);
     const float sq = tile_ssq(ev, 1, 4);
     if (in) {
 #pragma unroll
@@ -1623,6 +1690,21 @@ __device__ __forceinline__ void clear_tagged(const DevPlan& pl) {
   __syncthreads();
 }
 
+// Refills this workgroup's share (workgroup w of n) of the operand region
+// with the sentinel, with agent-coherent 16-byte stores.
+__device__ __forceinline__ void refill_operands(const DevPlan& pl, uint32_t w, uint32_t n) {
+  const uint64_t units = pl.opbuf_bytes / 16;
+  const uint64_t per = (units + n - 1) / n, u0 = (uint64_t)w * per;
+  const uint64_t u1 = u0 + per < units ? u0 + per : units;
+  uint8_t* base = (uint8_t*)pl.opbuf;
+  for (uint64_t u = u0 + threadIdx.x; u < u1; u += kThreads) {
+    // (one resource per 2 GiB window: buffer offsets are 32-bit)
+    const uint64_t byte = u * 16, win = byte >> 31;
+    const rsrc_t r = make_rsrc(base + (win << 31), 0x80000000u);
+    st16c(r, (uint32_t)(byte - (win << 31)), u32x4{~0u, ~0u, ~0u, ~0u});
+  }
+}
+
 // Moves the plan to the next frame's epoch.  Run by one whole workgroup once
 // every task of the frame has finished.  When the next epoch would leave the
 // tag space, every tagged buffer is cleared (a few milliseconds, once every
@@ -1637,7 +1719,6 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
   if (!defer) clear_tagged(pl);
   if (threadIdx.x == 0) {
     if (defer) __hip_atomic_store(pl.state + 96, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(pl.state + 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(pl.state, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -1695,17 +1776,31 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     stamp(tr, 7);
     cur = nxt;
   }
-  // The last workgroup to finish moves the plan to the next frame.  Before a
-  // wrapping frame's clear, partials held in an XCD's L2 (plain stores) are
-  // written back, so that none lands in memory after the clear.
+  // Frame end.  Every workgroup waits (bounded) until all have finished their
+  // tasks -- each has waited for its own loads, so no operand is read any
+  // more -- then refills its share of the operand region with the sentinel;
+  // the kernel's end makes those stores visible to the next frame.  Arrivals
+  // count on one of two counters by epoch parity; the last arriver zeroes
+  // the other one, which the next frame uses, and moves the plan to the next
+  // epoch.  Before a wrapping frame's clear, partials held in an XCD's L2
+  // (plain stores) are written back, so that none lands in memory after the
+  // clear.
   if (epoch + 1 >= kEpochWrap) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   wait_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(pl.state + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    misc[0] = old == (uint32_t)pl.n_wg * epoch - 1;
+    uint32_t* arrive = pl.state + 128 + 32 * (epoch & 1);
+    const uint32_t old = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t n = (uint32_t)pl.n_wg;
+    misc[0] = old == n - 1;
+    if (old == n - 1) __hip_atomic_store(pl.state + 128 + 32 * ((epoch + 1) & 1), 0u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    Spin sp;
+    while (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n)
+      if (!sp.next(pl)) break;
   }
   __syncthreads();
+  refill_operands(pl, blockIdx.x, (uint32_t)pl.n_wg);
   if (misc[0]) advance_epoch(pl, epoch, fr.defer_clear);
 }
 
@@ -1719,7 +1814,11 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr);
 }
 
-// The per-phase executor's last launch of a frame.
+// The per-phase executor's last launches of a frame: the sentinel refill of
+// the operand region (a grid of its own), then the epoch.
+__global__ __launch_bounds__(kThreads, 1) void refill_operands_kernel(DevPlan pl) {
+  refill_operands(pl, blockIdx.x, gridDim.x);
+}
 __global__ __launch_bounds__(kThreads, 1) void bump_epoch_kernel(DevPlan pl, int defer) {
   advance_epoch(pl, __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), defer != 0);
 }
@@ -1782,6 +1881,9 @@ hipError_t launch_phase(const DevPlan& pl, const DevFrame& fr, const DevTask* ta
 }
 
 hipError_t launch_bump_epoch(const DevPlan& pl, int defer_clear, hipStream_t s) {
+  hipLaunchKernelGGL(refill_operands_kernel, dim3(pl.n_wg), dim3(kThreads), 0, s, pl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bump_epoch_kernel, dim3(1), dim3(kThreads), 0, s, pl, defer_clear);
   return hipGetLastError();
 }

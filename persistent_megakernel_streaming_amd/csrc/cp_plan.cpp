@@ -36,7 +36,7 @@ hipError_t set_kernel_attributes();
 int occupancy_per_cu(int bf16);
 hipError_t check_xcd_dealing(int n_wg, bool& dealt, uint32_t* buf);
 hipError_t static_scratch(int device, void** ptr, size_t* bytes);
-hipError_t launch_fill_zero(void* p, size_t bytes);
+hipError_t launch_fill(void* p, size_t bytes, uint32_t pattern);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_chain(uint32_t* slots, int n_wg, int n_phases, uint32_t base, int local, int variant, uint32_t* err,
                         hipStream_t s);
@@ -641,11 +641,12 @@ static cp_status fetch(cp_plan* P, const void* dptr, size_t bytes, std::vector<u
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Device allocation, zero-filled: memory a previous plan freed may still hold
-// tagged words that a frame of this plan would otherwise accept.  Tagged
-// buffers are also recorded for the clear at the epoch wrap.  A static plan
-// carves it from the library's array and zeroes it with a kernel.
-static cp_status alloc(cp_plan* P, void** p, size_t bytes, bool tagged = false) {
+// Device allocation, zero-filled (or filled with `fill`, a byte repeated):
+// memory a previous plan freed may still hold tagged words that a frame of
+// this plan would otherwise accept.  Tagged buffers are also recorded for the
+// clear at the epoch wrap.  A static plan carves it from the library's array
+// and fills it with a kernel.
+static cp_status alloc(cp_plan* P, void** p, size_t bytes, bool tagged = false, uint8_t fill = 0) {
   if (bytes == 0) bytes = 256;
   bytes = (bytes + 15) & ~(size_t)15;
   if (P->is_static) {
@@ -654,7 +655,7 @@ static cp_status alloc(cp_plan* P, void** p, size_t bytes, bool tagged = false) 
     *p = P->st_base + off;  // (while measuring: a placeholder, never dereferenced)
     if (!P->measuring) {
       if (P->st_used > P->st_cap) return fail(P, CP_ERR_OUT_OF_MEMORY, "static scratch overflow");
-      HIPCHK(P, launch_fill_zero(*p, bytes));
+      HIPCHK(P, launch_fill(*p, bytes, 0x01010101u * fill));
     }
   } else {
     hipError_t e = hipMalloc(p, bytes);
@@ -663,7 +664,7 @@ static cp_status alloc(cp_plan* P, void** p, size_t bytes, bool tagged = false) 
       return CP_ERR_OUT_OF_MEMORY;
     }
     P->allocs.push_back(*p);
-    HIPCHK(P, hipMemset(*p, 0, bytes));
+    HIPCHK(P, hipMemset(*p, fill, bytes));
   }
   P->scratch_bytes += (int64_t)bytes;
   if (tagged) {
@@ -886,14 +887,21 @@ static cp_status alloc_scratch(cp_plan* P) {
   void* p;
   const size_t e2 = (size_t)esz * 2;  // tagged words: payload + tag per element pair (bf16) or element (fp32)
   // Projection operands (position inputs, residuals, attention and SwiGLU
-  // outputs) are kept in the kernels' operand order, whole 16-row tiles.
+  // outputs): plain values in the kernels' operand order, whole 16-row tiles,
+  // a plane per layer and position, in one region that starts (and every
+  // frame ends) filled with the sentinel, all bits set.
   const size_t Rp = (size_t)((R + 15) / 16) * 16;
-  TRY(alloc(P, &p, (size_t)Pn * Rp * H * e2, true)); dp.xin = p;
-  TRY(alloc(P, &p, (size_t)2 * 2 * Rp * H * e2, true)); dp.hres = p;    // [parity][layer parity]
-  TRY(alloc(P, &p, (size_t)2 * Rp * H * e2, true)); dp.hmid = p;
+  const size_t hb = Rp * H * esz, ab = Rp * nq * d * esz, mb = Rp * I * esz, planes = (size_t)L * Pn;
+  const size_t opb = Pn * hb + 2 * planes * hb + planes * ab + planes * mb;
+  TRY(alloc(P, &p, opb, false, 0xff));
+  dp.opbuf = p;
+  dp.opbuf_bytes = opb;  // a multiple of 16: Rp is
+  dp.xin = p;
+  dp.hres = (uint8_t*)dp.xin + Pn * hb;
+  dp.hmid = (uint8_t*)dp.hres + planes * hb;
+  dp.abuf = (uint8_t*)dp.hmid + planes * hb;
+  dp.mbuf = (uint8_t*)dp.abuf + planes * ab;
   TRY(alloc(P, &p, (size_t)2 * R * nq * d * e2, true)); dp.qbuf = p;     // row-major (attention input)
-  TRY(alloc(P, &p, (size_t)2 * Rp * nq * d * e2, true)); dp.abuf = p;
-  TRY(alloc(P, &p, (size_t)2 * Rp * I * e2, true)); dp.mbuf = p;
   TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.kc = p;
   TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.vc = p;
   const size_t part_one = (size_t)(H / 16) * 4 * R * 16;  // words per split-K phase buffer
@@ -905,8 +913,8 @@ static cp_status alloc_scratch(cp_plan* P) {
   TRY(alloc(P, &p, (size_t)(Pn + 6) * R * (H / 16) * 8, true)); dp.ssq = (uint32_t*)p;
   TRY(alloc(P, &p, (size_t)R * V * 8, true)); dp.zbuf = (uint64_t*)p;
   TRY(alloc(P, &p, (size_t)R * (V / 16) * 16, true)); dp.cand = (uint64_t*)p;
-  TRY(alloc(P, &p, 128 * 4)); dp.state = (uint32_t*)p;
-  std::vector<uint32_t> st(128, 0);
+  TRY(alloc(P, &p, 256 * 4)); dp.state = (uint32_t*)p;
+  std::vector<uint32_t> st(256, 0);
   st[0] = 1;  // first frame is epoch 1; zeroed buffers carry tag 0, which no frame expects
   TRY(upload(P, dp.state, st.data(), st.size() * 4));
   const std::vector<DevTask> dev_tasks = to_dev(P->tasks, P->xcd_dealing), dev_phase = to_dev(P->phase_tasks, false);
@@ -1202,11 +1210,13 @@ cp_status cp_plan_set_epoch(cp_plan* P, uint32_t epoch) {
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(P->device);
-  // [0] epoch; [32] the persistent executor's done count, n_wg per finished frame
-  const uint32_t st[2] = {epoch, (uint32_t)P->dp.n_wg * (epoch - 1)};
+  // [0] epoch; [128], [160] the persistent executor's frame-end arrival
+  // counters, both zero before a frame whatever its epoch's parity
+  const uint32_t st[2] = {epoch, 0u};
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(P->dp.state, &st[0], 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(P->dp.state + 32, &st[1], 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(P->dp.state + 128, &st[1], 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(P->dp.state + 160, &st[1], 4, hipMemcpyHostToDevice);
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("set epoch: ") + hipGetErrorString(e));
   return CP_OK;

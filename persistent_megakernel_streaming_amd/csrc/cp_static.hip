@@ -18,17 +18,16 @@ namespace cpms {
 namespace {
 
 // Every scratch buffer of one static plan: activations, partial sums, the K/V
-// cache, the task lists and the plan state (about 66 MiB for the 5-layer bf16
-// depth loop at 64 rows).
+// cache, the task lists and the plan state.
 static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 void* g_addr[kMaxDevices];
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, uint64_t n) {
+__global__ __launch_bounds__(256) void fill_kernel(uint4* p, uint64_t n, uint32_t pattern) {
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
-    p[i] = uint4{0, 0, 0, 0};
+    p[i] = uint4{pattern, pattern, pattern, pattern};
 }
 
 }  // namespace
@@ -48,12 +47,13 @@ hipError_t static_scratch(int device, void** ptr, size_t* bytes) {
   return hipSuccess;
 }
 
-// Zeroes [p, p + bytes) (bytes a multiple of 16) with a kernel on the null
-// stream: static plans clear their scratch without hipMemset.
-hipError_t launch_fill_zero(void* p, size_t bytes) {
+// Fills [p, p + bytes) (bytes a multiple of 16) with a repeated 32-bit
+// pattern, with a kernel on the null stream: static plans initialise their
+// scratch without hipMemset.
+hipError_t launch_fill(void* p, size_t bytes, uint32_t pattern) {
   const uint64_t n = bytes / 16;
   const unsigned blocks = (unsigned)(n < 256 * 1024 ? (n + 255) / 256 : 1024);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks ? blocks : 1), dim3(256), 0, 0, (uint4*)p, n);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks ? blocks : 1), dim3(256), 0, 0, (uint4*)p, n, pattern);
   return hipGetLastError();
 }
 
