@@ -71,6 +71,12 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
 
 /* Plan flags. */
 #define CP_FLAG_TRACE 0x1u /* record eight timestamps per task (persistent executor; see cp_frame_io.trace) */
+/* Normed projections (qkv, gate/up, heads) start their K loop once their own
+ * operand units are in and wait for the row's norm partials (one from every
+ * producer tile) only before the epilogue, the per-chunk start of section
+ * "What's left in the frame, open" (first item).  Same results, bit for bit;
+ * measured slower on MI355X at 1 and 64 rows, so off by default. */
+#define CP_FLAG_LATE_NORM 0x2u
 
 /* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
  * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a

@@ -22,6 +22,7 @@ STATUS = {0: "CP_OK", 1: "CP_ERR_INVALID_ARGUMENT", 2: "CP_ERR_UNSUPPORTED", 3: 
 CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
 CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1
+CP_FLAG_LATE_NORM = 2
 ABI_VERSION = 2
 EPOCH_WRAP = (1 << 22) - 1  # epochs run 1 .. EPOCH_WRAP - 1
 

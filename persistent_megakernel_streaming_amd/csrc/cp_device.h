@@ -112,6 +112,7 @@ struct DevPlan {
   int n_wg;
   int n_tasks;
   int tasks_in_lds;             // every workgroup's list fits kTaskLds: the executor copies it to LDS
+  int late_norm;                // CP_FLAG_LATE_NORM: normed projections wait for norm partials after the K loop
   // task lists
   const DevTask* tasks;         // all tasks, grouped by workgroup
   const uint32_t* wg_begin;     // [n_wg + 1]

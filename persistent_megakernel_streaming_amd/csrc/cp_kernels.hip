@@ -588,6 +588,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   constexpr bool PART = KIND == T_O || KIND == T_DOWN || KIND == T_INPROJ;
   constexpr bool RESID = KIND == T_O || KIND == T_DOWN;
   constexpr int NU = 4;                     // 16-byte loads per lane per group of 4 chunks
+  constexpr int DEPTH = 4;                  // operand groups in flight per wave
   constexpr uint32_t CST = 64;              // frame-input bytes per chunk step
   // ONE: a frame of one row.  Only row 0 of the operand tile is loaded, its
   // 16-byte units packed densely over the lanes (one load instruction per 16
@@ -662,8 +663,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   auto uoff = [=](int g) {
     return [=](int u) -> uint32_t { return xoff + (uint32_t)(g * 4 + u) * (XLL ? 1024u : CST); };
   };
-  // Four groups in flight: xa, xb, xc, xd hold groups g = 0, 1, 2, 3 (mod 4).
-  u32x4 xa[NU], xb[NU], xc[NU], xd[NU];
+  // DEPTH groups in flight: set xs[s] holds groups g = s (mod DEPTH).
+  u32x4 xs[DEPTH][NU];
   auto load = [&](u32x4 (&x)[NU], int g) {
     if (g < ng) {
 #pragma unroll
@@ -693,10 +694,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
         for (int u = 0; u < NU; ++u) x[u] = XLL ? ld16c(rx, uoff(gg)(u)) : ld16(rx, uoff(gg)(u));
       };
-      load0(xa, 0);
-      load0(xb, 1);
-      load0(xc, 2);
-      load0(xd, 3);
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) load0(xs[s], s);
     }
   }
   // Sum-of-squares partials of a normalised operand (H/16 per row, written
@@ -737,29 +736,36 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // stay in flight.  A wave with no live rows issued no operand loads but
   // still copied its share of the tile, and waits for every load; so do
   // one-row frames and untagged operands.  (wave_live is wave-uniform.)
+  // (late: the plan waits for the norm partials after the K loop instead)
+  const bool late = NORM && pl.late_norm;
   if constexpr (ONE)
-    await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live, 1));
+    await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live && !late, 1));
   else
-    await_all(pl, spend<BF, ASM>(xa, rx, uoff(0), XLL && live), pend<ASM>(ssv, rs, sso, in_tag, NORM && live, nsq / 2));
-  if (XLL && !ONE && wave_live) wait_for(xa[0]);
+    await_all(pl, spend<BF, ASM>(xs[0], rx, uoff(0), XLL && live),
+              pend<ASM>(ssv, rs, sso, in_tag, NORM && live && !late, nsq / 2));
+  if (XLL && !ONE && wave_live) wait_for(xs[0][0]);
   else wait_vm();
   __syncthreads();
   stamp(tr, 2);
 
-  float rinv = 1.f;
-  if constexpr (NORM && ONE) {
-    float ss = lane < H / 32 ? __uint_as_float(ssv[0][0]) + __uint_as_float(ssv[0][2]) : 0.f;
-    wave_tree([&](auto other) { ss += __uint_as_float(other(__float_as_uint(ss))); });
-    rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
-  } else if constexpr (NORM) {
+  // 1 / rms(x) of this lane's row, from its norm partials
+  auto row_rinv = [&]() -> float {
     float ss = 0.f;
+    if constexpr (ONE) {
+      ss = lane < H / 32 ? __uint_as_float(ssv[0][0]) + __uint_as_float(ssv[0][2]) : 0.f;
+      wave_tree([&](auto other) { ss += __uint_as_float(other(__float_as_uint(ss))); });
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (2 * i < nsq) ss += __uint_as_float(ssv[i][0]) + __uint_as_float(ssv[i][2]);
-    ss += shfl_xor_f(ss, 16);
-    ss += shfl_xor_f(ss, 32);
-    rinv = 1.0f / sqrtf(ss / (float)H + pl.eps);
-  }
+      for (int i = 0; i < 8; ++i)
+        if (2 * i < nsq) ss += __uint_as_float(ssv[i][0]) + __uint_as_float(ssv[i][2]);
+      ss += shfl_xor_f(ss, 16);
+      ss += shfl_xor_f(ss, 32);
+    }
+    return 1.0f / sqrtf(ss / (float)H + pl.eps);
+  };
+  float rinv = 1.f;
+  if constexpr (NORM)
+    if (!late) rinv = row_rinv();
 
   const uint8_t* wt = slot + lane * 16 + (size_t)c0 * NB * 1024;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
@@ -814,18 +820,21 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + acc1[v];
     }
   } else if (wave_live) {
-    // Each set is refilled with the group four ahead right after its use, so
-    // three or four groups are always on their way.  The compiler's waits are
-    // in issue order: a set's wait then covers only the loads issued before
-    // it (its polling reloads are in asm; compiler-issued reloads made every
-    // set look like the newest loads and drained all of them at each group).
-    for (int g = 0; g < ng; g += 4) {
-      step(xa, g);
-      if (g == 0) stamp(tr, 3);
-      load(xa, g + 4);
-      if (g + 1 < ng) { step(xb, g + 1); load(xb, g + 5); }
-      if (g + 2 < ng) { step(xc, g + 2); load(xc, g + 6); }
-      if (g + 3 < ng) { step(xd, g + 3); load(xd, g + 7); }
+    // Each set is refilled with the group DEPTH ahead right after its use,
+    // so DEPTH - 1 or DEPTH groups are always on their way.  The compiler's
+    // waits are in issue order: a set's wait then covers only the loads
+    // issued before it (its polling reloads are in asm; compiler-issued
+    // reloads made every set look like the newest loads and drained all of
+    // them at each group).
+    for (int g = 0; g < ng; g += DEPTH) {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        if (s == 0 || g + s < ng) {
+          step(xs[s], g + s);
+          if (s == 0 && g == 0) stamp(tr, 3);
+          load(xs[s], g + s + DEPTH);
+        }
+      }
     }
     if constexpr (NB == 1) {
 #pragma unroll
@@ -852,6 +861,16 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           for (int v = 0; v < 4; ++v) acc1[v] = acc1[v] + b[v];
         }
       }
+    }
+  }
+  if constexpr (NORM) {
+    if (late) {
+      // The norm partials of the row (every producer tile's) are needed only
+      // now: the K loop started as soon as this wave's own operand units were
+      // in.  (ks == 0: the waves that store the tile.)
+      if constexpr (ONE) await_all(pl, pend(ssv, rs, sso, in_tag, wave_live && ks == 0, 1));
+      else await_all(pl, pend<ASM>(ssv, rs, sso, in_tag, live && ks == 0, nsq / 2));
+      rinv = row_rinv();
     }
   }
   if constexpr (NORM) {  // W (g . x / rms(x)) = (W g) x / rms(x): the gain is in the packed tile

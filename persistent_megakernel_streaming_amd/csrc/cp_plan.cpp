@@ -272,7 +272,7 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   // an o split (n_q_heads / 4 heads) must read at most kMaxWaits kv heads
   const int gq = c->n_q_heads / c->n_kv_heads, hps = c->n_q_heads / 4;
   if ((hps - 1) / gq + 2 > kMaxWaits && hps / gq > kMaxWaits) { msg = "kv grouping not supported"; return CP_ERR_UNSUPPORTED; }
-  if (c->flags & ~CP_FLAG_TRACE) { msg = "unknown flag"; return CP_ERR_UNSUPPORTED; }
+  if (c->flags & ~(CP_FLAG_TRACE | CP_FLAG_LATE_NORM)) { msg = "unknown flag"; return CP_ERR_UNSUPPORTED; }
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) { msg = "rms_eps / rope_theta"; return CP_ERR_INVALID_ARGUMENT; }
   return CP_OK;
 }
@@ -1028,6 +1028,7 @@ static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights*
   TRY(pack_weights(P, w));
   TRY(check_schedule(P));
   dp.tasks_in_lds = (int64_t)P->max_tasks_wg * (int64_t)sizeof(DevTask) <= kTaskLds;
+  dp.late_norm = (cfg->flags & CP_FLAG_LATE_NORM) ? 1 : 0;
   TRY(alloc_scratch(P));
   HIPCHK(P, hipDeviceSynchronize());
   return CP_OK;

@@ -38,9 +38,9 @@ def _weights(cfg, seed=0, gain_jitter=False):
     return _cache[key]
 
 
-def _gpu_frame(cfg, wdev, inputs, exec_mode="persistent", max_rows=None, rows=None, kv=False):
+def _gpu_frame(cfg, wdev, inputs, exec_mode="persistent", max_rows=None, rows=None, kv=False, flags=0):
     cp = _cp()
-    plan = cp.Plan(cfg, wdev, exec_mode=exec_mode, max_rows=max_rows or inputs["rows"])
+    plan = cp.Plan(cfg, wdev, exec_mode=exec_mode, max_rows=max_rows or inputs["rows"], flags=flags)
     io = cp.make_io(cfg, inputs, rows=rows, kv=kv)
     plan.run(io)
     torch.cuda.synchronize()
@@ -170,6 +170,24 @@ def test_persistent_equals_per_phase_bitwise():
     b = _gpu_frame(cfg, wdev, inputs, "per_phase", max_rows=64, kv=True)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("rows,exec_mode", [(1, "persistent"), (40, "persistent"), (64, "persistent"),
+                                           (13, "per_phase")])
+def test_late_norm_wait_equals_default_bitwise(rows, exec_mode):
+    """CP_FLAG_LATE_NORM (normed projections wait for the row's norm partials
+    after the K loop, not before it) changes when a task waits, never what it
+    computes: every output equals the default plan's, bit for bit."""
+    cp = _cp()
+    cfg = synth.CONFIGS["l5_r64"]
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg, rows=rows, seed=21)
+    a = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=rows, kv=True)
+    b = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=rows, kv=True, flags=cp.CP_FLAG_LATE_NORM)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    if rows == 64:
+        _check(cfg, ow, inputs, b, range(0, 64, 9), 0.05, kv=True)
 
 
 def test_one_row_frame_on_64_row_plan():
