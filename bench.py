@@ -289,7 +289,7 @@ def main():
     import torch
     from persistent_megakernel_streaming_amd import cp, synth
 
-    everything = {"p64", "p1", "s64", "pp64", "pp1", "late", "l10", "floor", "chain", "cold", "pct"}
+    everything = {"p64", "p1", "s64", "pp64", "pp1", "late", "cross", "l10", "floor", "chain", "cold", "pct"}
     only = set(args.only.split(",")) if args.only else everything
     steps, warm, reps = args.steps, args.warmup, args.repeats
     cfg64 = synth.CONFIGS["l5_r64"]
@@ -341,6 +341,22 @@ def main():
             io = cp.make_io(c, synth.make_inputs(c), logits=False)
             res[f"late_norm_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
             pl.close()
+    if "cross" in only:
+        # the row-count crossover: persistent frame against the per-phase
+        # loop (captured as a graph) on one plan, rows 1 .. 64
+        pl = cp.Plan(cfg64, wdev, exec_mode="persistent", max_rows=64)
+        cross = {}
+        for r in (1, 2, 4, 8, 16, 32, 64):
+            io = cp.make_io(cfg64, synth.make_inputs(cfg64, rows=r), logits=False)
+            pl.set_crossover(0)
+            a = _time_frames(pl, io, 40, 5, 3)[0]
+            pl.set_crossover(r + 1)
+            b = _time_frames(pl, io, 40, 5, 3, graph=True)[0]
+            cross[r] = {"persistent_us": a, "per_phase_graph_us": b}
+        pl.set_crossover(0)
+        pl.close()
+        slower = [r for r, v in cross.items() if v["persistent_us"] >= v["per_phase_graph_us"]]
+        extra["crossover"] = {"by_rows": cross, "rows_where_per_phase_wins": slower}
     for tag, c, mr in (("pp64", cfg64, 64), ("pp1", cfg1, 1)):
         if tag in only:
             pp = cp.Plan(c, wdev, exec_mode="per_phase", max_rows=mr)

@@ -274,6 +274,20 @@ cp_status cp_plan_set_epoch(cp_plan* plan, uint32_t epoch);
  * forces it without any wait having to hang.  Touches no device. */
 cp_status cp_plan_set_spin_limit(cp_plan* plan, uint32_t polls);
 
+/* Row-count crossover dispatch (mstar pull request #1183, section "Cost": the
+ * frame costs about the same at any row count and lost to the unfused loop
+ * at 1 row on H200, so small steps should run the loop once the crossover is
+ * measured).  Frames of a persistent plan with fewer than `rows` rows then
+ * run the per-phase executor on the same buffers and task bodies (results
+ * bit for bit as the persistent executor's); 0 (the default) keeps every
+ * frame persistent.  On MI355X the persistent frame is measured faster at
+ * every row count from 1 to 64, so the default stays 0.  CP_ERR_INVALID_ARGUMENT
+ * for rows outside 0 .. max_rows + 1; CP_ERR_UNSUPPORTED for a per-phase
+ * plan or a schedule whose split-K phases need more workgroups than the
+ * device holds at once.  A traced frame (cp_frame_io.trace) below the
+ * crossover is refused.  Touches no device. */
+cp_status cp_plan_set_crossover(cp_plan* plan, int rows);
+
 const char* cp_status_string(cp_status s);
 
 /* Text of the last error recorded on the plan ("" if none). */

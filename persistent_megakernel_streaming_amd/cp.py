@@ -82,11 +82,12 @@ def load_library():
     lib.cp_plan_task_table.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
     lib.cp_plan_set_epoch.argtypes = [C.c_void_p, C.c_uint32]
     lib.cp_plan_set_spin_limit.argtypes = [C.c_void_p, C.c_uint32]
+    lib.cp_plan_set_crossover.argtypes = [C.c_void_p, C.c_int]
     lib.cp_stream_read.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]
     lib.cp_chain_run.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     for f in ("cp_plan_create", "cp_plan_create_static", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
               "cp_schedule_check", "cp_plan_task_table", "cp_plan_set_epoch", "cp_plan_set_spin_limit",
-              "cp_stream_read", "cp_chain_run"):
+              "cp_plan_set_crossover", "cp_stream_read", "cp_chain_run"):
         getattr(lib, f).restype = C.c_int
     return lib
 
@@ -236,6 +237,11 @@ class Plan:
         """Bounds every device-side wait of later frames to ``polls`` reloads
         (0: the default); exercises the time-out path."""
         self._check(_lib.cp_plan_set_spin_limit(self._h, int(polls)))
+
+    def set_crossover(self, rows: int):
+        """Frames with fewer than ``rows`` rows run the per-phase executor
+        (0: every frame persistent)."""
+        self._check(_lib.cp_plan_set_crossover(self._h, int(rows)))
 
     def device_status(self):
         self._check(_lib.cp_plan_device_status(self._h))

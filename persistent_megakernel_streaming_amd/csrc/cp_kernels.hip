@@ -1839,6 +1839,12 @@ __global__ __launch_bounds__(kThreads, 1) void refill_operands_kernel(DevPlan pl
   refill_operands(pl, blockIdx.x, gridDim.x);
 }
 __global__ __launch_bounds__(kThreads, 1) void bump_epoch_kernel(DevPlan pl, int defer) {
+  // (a plan may run its next frame on the persistent executor, whose
+  // arrival counters must then be zero whatever the epoch's parity)
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(pl.state + 128, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(pl.state + 160, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   advance_epoch(pl, __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), defer != 0);
 }
 

@@ -56,6 +56,7 @@ struct cp_plan {
   std::vector<CtrGroup> groups;
   uint32_t n_ctr = 0;
   int n_phases = 0;
+  int crossover = 0;  // frames with fewer rows run the per-phase executor
   int max_tasks_wg = 0;
   bool xcd_dealing = false;             // persistent workgroup i runs on XCD i % 8 (checked on the device)
   DevTask* d_phase_tasks = nullptr;
@@ -1149,7 +1150,9 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
                     (io->seed != nullptr) + (io->offset != nullptr);
   if (nsamp != 0 && nsamp != 5) return fail(P, CP_ERR_INVALID_ARGUMENT, "sampling arrays must be all set or all NULL");
   if (io->trace && !(c.flags & CP_FLAG_TRACE)) return fail(P, CP_ERR_INVALID_ARGUMENT, "trace needs CP_FLAG_TRACE");
-  if (io->trace && c.exec != CP_EXEC_PERSISTENT) return fail(P, CP_ERR_UNSUPPORTED, "trace needs the persistent executor");
+  // rows below the crossover run the per-phase executor (same buffers, same task bodies)
+  const bool persistent = c.exec == CP_EXEC_PERSISTENT && io->rows >= P->crossover;
+  if (io->trace && !persistent) return fail(P, CP_ERR_UNSUPPORTED, "trace needs the persistent executor");
   DevFrame fr{};
   fr.rows = io->rows;
   fr.sampled = nsamp == 5;
@@ -1170,7 +1173,7 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
   (void)hipGetDevice(&prev);
   if (prev != P->device) HIPCHK(P, hipSetDevice(P->device));
   hipError_t e = hipSuccess;
-  if (c.exec == CP_EXEC_PERSISTENT) {
+  if (persistent) {
     e = launch_persistent(P->dp, fr, s);
   } else {
     for (int ph = 0; ph < P->n_phases && e == hipSuccess; ++ph) {
@@ -1220,6 +1223,20 @@ cp_status cp_plan_set_epoch(cp_plan* P, uint32_t epoch) {
   if (e == hipSuccess) e = hipMemcpy(P->dp.state + 160, &st[1], 4, hipMemcpyHostToDevice);
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(P, CP_ERR_HIP, std::string("set epoch: ") + hipGetErrorString(e));
+  return CP_OK;
+}
+
+cp_status cp_plan_set_crossover(cp_plan* P, int rows) {
+  if (!P) return CP_ERR_INVALID_ARGUMENT;
+  if (rows < 0 || rows > P->cfg.max_rows + 1) return fail(P, CP_ERR_INVALID_ARGUMENT, "crossover rows out of range");
+  if (rows > 0 && P->cfg.exec != CP_EXEC_PERSISTENT) return fail(P, CP_ERR_UNSUPPORTED, "crossover needs a persistent plan");
+  // per-phase launches hold a phase's split-K partners and owner at once
+  for (size_t ph = 0; rows > 0 && ph + 1 < P->phase_begin.size(); ++ph) {
+    const Task& f = P->phase_tasks[P->phase_begin[ph]];
+    if (f.nsplit > 1 && (int)(P->phase_begin[ph + 1] - P->phase_begin[ph]) > P->cu_count)
+      return fail(P, CP_ERR_UNSUPPORTED, "schedule: split phase larger than the grid");
+  }
+  P->crossover = rows;
   return CP_OK;
 }
 

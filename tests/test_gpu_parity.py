@@ -190,6 +190,36 @@ def test_late_norm_wait_equals_default_bitwise(rows, exec_mode):
         _check(cfg, ow, inputs, b, range(0, 64, 9), 0.05, kv=True)
 
 
+def test_crossover_dispatch_runs_small_frames_per_phase():
+    """cp_plan_set_crossover: frames under the crossover run the per-phase
+    executor on the persistent plan's buffers, interleaved with persistent
+    frames; every frame equals a plain persistent plan's bit for bit."""
+    cp = _cp()
+    cfg = synth.CONFIGS["l5_r64"]
+    w, wdev, ow = _weights(cfg)
+    plan = cp.Plan(cfg, wdev, exec_mode="persistent", max_rows=16)
+    with pytest.raises(cp.CpError) as e:
+        plan.set_crossover(18)
+    assert e.value.status == cp.CP_ERR_INVALID_ARGUMENT
+    plan.set_crossover(9)
+    for rows, seed in ((4, 30), (16, 31), (1, 32), (4, 33), (16, 34)):
+        inputs = synth.make_inputs(cfg, rows=rows, seed=seed)
+        io = cp.make_io(cfg, inputs, kv=True)
+        plan.run(io)
+        torch.cuda.synchronize()
+        plan.device_status()
+        got = {k: v.cpu().numpy() for k, v in io.items() if k != "rows"}
+        ref = _gpu_frame(cfg, wdev, inputs, "persistent", max_rows=16, kv=True)
+        for k in ref:
+            assert np.array_equal(ref[k], got[k]), (rows, k)
+    plan.close()
+    pp = cp.Plan(cfg, wdev, exec_mode="per_phase", max_rows=4)
+    with pytest.raises(cp.CpError) as e:
+        pp.set_crossover(2)
+    assert e.value.status == cp.CP_ERR_UNSUPPORTED
+    pp.close()
+
+
 def test_one_row_frame_on_64_row_plan():
     """A one-row frame runs the one-row kernels (row 0 of each operand tile
     loaded densely and handed out with ds_bpermute) on a plan built for 64
