@@ -289,7 +289,7 @@ def main():
     import torch
     from persistent_megakernel_streaming_amd import cp, synth
 
-    everything = {"p64", "p1", "s64", "pp64", "pp1", "late", "cross", "l10", "floor", "chain", "cold", "pct"}
+    everything = {"p64", "p1", "s64", "pp64", "pp1", "late", "cross", "qk", "l10", "floor", "chain", "cold", "pct"}
     only = set(args.only.split(",")) if args.only else everything
     steps, warm, reps = args.steps, args.warmup, args.repeats
     cfg64 = synth.CONFIGS["l5_r64"]
@@ -341,6 +341,17 @@ def main():
             io = cp.make_io(c, synth.make_inputs(c), logits=False)
             res[f"late_norm_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
             pl.close()
+    if "qk" in only:
+        # the QK-norm variant (RMSNorm of every q and k head before RoPE)
+        cq = synth.CONFIGS["l5_qk_r64"]
+        wq = cp.upload_weights(cq, synth.make_weights(cq))
+        for mr in (64, 1):
+            c = cq.with_(rows=mr)
+            pl = cp.Plan(c, wq, exec_mode="persistent", max_rows=mr)
+            io = cp.make_io(c, synth.make_inputs(c), logits=False)
+            res[f"qk_norm_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
+            pl.close()
+        del wq
     if "cross" in only:
         # the row-count crossover: persistent frame against the per-phase
         # loop (captured as a graph) on one plan, rows 1 .. 64

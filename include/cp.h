@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CP_ABI_VERSION 2
+#define CP_ABI_VERSION 3
 
 typedef enum {
   CP_OK = 0,
@@ -102,6 +102,10 @@ typedef struct {
   float rope_theta;     /* RoPE base, e.g. 1e4 */
   int32_t exec;         /* cp_exec */
   uint32_t flags;       /* CP_FLAG_* */
+  int32_t qk_norm;      /* nonzero: the Qwen3-style variant, an RMSNorm of every q and k head (over
+                           head_dim, gains cp_weights.q_norm / k_norm, the same epsilon) between
+                           the qkv projection and RoPE; the handbook page "The gaps between kernels:
+                           PDL and megakernels" lists it fused with RoPE (section on fusing kernels) */
 } cp_config;
 
 /* Weights of the code predictor (section "Cost": hidden 1024, 16 q and 8 kv
@@ -122,6 +126,8 @@ typedef struct {
   const void* const* w_down;      /* n_layers x [hidden][intermediate] */
   const void* final_norm;         /* [hidden] */
   const void* const* w_head;      /* (n_positions - 1) x [vocab][hidden]; entry j-1 is head j */
+  const void* const* q_norm;      /* n_layers x [head_dim] (qk_norm only, else ignored) */
+  const void* const* k_norm;      /* n_layers x [head_dim] (qk_norm only, else ignored) */
 } cp_weights;
 
 /* One frame's inputs and outputs (section "Testing": codes and embedding

@@ -230,6 +230,22 @@ static void rmsnorm(const orc_cfg *c, const float *h, const float *g, float *out
   }
 }
 
+/* Head norm of the QK-norm variant (the per-head RMSNorm of q and k that
+   Qwen3-style attention applies before RoPE; the handbook page "The gaps
+   between kernels: PDL and megakernels" lists it fused with RoPE in one
+   kernel): over one head's d values, the same float products as rmsnorm, in
+   float, with no bf16 rounding (the head is rounded once, after RoPE). */
+static void headnorm(const orc_cfg *c, float *x, const float *g) {
+  const int d = c->head_dim;
+  double ss = 0.0;
+  for (int i = 0; i < d; ++i) ss += (double)x[i] * (double)x[i];
+  float r = (float)(1.0 / sqrt(ss / (double)d + c->rms_eps));
+  for (int i = 0; i < d; ++i) {
+    float t = x[i] * r;
+    x[i] = t * g[i];
+  }
+}
+
 int32_t orc_stage_width(const orc_cfg *c) {
   int32_t wd = c->hidden;
   const int32_t qkv = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
@@ -258,6 +274,7 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
     return -2;
   if (R == 0) return 0;
   if (!fr->hidden_in || !fr->code0 || !fr->codes || !fr->embsum) return -3;
+  if (c->qk_norm && (!w->q_norm || !w->k_norm)) return -3;
   const int sampled = fr->temperature != NULL;
   if (sampled && !(fr->top_k && fr->top_p && fr->seed && fr->offset_in)) return -4;
   for (int r = 0; r < R; ++r)
@@ -332,13 +349,15 @@ int orc_frame_run(const orc_cfg *c, const orc_weights *w, orc_frame *fr) {
           qkv[(size_t)r * QKV + n] = (float)dot(wqkv + (size_t)n * H, a + (size_t)r * H, H);
       record(c, fr, p, l, ORC_ST_QKV_RAW, qkv, QKV, QKV);
 
-      /* RoPE at position p on every q and k head (pairs i, i + d/2), then the
+      /* QK-norm variant: each q head and k head normed on its own; then RoPE
+         at position p on every q and k head (pairs i, i + d/2), then the
          stored Q, K, V. */
 #pragma omp parallel for schedule(static) num_threads(nt)
       for (int r = 0; r < R; ++r) {
         float *row = qkv + (size_t)r * QKV;
         for (int hd = 0; hd < nq + nkv; ++hd) {
           float *x = row + (size_t)hd * d;
+          if (c->qk_norm) headnorm(c, x, (hd < nq ? w->q_norm : w->k_norm) + (size_t)l * d);
           for (int i = 0; i < half; ++i) {
             double x1 = x[i], x2 = x[i + half], co = cs[p * half + i], si = sn[p * half + i];
             double y1 = x1 * co - x2 * si, y2 = x2 * co + x1 * si;

@@ -38,6 +38,7 @@ typedef struct {
   int32_t bf16;          /* nonzero: round activations to bf16 at the storage points */
   double rms_eps;        /* RMSNorm epsilon */
   double rope_theta;     /* RoPE base */
+  int32_t qk_norm;       /* nonzero: RMSNorm of every q and k head (gains q_norm, k_norm) before RoPE */
 } orc_cfg;
 
 /* Weights as float values (bf16 weights widened exactly), row-major [out][in]. */
@@ -53,6 +54,8 @@ typedef struct {
   const float *w_down;     /* [L][hidden][inter] */
   const float *final_norm; /* [hidden] */
   const float *w_head;     /* [P-1][vocab][hidden]; head j (position j) at index j-1 */
+  const float *q_norm;     /* [L][head_dim] (qk_norm only) */
+  const float *k_norm;     /* [L][head_dim] (qk_norm only) */
 } orc_weights;
 
 typedef struct {
@@ -89,7 +92,7 @@ typedef struct {
 enum {
   ORC_ST_H_IN = 0,   /* the layer's input residual row [hidden] */
   ORC_ST_A,          /* attention RMSNorm output [hidden] */
-  ORC_ST_QKV_RAW,    /* W_qkv . a as float, before RoPE [(nq + 2 nkv) d] */
+  ORC_ST_QKV_RAW,    /* W_qkv . a as float, before the head norms and RoPE [(nq + 2 nkv) d] */
   ORC_ST_QKV,        /* q, k, v after RoPE, as stored [(nq + 2 nkv) d] */
   ORC_ST_ATT,        /* attention output as stored [nq d] */
   ORC_ST_H_MID,      /* residual after o, as stored [hidden] */

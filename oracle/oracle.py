@@ -55,7 +55,7 @@ class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "hidden", "input_dim", "n_q_heads",
                                           "n_kv_heads", "head_dim", "intermediate",
                                           "n_positions", "vocab", "bf16")] + [
-        ("rms_eps", C.c_double), ("rope_theta", C.c_double)]
+        ("rms_eps", C.c_double), ("rope_theta", C.c_double), ("qk_norm", C.c_int32)]
 
 
 _FP = C.POINTER(C.c_float)
@@ -66,7 +66,7 @@ _DP = C.POINTER(C.c_double)
 
 class _Weights(C.Structure):
     _fields_ = [(n, _FP) for n in ("w_in", "embed", "attn_norm", "w_qkv", "w_o", "mlp_norm",
-                                   "w_gate", "w_up", "w_down", "final_norm", "w_head")]
+                                   "w_gate", "w_up", "w_down", "final_norm", "w_head", "q_norm", "k_norm")]
 
 
 class _Frame(C.Structure):
@@ -127,6 +127,9 @@ class OracleWeights:
             "final_norm": _widen(w["final_norm"], bf),
             "w_head": np.stack([_widen(w[f"w_head.{j}"], bf) for j in range(1, P)]),
         }
+        if getattr(cfg, "qk_norm", False):
+            self.arrays["q_norm"] = np.stack([_widen(w[f"q_norm.{l}"], bf) for l in range(L)])
+            self.arrays["k_norm"] = np.stack([_widen(w[f"k_norm.{l}"], bf) for l in range(L)])
         self.arrays = {k: np.ascontiguousarray(v, np.float32) for k, v in self.arrays.items()}
         self.c = _Weights(**{k: _ptr(v, _FP) for k, v in self.arrays.items()})
 
@@ -136,7 +139,7 @@ def _cfg(cfg):
                 n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim,
                 intermediate=cfg.intermediate, n_positions=cfg.n_positions, vocab=cfg.vocab,
                 bf16=1 if cfg.dtype == "bf16" else 0, rms_eps=cfg.rms_eps,
-                rope_theta=cfg.rope_theta)
+                rope_theta=cfg.rope_theta, qk_norm=1 if getattr(cfg, "qk_norm", False) else 0)
 
 
 def run_frame(cfg, weights, inputs: dict, forced_codes=None, keep_kv: bool = False,

@@ -23,7 +23,7 @@ CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
 CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1
 CP_FLAG_LATE_NORM = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 EPOCH_WRAP = (1 << 22) - 1  # epochs run 1 .. EPOCH_WRAP - 1
 
 _VP = C.c_void_p
@@ -33,14 +33,16 @@ class Config(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("abi_version", "n_layers", "hidden", "input_dim", "n_q_heads",
                                           "n_kv_heads", "head_dim", "intermediate", "n_positions", "vocab",
                                           "max_rows", "dtype")] + [
-        ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("exec", C.c_int32), ("flags", C.c_uint32)]
+        ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("exec", C.c_int32), ("flags", C.c_uint32),
+        ("qk_norm", C.c_int32)]
 
 
 class Weights(C.Structure):
     _fields_ = [("w_in", _VP), ("embed", C.POINTER(_VP)), ("attn_norm", C.POINTER(_VP)),
                 ("w_qkv", C.POINTER(_VP)), ("w_o", C.POINTER(_VP)), ("mlp_norm", C.POINTER(_VP)),
                 ("w_gate", C.POINTER(_VP)), ("w_up", C.POINTER(_VP)), ("w_down", C.POINTER(_VP)),
-                ("final_norm", _VP), ("w_head", C.POINTER(_VP))]
+                ("final_norm", _VP), ("w_head", C.POINTER(_VP)), ("q_norm", C.POINTER(_VP)),
+                ("k_norm", C.POINTER(_VP))]
 
 
 class FrameIO(C.Structure):
@@ -107,7 +109,8 @@ def make_config(cfg, max_rows=None, exec_mode="persistent", flags=0) -> Config:
                   max_rows=cfg.rows if max_rows is None else max_rows,
                   dtype=CP_DTYPE_BF16 if cfg.dtype == "bf16" else CP_DTYPE_F32,
                   rms_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
-                  exec=CP_EXEC_PER_PHASE if exec_mode == "per_phase" else CP_EXEC_PERSISTENT, flags=flags)
+                  exec=CP_EXEC_PER_PHASE if exec_mode == "per_phase" else CP_EXEC_PERSISTENT, flags=flags,
+                  qk_norm=1 if getattr(cfg, "qk_norm", False) else 0)
 
 
 def schedule_check(cfg, cu_count=256, max_rows=None):
@@ -187,6 +190,10 @@ class Plan:
                            ("w_head", [f"w_head.{j}" for j in range(1, P)])):
             fields[key], a = arr(names)
             keep.append(a)
+        if getattr(cfg, "qk_norm", False):
+            for key in ("q_norm", "k_norm"):
+                fields[key], a = arr([f"{key}.{l}" for l in range(L)])
+                keep.append(a)
         self._w = Weights(w_in=weights["w_in"].data_ptr(), final_norm=weights["final_norm"].data_ptr(), **fields)
         h = C.c_void_p()
         if weight_arena is None:

@@ -122,6 +122,8 @@ struct DevPlan {
   const uint8_t* wblob;         // packed projection tiles
   const void* embed;            // [P][V][H]
   const float* rope;            // [P][d/2][2]: cos, sin
+  const float* qk_gain;         // QK-norm: [L][q, k][d] head-norm gains (else null)
+  int qk_norm;                  // the QK-norm variant
   // activations and scratch (act = dtype)
   // The buffers a projection reads (position inputs, residuals, attention
   // and SwiGLU outputs) hold plain activations in the kernels' operand order
@@ -141,6 +143,8 @@ struct DevPlan {
   uint64_t opbuf_bytes;
   void* qbuf;                   // [2][Rmax][nq d] rotated q, row-major, tagged
   void* kc;                     // [L][Rmax][nkv][P][d]
+  void* kraw;                   // QK-norm: [2][Rmax][nkv][d] K before its head norm, right after kc
+  uint64_t* qkn;                // QK-norm: [2][Rmax][nq + nkv][d/16] per-tile sums of squares of q, k heads
   void* vc;
   uint64_t* part;               // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16] words
   uint32_t* ssq;                // [P + 6][Rmax][H/16] words: sum-of-squares partials of residual rows

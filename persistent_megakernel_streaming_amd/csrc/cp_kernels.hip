@@ -201,6 +201,17 @@ __device__ __forceinline__ bool ll_ok(const u32x4& v, uint32_t tag) { return v[1
 // Tagged pair of payload words for a 16-byte store.
 __device__ __forceinline__ u32x4 ll_pair(uint32_t p0, uint32_t p1, uint32_t tag) { return u32x4{p0, tag, p1, tag}; }
 
+// The payloads of a 16-byte pair of tagged words times s, in the activation
+// type (bf16: each value rounded to nearest even); tags kept.
+template <int BF>
+__device__ __forceinline__ u32x4 scale_pair(const u32x4& v, float s) {
+  if constexpr (BF)
+    return u32x4{pack_bf16(bf2f(v[0] & 0xffffu) * s, bf2f(v[0] >> 16) * s), v[1],
+                 pack_bf16(bf2f(v[2] & 0xffffu) * s, bf2f(v[2] >> 16) * s), v[3]};
+  else
+    return u32x4{__float_as_uint(__uint_as_float(v[0]) * s), v[1], __float_as_uint(__uint_as_float(v[2]) * s), v[3]};
+}
+
 // ------------------------------------------------------------------ sentinel operands
 
 // Operand buffers hold plain values; an element not yet written this frame
@@ -987,18 +998,48 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           const bool isq = lt < gq * th;
           const int hq = g * gq + lt / th;
           const int i0 = 8 * tih + 2 * q;
+          // QK-norm: the head's RMSNorm scales it by one number, 1 / rms of
+          // the whole head, which RoPE (a rotation of pairs) commutes with.
+          // The tile applies the gains and RoPE and stores the head unscaled
+          // (K in a staging buffer), with its 16 dims' sum of squares; the
+          // attention task adds the head's partials and scales.
+          const bool qkn = pl.qk_norm;
+          float xg[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) xg[v] = acc0[v];
+          if (qkn) {
+            float ss = ((acc0[0] * acc0[0] + acc0[1] * acc0[1]) + acc0[2] * acc0[2]) + acc0[3] * acc0[3];
+            ss += shfl_xor_f(ss, 16);
+            ss += shfl_xor_f(ss, 32);
+            const float* gn = pl.qk_gain + ((size_t)l * 2 + (isq ? 0 : 1)) * d;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              xg[2 * pr] = acc0[2 * pr] * gn[i0 + pr];
+              xg[2 * pr + 1] = acc0[2 * pr + 1] * gn[i0 + pr + d / 2];
+            }
+            const int nh = pl.nq + nkv;
+            const uint32_t nbytes = (uint32_t)2 * Rmax * nh * th * 8;
+            if (q == 0)
+              st8x(make_rsrc(pl.qkn, nbytes), (uint32_t)((((par * Rmax + row) * nh + (isq ? hq : pl.nq + g)) * th + tih) * 8),
+                   u32x2{__float_as_uint(ss), my_tag}, lqkv);
+          }
           float y[4];
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
-            const float x1 = acc0[2 * pr], x2 = acc0[2 * pr + 1];
+            const float x1 = xg[2 * pr], x2 = xg[2 * pr + 1];
             y[2 * pr] = x1 * rope_cs[pr] - x2 * rope_sn[pr];
             y[2 * pr + 1] = x2 * rope_cs[pr] + x1 * rope_sn[pr];
           }
           // dims i0, i0 + 1 (first halves) and i0 + d/2, i0 + d/2 + 1 (second halves)
           const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * d * ESZ * 2;
-          const rsrc_t r = isq ? make_rsrc((uint8_t*)pl.qbuf + (size_t)par * qdbytes, qdbytes) : make_rsrc(pl.kc, kvbytes);
-          const uint32_t base = isq ? (uint32_t)(row * pl.nq * d + hq * d) : kvoff;
-          const uint32_t tg = isq ? my_tag : kv_tag;
+          const uint32_t kvelems = (uint32_t)pl.L * Rmax * nkv * P * d;
+          const uint32_t krbytes = qkn ? (uint32_t)2 * Rmax * nkv * d * ESZ * 2 : 0u;
+          const rsrc_t r = isq ? make_rsrc((uint8_t*)pl.qbuf + (size_t)par * qdbytes, qdbytes)
+                               : make_rsrc(pl.kc, kvbytes + krbytes);
+          // (QK-norm: K before its scale goes to the staging buffer behind the cache)
+          const uint32_t base = isq ? (uint32_t)(row * pl.nq * d + hq * d)
+                                    : (qkn ? kvelems + (uint32_t)(((par * Rmax + row) * nkv + g) * d) : kvoff);
+          const uint32_t tg = (isq || qkn) ? my_tag : kv_tag;
           if constexpr (BF) {
             st8x(r, (base + i0) * 4, u32x2{pack_bf16(y[0], y[2]), tg}, lqkv);
             st8x(r, (base + i0 + d / 2) * 4, u32x2{pack_bf16(y[1], y[3]), tg}, lqkv);
@@ -1081,7 +1122,13 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
   const uint32_t qdbytes = (uint32_t)Rmax * pl.nq * d * ESZ * 2;
   const rsrc_t rq = make_rsrc((uint8_t*)pl.qbuf + (size_t)(p & 1) * qdbytes, qdbytes);
   const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
-  const rsrc_t rk = make_rsrc(pl.kc, kvbytes), rv = make_rsrc(pl.vc, kvbytes);
+  // QK-norm: this position's K comes unscaled from the staging buffer behind
+  // the cache, with the per-tile sums of squares of the q and k heads
+  const bool qkn = pl.qk_norm;
+  const uint32_t krbytes = qkn ? (uint32_t)2 * Rmax * nkv * d * ESZ * 2 : 0u;
+  const rsrc_t rk = make_rsrc(pl.kc, kvbytes + krbytes), rv = make_rsrc(pl.vc, kvbytes);
+  const int th = d / 16, nh = pl.nq + nkv;
+  const rsrc_t rn = make_rsrc(pl.qkn, qkn ? (uint32_t)2 * Rmax * nh * th * 8 : 0u);
   const uint32_t abytes = sop_bytes<BF>(Rmax, pl.nq * d);  // attention output, operand order for o
   const rsrc_t ra = make_rsrc((uint8_t*)pl.abuf + (size_t)(l * P + p) * abytes, abytes);
   const uint32_t q_tag = tag_of(epoch, tk.ph_in0), kv_tag = tag_of(epoch, kKvPhase);
@@ -1101,15 +1148,34 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     const uint32_t q0 = ((uint32_t)(row * pl.nq * d + hq * d + c * dq)) * ESZ * 2;
     const uint32_t k0 = ((uint32_t)((kvrow + t) * d + c * dq)) * ESZ * 2;
     auto qo = [=](int i) { return q0 + i * 16; };
-    auto ko = [=](int i) { return k0 + i * 16; };
     // (loads without branches: units past nld repeat the last one and
     // positions past p read position p; neither is part of the wait)
     const uint32_t kclamp = (uint32_t)(min(t, p) - t) * (uint32_t)(d * ESZ * 2);
+    // QK-norm: position p (and the clamped lanes past it) read the staging
+    // buffer, written by the qkv phase with its tag
+    const bool rawk = qkn && t >= p;
+    const uint32_t kr0 = kvbytes + ((uint32_t)((((p & 1) * Rmax + row) * nkv + g) * d + c * dq)) * ESZ * 2;
+    auto ko = [=](int i) { return rawk ? kr0 + i * 16 : k0 + kclamp + i * 16; };
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int iu = i < nld ? i : nld - 1;
       qv[i] = ld16c(rq, qo(iu));
-      kv[i] = ld16c(rk, ko(iu) + kclamp);
+      kv[i] = ld16c(rk, ko(iu));
+    }
+    // QK-norm: the head's per-tile sums of squares, q head hq and kv head g
+    // (every lane the same words)
+    u32x4 qs[4] = {}, ks[4] = {};
+    const uint32_t qn0 = (uint32_t)((((p & 1) * Rmax + row) * nh + hq) * th) * 8;
+    const uint32_t kn0 = (uint32_t)((((p & 1) * Rmax + row) * nh + pl.nq + g) * th) * 8;
+    auto qso = [=](int i) { return qn0 + i * 16; };
+    auto kso = [=](int i) { return kn0 + i * 16; };
+    if (qkn) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int iu = i < th / 2 ? i : th / 2 - 1;
+        qs[i] = ld16c(rn, qso(iu));
+        ks[i] = ld16c(rn, kso(iu));
+      }
     }
     // V of this lane's dims for every t <= p: the word holding them (bf16),
     // or the aligned pair of words (fp32)
@@ -1128,12 +1194,38 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     }
     // Q and K (this position's from the qkv phase just before, earlier ones
     // long ready) and V, all in one wait
+    const uint32_t k_tag = rawk ? q_tag : kv_tag;
     if constexpr (BF)
-      await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, kv_tag, t <= p, nld),
-                pend<ASM>(vw, rv, vo, kv_tag, true, p + 1));
+      await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, k_tag, t <= p, nld),
+                pend<ASM>(vw, rv, vo, kv_tag, true, p + 1), pend(qs, rn, qso, q_tag, qkn, th / 2),
+                pend(ks, rn, kso, q_tag, qkn, th / 2));
     else
-      await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, kv_tag, t <= p, nld),
-                pend<ASM>(vv, rv, vo, kv_tag, true, p + 1));
+      await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, k_tag, t <= p, nld),
+                pend<ASM>(vv, rv, vo, kv_tag, true, p + 1), pend(qs, rn, qso, q_tag, qkn, th / 2),
+                pend(ks, rn, kso, q_tag, qkn, th / 2));
+    if (qkn) {
+      // 1 / rms of the q head and of the k head (partials in tile order),
+      // then Q and this position's K scaled and rounded as stored; the
+      // row's first q head writes that K into the cache for later positions
+      float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < th / 2) {
+          ssq = (ssq + __uint_as_float(qs[i][0])) + __uint_as_float(qs[i][2]);
+          ssk = (ssk + __uint_as_float(ks[i][0])) + __uint_as_float(ks[i][2]);
+        }
+      const float rnq = 1.0f / sqrtf(ssq / (float)d + pl.eps), rnk = 1.0f / sqrtf(ssk / (float)d + pl.eps);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        qv[i] = scale_pair<BF>(qv[i], rnq);
+        if (t == p) kv[i] = scale_pair<BF>(kv[i], rnk);
+      }
+      if (t == p && pi % gq == 0) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+          if (i < nld) st16c(rk, k0 + i * 16, ll_pair(kv[i][0], kv[i][2], kv_tag));
+      }
+    }
     if (pi < 4) stamp(tr, 2);
     float dot = 0.f;
 #pragma unroll

@@ -372,6 +372,8 @@ static cp_status build_schedule(cp_plan* P) {
   }
 
   std::vector<std::vector<uint32_t>> g_qkv(Pn * L);  // [p * L + l][g]
+  std::vector<std::vector<uint32_t>> g_attn(Pn * L);  // [p * L + l][o split]
+  const bool qkn = P->cfg.qk_norm != 0;
   uint32_t g_prev_draw = kNone;
   int ph_prev_draw = -1;
   for (int p = 0; p < Pn; ++p) {
@@ -402,8 +404,9 @@ static cp_status build_schedule(cp_plan* P) {
         }
       }
       // Position 0 has no head: the residual after its last layer feeds
-      // nothing, so only the last layer's qkv (its K/V) is computed there.
-      if (p == 0 && l == L - 1) break;
+      // nothing, so only the last layer's qkv (its K/V) is computed there --
+      // and, with QK-norm, its attention, which writes the normed K.
+      if (p == 0 && l == L - 1 && !qkn) break;
       // attention, per kv head; it completes the group of the o split that reads it
       std::vector<uint32_t> g_att(ns_o);
       for (int s = 0; s < ns_o; ++s) g_att[s] = B.group(kv_per_osplit * agroups);
@@ -415,6 +418,8 @@ static cp_status build_schedule(cp_plan* P) {
             Task k = make_task(T_ATTN, l, p, g * agroups + rg);
             add_wait(k, gq_groups[g]);
             if (p == 1) add_wait(k, g_qkv[0 * L + l][g]);  // position 0's K/V of this layer
+            // QK-norm: earlier positions' K, normed and stored by their attention
+            if (qkn && p >= 1) add_wait(k, g_attn[(p - 1) * L + l][g / kv_per_osplit]);
             k.ph_in0 = (uint16_t)ph_qkv;
             k.sig = g_att[g / kv_per_osplit]; k.sig_slot = (g % kv_per_osplit) * agroups + rg;
             ts.push_back(k);
@@ -427,6 +432,8 @@ static cp_status build_schedule(cp_plan* P) {
           B.phase(ts, spread(nkv * agroups, n_wg, rot));
         }
       }
+      g_attn[p * L + l] = g_att;
+      if (p == 0 && l == L - 1) break;
       // o (split-K over q heads; a split reads only the kv heads of its slice)
       const uint32_t g_o = B.group(ht);
       const int ph_o = B.next_phase();
@@ -700,7 +707,8 @@ static int64_t const_bytes(const cp_config& c) {
   const int64_t L = c.n_layers, H = c.hidden, nq = c.n_q_heads, nkv = c.n_kv_heads, d = c.head_dim;
   const int64_t I = c.intermediate, Pn = c.n_positions, V = c.vocab, Din = c.input_dim;
   const int64_t blob = esz * (L * ((nq + 2 * nkv) * d * H + H * nq * d + 3 * I * H) + (Pn - 1) * V * H + H * Din);
-  return (int64_t)(round256((size_t)blob) + round256((size_t)(Pn * V * H * esz)) + round256((size_t)(Pn * d * 4)));
+  return (int64_t)(round256((size_t)blob) + round256((size_t)(Pn * V * H * esz)) + round256((size_t)(Pn * d * 4)) +
+                   (c.qk_norm ? round256((size_t)(L * 2 * d * 4)) : 0));
 }
 
 
@@ -857,6 +865,32 @@ static cp_status pack_weights(cp_plan* P, const cp_weights* w) {
   TRY(alloc_const(P, &dr, rope.size() * 4));
   HIPCHK(P, hipMemcpy(dr, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
   P->dp.rope = (const float*)dr;
+  if (c.qk_norm) {
+    // head-norm gains [L][q, k][d], fp32 (exact for bf16)
+    if (!w->q_norm || !w->k_norm) return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL q_norm / k_norm list");
+    std::vector<float> qk((size_t)L * 2 * d);
+    for (int l = 0; l < L; ++l)
+      for (int k = 0; k < 2; ++k) {
+        const void* src = (k ? w->k_norm : w->q_norm)[l];
+        if (!src) return fail(P, CP_ERR_INVALID_ARGUMENT, "NULL q_norm / k_norm");
+        TRY(fetch(P, src, (size_t)d * esz, m));
+        for (int i = 0; i < d; ++i) {
+          float v;
+          if (esz == 2) {
+            const uint32_t bits = (uint32_t)((const uint16_t*)m.data())[i] << 16;
+            std::memcpy(&v, &bits, 4);
+          } else {
+            std::memcpy(&v, m.data() + (size_t)i * 4, 4);
+          }
+          if (!std::isfinite(v)) return fail(P, CP_ERR_INVALID_ARGUMENT, "non-finite q_norm / k_norm gain");
+          qk[((size_t)l * 2 + k) * d + i] = v;
+        }
+      }
+    void* dq;
+    TRY(alloc_const(P, &dq, qk.size() * 4));
+    HIPCHK(P, hipMemcpy(dq, qk.data(), qk.size() * 4, hipMemcpyHostToDevice));
+    P->dp.qk_gain = (const float*)dq;
+  }
   int64_t wb = (int64_t)esz * ((int64_t)Pn * L * ((nq + 2 * nkv) * d * H + (int64_t)H * qd + 3LL * I * H) +
                                (int64_t)(Pn - 1) * V * H + (int64_t)H * Din);
   P->weight_bytes_frame = wb;
@@ -903,7 +937,16 @@ static cp_status alloc_scratch(cp_plan* P) {
   dp.abuf = (uint8_t*)dp.hmid + planes * hb;
   dp.mbuf = (uint8_t*)dp.abuf + planes * ab;
   TRY(alloc(P, &p, (size_t)2 * R * nq * d * e2, true)); dp.qbuf = p;     // row-major (attention input)
-  TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.kc = p;
+  // QK-norm: behind the K cache (one buffer resource covers both), the raw
+  // normed-to-be K of the position in flight, [2 parity][Rmax][nkv][d]
+  const size_t kcb = (size_t)L * R * nkv * Pn * d * e2, krb = c.qk_norm ? (size_t)2 * R * nkv * d * e2 : 0;
+  TRY(alloc(P, &p, kcb + krb, true)); dp.kc = p;
+  dp.kraw = c.qk_norm ? (uint8_t*)p + kcb : nullptr;
+  if (c.qk_norm) {
+    // per-tile sums of squares of every q and k head, [2 parity][Rmax][nq + nkv][d / 16] words
+    TRY(alloc(P, &p, (size_t)2 * R * (nq + nkv) * (d / 16) * 8, true)); dp.qkn = (uint64_t*)p;
+  }
+  dp.qk_norm = c.qk_norm ? 1 : 0;
   TRY(alloc(P, &p, (size_t)L * R * nkv * Pn * d * e2, true)); dp.vc = p;
   const size_t part_one = (size_t)(H / 16) * 4 * R * 16;  // words per split-K phase buffer
   TRY(alloc(P, &p, part_one * 5 * 8, true)); dp.part = (uint64_t*)p;       // o[2], down[2], in

@@ -13,7 +13,8 @@ and real Talker hidden states are not available, so every tensor is drawn from
 a fixed seeded distribution instead:
 
 * weight matrices and embedding tables ~ N(0, 0.02);
-* RMSNorm gains 1.0 (or 1 + N(0, 0.1) in the test-only ``gain_jitter`` variant);
+* RMSNorm gains 1.0 (or 1 + N(0, 0.1) in the test-only ``gain_jitter`` variant),
+  the per-head q and k norm gains of the QK-norm variant included;
 * the input hidden ~ N(0, 1), one independent vector per row;
 * code 0 (supplied by the Talker in the real model) ~ U[0, vocab);
 * sampling parameters per row: temperature ~ U[0.6, 1.2], top-k uniform in
@@ -55,6 +56,7 @@ class DepthLoopConfig:
     sampled: bool = False
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
+    qk_norm: bool = False  # Qwen3-style RMSNorm of each q and k head before RoPE
 
     @property
     def n_heads_out(self) -> int:
@@ -109,6 +111,8 @@ CONFIGS: dict[str, DepthLoopConfig] = {
     "l10_r1": DepthLoopConfig(name="l10_r1", rows=1, **{**_FULL, "n_layers": 10}),
     "l10_r16": DepthLoopConfig(name="l10_r16", rows=16, **{**_FULL, "n_layers": 10}),
     "l10_r64": DepthLoopConfig(name="l10_r64", rows=64, **{**_FULL, "n_layers": 10}),
+    # Qwen3-style variant: RMSNorm of every q and k head before RoPE.
+    "l5_qk_r64": DepthLoopConfig(name="l5_qk_r64", rows=64, qk_norm=True, **_FULL),
     # Input projection from a 2048-wide hidden (a larger text model) to 1024.
     "l5_in2048_r8": DepthLoopConfig(name="l5_in2048_r8", rows=8, **{**_FULL, "input_dim": 2048}),
 }
@@ -177,7 +181,8 @@ def make_weights(cfg: DepthLoopConfig, seed: int = 0, gain_jitter: bool = False)
     """All weights of one configuration, keyed by name, in the storage type.
 
     Matrices are ``weight_names`` order; norm gains are ``attn_norm.l``,
-    ``mlp_norm.l`` and ``final_norm`` of length ``hidden``.
+    ``mlp_norm.l`` and ``final_norm`` of length ``hidden`` and, with
+    ``qk_norm``, ``q_norm.l`` and ``k_norm.l`` of length ``head_dim``.
     """
     w = {}
     for idx, name in enumerate(weight_names(cfg)):
@@ -192,6 +197,14 @@ def make_weights(cfg: DepthLoopConfig, seed: int = 0, gain_jitter: bool = False)
     if gain_jitter:
         g += _rng(seed, TAG_GAIN, 2 * cfg.n_layers).standard_normal(cfg.hidden, dtype=np.float32) * np.float32(0.1)
     w["final_norm"] = _store(cfg, g)
+    if cfg.qk_norm:
+        for l in range(cfg.n_layers):
+            for k, nm in enumerate(("q_norm", "k_norm")):
+                g = np.ones(cfg.head_dim, np.float32)
+                if gain_jitter:
+                    g += _rng(seed, TAG_GAIN, 2 * cfg.n_layers + 1 + 2 * l + k).standard_normal(
+                        cfg.head_dim, dtype=np.float32) * np.float32(0.1)
+                w[f"{nm}.{l}"] = _store(cfg, g)
     return w
 
 

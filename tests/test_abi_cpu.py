@@ -59,7 +59,7 @@ def test_unsupported_shapes_are_refused_on_the_host(change, status):
     assert cp.lib().cp_last_create_error()
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "l5_r1", "l5_r64", "l10_r64", "l5_in2048_r8"])
+@pytest.mark.parametrize("name", ["tiny_f32", "l5_r1", "l5_r64", "l10_r64", "l5_in2048_r8", "l5_qk_r64"])
 @pytest.mark.parametrize("cus", [256, 64, 7])
 def test_schedule_invariants(name, cus):
     cp = _cp()
@@ -67,10 +67,23 @@ def test_schedule_invariants(name, cus):
     info = cp.schedule_check(cfg, cu_count=cus)
     L, P = cfg.n_layers, cfg.n_positions
     # 5 L P + 2 P phases (input projection, 15 heads, 16 embedding steps), less
-    # the four phases after position 0's last qkv, whose results nothing reads.
-    assert info.n_phases == 5 * L * P + 2 * P - 4
+    # the four phases after position 0's last qkv, whose results nothing reads
+    # (three with QK-norm, whose attention there writes the normed K).
+    assert info.n_phases == 5 * L * P + 2 * P - (3 if cfg.qk_norm else 4)
     assert info.n_workgroups == cus
     assert info.max_tasks_per_workgroup * cus >= info.n_tasks
+
+
+def test_qk_norm_gains_are_plan_constants():
+    """The QK-norm variant keeps its head-norm gains ([L][q, k][head_dim]
+    fp32) with the plan's constants; the schedule gains one phase, position
+    0's last-layer attention, which writes that position's normed K."""
+    cp = _cp()
+    base, qk = synth.CONFIGS["l5_r64"], synth.CONFIGS["l5_qk_r64"]
+    a, b = cp.schedule_check(base), cp.schedule_check(qk)
+    assert b.const_bytes - a.const_bytes == -(-(qk.n_layers * 2 * qk.head_dim * 4) // 256) * 256
+    assert b.n_phases == a.n_phases + 1
+    assert b.n_tasks == a.n_tasks + qk.n_kv_heads * 32  # 64 rows: 32 two-row attention tasks per kv head
 
 
 def test_inline_asm_vector_memory_blocks_start_with_the_guard(tmp_path):

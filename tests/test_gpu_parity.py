@@ -29,7 +29,7 @@ def _cp():
 
 def _weights(cfg, seed=0, gain_jitter=False):
     key = (cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate,
-           cfg.n_positions, cfg.vocab, cfg.input_dim, cfg.dtype, seed, gain_jitter)
+           cfg.n_positions, cfg.vocab, cfg.input_dim, cfg.dtype, cfg.qk_norm, seed, gain_jitter)
     if key not in _cache:
         from oracle import oracle
         w = synth.make_weights(cfg, seed=seed, gain_jitter=gain_jitter)
@@ -96,6 +96,39 @@ def test_tiny_bf16_ragged(exec_mode):
     inputs = synth.make_inputs(cfg, seed=2)
     gpu = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=8, kv=True)
     _check(cfg, ow, inputs, gpu, range(5), 0.05, kv=True)
+
+
+@pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
+@pytest.mark.parametrize("dtype,rows,tol", [("f32", 3, 1e-4), ("bf16", 5, 0.05), ("bf16", 1, 0.05)])
+def test_tiny_qk_norm(exec_mode, dtype, rows, tol):
+    """The QK-norm variant (RMSNorm of every q and k head before RoPE, own
+    gains, jittered here) against the oracle: logits, codes, embedding sums
+    and the K/V cache (K normed)."""
+    cfg = synth.CONFIGS["tiny_f32"].with_(rows=rows, dtype=dtype, qk_norm=True)
+    w, wdev, ow = _weights(cfg, seed=6, gain_jitter=True)
+    inputs = synth.make_inputs(cfg, seed=6)
+    gpu = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=8, kv=True)
+    err, _ = _check(cfg, ow, inputs, gpu, range(rows), tol, kv=True)
+    print(f"tiny qk-norm {dtype} {rows} rows {exec_mode}: max logit err {err:.2e}")
+
+
+def test_full_l5_qk_norm():
+    """Full-size QK-norm variant with jittered gains: every one of 64 rows
+    against the oracle, the per-phase executor bit for bit equal to the
+    persistent one, and a one-row frame (one-row kernels) against the
+    oracle."""
+    cfg = synth.CONFIGS["l5_qk_r64"]
+    w, wdev, ow = _weights(cfg, seed=7, gain_jitter=True)
+    inputs = synth.make_inputs(cfg, seed=7)
+    a = _gpu_frame(cfg, wdev, inputs, "persistent", kv=True)
+    err, frac = _check(cfg, ow, inputs, a, range(64), 0.05, kv=True)
+    print(f"l5 qk-norm 64 rows: max logit err {err:.4f}, decided {frac:.2f}")
+    b = _gpu_frame(cfg, wdev, inputs, "per_phase", kv=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    one = synth.make_inputs(cfg, rows=1, seed=8)
+    g1 = _gpu_frame(cfg, wdev, one, "persistent", max_rows=1, kv=True)
+    _check(cfg, ow, one, g1, range(1), 0.05, kv=True)
 
 
 @pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])

@@ -32,14 +32,20 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 # ------------------------------------------------------------------ helpers
 
 def _hf_model(cfg, w):
-    from transformers import LlamaConfig, LlamaModel
-    hc = LlamaConfig(vocab_size=cfg.vocab, hidden_size=cfg.hidden,
-                     intermediate_size=cfg.intermediate, num_hidden_layers=cfg.n_layers,
-                     num_attention_heads=cfg.n_q_heads, num_key_value_heads=cfg.n_kv_heads,
-                     head_dim=cfg.head_dim, rms_norm_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
-                     max_position_embeddings=64, attention_bias=False, mlp_bias=False,
-                     tie_word_embeddings=False, attn_implementation="eager")
-    m = LlamaModel(hc).double().eval()
+    """The transformers stack of the same shapes: Llama, or Qwen3 (whose
+    attention norms every q and k head before RoPE) for the QK-norm variant."""
+    kw = dict(vocab_size=cfg.vocab, hidden_size=cfg.hidden,
+              intermediate_size=cfg.intermediate, num_hidden_layers=cfg.n_layers,
+              num_attention_heads=cfg.n_q_heads, num_key_value_heads=cfg.n_kv_heads,
+              head_dim=cfg.head_dim, rms_norm_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
+              max_position_embeddings=64, attention_bias=False,
+              tie_word_embeddings=False, attn_implementation="eager")
+    if cfg.qk_norm:
+        from transformers import Qwen3Config, Qwen3Model
+        m = Qwen3Model(Qwen3Config(**kw)).double().eval()
+    else:
+        from transformers import LlamaConfig, LlamaModel
+        m = LlamaModel(LlamaConfig(mlp_bias=False, **kw)).double().eval()
     f = lambda a: torch.from_numpy(synth.as_f32(cfg, a).astype(np.float64))
     sd = m.state_dict()
     qd, kd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
@@ -55,6 +61,9 @@ def _hf_model(cfg, w):
         sd[p + "mlp.down_proj.weight"] = f(w[f"w_down.{l}"])
         sd[p + "input_layernorm.weight"] = f(w[f"attn_norm.{l}"])
         sd[p + "post_attention_layernorm.weight"] = f(w[f"mlp_norm.{l}"])
+        if cfg.qk_norm:
+            sd[p + "self_attn.q_norm.weight"] = f(w[f"q_norm.{l}"])
+            sd[p + "self_attn.k_norm.weight"] = f(w[f"k_norm.{l}"])
     sd["norm.weight"] = f(w["final_norm"])
     m.load_state_dict(sd)
     return m, f
@@ -100,6 +109,60 @@ def test_oracle_matches_transformers_llama_fp64(oracle_mod, variant):
         v_or = out["v_cache"][:, r].transpose(0, 2, 1, 3)
         assert np.abs(k_or - ks).max() <= 2e-6 * max(1.0, np.abs(ks).max())
         assert np.abs(v_or - vs).max() <= 2e-6 * max(1.0, np.abs(vs).max())
+
+
+@pytest.mark.parametrize("variant", [
+    dict(),                                           # tiny fp32 shapes
+    dict(n_kv_heads=1, n_positions=6, vocab=64),      # one kv head, more positions
+    dict(head_dim=128, n_q_heads=2, n_kv_heads=2),    # the full model's head size
+])
+def test_oracle_qk_norm_matches_transformers_qwen3_fp64(oracle_mod, variant):
+    """The QK-norm variant (per-head RMSNorm of q and k with their own gains,
+    before RoPE) against transformers' Qwen3 stack in fp64, with jittered
+    gains so that q_norm and k_norm cannot be swapped or dropped unseen."""
+    cfg = TINY.with_(rows=2, qk_norm=True, **variant)
+    w = synth.make_weights(cfg, seed=13, gain_jitter=True)
+    inp = synth.make_inputs(cfg, seed=13)
+    out = oracle_mod.run_frame(cfg, w, inp, keep_kv=True)
+    for r in range(cfg.rows):
+        z, ks, vs = _hf_frame(cfg, w, inp, r, out["codes"][r])
+        assert np.abs(out["logits"][r] - z).max() <= 2e-6 * max(1.0, np.abs(z).max())
+        k_or = out["k_cache"][:, r].transpose(0, 2, 1, 3)
+        v_or = out["v_cache"][:, r].transpose(0, 2, 1, 3)
+        assert np.abs(k_or - ks).max() <= 2e-6 * max(1.0, np.abs(ks).max())
+        assert np.abs(v_or - vs).max() <= 2e-6 * max(1.0, np.abs(vs).max())
+    # the variant changes the frame (it is not silently ignored)
+    plain = oracle_mod.run_frame(cfg.with_(qk_norm=False), w, inp, forced_codes=out["codes"])
+    assert np.abs(plain["logits"] - out["logits"]).max() > 1e-3
+
+
+def test_oracle_qk_norm_is_per_head_and_scale_free(oracle_mod):
+    """RMSNorm of a head makes it independent of that head's scale: scaling
+    the W_q rows of one q head, or the W_k rows of one k head, by 3 leaves
+    the logits unchanged to fp32 rounding, while the same scaling without
+    the norm changes them.  Scaling every row of the q block by a different
+    factor per head also leaves them unchanged (a norm over all heads at once
+    would not)."""
+    cfg = TINY.with_(rows=2, qk_norm=True, n_positions=4)
+    w = synth.make_weights(cfg, seed=17, gain_jitter=True)
+    inp = synth.make_inputs(cfg, seed=17)
+    base = oracle_mod.run_frame(cfg, w, inp)
+    d, qd = cfg.head_dim, cfg.n_q_heads * cfg.head_dim
+    for rows_sl, fac in ((slice(0, d), 3.0), (slice(qd + d, qd + 2 * d), 3.0), (None, None)):
+        w2 = dict(w)
+        for l in range(cfg.n_layers):
+            m = w[f"w_qkv.{l}"].copy()
+            if rows_sl is None:
+                for h in range(cfg.n_q_heads):
+                    m[h * d:(h + 1) * d] *= np.float32(0.5 + h)
+            else:
+                m[rows_sl] *= np.float32(fac)
+            w2[f"w_qkv.{l}"] = m
+        alt = oracle_mod.run_frame(cfg, w2, inp, forced_codes=base["codes"])
+        assert np.abs(alt["logits"] - base["logits"]).max() <= 1e-5 * np.abs(base["logits"]).max()
+        off = oracle_mod.run_frame(cfg.with_(qk_norm=False), w2, inp, forced_codes=base["codes"])
+        ref = oracle_mod.run_frame(cfg.with_(qk_norm=False), w, inp, forced_codes=base["codes"])
+        assert np.abs(off["logits"] - ref["logits"]).max() > 1e-4
 
 
 def test_oracle_bf16_close_to_fp64_stack(oracle_mod):
