@@ -289,7 +289,8 @@ def main():
     import torch
     from persistent_megakernel_streaming_amd import cp, synth
 
-    everything = {"p64", "p1", "s64", "pp64", "pp1", "late", "cross", "qk", "l10", "floor", "chain", "cold", "pct"}
+    everything = {"p64", "p1", "p128", "s64", "pp64", "pp1", "late", "cross", "qk", "l10", "floor", "chain", "cold",
+                  "pct"}
     only = set(args.only.split(",")) if args.only else everything
     steps, warm, reps = args.steps, args.warmup, args.repeats
     cfg64 = synth.CONFIGS["l5_r64"]
@@ -341,6 +342,13 @@ def main():
             io = cp.make_io(c, synth.make_inputs(c), logits=False)
             res[f"late_norm_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
             pl.close()
+    if "p128" in only:
+        # the 128-row frame (two groups of 64 rows per projection task)
+        c = synth.CONFIGS["l5_r128"]
+        pl = cp.Plan(c, wdev, exec_mode="persistent", max_rows=128)
+        io = cp.make_io(c, synth.make_inputs(c), logits=False)
+        res["persistent_us_128"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
+        pl.close()
     if "qk" in only:
         # the QK-norm variant (RMSNorm of every q and k head before RoPE)
         cq = synth.CONFIGS["l5_qk_r64"]

@@ -82,9 +82,11 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
  * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a
  * multiple of 256 up to 1024; input_dim and intermediate multiples of 64;
  * vocab 256, 512, 1024, 2048 or 4096; 2 <= n_positions <= 16;
- * 1 <= max_rows <= 64 (a step of more rows is refused and runs the loop:
- * section "How it works", opening paragraphs; the 128-row frame is listed
- * under "What's left in the frame, open"). */
+ * 1 <= max_rows <= 128 (the pages' frame stops at 64 rows, section "How it
+ * works", opening paragraphs, and lists the 128-row frame under "What's left
+ * in the frame, open"; here a projection task of a frame over 64 rows runs
+ * its two groups of 64 rows one after the other on the weight tile it holds
+ * in LDS). */
 typedef struct {
   int32_t abi_version;  /* CP_ABI_VERSION */
   int32_t n_layers;

@@ -21,7 +21,7 @@ enum TaskType : uint8_t {
 constexpr int kMaxWaits = 4;
 constexpr uint32_t kNone = 0xffffffffu;
 constexpr int kTileN = 16;          // output slots per projection tile
-constexpr int kMaxRows = 64;
+constexpr int kMaxRows = 128;
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kSlotBytes = 64 * 1024;  // one weight-tile slot in LDS (two slots)
 constexpr int kMiscLds = 12288;  // flags, cross-wave reductions

@@ -589,7 +589,7 @@ __device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
 template <int BF, int KIND, bool ONE = false, bool ASM = !ONE>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, uint64_t* tr) {
+                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, int rh = 0) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
@@ -647,16 +647,20 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   }
   const int nck = kt * ESZ / 64;  // 16-byte payload chunks per lane over the task's K range
 
-  // Waves and row tiles: a wave owns 16 rows; with few rows the waves of a
-  // row tile split K and add their results through LDS in a fixed order.
-  const int nrt = (rows + 15) >> 4;                   // row tiles holding live rows (1..4)
+  // Waves and row tiles: a wave owns 16 rows of a group of 64; with few rows
+  // the waves of a row tile split K and add their results through LDS in a
+  // fixed order.  A frame of more than 64 rows runs the task once per group
+  // of 64 (rh), the weight tile staying in LDS.
+  const int rows_h = min(rows - 64 * rh, 64);
+  const int nrt = (rows_h + 15) >> 4;                 // row tiles of this group holding live rows (1..4)
   int wpr = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);        // waves per row tile
   while (wpr > 1 && nck % (4 * wpr)) wpr >>= 1;        // each wave takes whole groups of 4 chunks
   const int rt = wave / wpr, ks = wave % wpr;
+  const int rta = rh * 4 + rt;                        // the row tile in the frame
   const int ncw = nck / wpr;                          // chunks this wave handles (a multiple of 4)
   const int ng = ncw / 4;
   const int c0 = ks * ncw;
-  const int row = rt * 16 + rl;
+  const int row = rta * 16 + rl;
   const bool wave_live = rt < nrt;
   const bool live = wave_live && row < rows;
 
@@ -669,7 +673,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // holds a sentinel is loaded again.
   const uint32_t xrow = (uint32_t)ld * ESZ;  // frame input only
   const rsrc_t rx = XLL ? make_rsrc(xsrc, sop_bytes<BF>(Rmax, ld)) : make_rsrc(xsrc, (uint32_t)rows * xrow);
-  const uint32_t xoff = XLL ? (uint32_t)(rt * (ld / KS) + k0 / KS + c0) * 1024 + (uint32_t)lane * 16
+  const uint32_t xoff = XLL ? (uint32_t)(rta * (ld / KS) + k0 / KS + c0) * 1024 + (uint32_t)lane * 16
                             : (uint32_t)row * xrow + (uint32_t)(k0 + q * E) * ESZ + c0 * CST;
   auto uoff = [=](int g) {
     return [=](int u) -> uint32_t { return xoff + (uint32_t)(g * 4 + u) * (XLL ? 1024u : CST); };
@@ -1776,14 +1780,16 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
       break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
-#define CP_PROJ(K) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr);
+#define CP_PROJ(K) for (int rh = 0; rh * 64 < fr.rows; ++rh) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, rh);
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
     case T_GU: CP_PROJ(T_GU) break;
     case T_DOWN: CP_PROJ(T_DOWN) break;
     case T_HEAD: CP_PROJ(T_HEAD) break;
 #undef CP_PROJ
-    default: proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
+    default:
+      for (int rh = 0; rh * 64 < fr.rows; ++rh) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, rh);
+      break;
   }
 }
 

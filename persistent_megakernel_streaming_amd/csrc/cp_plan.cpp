@@ -254,7 +254,7 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   if (c->head_dim != 64 && c->head_dim != 128) { msg = "head_dim must be 64 or 128"; return CP_ERR_UNSUPPORTED; }
   if (c->n_q_heads % c->n_kv_heads) { msg = "n_q_heads must be a multiple of n_kv_heads"; return CP_ERR_UNSUPPORTED; }
   if (c->n_positions < 2 || c->n_positions > 16) { msg = "n_positions must be in 2..16"; return CP_ERR_UNSUPPORTED; }
-  if (c->max_rows > kMaxRows) { msg = "max_rows must be <= 64"; return CP_ERR_UNSUPPORTED; }
+  if (c->max_rows > kMaxRows) { msg = "max_rows must be <= 128"; return CP_ERR_UNSUPPORTED; }
   if (c->vocab != 256 && c->vocab != 512 && c->vocab != 1024 && c->vocab != 2048 && c->vocab != 4096) {
     msg = "vocab must be 256, 512, 1024, 2048 or 4096";
     return CP_ERR_UNSUPPORTED;

@@ -107,6 +107,8 @@ CONFIGS: dict[str, DepthLoopConfig] = {
     "l5_r1": DepthLoopConfig(name="l5_r1", rows=1, **_FULL),
     "l5_r64": DepthLoopConfig(name="l5_r64", rows=64, **_FULL),
     "l5_r64_sampled": DepthLoopConfig(name="l5_r64_sampled", rows=64, sampled=True, **_FULL),
+    # A frame of 128 rows (two groups of 64 per projection task).
+    "l5_r128": DepthLoopConfig(name="l5_r128", rows=128, **_FULL),
     # 10-layer variant: 314 MB of layer weights, more than the 256 MB Infinity Cache.
     "l10_r1": DepthLoopConfig(name="l10_r1", rows=1, **{**_FULL, "n_layers": 10}),
     "l10_r16": DepthLoopConfig(name="l10_r16", rows=16, **{**_FULL, "n_layers": 10}),

@@ -47,7 +47,7 @@ def test_status_strings_and_null_arguments():
 
 @pytest.mark.parametrize("change,status", [
     (dict(head_dim=96), 2), (dict(n_positions=17), 2), (dict(n_kv_heads=3), 2),
-    (dict(hidden=1000), 2), (dict(n_layers=0), 1), (dict(rows=65), 2),
+    (dict(hidden=1000), 2), (dict(n_layers=0), 1), (dict(rows=129), 2),
 ])
 def test_unsupported_shapes_are_refused_on_the_host(change, status):
     cp = _cp()
@@ -59,7 +59,7 @@ def test_unsupported_shapes_are_refused_on_the_host(change, status):
     assert cp.lib().cp_last_create_error()
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "l5_r1", "l5_r64", "l10_r64", "l5_in2048_r8", "l5_qk_r64"])
+@pytest.mark.parametrize("name", ["tiny_f32", "l5_r1", "l5_r64", "l10_r64", "l5_in2048_r8", "l5_qk_r64", "l5_r128"])
 @pytest.mark.parametrize("cus", [256, 64, 7])
 def test_schedule_invariants(name, cus):
     cp = _cp()

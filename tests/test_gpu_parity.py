@@ -253,6 +253,27 @@ def test_crossover_dispatch_runs_small_frames_per_phase():
     pp.close()
 
 
+def test_full_l5_128_rows():
+    """The 128-row frame: every row against the oracle, the per-phase
+    executor bit for bit equal, and a ragged 100-row frame on the same plan
+    shape equal to its rows of a full frame where inputs agree."""
+    cfg = synth.CONFIGS["l5_r128"]
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg, seed=9)
+    a = _gpu_frame(cfg, wdev, inputs, "persistent", kv=True)
+    err, frac = _check(cfg, ow, inputs, a, range(128), 0.05, kv=True)
+    print(f"l5 128 rows: max logit err {err:.4f}, decided {frac:.2f}")
+    b = _gpu_frame(cfg, wdev, inputs, "per_phase", kv=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    part = {k: (v[:100] if k != "rows" else 100) for k, v in inputs.items()}
+    c = _gpu_frame(cfg, wdev, part, "persistent", max_rows=128, kv=True)
+    for k in ("codes", "embsum", "logits"):
+        assert np.array_equal(a[k][:100], c[k]), k
+    for k in ("k_cache", "v_cache"):
+        assert np.array_equal(a[k][:, :100], c[k][:, :100]), k
+
+
 def test_one_row_frame_on_64_row_plan():
     """A one-row frame runs the one-row kernels (row 0 of each operand tile
     loaded densely and handed out with ds_bpermute) on a plan built for 64
