@@ -289,8 +289,8 @@ def main():
     import torch
     from persistent_megakernel_streaming_amd import cp, synth
 
-    everything = {"p64", "p1", "p128", "s64", "pp64", "pp1", "late", "cross", "qk", "l10", "floor", "chain", "cold",
-                  "pct"}
+    everything = {"p64", "p1", "p128", "s64", "pp64", "pp1", "late", "nolocal", "cross", "qk", "l10", "floor", "chain",
+                  "cold", "pct"}
     only = set(args.only.split(",")) if args.only else everything
     steps, warm, reps = args.steps, args.warmup, args.repeats
     cfg64 = synth.CONFIGS["l5_r64"]
@@ -360,6 +360,13 @@ def main():
             res[f"qk_norm_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
             pl.close()
         del wq
+    if "nolocal" in only:
+        # every hand-off written through to memory (no XCD-local L2 hand-offs)
+        for c, mr in ((cfg64, 64), (cfg1, 1)):
+            pl = cp.Plan(c, wdev, exec_mode="persistent", max_rows=mr, flags=cp.CP_FLAG_NO_LOCAL)
+            io = cp.make_io(c, synth.make_inputs(c), logits=False)
+            res[f"write_through_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
+            pl.close()
     if "cross" in only:
         # the row-count crossover: persistent frame against the per-phase
         # loop (captured as a graph) on one plan, rows 1 .. 64

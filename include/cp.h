@@ -77,6 +77,13 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
  * "What's left in the frame, open" (first item).  Same results, bit for bit;
  * measured slower on MI355X at 1 and 64 rows, so off by default. */
 #define CP_FLAG_LATE_NORM 0x2u
+/* Every hand-off writes through to memory: no split-K partials or q/k/v kept
+ * in one XCD's L2 for readers on that XCD.  A plan also runs this way when,
+ * at its creation, the device did not deal workgroup i to XCD (i + r) mod 8
+ * for one rotation r (the readers of an XCD-local hand-off must share the
+ * writer's XCD).  For measurement, and for a device whose dealing could
+ * change after that check. */
+#define CP_FLAG_NO_LOCAL 0x4u
 
 /* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
  * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a

@@ -23,6 +23,7 @@ CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
 CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1
 CP_FLAG_LATE_NORM = 2
+CP_FLAG_NO_LOCAL = 4
 ABI_VERSION = 3
 EPOCH_WRAP = (1 << 22) - 1  # epochs run 1 .. EPOCH_WRAP - 1
 
@@ -211,6 +212,10 @@ class Plan:
         i = PlanInfo()
         self._check(_lib.cp_plan_query(self._h, C.byref(i)))
         return i
+
+    def last_error(self) -> str:
+        """Text of the last error or note recorded on the plan ("" if none)."""
+        return _lib.cp_plan_last_error(self._h).decode()
 
     def _check(self, st):
         if st != CP_OK:

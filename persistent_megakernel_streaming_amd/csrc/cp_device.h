@@ -113,6 +113,7 @@ struct DevPlan {
   int n_tasks;
   int tasks_in_lds;             // every workgroup's list fits kTaskLds: the executor copies it to LDS
   int late_norm;                // CP_FLAG_LATE_NORM: normed projections wait for norm partials after the K loop
+  int local_ok;                 // XCD-local hand-offs allowed (not CP_FLAG_NO_LOCAL)
   // task lists
   const DevTask* tasks;         // all tasks, grouped by workgroup
   const uint32_t* wg_begin;     // [n_wg + 1]

@@ -88,8 +88,6 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return v & 0xfu;
 }
 
-// Whether this workgroup runs on the XCD the schedule dealt it to (i % 8).
-__device__ __forceinline__ bool on_dealt_xcd() { return xcc_id() == (blockIdx.x & 7u); }
 
 // Tagged-word stores that stay in this XCD's L2 (`local`: every reader runs
 // on this XCD and loads agent-coherently) or write through to memory.
@@ -589,7 +587,7 @@ __device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
 template <int BF, int KIND, bool ONE = false, bool ASM = !ONE>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, int rh = 0) {
+                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, int rh = 0) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
@@ -935,7 +933,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         const uint32_t o = pbase + tk.split * pstep;
         const u32x4 p0 = ll_pair(__float_as_uint(acc0[0]), __float_as_uint(acc0[1]), my_tag);
         const u32x4 p1 = ll_pair(__float_as_uint(acc0[2]), __float_as_uint(acc0[3]), my_tag);
-        if ((tk.flags & kTaskLocalPartials) && on_dealt_xcd()) {
+        if ((tk.flags & kTaskLocalPartials) && lcl) {
           st16(rp, o, p0);
           st16(rp, o + 16, p1);
         } else {
@@ -995,7 +993,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
         const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
         const uint32_t kv_tag = tag_of(epoch, kKvPhase);
         // q, k and v stay in this XCD's L2 when the attention of kv group g runs here
-        const bool lqkv = (tk.flags & kTaskLocalQkv) && on_dealt_xcd();
+        const bool lqkv = (tk.flags & kTaskLocalQkv) && lcl;
         if (lt < (gq + 1) * th) {
           // q or k head: slots (4q + v) hold rotary pairs 8 tih + 2q + (v >> 1), half v & 1
           const int tih = lt % th;
@@ -1771,8 +1769,9 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 // ONE: the executor was launched for a one-row frame (the densely loaded
 // operand path; a separate kernel, so the many-row code is left as it is).
 template <int BF, bool ONE>
+// lcl: XCD-local hand-offs allowed in this frame.
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                         uint8_t* slot, uint32_t* misc, uint64_t* tr) {
+                                         uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl) {
   switch (tk.type) {
     case T_ATTN:
       if (pl.d == 128) attn_task<BF, 128, !ONE>(pl, fr, tk, epoch, tr);
@@ -1780,7 +1779,7 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
       break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
-#define CP_PROJ(K) for (int rh = 0; rh * 64 < fr.rows; ++rh) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, rh);
+#define CP_PROJ(K) for (int rh = 0; rh * 64 < fr.rows; ++rh) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh);
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
     case T_GU: CP_PROJ(T_GU) break;
@@ -1788,7 +1787,8 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
     case T_HEAD: CP_PROJ(T_HEAD) break;
 #undef CP_PROJ
     default:
-      for (int rh = 0; rh * 64 < fr.rows; ++rh) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, rh);
+      for (int rh = 0; rh * 64 < fr.rows; ++rh)
+        proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh);
       break;
   }
 }
@@ -1845,6 +1845,15 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // XCD-local hand-offs need the workgroups that share one (the split-K
+  // partners and owner of a tile; the qkv tiles and attention tasks of a kv
+  // group) on one XCD.  The schedule puts them on workgroups of one residue
+  // mod 8, and the hardware deals workgroup i to XCD (i + r) mod 8, with a
+  // rotation r that changes from launch to launch (a graph replay or the
+  // next launch on a stream can start at another XCD) but is the same for
+  // every workgroup of a launch: residues stay together whatever r is.  The
+  // plan checks at creation that the dealing is such a rotation.
+  const bool lcl = __builtin_amdgcn_readfirstlane(pl.local_ok) != 0;
   const uint32_t b = pl.wg_begin[blockIdx.x], e = pl.wg_begin[blockIdx.x + 1];
   // With TL the workgroup's task records are copied to LDS once: reading a
   // record from memory between tasks would make the wave wait for every
@@ -1881,7 +1890,7 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
     stamp(tr, 1);
-    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr);
+    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
     stamp(tr, 6);
     // The next task's tile copy goes out once every wave has issued this
@@ -1928,7 +1937,7 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const DevTask tk = tasks[blockIdx.x];
   issue_tile(pl, tk, lds);
-  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr);
+  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr, false);  // (per-phase tasks carry no local flags)
 }
 
 // The per-phase executor's last launches of a frame: the sentinel refill of
@@ -2066,8 +2075,9 @@ hipError_t check_xcd_dealing(int n_wg, bool& dealt, uint32_t* buf) {
   const hipError_t f = buf ? hipSuccess : hipFree(d);
   if (e != hipSuccess) return e;
   if (f != hipSuccess) return f;
+  // workgroup i on XCD (i + r) mod 8 for one rotation r
   dealt = true;
-  for (int i = 0; i < n_wg; ++i) dealt = dealt && h[i] == (uint32_t)(i % 8);
+  for (int i = 0; i < n_wg; ++i) dealt = dealt && h[i] == ((uint32_t)i + h[0]) % 8;
   return hipSuccess;
 }
 

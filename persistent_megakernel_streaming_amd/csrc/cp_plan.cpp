@@ -58,7 +58,7 @@ struct cp_plan {
   int n_phases = 0;
   int crossover = 0;  // frames with fewer rows run the per-phase executor
   int max_tasks_wg = 0;
-  bool xcd_dealing = false;             // persistent workgroup i runs on XCD i % 8 (checked on the device)
+  bool xcd_dealing = false;             // persistent workgroup i runs on XCD (i + r) % 8, one r per launch (checked)
   DevTask* d_phase_tasks = nullptr;
   std::vector<void*> allocs;
   int64_t packed_bytes = 0, scratch_bytes = 0, weight_bytes_frame = 0;
@@ -273,7 +273,7 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   // an o split (n_q_heads / 4 heads) must read at most kMaxWaits kv heads
   const int gq = c->n_q_heads / c->n_kv_heads, hps = c->n_q_heads / 4;
   if ((hps - 1) / gq + 2 > kMaxWaits && hps / gq > kMaxWaits) { msg = "kv grouping not supported"; return CP_ERR_UNSUPPORTED; }
-  if (c->flags & ~(CP_FLAG_TRACE | CP_FLAG_LATE_NORM)) { msg = "unknown flag"; return CP_ERR_UNSUPPORTED; }
+  if (c->flags & ~(CP_FLAG_TRACE | CP_FLAG_LATE_NORM | CP_FLAG_NO_LOCAL)) { msg = "unknown flag"; return CP_ERR_UNSUPPORTED; }
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) { msg = "rms_eps / rope_theta"; return CP_ERR_INVALID_ARGUMENT; }
   return CP_OK;
 }
@@ -1073,6 +1073,7 @@ static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights*
   TRY(check_schedule(P));
   dp.tasks_in_lds = (int64_t)P->max_tasks_wg * (int64_t)sizeof(DevTask) <= kTaskLds;
   dp.late_norm = (cfg->flags & CP_FLAG_LATE_NORM) ? 1 : 0;
+  dp.local_ok = (cfg->flags & CP_FLAG_NO_LOCAL) ? 0 : 1;
   TRY(alloc_scratch(P));
   HIPCHK(P, hipDeviceSynchronize());
   return CP_OK;

@@ -223,6 +223,26 @@ def test_late_norm_wait_equals_default_bitwise(rows, exec_mode):
         _check(cfg, ow, inputs, b, range(0, 64, 9), 0.05, kv=True)
 
 
+@pytest.mark.parametrize("rows", [64, 1])
+def test_write_through_hand_offs_equal_xcd_local_ones(rows):
+    """CP_FLAG_NO_LOCAL (every hand-off written through to memory, what a plan
+    falls back to when a workgroup runs off its dealt XCD) changes where the
+    split-K partials and q/k/v travel, not what is computed: outputs equal the
+    default plan's bit for bit, and the device reports no placement fault."""
+    cp = _cp()
+    cfg = synth.CONFIGS["l5_r64"]
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg, rows=rows, seed=23)
+    a = _gpu_frame(cfg, wdev, inputs, "persistent", max_rows=rows, kv=True)
+    b = _gpu_frame(cfg, wdev, inputs, "persistent", max_rows=rows, kv=True, flags=cp.CP_FLAG_NO_LOCAL)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    plan = cp.Plan(cfg, wdev, max_rows=rows)
+    plan.run(cp.make_io(cfg, inputs))
+    plan.device_status()
+    plan.close()
+
+
 def test_crossover_dispatch_runs_small_frames_per_phase():
     """cp_plan_set_crossover: frames under the crossover run the per-phase
     executor on the persistent plan's buffers, interleaved with persistent
