@@ -87,7 +87,7 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
 
 /* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
  * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a
- * multiple of 256 up to 1024; input_dim and intermediate multiples of 64;
+ * multiple of 256 up to 1024; input_dim and intermediate multiples of 256;
  * vocab 256, 512, 1024, 2048 or 4096; 2 <= n_positions <= 16;
  * 1 <= max_rows <= 128 (the pages' frame stops at 64 rows, section "How it
  * works", opening paragraphs, and lists the 128-row frame under "What's left

@@ -596,8 +596,17 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   constexpr int NB = KIND == T_GU ? 2 : 1;  // weight tiles per chunk (gate and up)
   constexpr bool PART = KIND == T_O || KIND == T_DOWN || KIND == T_INPROJ;
   constexpr bool RESID = KIND == T_O || KIND == T_DOWN;
-  constexpr int NU = 4;                     // 16-byte loads per lane per group of 4 chunks
-  constexpr int DEPTH = 4;                  // operand groups in flight per wave
+  // Operand groups: NU chunks (one 16-byte load per lane each) per group,
+  // DEPTH groups in flight per wave.  Groups of 8 have half the waits and
+  // checks of groups of 4 (four of 4 in flight: 2646 us per 64-row frame;
+  // three of 8: 2516; three of 8 for the normed projections and two for the
+  // split-K ones, whose K slices are two or three groups at 64 rows: 2504;
+  // two of 8 everywhere 2531, four of 8 2900, eight of 2 2977, two of 16
+  // spill).  A wave's K range is whole groups (wpr below; the plan keeps
+  // split-K slices in whole groups), which at 32 rows or fewer can leave
+  // waves of a split-K task idle: measured no slower than groups of 4 there.
+  constexpr int NU = 8;
+  constexpr int DEPTH = NORM ? 3 : 2;
   constexpr uint32_t CST = 64;              // frame-input bytes per chunk step
   // ONE: a frame of one row.  Only row 0 of the operand tile is loaded, its
   // 16-byte units packed densely over the lanes (one load instruction per 16
@@ -652,11 +661,12 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const int rows_h = min(rows - 64 * rh, 64);
   const int nrt = (rows_h + 15) >> 4;                 // row tiles of this group holding live rows (1..4)
   int wpr = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);        // waves per row tile
-  while (wpr > 1 && nck % (4 * wpr)) wpr >>= 1;        // each wave takes whole groups of 4 chunks
+  // each wave takes whole groups of NU chunks (one-row frames: blocks of 4)
+  while (wpr > 1 && nck % ((ONE ? 4 : NU) * wpr)) wpr >>= 1;
   const int rt = wave / wpr, ks = wave % wpr;
   const int rta = rh * 4 + rt;                        // the row tile in the frame
-  const int ncw = nck / wpr;                          // chunks this wave handles (a multiple of 4)
-  const int ng = ncw / 4;
+  const int ncw = nck / wpr;                          // chunks this wave handles (a multiple of NU)
+  const int ng = ncw / NU;
   const int c0 = ks * ncw;
   const int row = rta * 16 + rl;
   const bool wave_live = rt < nrt;
@@ -674,7 +684,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const uint32_t xoff = XLL ? (uint32_t)(rta * (ld / KS) + k0 / KS + c0) * 1024 + (uint32_t)lane * 16
                             : (uint32_t)row * xrow + (uint32_t)(k0 + q * E) * ESZ + c0 * CST;
   auto uoff = [=](int g) {
-    return [=](int u) -> uint32_t { return xoff + (uint32_t)(g * 4 + u) * (XLL ? 1024u : CST); };
+    return [=](int u) -> uint32_t { return xoff + (uint32_t)(g * NU + u) * (XLL ? 1024u : CST); };
   };
   // DEPTH groups in flight: set xs[s] holds groups g = s (mod DEPTH).
   u32x4 xs[DEPTH][NU];
@@ -785,8 +795,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   auto step = [&](u32x4 (&xr)[NU], int g) {
     if constexpr (XLL) await_all(pl, spend<BF, ASM>(xr, rx, uoff(g), live));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = g * 4 + i;
+    for (int i = 0; i < NU; ++i) {
+      const int c = g * NU + i;
       const u32x4 x = xr[i];
       const u32x4 w0 = *(const u32x4*)(wt + c * NB * 1024);
       if constexpr (NB == 2) {

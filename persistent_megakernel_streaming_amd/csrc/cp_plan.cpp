@@ -259,8 +259,8 @@ static cp_status validate(const cp_config* c, std::string& msg) {
     msg = "vocab must be 256, 512, 1024, 2048 or 4096";
     return CP_ERR_UNSUPPORTED;
   }
-  if (c->hidden % 64 || c->input_dim % 64 || c->intermediate % 64 || c->vocab % 64) {
-    msg = "hidden, input_dim, intermediate and vocab must be multiples of 64";
+  if (c->hidden % 64 || c->input_dim % 256 || c->intermediate % 256 || c->vocab % 64) {
+    msg = "input_dim and intermediate must be multiples of 256, hidden and vocab of 64";
     return CP_ERR_UNSUPPORTED;
   }
   if (c->hidden % 256 || c->hidden > 1024) { msg = "hidden must be a multiple of 256, at most 1024"; return CP_ERR_UNSUPPORTED; }
@@ -284,7 +284,8 @@ static cp_status validate(const cp_config* c, std::string& msg) {
 // count: it cuts the activation bytes each workgroup streams by four (at 1
 // row, 2.75 -> 2.41 ms per frame against unsplit o and halved down).  A
 // choice must keep the weight tile within one LDS slot, each wave's K share
-// within 32 chunks, and every o split on whole kv heads.
+// within 32 chunks and in whole operand groups of 8 chunks, and every o split
+// on whole kv heads.
 static cp_status choose_splits(cp_plan* P) {
   const cp_config& c = P->cfg;
   const int esz = c.dtype == CP_DTYPE_BF16 ? 2 : 4;
@@ -295,7 +296,7 @@ static cp_status choose_splits(cp_plan* P) {
     if (K % (16 * ns)) return false;
     const int kt = K / ns;
     const int nck = kt * esz / 64;
-    return kt * esz * 64 % 64 == 0 && nck % 4 == 0 && 16 * kt * esz <= kSlotBytes && nck / wpr_min <= 32;
+    return kt * esz * 64 % 64 == 0 && nck % 8 == 0 && 16 * kt * esz <= kSlotBytes && nck / wpr_min <= 32;
   };
   const int order[3] = {4, 2, 1};
   int ns_o = 0, ns_d = 0, ns_in = 0;
