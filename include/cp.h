@@ -74,8 +74,9 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
 /* Normed projections (qkv, gate/up, heads) start their K loop once their own
  * operand units are in and wait for the row's norm partials (one from every
  * producer tile) only before the epilogue, the per-chunk start of section
- * "What's left in the frame, open" (first item).  Same results, bit for bit;
- * measured slower on MI355X at 1 and 64 rows, so off by default. */
+ * "What's left in the frame, open" (first item).  Same results, bit for bit.
+ * One-row frames always run this way (measured faster there); frames of more
+ * rows only with this flag (measured slower at 64 rows on MI355X). */
 #define CP_FLAG_LATE_NORM 0x2u
 /* Every hand-off writes through to memory: no split-K partials or q/k/v kept
  * in one XCD's L2 for readers on that XCD.  A plan also runs this way when,

@@ -759,8 +759,10 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // stay in flight.  A wave with no live rows issued no operand loads but
   // still copied its share of the tile, and waits for every load; so do
   // one-row frames and untagged operands.  (wave_live is wave-uniform.)
-  // (late: the plan waits for the norm partials after the K loop instead)
-  const bool late = NORM && pl.late_norm;
+  // (late: the norm partials are awaited after the K loop instead; always
+  // for one-row frames, 1596 -> 1575 us per frame, with CP_FLAG_LATE_NORM
+  // for the others, where it measured slower: 2545 vs 2509 us at 64 rows)
+  const bool late = NORM && (ONE || pl.late_norm);
   if constexpr (ONE)
     await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live && !late, 1));
   else
