@@ -240,16 +240,17 @@ def calibrate_copy():
 
 
 def _trace_frames(out_dir, wdev, steps=3):
-    """Traced frames of the 5-layer loop at 64 and 1 rows: the decoded split
-    (markdown) and the raw stamps and task table, written to out_dir."""
+    """Traced frames of the 5-layer loop at 64 and 1 rows, greedy, and at 64
+    rows sampled: the decoded split (markdown) and the raw stamps and task
+    table, written to out_dir."""
     import torch
     from persistent_megakernel_streaming_amd import cp, synth, trace
     os.makedirs(out_dir, exist_ok=True)
     res = {}
-    for rows in (64, 1):
-        cfg = synth.CONFIGS["l5_r64"].with_(rows=rows)
+    for rows, sampled in ((64, False), (1, False), (64, True)):
+        cfg = synth.CONFIGS["l5_r64_sampled" if sampled else "l5_r64"].with_(rows=rows)
         plan = cp.Plan(cfg, wdev, exec_mode="persistent", max_rows=rows, flags=cp.CP_FLAG_TRACE)
-        io = cp.make_io(cfg, synth.make_inputs(cfg), logits=False)
+        io = cp.make_io(cfg, synth.make_inputs(cfg, sampled=sampled), logits=False)
         io["trace"] = torch.zeros(plan.info().trace_words, dtype=torch.int64, device="cuda")
         for _ in range(steps):
             plan.run(io)
@@ -257,11 +258,12 @@ def _trace_frames(out_dir, wdev, steps=3):
         plan.device_status()
         table = plan.task_table()
         words = io["trace"].cpu().numpy().view(np.uint64)
-        np.savez(os.path.join(out_dir, f"trace_l5_r{rows}.npz"), words=words, table=table)
+        name = f"trace_l5_r{rows}" + ("_sampled" if sampled else "")
+        np.savez(os.path.join(out_dir, name + ".npz"), words=words, table=table)
         s = trace.summary(trace.decode(words, table), table)
-        with open(os.path.join(out_dir, f"trace_l5_r{rows}.md"), "w") as f:
+        with open(os.path.join(out_dir, name + ".md"), "w") as f:
             f.write(trace.markdown(s) + "\n")
-        res[rows] = s
+        res[str(rows) + ("s" if sampled else "")] = s
         plan.close()
     return res
 

@@ -1590,8 +1590,9 @@ __device__ __forceinline__ uint32_t block_argmax(double sc, uint32_t idx, double
 // key (seed, 0) and counter (offset + j - 1, i, 0, 0): the top 23 bits m of
 // word 0 give u = (2m + 1) / 2^24.  T <= 0 is a greedy draw on z.
 // z: this thread's NE logits, element index threadIdx.x * NE + e (V = 256 NE).
-// scratch: LDS, V * 8 + 128 bytes.  Kept out of line: it runs once per draw
-// and would otherwise add to the register pressure of every task body.
+// lds_scratch: the LDS scratch (at most V * 8 + 128 + 12 KiB is used).
+// Kept out of line: it runs once per draw and would otherwise add to the
+// register pressure of every task body.
 template <int NE>
 struct ZRow {
   float v[NE];
@@ -1601,8 +1602,148 @@ struct DrawArgs {
   int top_k;
   uint64_t seed, ctr;  // Philox key word 0 and counter word 0 of this draw
 };
+// A byte in LDS.  The sampler's out-of-line functions take their scratch as
+// this type: through a generic pointer argument every access would be a FLAT
+// access, which waits on both memory counters.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// 64-bit v from lane ^ 1 (CTRL 0xB1) or lane ^ 2 (0x4E), by DPP.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u<CTRL>((uint32_t)v);
+}
+
+// The Gumbel-max code of one row for top-k cuts of at most 64 keys, or -1
+// (the same in every thread) when the candidates below are too many and the
+// caller has to select in full.  k[]: the row's sort keys, as in
+// block_sort_desc.  The kk-th largest of the 64 quad maxima (the largest key
+// of each four threads) is a floor for the kk-th largest key, since kk
+// distinct keys reach it; only keys at or above it can be kept.  For logits
+// in no particular order they are about twice kk; up to 256 of them are
+// ranked by counting.  Then one wave computes the top-p prefix while another
+// computes the Gumbel noise of the kept ranks, one rank per lane.  The result
+// is the one the full selection gives.  (Out of line: inlined into the
+// sampler it changed the register allocation of the executors' task bodies,
+// which then ran slower.)
 template <int NE>
-__device__ __noinline__ int sampled_code(ZRow<NE> zr, DrawArgs da, uint8_t* scratch) {
+__device__ __noinline__ int small_k_code(const uint64_t (&k)[NE], int kk, const DrawArgs& da, lds_u8* lds_scratch) {
+  uint8_t* scratch = (uint8_t*)lds_scratch;
+  constexpr int kCand = kThreads;  // candidate list size
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t* xch = (uint64_t*)scratch;               // ranks 0 .. kk-1
+  double* noise = (double*)(scratch + 512);         // their Gumbel noise
+  uint64_t* qmx = (uint64_t*)(scratch + 1024);      // the 64 quad maxima
+  uint64_t* floor_key = (uint64_t*)(scratch + 1536);
+  uint32_t* cnt = (uint32_t*)(scratch + 1544);      // [0] candidates, [1] the code
+  uint64_t* cand = (uint64_t*)(scratch + 2048);     // kCand + 16 keys, zero-padded
+  uint64_t mx = k[0];
+#pragma unroll
+  for (int e = 1; e < NE; ++e) mx = k[e] > mx ? k[e] : mx;
+  uint64_t o = dpp_u64<0xB1>(mx);
+  mx = o > mx ? o : mx;
+  o = dpp_u64<0x4E>(mx);
+  mx = o > mx ? o : mx;
+  if ((lane & 3) == 0) qmx[tid >> 2] = mx;
+  cand[tid] = 0;  // zero keys count as smaller than every key
+  if (tid < 16) cand[kCand + tid] = 0;
+  if (tid == 0) cnt[0] = 0;
+  __syncthreads();
+  if (wave == 0) {  // the kk-th largest quad maximum (they are distinct)
+    const uint64_t x = qmx[lane];
+    const u32x4* mv = (const u32x4*)qmx;
+    int above = 0;
+#pragma unroll
+    for (int j0 = 0; j0 < 32; j0 += 16) {
+      u32x4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = mv[j0 + u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint64_t a = ((uint64_t)v[u][1] << 32) | v[u][0], c = ((uint64_t)v[u][3] << 32) | v[u][2];
+        above += (a > x ? 1 : 0) + (c > x ? 1 : 0);
+      }
+    }
+    if (above == kk - 1) floor_key[0] = x;
+  }
+  __syncthreads();
+  const uint64_t fl = floor_key[0];
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+    if (k[e] >= fl) {
+      const uint32_t at = atomicAdd(cnt, 1u);
+      if (at < (uint32_t)kCand) cand[at] = k[e];
+    }
+  __syncthreads();
+  const int C = (int)cnt[0];
+  if (C > kCand) return -1;
+  if (tid < C) {
+    // rank among the candidates, 16 keys a step (the zero padding past C
+    // counts for nothing)
+    const uint64_t key = cand[tid];
+    const u32x4* cv = (const u32x4*)cand;
+    int r = 0;
+    for (int j0 = 0; j0 < C; j0 += 16) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cv[j0 / 2 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint64_t a = ((uint64_t)v[u][1] << 32) | v[u][0], c = ((uint64_t)v[u][3] << 32) | v[u][2];
+        r += (a > key ? 1 : 0) + (c > key ? 1 : 0);
+      }
+    }
+    if (r < kk) xch[r] = key;
+  }
+  __syncthreads();
+  const float pp = da.top_p;
+  int n_keep = kk;
+  uint64_t key = 0;
+  if (wave == 0) {
+    key = lane < kk ? xch[lane] : 0ull;
+    if (pp <= 0.0f) {
+      n_keep = 1;
+    } else if (pp < 1.0f) {  // softmax weights relative to the largest y, fp64, rank order
+      const double ymax = (double)key_value(xch[0]);
+      const double w = lane < kk ? exp((double)key_value(key) - ymax) : 0.0;
+      double cum = w;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const double y = __shfl_up(cum, d, 64);
+        if (lane >= d) cum += y;
+      }
+      const double Z = __shfl(cum, 63, 64);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < kk && cum / Z >= (double)pp);
+      if (hit) n_keep = __ffsll((unsigned long long)hit);  // the first crossing rank, included
+    }
+  } else if (wave == 1 && lane < kk) {
+    // -log(-log u) of rank `lane`, u from word 0 of the token's Philox block
+    const uint64_t m = philox4x64_w0(da.ctr, (uint64_t)key_index(xch[lane]), 0, 0, da.seed, 0) >> 41;
+    const double u = (double)(2 * m + 1) * (1.0 / 16777216.0);
+    noise[lane] = -log(-log(u));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    double sc = -INFINITY;
+    uint32_t bi = 0xffffffffu;
+    if (lane < n_keep) {
+      bi = key_index(key);
+      sc = (double)key_value(key) + noise[lane];
+    }
+    wave_tree([&](auto other) {
+      const uint64_t sb = (uint64_t)__double_as_longlong(sc);
+      const double os = __longlong_as_double(
+          (long long)(((uint64_t)other((uint32_t)(sb >> 32)) << 32) | other((uint32_t)sb)));
+      const uint32_t oi = other(bi);
+      if (os > sc || (os == sc && oi < bi)) { sc = os; bi = oi; }
+    });
+    if (lane == 0) cnt[1] = bi;
+  }
+  __syncthreads();
+  return (int)cnt[1];
+}
+
+template <int NE>
+__device__ __noinline__ int sampled_code(ZRow<NE> zr, DrawArgs da, lds_u8* lds_scratch) {
+  uint8_t* scratch = (uint8_t*)lds_scratch;
   const int V = kThreads * NE;
   uint64_t* xch = (uint64_t*)scratch;
   double* red = (double*)(scratch + (size_t)V * 8);
@@ -1624,6 +1765,10 @@ __device__ __noinline__ int sampled_code(ZRow<NE> zr, DrawArgs da, uint8_t* scra
   for (int e = 0; e < NE; ++e) k[e] = rank_key(z[e] / T, (uint32_t)(tid * NE + e));
   const int tk = da.top_k;
   const int kk = (tk <= 0 || tk >= V) ? V : tk;
+  if (kk <= 64) {
+    const int code = small_k_code<NE>(k, kk, da, (lds_u8*)scratch);
+    if (code >= 0) return code;
+  }
   if (kk < kThreads) {
     // only the top kk ranks matter: select them instead of sorting all V
     uint64_t* tmp = (uint64_t*)(scratch + (size_t)V * 8 + 128);
@@ -1706,7 +1851,7 @@ __device__ __forceinline__ int sampled_row(const DevPlan& pl, const DevFrame& fr
   for (int e = 0; e < NE; ++e) zr.v[e] = z[e];
   const DrawArgs da = {fr.temperature[row], fr.top_p[row], fr.top_k[row], fr.seed[row],
                        fr.offset[row] + (uint64_t)(j - 1)};
-  return sampled_code<NE>(zr, da, scratch);
+  return sampled_code<NE>(zr, da, (lds_u8*)scratch);
 }
 
 template <int BF, bool ASM>

@@ -557,22 +557,57 @@ def test_sampled_l5_64_rows():
     print(f"sampled l5 r64: max logit err {err:.4f}, robust draws {frac:.2f}")
 
 
-@pytest.mark.parametrize("name,top_ks", [
-    ("tiny_f32", [255, 256, 254, 2]),           # 255 = the largest cut below V that is selected, 256 = V
-    ("l5_r64_sampled", [255, 256, 2047, 64]),   # below / at the 256-key selection limit, V - 1
+@pytest.mark.parametrize("name,top_ks,top_p", [
+    ("tiny_f32", [255, 256, 254, 2], None),           # 255 = the largest cut below V that is selected, 256 = V
+    ("l5_r64_sampled", [255, 256, 2047, 65], None),   # below / at the 256-key selection limit, V - 1
+    ("tiny_f32", [64, 65, 63, 1], None),              # around the 64-key candidate limit
+    ("l5_r64_sampled", [64, 65, 63, 1], None),
+    ("l5_r64_sampled", [64, 65, 50, 10], 0.9),        # the same with top-p cutting inside the kept keys
+    ("tiny_f32", [64, 65, 20, 2], 0.9),
 ])
-def test_sampled_top_k_around_selection_limit(name, top_ks):
-    """Top-k cuts of fewer than 256 keys are selected a byte at a time, larger
-    ones sorted in full: draws on both sides of the limit against the oracle,
-    with top-p off so that top-k alone sets the kept set."""
+def test_sampled_top_k_around_selection_limit(name, top_ks, top_p):
+    """Top-k cuts of at most 64 keys are ranked among the candidates at or
+    above the kk-th largest per-thread maximum, other cuts below 256 keys are
+    selected a byte at a time, larger ones sorted in full: draws on both sides
+    of each limit against the oracle, with top-p off (so that top-k alone sets
+    the kept set) or at 0.9."""
     cfg = synth.CONFIGS[name].with_(rows=4, sampled=True)
     w, wdev, ow = _weights(cfg, seed=7)
     inputs = synth.make_inputs(cfg, seed=7, sampled=True)
     inputs["top_k"] = np.array(top_ks, dtype=np.int32)
-    inputs["top_p"] = np.ones(4, dtype=np.float32)
+    inputs["top_p"] = np.full(4, 1.0 if top_p is None else top_p, dtype=np.float32)
     gpu = _gpu_frame(cfg, wdev, inputs)
     err, frac = _check_sampled(cfg, ow, inputs, gpu, range(4), 1e-4 if cfg.dtype == "f32" else 0.05)
     print(f"top-k {top_ks} {name}: max logit err {err:.2e}, robust draws {frac:.2f}")
+
+
+@pytest.mark.parametrize("name", ["l5_r64_sampled", "tiny_f32"])
+def test_sampled_tied_logits_against_oracle_draws(name):
+    """All logits equal (zero head weights): the keys tie on value and order
+    by index alone.  Then the kk-th largest of the 64 four-thread maxima leaves
+    about 4 NE (kk - 1) candidates, so at vocab 2048 cuts of 9 keys and more
+    overflow the 256 the counting path ranks and take the byte-wise selection,
+    while a cut of 8 stays on the counting path (at vocab 256 all of them
+    do).  Every draw against the oracle's draw on the same (exactly zero)
+    logits: ties go to the lower index on both sides."""
+    from oracle import oracle
+    cfg = synth.CONFIGS[name].with_(rows=4, sampled=True)
+    w = synth.make_weights(cfg, seed=3)
+    for key in list(w):
+        if key.startswith("w_head"):
+            w[key] = np.zeros_like(w[key])
+    wdev = _cp().upload_weights(cfg, w)
+    inputs = synth.make_inputs(cfg, seed=3, sampled=True)
+    inputs["top_k"] = np.array([8, 9, 50, 64], dtype=np.int32)
+    inputs["top_p"] = np.array([1.0, 0.9, 0.85, 1.0], dtype=np.float32)
+    gpu = _gpu_frame(cfg, wdev, inputs)
+    assert np.all(gpu["logits"] == 0)
+    for r in range(4):
+        for j in range(1, cfg.n_positions):
+            code, m = oracle.draw(np.zeros(cfg.vocab, np.float32), inputs["temperature"][r], inputs["top_k"][r],
+                                  inputs["top_p"][r], int(inputs["seed"][r]), int(inputs["offset"][r]) + j - 1)
+            assert min(m[0], m[2], m[3]) > 1e-9, (r, j, m.tolist())
+            assert gpu["codes"][r, j - 1] == code, (r, j, int(gpu["codes"][r, j - 1]), code)
 
 
 def test_sampled_persistent_equals_per_phase_and_repeats():
