@@ -158,6 +158,22 @@ std::vector<int> spread(int n, int n_wg, int& rot) {
   return m;
 }
 
+// Spreads n tasks over the workgroups in rotation order like spread, but
+// (when n <= n_wg) puts the workgroups marked late -- the owners of the last
+// split-K phase, which add their partners' partial sums after their own K
+// part -- after all the others.
+std::vector<int> spread_late_last(int n, int n_wg, int& rot, const std::vector<char>& late) {
+  if (n > n_wg) return spread(n, n_wg, rot);
+  std::vector<int> m;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int i = 0; i < n_wg && (int)m.size() < n; ++i) {
+      const int w = (rot + i) % n_wg;
+      if ((late[w] != 0) == (pass == 1)) m.push_back(w);
+    }
+  rot = (rot + n) % n_wg;
+  return m;
+}
+
 // Split-K tasks (tile t, split s): the nsplit partners of a tile share an XCD
 // (workgroups are dealt to XCDs round-robin by id) when the phase fills the
 // grid; `local` tells whether they do.
@@ -335,6 +351,7 @@ static cp_status build_schedule(cp_plan* P) {
   const int gu_per_split = gu_tiles / ns_d;
   const int kv_per_osplit = nkv / ns_o;  // kv heads whose attention output one o split reads
   int rot = 0;
+  std::vector<char> late(n_wg, 0);  // owners of the last split-K phase
 
   // Every task records the phases whose outputs it reads (ph_in0, ph_in1):
   // its input words must carry those phases' tags.  The counter groups below
@@ -453,6 +470,8 @@ static cp_status build_schedule(cp_plan* P) {
         bool local = false;
         const std::vector<int> m = split_map(ht, ns_o, n_wg, rot, local);
         mark_local(ts, local);
+        late.assign(n_wg, 0);
+        for (int t = 0; t < ht; ++t) late[m[t * ns_o] % n_wg] = 1;
         B.phase(ts, m);
       }
       // gate/up
@@ -468,7 +487,9 @@ static cp_status build_schedule(cp_plan* P) {
           k.sig = g_gu[t / gu_per_split]; k.sig_slot = t % gu_per_split;
           ts.push_back(k);
         }
-        B.phase(ts, spread(gu_tiles, n_wg, rot));
+        // One-row frames: off the o owners, whose sums come last (about 30 us
+        // per frame; slower by 20 us at 64 rows, where it is not used).
+        B.phase(ts, R == 1 ? spread_late_last(gu_tiles, n_wg, rot, late) : spread(gu_tiles, n_wg, rot));
       }
       // down (split-K over the intermediate; a split reads the gate/up tiles of its slice)
       const uint32_t g_down = B.group(ht);
@@ -488,6 +509,8 @@ static cp_status build_schedule(cp_plan* P) {
         bool local = false;
         const std::vector<int> m = split_map(ht, ns_d, n_wg, rot, local);
         mark_local(ts, local);
+        late.assign(n_wg, 0);
+        for (int t = 0; t < ht; ++t) late[m[t * ns_d] % n_wg] = 1;
         B.phase(ts, m);
       }
       g_layer_in = g_down;
@@ -506,7 +529,7 @@ static cp_status build_schedule(cp_plan* P) {
         k.sig = g_head; k.sig_slot = t;
         ts.push_back(k);
       }
-      B.phase(ts, spread(head_tiles, n_wg, rot));
+      B.phase(ts, spread_late_last(head_tiles, n_wg, rot, late));  // off the down owners
     }
     const uint32_t g_draw = B.group(R);
     const int ph_draw = B.next_phase();
