@@ -291,7 +291,7 @@ def main():
     import torch
     from persistent_megakernel_streaming_amd import cp, synth
 
-    everything = {"p64", "p1", "p128", "s64", "pp64", "pp1", "late", "nolocal", "cross", "qk", "l10", "floor", "chain",
+    everything = {"p64", "p1", "p128", "s64", "pp64", "pp1", "late", "nolocal", "rg", "cross", "qk", "l10", "floor", "chain",
                   "cold", "pct"}
     only = set(args.only.split(",")) if args.only else everything
     steps, warm, reps = args.steps, args.warmup, args.repeats
@@ -369,6 +369,12 @@ def main():
             io = cp.make_io(c, synth.make_inputs(c), logits=False)
             res[f"write_through_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
             pl.close()
+    if "rg" in only:
+        # two 32-row groups per projection tile, run back to back (CP_FLAG_ROW_GROUPS)
+        pl = cp.Plan(cfg64, wdev, exec_mode="persistent", max_rows=64, flags=cp.CP_FLAG_ROW_GROUPS)
+        io = cp.make_io(cfg64, synth.make_inputs(cfg64), logits=False)
+        res["row_groups_persistent_us_64"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
+        pl.close()
     if "cross" in only:
         # the row-count crossover: persistent frame against the per-phase
         # loop (captured as a graph) on one plan, rows 1 .. 64

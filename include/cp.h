@@ -85,6 +85,17 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
  * writer's XCD).  For measurement, and for a device whose dealing could
  * change after that check. */
 #define CP_FLAG_NO_LOCAL 0x4u
+/* Two (or more) row groups in flight, the second item of section "What's
+ * left in the frame, open": every projection task of a frame of more than 32
+ * rows is split into tasks of 32 rows that one workgroup runs back to back
+ * on the same weight tile, so that while one group's operands are in flight
+ * the workgroup computes the other's.  Not bit for bit the default plan's
+ * results: the waves of a 32-row task split K and add their parts in another
+ * order (within the same tolerances against the reference).  Measured slower
+ * than the default on MI355X (the groups never drift apart, and every phase
+ * pays two task overheads).  Persistent executor only (CP_ERR_UNSUPPORTED
+ * with CP_EXEC_PER_PHASE). */
+#define CP_FLAG_ROW_GROUPS 0x8u
 
 /* Shapes and settings of a plan.  Supported (else CP_ERR_UNSUPPORTED):
  * head_dim 64 or 128; n_q_heads a multiple of 4 and of n_kv_heads; hidden a

@@ -24,6 +24,7 @@ CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1
 CP_FLAG_LATE_NORM = 2
 CP_FLAG_NO_LOCAL = 4
+CP_FLAG_ROW_GROUPS = 8
 ABI_VERSION = 3
 EPOCH_WRAP = (1 << 22) - 1  # epochs run 1 .. EPOCH_WRAP - 1
 
@@ -114,9 +115,9 @@ def make_config(cfg, max_rows=None, exec_mode="persistent", flags=0) -> Config:
                   qk_norm=1 if getattr(cfg, "qk_norm", False) else 0)
 
 
-def schedule_check(cfg, cu_count=256, max_rows=None):
+def schedule_check(cfg, cu_count=256, max_rows=None, flags=0):
     """Builds and checks the task lists for a device of cu_count CUs (host only)."""
-    c = make_config(cfg, max_rows=max_rows)
+    c = make_config(cfg, max_rows=max_rows, flags=flags)
     info = PlanInfo()
     st = _lib.cp_schedule_check(C.byref(c), int(cu_count), C.byref(info))
     if st != CP_OK:

@@ -60,6 +60,9 @@ constexpr uint8_t kTaskLocalPartials = 1;
 // Task flag (qkv): the attention tasks that read this tile's q, k and v run on
 // this workgroup's XCD, so the stores stay in its L2.
 constexpr uint8_t kTaskLocalQkv = 2;
+// Task flags, bits 4-7: the row group of a projection task when the plan
+// runs row groups (DevPlan::grp_rows rows each).
+constexpr int kTaskGroupShift = 4;
 
 struct Span {
   void* p;
@@ -114,6 +117,7 @@ struct DevPlan {
   int tasks_in_lds;             // every workgroup's list fits kTaskLds: the executor copies it to LDS
   int late_norm;                // CP_FLAG_LATE_NORM: normed projections wait for norm partials after the K loop
   int local_ok;                 // XCD-local hand-offs allowed (not CP_FLAG_NO_LOCAL)
+  int grp_rows;                 // CP_FLAG_ROW_GROUPS: rows per projection task (0: all, in passes of 64)
   // task lists
   const DevTask* tasks;         // all tasks, grouped by workgroup
   const uint32_t* wg_begin;     // [n_wg + 1]

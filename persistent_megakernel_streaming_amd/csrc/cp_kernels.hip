@@ -587,7 +587,8 @@ __device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
 template <int BF, int KIND, bool ONE = false, bool ASM = !ONE>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, int rh = 0) {
+                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, int r0 = 0,
+                                          int gr = 64) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
@@ -654,17 +655,18 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   }
   const int nck = kt * ESZ / 64;  // 16-byte payload chunks per lane over the task's K range
 
-  // Waves and row tiles: a wave owns 16 rows of a group of 64; with few rows
-  // the waves of a row tile split K and add their results through LDS in a
-  // fixed order.  A frame of more than 64 rows runs the task once per group
-  // of 64 (rh), the weight tile staying in LDS.
-  const int rows_h = min(rows - 64 * rh, 64);
+  // Waves and row tiles: a wave owns 16 rows of a group of gr <= 64 rows
+  // starting at row r0; with few rows the waves of a row tile split K and add
+  // their results through LDS in a fixed order.  A frame of more than 64 rows
+  // runs the task once per group of 64, the weight tile staying in LDS; with
+  // row groups each task is one group of 32.
+  const int rows_h = min(rows - r0, gr);
   const int nrt = (rows_h + 15) >> 4;                 // row tiles of this group holding live rows (1..4)
   int wpr = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);        // waves per row tile
   // each wave takes whole groups of NU chunks (one-row frames: blocks of 4)
   while (wpr > 1 && nck % ((ONE ? 4 : NU) * wpr)) wpr >>= 1;
   const int rt = wave / wpr, ks = wave % wpr;
-  const int rta = rh * 4 + rt;                        // the row tile in the frame
+  const int rta = (r0 >> 4) + rt;                     // the row tile in the frame
   const int ncw = nck / wpr;                          // chunks this wave handles (a multiple of NU)
   const int ng = ncw / NU;
   const int c0 = ks * ncw;
@@ -1936,7 +1938,14 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
       break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
-#define CP_PROJ(K) for (int rh = 0; rh * 64 < fr.rows; ++rh) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh);
+#define CP_PROJ(K)                                                                                  \
+  if (pl.grp_rows) {                                                                                \
+    const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;                                     \
+    if (r0 < fr.rows) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows); \
+  } else {                                                                                          \
+    for (int rh = 0; rh * 64 < fr.rows; ++rh)                                                       \
+      proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh * 64, 64);                   \
+  }
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
     case T_GU: CP_PROJ(T_GU) break;
@@ -1944,8 +1953,13 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
     case T_HEAD: CP_PROJ(T_HEAD) break;
 #undef CP_PROJ
     default:
-      for (int rh = 0; rh * 64 < fr.rows; ++rh)
-        proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh);
+      if (pl.grp_rows) {
+        const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;
+        if (r0 < fr.rows) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows);
+      } else {
+        for (int rh = 0; rh * 64 < fr.rows; ++rh)
+          proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh * 64, 64);
+      }
       break;
   }
 }

@@ -289,7 +289,14 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   // an o split (n_q_heads / 4 heads) must read at most kMaxWaits kv heads
   const int gq = c->n_q_heads / c->n_kv_heads, hps = c->n_q_heads / 4;
   if ((hps - 1) / gq + 2 > kMaxWaits && hps / gq > kMaxWaits) { msg = "kv grouping not supported"; return CP_ERR_UNSUPPORTED; }
-  if (c->flags & ~(CP_FLAG_TRACE | CP_FLAG_LATE_NORM | CP_FLAG_NO_LOCAL)) { msg = "unknown flag"; return CP_ERR_UNSUPPORTED; }
+  if (c->flags & ~(CP_FLAG_TRACE | CP_FLAG_LATE_NORM | CP_FLAG_NO_LOCAL | CP_FLAG_ROW_GROUPS)) {
+    msg = "unknown flag";
+    return CP_ERR_UNSUPPORTED;
+  }
+  if ((c->flags & CP_FLAG_ROW_GROUPS) && c->exec != CP_EXEC_PERSISTENT) {
+    msg = "CP_FLAG_ROW_GROUPS needs the persistent executor";
+    return CP_ERR_UNSUPPORTED;
+  }
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) { msg = "rms_eps / rope_theta"; return CP_ERR_INVALID_ARGUMENT; }
   return CP_OK;
 }
@@ -344,6 +351,24 @@ static cp_status build_schedule(cp_plan* P) {
   const int ht = H / 16, qkv_tiles = (nq + 2 * nkv) * d / 16, tpg = (gq + 2) * d / 16;
   const int gu_tiles = I / 16, head_tiles = V / 16;
   const int ns_o = P->dp.n_o_split, ns_d = P->dp.n_d_split, ns_in = P->dp.n_in_split;
+  // Row groups: projection tasks of 32 rows, G per tile, run back to back by
+  // one workgroup (their signals count G times).
+  const int G = (P->cfg.flags & CP_FLAG_ROW_GROUPS) && R > 32 ? (R + 31) / 32 : 1;
+  P->dp.grp_rows = G > 1 ? 32 : 0;
+  auto grouped = [&](std::vector<Task>& ts, std::vector<int>& m) {
+    if (G == 1) return;
+    std::vector<Task> t2;
+    std::vector<int> m2;
+    for (size_t i = 0; i < ts.size(); ++i)
+      for (int g = 0; g < G; ++g) {
+        Task k = ts[i];
+        k.flags |= (uint8_t)(g << kTaskGroupShift);
+        t2.push_back(k);
+        m2.push_back(m[i]);
+      }
+    ts.swap(t2);
+    m.swap(m2);
+  };
   int ar = std::max(1, 4 / gq);
   while (R % ar) --ar;
   const int agroups = R / ar;
@@ -362,7 +387,7 @@ static cp_status build_schedule(cp_plan* P) {
   for (int r = 0; r < R; ++r) row_wg[r] = r % n_wg;
 
   // input projection (split-K) and code-0 embedding: no inputs from the frame
-  const uint32_t g_inp = B.group(ht);
+  const uint32_t g_inp = B.group(ht * G);
   const int ph_inp = B.next_phase();
   {
     std::vector<Task> ts;
@@ -373,8 +398,9 @@ static cp_status build_schedule(cp_plan* P) {
         ts.push_back(k);
       }
     bool local = false;
-    const std::vector<int> m = split_map(ht, ns_in, n_wg, rot, local);
+    std::vector<int> m = split_map(ht, ns_in, n_wg, rot, local);
     mark_local(ts, local);
+    grouped(ts, m);
     B.phase(ts, m);
   }
   const uint32_t g_emb0 = B.group(R);
@@ -400,7 +426,7 @@ static cp_status build_schedule(cp_plan* P) {
     for (int l = 0; l < L; ++l) {
       // qkv
       std::vector<uint32_t>& gq_groups = g_qkv[p * L + l];
-      for (int g = 0; g < nkv; ++g) gq_groups.push_back(B.group(tpg, 4));
+      for (int g = 0; g < nkv; ++g) gq_groups.push_back(B.group(tpg * G, 4));
       const int ph_qkv = B.next_phase();
       {
         std::vector<Task> ts;
@@ -416,9 +442,13 @@ static cp_status build_schedule(cp_plan* P) {
           std::vector<int> x(qkv_tiles);
           for (int t = 0; t < qkv_tiles; ++t) x[t] = t / tpg;
           mark_local(ts, true, kTaskLocalQkv);
-          B.phase(ts, xcd_deal(x, n_wg, rot));
+          std::vector<int> m = xcd_deal(x, n_wg, rot);
+          grouped(ts, m);
+          B.phase(ts, m);
         } else {
-          B.phase(ts, spread(qkv_tiles, n_wg, rot));
+          std::vector<int> m = spread(qkv_tiles, n_wg, rot);
+          grouped(ts, m);
+          B.phase(ts, m);
         }
       }
       // Position 0 has no head: the residual after its last layer feeds
@@ -453,7 +483,7 @@ static cp_status build_schedule(cp_plan* P) {
       g_attn[p * L + l] = g_att;
       if (p == 0 && l == L - 1) break;
       // o (split-K over q heads; a split reads only the kv heads of its slice)
-      const uint32_t g_o = B.group(ht);
+      const uint32_t g_o = B.group(ht * G);
       const int ph_o = B.next_phase();
       {
         std::vector<Task> ts;
@@ -468,15 +498,16 @@ static cp_status build_schedule(cp_plan* P) {
             ts.push_back(k);
           }
         bool local = false;
-        const std::vector<int> m = split_map(ht, ns_o, n_wg, rot, local);
+        std::vector<int> m = split_map(ht, ns_o, n_wg, rot, local);
         mark_local(ts, local);
         late.assign(n_wg, 0);
         for (int t = 0; t < ht; ++t) late[m[t * ns_o] % n_wg] = 1;
+        grouped(ts, m);
         B.phase(ts, m);
       }
       // gate/up
       std::vector<uint32_t> g_gu(ns_d);
-      for (int s = 0; s < ns_d; ++s) g_gu[s] = B.group(gu_per_split, 4);
+      for (int s = 0; s < ns_d; ++s) g_gu[s] = B.group(gu_per_split * G, 4);
       const int ph_gu = B.next_phase();
       {
         std::vector<Task> ts;
@@ -489,10 +520,12 @@ static cp_status build_schedule(cp_plan* P) {
         }
         // One-row frames: off the o owners, whose sums come last (about 30 us
         // per frame; slower by 20 us at 64 rows, where it is not used).
-        B.phase(ts, R == 1 ? spread_late_last(gu_tiles, n_wg, rot, late) : spread(gu_tiles, n_wg, rot));
+        std::vector<int> m = R == 1 ? spread_late_last(gu_tiles, n_wg, rot, late) : spread(gu_tiles, n_wg, rot);
+        grouped(ts, m);
+        B.phase(ts, m);
       }
       // down (split-K over the intermediate; a split reads the gate/up tiles of its slice)
-      const uint32_t g_down = B.group(ht);
+      const uint32_t g_down = B.group(ht * G);
       const int ph_down = B.next_phase();
       {
         std::vector<Task> ts;
@@ -507,10 +540,11 @@ static cp_status build_schedule(cp_plan* P) {
             ts.push_back(k);
           }
         bool local = false;
-        const std::vector<int> m = split_map(ht, ns_d, n_wg, rot, local);
+        std::vector<int> m = split_map(ht, ns_d, n_wg, rot, local);
         mark_local(ts, local);
         late.assign(n_wg, 0);
         for (int t = 0; t < ht; ++t) late[m[t * ns_d] % n_wg] = 1;
+        grouped(ts, m);
         B.phase(ts, m);
       }
       g_layer_in = g_down;
@@ -518,7 +552,7 @@ static cp_status build_schedule(cp_plan* P) {
     }
     if (p == 0) continue;
     // head p and draw p
-    const uint32_t g_head = B.group(head_tiles);
+    const uint32_t g_head = B.group(head_tiles * G);
     const int ph_head = B.next_phase();
     {
       std::vector<Task> ts;
@@ -529,7 +563,9 @@ static cp_status build_schedule(cp_plan* P) {
         k.sig = g_head; k.sig_slot = t;
         ts.push_back(k);
       }
-      B.phase(ts, spread_late_last(head_tiles, n_wg, rot, late));  // off the down owners
+      std::vector<int> m = spread_late_last(head_tiles, n_wg, rot, late);  // off the down owners
+      grouped(ts, m);
+      B.phase(ts, m);
     }
     const uint32_t g_draw = B.group(R);
     const int ph_draw = B.next_phase();
@@ -619,7 +655,9 @@ static cp_status check_schedule(cp_plan* P) {
       const Task& a = P->tasks[i];
       if (a.nsplit > 1 && a.split == 0)
         for (uint32_t j = i + 1; j < P->wg_begin[w + 1] && P->tasks[j].phase == a.phase; ++j)
-          if (P->tasks[j].tile == a.tile) return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: split partner after its owner");
+          if (P->tasks[j].tile == a.tile && P->tasks[j].split != 0 &&
+              (P->tasks[j].flags >> kTaskGroupShift) == (a.flags >> kTaskGroupShift))
+            return fail(P, CP_ERR_INVALID_ARGUMENT, "schedule: split partner after its owner");
     }
   for (size_t ph = 0; ph + 1 < P->phase_begin.size() && P->cfg.exec == CP_EXEC_PER_PHASE; ++ph) {
     const Task& f = P->phase_tasks[P->phase_begin[ph]];

@@ -74,6 +74,26 @@ def test_schedule_invariants(name, cus):
     assert info.max_tasks_per_workgroup * cus >= info.n_tasks
 
 
+@pytest.mark.parametrize("name", ["l5_r64", "l5_r128", "l5_qk_r64", "l5_in2048_r8", "l5_r1"])
+@pytest.mark.parametrize("cus", [256, 64, 7])
+def test_row_group_schedule_invariants(name, cus):
+    """CP_FLAG_ROW_GROUPS: every projection task of a plan of more than 32
+    rows becomes one task per 32-row group on the same workgroup (the
+    schedule check accepts the lists); plans of at most 32 rows are unchanged."""
+    cp = _cp()
+    cfg = synth.CONFIGS[name]
+    a = cp.schedule_check(cfg, cu_count=cus)
+    b = cp.schedule_check(cfg, cu_count=cus, flags=cp.CP_FLAG_ROW_GROUPS)
+    assert b.n_phases == a.n_phases
+    if cfg.rows <= 32:
+        assert b.n_tasks == a.n_tasks
+    else:
+        assert b.n_tasks > a.n_tasks
+    c = cp.make_config(cfg, exec_mode="per_phase", flags=cp.CP_FLAG_ROW_GROUPS)
+    info = cp.PlanInfo()
+    assert cp.lib().cp_schedule_check(C.byref(c), cus, C.byref(info)) == 2  # persistent executor only
+
+
 def test_qk_norm_gains_are_plan_constants():
     """The QK-norm variant keeps its head-norm gains ([L][q, k][head_dim]
     fp32) with the plan's constants; the schedule gains one phase, position

@@ -181,6 +181,21 @@ def test_full_l5_40_rows_idle_wave():
     print(f"l5 r40: max logit err {err:.4f}, decided {frac:.2f}")
 
 
+@pytest.mark.parametrize("rows", [64, 40])
+def test_row_groups_against_oracle(rows):
+    """CP_FLAG_ROW_GROUPS: projection tasks of 32 rows, two per tile run back
+    to back (at 40 rows the second group holds 8).  Against the oracle on
+    every row, K/V included; not bitwise equal to the default plan, whose
+    64-row tasks add the waves' K parts in another order."""
+    cp = _cp()
+    cfg = synth.CONFIGS["l5_r64"].with_(rows=rows)
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg)
+    gpu = _gpu_frame(cfg, wdev, inputs, max_rows=64, kv=True, flags=cp.CP_FLAG_ROW_GROUPS)
+    err, frac = _check(cfg, ow, inputs, gpu, range(rows), 0.05, kv=True)
+    print(f"row groups, l5 r{rows}: max logit err {err:.4f}, decided {frac:.2f}")
+
+
 @pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
 def test_full_l5_gain_jitter(exec_mode):
     """Full-size bf16 with RMSNorm gains 1 + N(0, 0.1): the plan folds each
