@@ -1938,8 +1938,11 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
       break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
+// (one-row frames: only a task of row group 0 has the row)
 #define CP_PROJ(K)                                                                                  \
-  if (pl.grp_rows) {                                                                                \
+  if constexpr (ONE) {                                                                              \
+    if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, 0, 64); \
+  } else if (pl.grp_rows) {                                                                         \
     const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;                                     \
     if (r0 < fr.rows) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows); \
   } else {                                                                                          \
@@ -1953,7 +1956,9 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
     case T_HEAD: CP_PROJ(T_HEAD) break;
 #undef CP_PROJ
     default:
-      if (pl.grp_rows) {
+      if constexpr (ONE) {
+        if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, 0, 64);
+      } else if (pl.grp_rows) {
         const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;
         if (r0 < fr.rows) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows);
       } else {
