@@ -196,6 +196,22 @@ def test_row_groups_against_oracle(rows):
     print(f"row groups, l5 r{rows}: max logit err {err:.4f}, decided {frac:.2f}")
 
 
+def test_row_groups_128_rows_task_records_from_memory():
+    """CP_FLAG_ROW_GROUPS at 128 rows: four 32-row groups per tile, and task
+    lists too long for the LDS copy (more than 832 records per workgroup), so
+    the executor reads each record from memory.  Every row against the
+    oracle."""
+    cp = _cp()
+    cfg = synth.CONFIGS["l5_r128"]
+    info = cp.schedule_check(cfg, flags=cp.CP_FLAG_ROW_GROUPS)
+    assert info.max_tasks_per_workgroup * 24 > 19968  # the LDS copy holds 832 records
+    w, wdev, ow = _weights(cfg)
+    inputs = synth.make_inputs(cfg, seed=9)
+    gpu = _gpu_frame(cfg, wdev, inputs, kv=True, flags=cp.CP_FLAG_ROW_GROUPS)
+    err, frac = _check(cfg, ow, inputs, gpu, range(128), 0.05, kv=True)
+    print(f"row groups, l5 r128: max logit err {err:.4f}, decided {frac:.2f}")
+
+
 @pytest.mark.parametrize("exec_mode", ["persistent", "per_phase"])
 def test_full_l5_gain_jitter(exec_mode):
     """Full-size bf16 with RMSNorm gains 1 + N(0, 0.1): the plan folds each
