@@ -292,6 +292,9 @@ __device__ __forceinline__ void issue_tile(const DevPlan& pl, const DevTask& tk,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const uint32_t nch = tk.w_bytes >> 10;
   const uint8_t* src = pl.wblob + tk.w_off;
+  // (unrolled: 1516 -> 1510 us per one-row frame; a buffer-resource form
+  // of the same copy measured 20-30 us slower)
+#pragma unroll 4
   for (uint32_t c = wave; c < nch; c += 4) {
     __builtin_amdgcn_global_load_lds((const void*)(src + c * 1024 + lane * 16),
                                      (void __attribute__((address_space(3)))*)(slot + c * 1024), 16, 0, 0);
