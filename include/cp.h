@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   CP_OK = 0,
   CP_ERR_INVALID_ARGUMENT = 1, /* NULL where a pointer is required, rows out of range, ... */
-  CP_ERR_UNSUPPORTED = 2,      /* shape, dtype or setting this build does not run */
+  CP_ERR_UNSUPPORTED = 2,      /* shape, dtype or setting the library does not run */
   CP_ERR_NOT_CORESIDENT = 3,   /* the persistent grid cannot be resident all at once */
   CP_ERR_OUT_OF_MEMORY = 4,
   CP_ERR_HIP = 5,              /* a HIP runtime call failed; see cp_plan_last_error */
