@@ -335,6 +335,15 @@ const char* cp_last_create_error(void);
  * planning tools; cp_plan_create runs the same checks. */
 cp_status cp_schedule_check(const cp_config* cfg, int cu_count, cp_plan_info* info);
 
+/* The task table of the schedule cp_schedule_check builds for cfg and
+ * cu_count, in cp_plan_task_table's layout ([n_tasks][8] int32: phase, type,
+ * layer, pos, tile, split, workgroup, index in the workgroup's list), touching
+ * no device (section "Testing": task lists are inspected on the host).
+ * n_tasks must equal the count cp_schedule_check reports, else
+ * CP_ERR_INVALID_ARGUMENT; other errors as cp_schedule_check.  For tests of
+ * the placement and for planning tools. */
+cp_status cp_schedule_task_table(const cp_config* cfg, int cu_count, int32_t* out, int64_t n_tasks);
+
 /* ---------------------------------------------------------------- measurement
  * Two floors the pull request prices a frame against (section "Where the
  * depth loop's time goes"): the weight-read floor (bullet "The floor") and the

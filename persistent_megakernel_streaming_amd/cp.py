@@ -83,6 +83,7 @@ def load_library():
     lib.cp_plan_last_error.restype = C.c_char_p
     lib.cp_last_create_error.restype = C.c_char_p
     lib.cp_schedule_check.argtypes = [C.POINTER(Config), C.c_int, C.POINTER(PlanInfo)]
+    lib.cp_schedule_task_table.argtypes = [C.POINTER(Config), C.c_int, C.c_void_p, C.c_int64]
     lib.cp_plan_task_table.argtypes = [C.c_void_p, C.c_void_p, C.c_int64]
     lib.cp_plan_set_epoch.argtypes = [C.c_void_p, C.c_uint32]
     lib.cp_plan_set_spin_limit.argtypes = [C.c_void_p, C.c_uint32]
@@ -90,7 +91,7 @@ def load_library():
     lib.cp_stream_read.argtypes = [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]
     lib.cp_chain_run.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     for f in ("cp_plan_create", "cp_plan_create_static", "cp_frame_run", "cp_plan_destroy", "cp_plan_query", "cp_plan_device_status",
-              "cp_schedule_check", "cp_plan_task_table", "cp_plan_set_epoch", "cp_plan_set_spin_limit",
+              "cp_schedule_check", "cp_schedule_task_table", "cp_plan_task_table", "cp_plan_set_epoch", "cp_plan_set_spin_limit",
               "cp_plan_set_crossover", "cp_stream_read", "cp_chain_run"):
         getattr(lib, f).restype = C.c_int
     return lib
@@ -123,6 +124,18 @@ def schedule_check(cfg, cu_count=256, max_rows=None, flags=0):
     if st != CP_OK:
         raise CpError(st, _lib.cp_last_create_error().decode())
     return info
+
+
+def schedule_task_table(cfg, cu_count=256, max_rows=None, flags=0) -> np.ndarray:
+    """[n_tasks][8] int32 task table of the host-built schedule (phase, type,
+    layer, pos, tile, split, workgroup, index in list); touches no device."""
+    c = make_config(cfg, max_rows=max_rows, flags=flags)
+    info = schedule_check(cfg, cu_count=cu_count, max_rows=max_rows, flags=flags)
+    out = np.zeros((info.n_tasks, 8), np.int32)
+    st = _lib.cp_schedule_task_table(C.byref(c), int(cu_count), out.ctypes.data, info.n_tasks)
+    if st != CP_OK:
+        raise CpError(st, _lib.cp_last_create_error().decode())
+    return out
 
 
 def _stream(stream):

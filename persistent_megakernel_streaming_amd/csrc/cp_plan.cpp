@@ -1302,8 +1302,7 @@ cp_status cp_frame_run(cp_plan* P, const cp_frame_io* io, void* stream) {
   return CP_OK;
 }
 
-cp_status cp_plan_task_table(const cp_plan* P, int32_t* out, int64_t n_tasks) {
-  if (!P || !out || n_tasks != (int64_t)P->tasks.size()) return CP_ERR_INVALID_ARGUMENT;
+static void fill_task_table(const cp_plan* P, int32_t* out) {
   for (size_t w = 0; w + 1 < P->wg_begin.size(); ++w)
     for (uint32_t i = P->wg_begin[w]; i < P->wg_begin[w + 1]; ++i) {
       const Task& t = P->tasks[i];
@@ -1311,6 +1310,40 @@ cp_status cp_plan_task_table(const cp_plan* P, int32_t* out, int64_t n_tasks) {
       o[0] = (int32_t)t.phase; o[1] = t.type; o[2] = t.layer; o[3] = t.pos;
       o[4] = (int32_t)t.tile; o[5] = t.split; o[6] = (int32_t)w; o[7] = (int32_t)(i - P->wg_begin[w]);
     }
+}
+
+cp_status cp_plan_task_table(const cp_plan* P, int32_t* out, int64_t n_tasks) {
+  if (!P || !out || n_tasks != (int64_t)P->tasks.size()) return CP_ERR_INVALID_ARGUMENT;
+  fill_task_table(P, out);
+  return CP_OK;
+}
+
+cp_status cp_schedule_task_table(const cp_config* cfg, int cu_count, int32_t* out, int64_t n_tasks) {
+  g_create_err.clear();
+  if (!cfg || !out || cu_count < 1) {
+    g_create_err = "NULL argument or cu_count < 1";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  cp_plan P;
+  std::string msg;
+  cp_status s = validate(cfg, msg);
+  if (s == CP_OK) {
+    P.cfg = *cfg;
+    P.cu_count = cu_count;
+    P.packed_bytes = INT64_MAX;
+    s = build_schedule(&P);
+    if (s == CP_OK) s = check_schedule(&P);
+    msg = P.err;
+  }
+  if (s != CP_OK) {
+    g_create_err = msg;
+    return s;
+  }
+  if (n_tasks != (int64_t)P.tasks.size()) {
+    g_create_err = "n_tasks does not match the schedule";
+    return CP_ERR_INVALID_ARGUMENT;
+  }
+  fill_task_table(&P, out);
   return CP_OK;
 }
 

@@ -2,6 +2,8 @@
 include/cp.h declares, rejects bad arguments before touching a device, and its
 planner builds deadlock-free task lists (no GPU needed)."""
 import ctypes as C
+
+import numpy as np
 import os
 import re
 
@@ -92,6 +94,50 @@ def test_row_group_schedule_invariants(name, cus):
     c = cp.make_config(cfg, exec_mode="per_phase", flags=cp.CP_FLAG_ROW_GROUPS)
     info = cp.PlanInfo()
     assert cp.lib().cp_schedule_check(C.byref(c), cus, C.byref(info)) == 2  # persistent executor only
+
+
+def test_head_and_one_row_gate_up_tiles_avoid_the_split_k_owners():
+    """The head tiles of each position go to workgroups other than the last
+    down phase's split-K owners (at 256 CUs there are enough of them), and in
+    a one-row plan the gate/up tiles go to workgroups other than the o
+    owners; 64-row gate/up keeps its plain rotation."""
+    cp = _cp()
+    T_O, T_GU, T_DOWN, T_HEAD = 5, 6, 7, 8
+    for name in ("l5_r1", "l5_r64"):
+        cfg = synth.CONFIGS[name]
+        tab = cp.schedule_task_table(cfg, cu_count=256)
+        ph, ty, lay, pos, split, wg = tab[:, 0], tab[:, 1], tab[:, 2], tab[:, 3], tab[:, 5], tab[:, 6]
+        for p in range(1, cfg.n_positions):
+            owners = set(wg[(ty == T_DOWN) & (lay == cfg.n_layers - 1) & (pos == p) & (split == 0)].tolist())
+            heads = set(wg[(ty == T_HEAD) & (pos == p)].tolist())
+            assert heads and not heads & owners, (name, p)
+        clash = 0
+        for p in range(1, cfg.n_positions):
+            for l in range(cfg.n_layers):
+                owners = set(wg[(ty == T_O) & (lay == l) & (pos == p) & (split == 0)].tolist())
+                gu = set(wg[(ty == T_GU) & (lay == l) & (pos == p)].tolist())
+                clash += len(gu & owners)
+        if cfg.rows == 1:
+            assert clash == 0
+        else:
+            assert clash > 0  # plain rotation at 64 rows
+
+
+def test_schedule_task_table_matches_the_schedule_check():
+    cp = _cp()
+    cfg = synth.CONFIGS["tiny_f32"]
+    info = cp.schedule_check(cfg, cu_count=7)
+    tab = cp.schedule_task_table(cfg, cu_count=7)
+    assert tab.shape == (info.n_tasks, 8)
+    assert len(np.unique(tab[:, 0])) == info.n_phases
+    assert tab[:, 6].max() == 6
+    for w in range(7):  # each workgroup's list is in phase order, indexed 0..n-1
+        mine = tab[tab[:, 6] == w]
+        assert np.array_equal(mine[:, 7], np.arange(len(mine)))
+        assert np.all(np.diff(mine[:, 0]) >= 0)
+    c = cp.make_config(cfg)
+    out = np.zeros((info.n_tasks + 1, 8), np.int32)
+    assert cp.lib().cp_schedule_task_table(C.byref(c), 7, out.ctypes.data, info.n_tasks + 1) == 1
 
 
 def test_qk_norm_gains_are_plan_constants():
