@@ -1212,16 +1212,18 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
       else vv[tt] = ld16c(rv, o);
     }
     // Q and K (this position's from the qkv phase just before, earlier ones
-    // long ready) and V, all in one wait
+    // long ready) and V, all in one wait.  Every set reloads in asm, the
+    // QK-norm partials too: a compiler-issued reload in the wait loop, even
+    // one that never runs, measured 30 us slower per 64-row frame.
     const uint32_t k_tag = rawk ? q_tag : kv_tag;
     if constexpr (BF)
       await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, k_tag, t <= p, nld),
-                pend<ASM>(vw, rv, vo, kv_tag, true, p + 1), pend(qs, rn, qso, q_tag, qkn, th / 2),
-                pend(ks, rn, kso, q_tag, qkn, th / 2));
+                pend<ASM>(vw, rv, vo, kv_tag, true, p + 1), pend<ASM>(qs, rn, qso, q_tag, qkn, th / 2),
+                pend<ASM>(ks, rn, kso, q_tag, qkn, th / 2));
     else
       await_all(pl, pend<ASM>(qv, rq, qo, q_tag, true, nld), pend<ASM>(kv, rk, ko, k_tag, t <= p, nld),
-                pend<ASM>(vv, rv, vo, kv_tag, true, p + 1), pend(qs, rn, qso, q_tag, qkn, th / 2),
-                pend(ks, rn, kso, q_tag, qkn, th / 2));
+                pend<ASM>(vv, rv, vo, kv_tag, true, p + 1), pend<ASM>(qs, rn, qso, q_tag, qkn, th / 2),
+                pend<ASM>(ks, rn, kso, q_tag, qkn, th / 2));
     if (qkn) {
       // 1 / rms of the q head and of the k head (partials in tile order),
       // then Q and this position's K scaled and rounded as stored; the
