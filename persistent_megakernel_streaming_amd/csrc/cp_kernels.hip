@@ -590,8 +590,8 @@ __device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
 template <int BF, int KIND, bool ONE = false, bool ASM = !ONE>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, int r0 = 0,
-                                          int gr = 64) {
+                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, bool lnorm,
+                                          int r0, int gr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
   constexpr int KS = 4 * E;           // K elements one chunk step covers across the 4 lane groups
@@ -767,7 +767,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // (late: the norm partials are awaited after the K loop instead; always
   // for one-row frames, 1596 -> 1575 us per frame, with CP_FLAG_LATE_NORM
   // for the others, where it measured slower: 2545 vs 2509 us at 64 rows)
-  const bool late = NORM && (ONE || pl.late_norm);
+  const bool late = NORM && (ONE || lnorm);
   if constexpr (ONE)
     await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live && !late, 1));
   else
@@ -1935,7 +1935,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 template <int BF, bool ONE>
 // lcl: XCD-local hand-offs allowed in this frame.
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                         uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl) {
+                                         uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, bool lnorm) {
   switch (tk.type) {
     case T_ATTN:
       if (pl.d == 128) attn_task<BF, 128, !ONE>(pl, fr, tk, epoch, tr);
@@ -1946,13 +1946,13 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
 // (one-row frames: only a task of row group 0 has the row)
 #define CP_PROJ(K)                                                                                  \
   if constexpr (ONE) {                                                                              \
-    if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, 0, 64); \
+    if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, 0, 64); \
   } else if (pl.grp_rows) {                                                                         \
     const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;                                     \
-    if (r0 < fr.rows) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows); \
+    if (r0 < fr.rows) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, r0, pl.grp_rows); \
   } else {                                                                                          \
     for (int rh = 0; rh * 64 < fr.rows; ++rh)                                                       \
-      proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh * 64, 64);                   \
+      proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, rh * 64, 64);            \
   }
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
@@ -1962,13 +1962,13 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
 #undef CP_PROJ
     default:
       if constexpr (ONE) {
-        if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, 0, 64);
+        if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, 0, 64);
       } else if (pl.grp_rows) {
         const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;
-        if (r0 < fr.rows) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows);
+        if (r0 < fr.rows) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, r0, pl.grp_rows);
       } else {
         for (int rh = 0; rh * 64 < fr.rows; ++rh)
-          proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh * 64, 64);
+          proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, rh * 64, 64);
       }
       break;
   }
@@ -2021,7 +2021,10 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
   }
 }
 
-template <int BF, bool TL, bool ONE>
+// PLAIN: neither trace stamps nor CP_FLAG_LATE_NORM (many-row frames); those
+// paths are then compiled out of the task bodies (with them present but
+// unused, 64-row frames measured 40 us slower and one-row frames 20).
+template <int BF, bool TL, bool ONE, bool PLAIN>
 __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
@@ -2064,14 +2067,14 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     issue_tile(pl, cur, lds);
   }
   for (uint32_t i = b; i < e; ++i) {
-    uint64_t* tr = pl.trace_on ? pl.trace + (size_t)i * kTraceStamps : nullptr;
+    uint64_t* tr = (!PLAIN && pl.trace_on) ? pl.trace + (size_t)i * kTraceStamps : nullptr;
     stamp(tr, 0);
     const int s = (i - b) & 1;
     const bool more = i + 1 < e;
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
     stamp(tr, 1);
-    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl);
+    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl, !PLAIN && pl.late_norm != 0);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
     stamp(tr, 6);
     // The next task's tile copy goes out once every wave has issued this
@@ -2118,7 +2121,7 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const DevTask tk = tasks[blockIdx.x];
   issue_tile(pl, tk, lds);
-  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr, false);  // (per-phase tasks carry no local flags)
+  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr, false, pl.late_norm != 0);  // (per-phase tasks carry no local flags)
 }
 
 // The per-phase executor's last launches of a frame: the sentinel refill of
@@ -2164,17 +2167,23 @@ namespace cpms {
 // Executor variants: activation type, task list in LDS (persistent), and a
 // one-row frame (its own code path; task lists that do not fit LDS keep the
 // general path).
-#define CP_PERSISTENT_VARIANTS(X) \
-  X(1, true, true) X(1, true, false) X(1, false, false) X(0, true, true) X(0, true, false) X(0, false, false)
+// (the plain form only with task lists in LDS; lists too long for LDS take
+// the general form with its runtime checks)
+#define CP_PERSISTENT_VARIANTS(X)                                                                       \
+  X(1, true, true, true) X(1, true, true, false) X(1, true, false, true) X(1, true, false, false)         \
+  X(1, false, false, false) X(0, true, true, true) X(0, true, true, false) X(0, true, false, true)        \
+  X(0, true, false, false) X(0, false, false, false)
 #define CP_PHASE_VARIANTS(X) X(1, true) X(1, false) X(0, true) X(0, false)
 
 hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s) {
   const dim3 g(pl.n_wg), t(kThreads);
   const bool one = fr.rows == 1 && pl.tasks_in_lds;
-#define X(B, T, O)                                                                      \
-  if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O) {                        \
-    hipLaunchKernelGGL((persistent_kernel<B, T, O>), g, t, kLdsBytes, s, pl, fr);       \
-    return hipGetLastError();                                                          \
+  // (one-row frames always wait late for the norm partials)
+  const bool plain = pl.tasks_in_lds && !pl.trace_on && (one || !pl.late_norm);
+#define X(B, T, O, PL)                                                                            \
+  if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O && plain == PL) {                   \
+    hipLaunchKernelGGL((persistent_kernel<B, T, O, PL>), g, t, kLdsBytes, s, pl, fr);             \
+    return hipGetLastError();                                                                    \
   }
   CP_PERSISTENT_VARIANTS(X)
 #undef X
@@ -2215,8 +2224,8 @@ hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, 
 
 hipError_t set_kernel_attributes() {
   hipError_t e;
-#define X(B, T, O)                                                                                          \
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<B, T, O>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+#define X(B, T, O, PL)                                                                                      \
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<B, T, O, PL>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                kLdsBytes)))                                                                   \
     return e;
   CP_PERSISTENT_VARIANTS(X)
@@ -2263,11 +2272,19 @@ hipError_t check_xcd_dealing(int n_wg, bool& dealt, uint32_t* buf) {
 }
 
 int occupancy_per_cu(int bf16) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bf16 ? persistent_kernel<1, true, false> : persistent_kernel<0, true, false>, kThreads,
-                                                   kLdsBytes) != hipSuccess)
-    return -1;
-  return n;
+  // the smallest over the executor's forms for this activation type
+  int best = INT32_MAX;
+#define X(B, T, O, PL)                                                                                     \
+  if (bf16 == B) {                                                                                         \
+    int n = 0;                                                                                             \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel<B, T, O, PL>, kThreads, kLdsBytes) != \
+        hipSuccess)                                                                                        \
+      return -1;                                                                                           \
+    best = n < best ? n : best;                                                                            \
+  }
+  CP_PERSISTENT_VARIANTS(X)
+#undef X
+  return best == INT32_MAX ? -1 : best;
 }
 
 }  // namespace cpms
