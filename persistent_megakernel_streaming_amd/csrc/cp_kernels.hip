@@ -2021,9 +2021,10 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
   }
 }
 
-// PLAIN: neither trace stamps nor CP_FLAG_LATE_NORM (many-row frames); those
-// paths are then compiled out of the task bodies (with them present but
-// unused, 64-row frames measured 40 us slower and one-row frames 20).
+// PLAIN: no trace stamps, no CP_FLAG_LATE_NORM (many-row frames), and
+// XCD-local hand-offs allowed; those choices are then constants in the task
+// bodies (as runtime checks, 64-row frames measured 76 us slower, and the
+// local-hand-off check alone cost one-row frames 44 us).
 template <int BF, bool TL, bool ONE, bool PLAIN>
 __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
   extern __shared__ __align__(1024) uint8_t lds[];
@@ -2037,7 +2038,7 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
   // next launch on a stream can start at another XCD) but is the same for
   // every workgroup of a launch: residues stay together whatever r is.  The
   // plan checks at creation that the dealing is such a rotation.
-  const bool lcl = __builtin_amdgcn_readfirstlane(pl.local_ok) != 0;
+  const bool lcl = PLAIN || __builtin_amdgcn_readfirstlane(pl.local_ok) != 0;
   const uint32_t b = pl.wg_begin[blockIdx.x], e = pl.wg_begin[blockIdx.x + 1];
   // With TL the workgroup's task records are copied to LDS once: reading a
   // record from memory between tasks would make the wave wait for every
@@ -2179,7 +2180,7 @@ hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t 
   const dim3 g(pl.n_wg), t(kThreads);
   const bool one = fr.rows == 1 && pl.tasks_in_lds;
   // (one-row frames always wait late for the norm partials)
-  const bool plain = pl.tasks_in_lds && !pl.trace_on && (one || !pl.late_norm);
+  const bool plain = pl.tasks_in_lds && !pl.trace_on && (one || !pl.late_norm) && pl.local_ok;
 #define X(B, T, O, PL)                                                                            \
   if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O && plain == PL) {                   \
     hipLaunchKernelGGL((persistent_kernel<B, T, O, PL>), g, t, kLdsBytes, s, pl, fr);             \
