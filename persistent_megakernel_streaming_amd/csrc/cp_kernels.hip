@@ -1932,13 +1932,15 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 
 // ONE: the executor was launched for a one-row frame (the densely loaded
 // operand path; a separate kernel, so the many-row code is left as it is).
-template <int BF, bool ONE>
+// PLAIN: the executor's plain form (head_dim 128 only: attention for head_dim
+// 64 is not compiled into it, which keeps the kernel's code smaller).
+template <int BF, bool ONE, bool PLAIN = false>
 // lcl: XCD-local hand-offs allowed in this frame.
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, bool lnorm) {
   switch (tk.type) {
     case T_ATTN:
-      if (pl.d == 128) attn_task<BF, 128, !ONE>(pl, fr, tk, epoch, tr);
+      if (PLAIN || pl.d == 128) attn_task<BF, 128, !ONE>(pl, fr, tk, epoch, tr);
       else attn_task<BF, 64, !ONE>(pl, fr, tk, epoch, tr);
       break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
@@ -2021,10 +2023,12 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
   }
 }
 
-// PLAIN: no trace stamps, no CP_FLAG_LATE_NORM (many-row frames), and
-// XCD-local hand-offs allowed; those choices are then constants in the task
-// bodies (as runtime checks, 64-row frames measured 76 us slower, and the
-// local-hand-off check alone cost one-row frames 44 us).
+// PLAIN: no trace stamps, no CP_FLAG_LATE_NORM (many-row frames), XCD-local
+// hand-offs allowed and head_dim 128; those choices are then constants in
+// the task bodies (as runtime checks, 64-row frames measured 76 us slower,
+// the local-hand-off check alone cost one-row frames 44 us, and the unused
+// head_dim-64 attention 19 us per 64-row frame: the kernel's code is larger
+// than the instruction cache, so code that never runs still costs).
 template <int BF, bool TL, bool ONE, bool PLAIN>
 __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
   extern __shared__ __align__(1024) uint8_t lds[];
@@ -2075,7 +2079,7 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
     stamp(tr, 1);
-    run_task<BF, ONE>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl, !PLAIN && pl.late_norm != 0);
+    run_task<BF, ONE, PLAIN>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl, !PLAIN && pl.late_norm != 0);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
     stamp(tr, 6);
     // The next task's tile copy goes out once every wave has issued this
@@ -2180,7 +2184,7 @@ hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t 
   const dim3 g(pl.n_wg), t(kThreads);
   const bool one = fr.rows == 1 && pl.tasks_in_lds;
   // (one-row frames always wait late for the norm partials)
-  const bool plain = pl.tasks_in_lds && !pl.trace_on && (one || !pl.late_norm) && pl.local_ok;
+  const bool plain = pl.tasks_in_lds && !pl.trace_on && (one || !pl.late_norm) && pl.local_ok && pl.d == 128;
 #define X(B, T, O, PL)                                                                            \
   if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O && plain == PL) {                   \
     hipLaunchKernelGGL((persistent_kernel<B, T, O, PL>), g, t, kLdsBytes, s, pl, fr);             \
