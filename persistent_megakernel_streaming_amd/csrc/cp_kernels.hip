@@ -588,7 +588,9 @@ __device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
 // RMSNorm: the gain g is folded into the packed weight tile at plan creation
 // (W . (g x / rms(x)) = (W g) . x / rms(x)), so the MFMAs take the residual
 // rows as they are and the fp32 result is scaled by 1 / rms(x) of its row.
-template <int BF, int KIND, bool ONE = false, bool ASM = !ONE>
+// NOQK: the QK-norm variant is not compiled in (the plain many-row form of
+// plans without it: 2392 -> 2369 us per 64-row frame).
+template <int BF, int KIND, bool ONE = false, bool ASM = !ONE, bool NOQK = false>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                           uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, bool lnorm,
                                           int r0, int gr) {
@@ -1022,7 +1024,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
           // The tile applies the gains and RoPE and stores the head unscaled
           // (K in a staging buffer), with its 16 dims' sum of squares; the
           // attention task adds the head's partials and scales.
-          const bool qkn = pl.qk_norm;
+          const bool qkn = !NOQK && pl.qk_norm;
           float xg[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) xg[v] = acc0[v];
@@ -1127,7 +1129,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 // One kv head g for a group of rows: every (row, q head of g) pair is one
 // wave's work.  Scores: lane (t, c) takes position t and a quarter c of the
 // head dimension; softmax over t <= p in float; output: lane owns d/64 dims.
-template <int BF, int D, bool ASM>
+template <int BF, int D, bool ASM, bool NOQK = false>
 __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                           uint64_t* tr) {
   constexpr int ESZ = BF ? 2 : 4;
@@ -1143,7 +1145,7 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
   const uint32_t kvbytes = (uint32_t)pl.L * Rmax * nkv * P * d * ESZ * 2;
   // QK-norm: this position's K comes unscaled from the staging buffer behind
   // the cache, with the per-tile sums of squares of the q and k heads
-  const bool qkn = pl.qk_norm;
+  const bool qkn = !NOQK && pl.qk_norm;
   const uint32_t krbytes = qkn ? (uint32_t)2 * Rmax * nkv * d * ESZ * 2 : 0u;
   const rsrc_t rk = make_rsrc(pl.kc, kvbytes + krbytes), rv = make_rsrc(pl.vc, kvbytes);
   const int th = d / 16, nh = pl.nq + nkv;
@@ -1934,27 +1936,27 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 // operand path; a separate kernel, so the many-row code is left as it is).
 // PLAIN: the executor's plain form (head_dim 128 only: attention for head_dim
 // 64 is not compiled into it, which keeps the kernel's code smaller).
-template <int BF, bool ONE, bool PLAIN = false>
+template <int BF, bool ONE, bool PLAIN = false, bool NOQK = false>
 // lcl: XCD-local hand-offs allowed in this frame.
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, bool lnorm) {
   switch (tk.type) {
     case T_ATTN:
-      if (PLAIN || pl.d == 128) attn_task<BF, 128, !ONE>(pl, fr, tk, epoch, tr);
-      else attn_task<BF, 64, !ONE>(pl, fr, tk, epoch, tr);
+      if (PLAIN || pl.d == 128) attn_task<BF, 128, !ONE, NOQK>(pl, fr, tk, epoch, tr);
+      else attn_task<BF, 64, !ONE, NOQK>(pl, fr, tk, epoch, tr);
       break;
     case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
 // (one-row frames: only a task of row group 0 has the row)
 #define CP_PROJ(K)                                                                                  \
   if constexpr (ONE) {                                                                              \
-    if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, 0, 64); \
+    if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, 0, 64); \
   } else if (pl.grp_rows) {                                                                         \
     const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;                                     \
-    if (r0 < fr.rows) proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, r0, pl.grp_rows); \
+    if (r0 < fr.rows) proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, r0, pl.grp_rows); \
   } else {                                                                                          \
     for (int rh = 0; rh * 64 < fr.rows; ++rh)                                                       \
-      proj_task<BF, K, ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, rh * 64, 64);            \
+      proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, rh * 64, 64);  \
   }
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
@@ -2029,7 +2031,7 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
 // the local-hand-off check alone cost one-row frames 44 us, and the unused
 // head_dim-64 attention 19 us per 64-row frame: the kernel's code is larger
 // than the instruction cache, so code that never runs still costs).
-template <int BF, bool TL, bool ONE, bool PLAIN>
+template <int BF, bool TL, bool ONE, bool PLAIN, bool NOQK>
 __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, DevFrame fr) {
   extern __shared__ __align__(1024) uint8_t lds[];
   uint32_t* misc = (uint32_t*)(lds + 2 * kSlotBytes);
@@ -2079,7 +2081,7 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
     stamp(tr, 1);
-    run_task<BF, ONE, PLAIN>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl, !PLAIN && pl.late_norm != 0);
+    run_task<BF, ONE, PLAIN, NOQK>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl, !PLAIN && pl.late_norm != 0);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
     stamp(tr, 6);
     // The next task's tile copy goes out once every wave has issued this
@@ -2174,10 +2176,11 @@ namespace cpms {
 // general path).
 // (the plain form only with task lists in LDS; lists too long for LDS take
 // the general form with its runtime checks)
-#define CP_PERSISTENT_VARIANTS(X)                                                                       \
-  X(1, true, true, true) X(1, true, true, false) X(1, true, false, true) X(1, true, false, false)         \
-  X(1, false, false, false) X(0, true, true, true) X(0, true, true, false) X(0, true, false, true)        \
-  X(0, true, false, false) X(0, false, false, false)
+#define CP_PERSISTENT_VARIANTS(X)                                                                         \
+  X(1, true, true, true, false) X(1, true, true, false, false) X(1, true, false, true, true)                 \
+  X(1, true, false, true, false) X(1, true, false, false, false) X(1, false, false, false, false)            \
+  X(0, true, true, true, false) X(0, true, true, false, false) X(0, true, false, true, true)                 \
+  X(0, true, false, true, false) X(0, true, false, false, false) X(0, false, false, false, false)
 #define CP_PHASE_VARIANTS(X) X(1, true) X(1, false) X(0, true) X(0, false)
 
 hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s) {
@@ -2185,9 +2188,10 @@ hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t 
   const bool one = fr.rows == 1 && pl.tasks_in_lds;
   // (one-row frames always wait late for the norm partials)
   const bool plain = pl.tasks_in_lds && !pl.trace_on && (one || !pl.late_norm) && pl.local_ok && pl.d == 128;
-#define X(B, T, O, PL)                                                                            \
-  if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O && plain == PL) {                   \
-    hipLaunchKernelGGL((persistent_kernel<B, T, O, PL>), g, t, kLdsBytes, s, pl, fr);             \
+  const bool nq = plain && !one && !pl.qk_norm;
+#define X(B, T, O, PL, NQK)                                                                        \
+  if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O && plain == PL && nq == NQK) {       \
+    hipLaunchKernelGGL((persistent_kernel<B, T, O, PL, NQK>), g, t, kLdsBytes, s, pl, fr);         \
     return hipGetLastError();                                                                    \
   }
   CP_PERSISTENT_VARIANTS(X)
@@ -2229,8 +2233,8 @@ hipError_t launch_unpack_kv(const void* src, void* dst, uint32_t words_per_row, 
 
 hipError_t set_kernel_attributes() {
   hipError_t e;
-#define X(B, T, O, PL)                                                                                      \
-  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<B, T, O, PL>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+#define X(B, T, O, PL, NQK)                                                                                  \
+  if ((e = hipFuncSetAttribute((const void*)persistent_kernel<B, T, O, PL, NQK>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                kLdsBytes)))                                                                   \
     return e;
   CP_PERSISTENT_VARIANTS(X)
@@ -2279,10 +2283,10 @@ hipError_t check_xcd_dealing(int n_wg, bool& dealt, uint32_t* buf) {
 int occupancy_per_cu(int bf16) {
   // the smallest over the executor's forms for this activation type
   int best = INT32_MAX;
-#define X(B, T, O, PL)                                                                                     \
+#define X(B, T, O, PL, NQK)                                                                                 \
   if (bf16 == B) {                                                                                         \
     int n = 0;                                                                                             \
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel<B, T, O, PL>, kThreads, kLdsBytes) != \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel<B, T, O, PL, NQK>, kThreads, kLdsBytes) != \
         hipSuccess)                                                                                        \
       return -1;                                                                                           \
     best = n < best ? n : best;                                                                            \
