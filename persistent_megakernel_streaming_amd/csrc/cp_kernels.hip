@@ -648,7 +648,14 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   } else if constexpr (KIND == T_HEAD) {
     xsrc = hres + plane(pl.L - 1, p) * hbytes; in_ssq = P + 2 * par + ((pl.L - 1) & 1); ld = H;
   } else if constexpr (KIND == T_O) {
-    ld = pl.nq * pl.d; xsrc = (const uint8_t*)pl.abuf + plane(l, p) * sop_bytes<BF>(Rmax, ld);
+    // (the many-row executor runs down tasks through this instantiation too:
+    // one body for both split-K kinds keeps the kernel's code smaller,
+    // 2375 -> 2351 us per 64-row frame; the one-row kernel keeps two)
+    if (ONE || tk.type == T_O) {
+      ld = pl.nq * pl.d; xsrc = (const uint8_t*)pl.abuf + plane(l, p) * sop_bytes<BF>(Rmax, ld);
+    } else {
+      ld = pl.I; xsrc = (const uint8_t*)pl.mbuf + plane(l, p) * sop_bytes<BF>(Rmax, ld);
+    }
   } else if constexpr (KIND == T_DOWN) {
     ld = pl.I; xsrc = (const uint8_t*)pl.mbuf + plane(l, p) * sop_bytes<BF>(Rmax, ld);
   } else {
@@ -924,9 +931,14 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     int out_ssq;
     const void* resid = nullptr;
     if constexpr (KIND == T_O) {
-      part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; out = hmid + plane(l, p) * hbytes;
-      out_ssq = P + 4 + par;
-      resid = (l == 0) ? xin + (size_t)p * hbytes : hres + plane(l - 1, p) * hbytes;
+      if (ONE || tk.type == T_O) {
+        part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; out = hmid + plane(l, p) * hbytes;
+        out_ssq = P + 4 + par;
+        resid = (l == 0) ? xin + (size_t)p * hbytes : hres + plane(l - 1, p) * hbytes;
+      } else {  // a down task (many-row executor)
+        part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; out = hres + plane(l, p) * hbytes;
+        out_ssq = P + 2 * par + (l & 1); resid = hmid + plane(l, p) * hbytes;
+      }
     } else if constexpr (KIND == T_DOWN) {
       part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; out = hres + plane(l, p) * hbytes;
       out_ssq = P + 2 * par + (l & 1); resid = hmid + plane(l, p) * hbytes;
@@ -1961,7 +1973,13 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
     case T_GU: CP_PROJ(T_GU) break;
-    case T_DOWN: CP_PROJ(T_DOWN) break;
+    case T_DOWN:
+      if constexpr (ONE) {
+        CP_PROJ(T_DOWN)
+      } else {
+        CP_PROJ(T_O)
+      }
+      break;
     case T_HEAD: CP_PROJ(T_HEAD) break;
 #undef CP_PROJ
     default:
