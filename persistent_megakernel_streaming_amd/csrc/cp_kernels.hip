@@ -50,6 +50,7 @@ constexpr int kSC1 = 16;  // buffer cache policy bit: coherent at agent scope
 
 // LDS layout of the misc region (after the two weight-tile slots).
 constexpr int kRedAccLds = 1024;  // cross-wave MFMA accumulators (8 KiB)
+constexpr int kRedSsLds = 9216;   // cross-wave sums of squares (1 KiB)
 
 // ------------------------------------------------------------------ memory helpers
 
@@ -617,7 +618,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // ONE: a frame of one row.  Only row 0 of the operand tile is loaded, its
   // 16-byte units packed densely over the lanes (one load instruction per 16
   // chunks instead of one per chunk), and handed to the MFMA lanes with
-  // ds_bpermute; the norm partials of the row come in one load as well.
+  // ds_bpermute; the row's sum of squares is taken from those units.
   static_assert(!ONE || XLL, "one-row operands are tagged");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 4, rl = lane & 15;
@@ -736,19 +737,15 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     }
   }
   // Sum-of-squares partials of a normalised operand (H/16 per row, written
-  // with the rows): lane group q adds H/64 of them (ONE: lane i of the wave
-  // loads partials 2i, 2i + 1 of row 0).
+  // with the rows): lane group q adds H/64 of them.  (ONE: not read; the
+  // row's sum of squares comes from its operand units, below.)
   u32x4 ssv[8];
   const int nsq = H / 64;
   const uint32_t ss_row = (uint32_t)(H / 16) * 8;
   const rsrc_t rs = make_rsrc(ssq_slot(pl, in_ssq), (uint32_t)rows * ss_row);
   const uint32_t ss0 = (uint32_t)row * ss_row + (uint32_t)(q * nsq) * 8;
   auto sso = [=](int i) -> uint32_t { return ONE ? (uint32_t)(lane % (H / 32)) * 16 : ss0 + i * 16; };
-  if constexpr (NORM && ONE) {
-    ssv[0] = ld16(rs, sso(0));
-#pragma unroll
-    for (int i = 1; i < 8; ++i) ssv[i] = u32x4{0, in_tag, 0, in_tag};
-  } else if constexpr (NORM) {
+  if constexpr (NORM && !ONE) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) ssv[i] = ld16(rs, sso(2 * i < nsq ? i : nsq / 2 - 1));  // (past nsq: not waited for)
   }
@@ -773,12 +770,12 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   // stay in flight.  A wave with no live rows issued no operand loads but
   // still copied its share of the tile, and waits for every load; so do
   // one-row frames and untagged operands.  (wave_live is wave-uniform.)
-  // (late: the norm partials are awaited after the K loop instead; always
-  // for one-row frames, 1596 -> 1575 us per frame, with CP_FLAG_LATE_NORM
-  // for the others, where it measured slower: 2545 vs 2509 us at 64 rows)
+  // (late: the norm partials are awaited after the K loop instead, with
+  // CP_FLAG_LATE_NORM, where it measured slower: 2545 vs 2509 us at 64 rows;
+  // one-row frames need no partials, and take rms(x) after the K loop)
   const bool late = NORM && (ONE || lnorm);
   if constexpr (ONE)
-    await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1), pend(ssv, rs, sso, in_tag, NORM && wave_live && !late, 1));
+    await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1));
   else
     await_all(pl, spend<BF, ASM>(xs[0], rx, uoff(0), XLL && live),
               pend<ASM>(ssv, rs, sso, in_tag, NORM && live && !late, nsq / 2));
@@ -787,12 +784,37 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   __syncthreads();
   stamp(tr, 2);
 
+  // ONE: the row's sum of squares for RMSNorm from the operand pieces this
+  // wave holds (each piece of its chunks once), added over the wave; the
+  // waves that split K add theirs after the K loop.  No wait for the
+  // producers' norm partials then: 1575 -> 1547 us per one-row frame.  (At
+  // 64 rows the squares in the K loop cost more than the partials' wait
+  // saves: 2349 -> 2422 us.)
+  float ssl = 0.f;
+  if constexpr (NORM && ONE) {
+#pragma unroll
+    for (int j = 0; j < NJ1; ++j)
+      if (j < nj1 && j * 64 + lane < npc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (BF) {
+            const float lo = __uint_as_float(xo[j][e] << 16), hi = __uint_as_float(xo[j][e] & 0xffff0000u);
+            ssl = fmaf(lo, lo, ssl);
+            ssl = fmaf(hi, hi, ssl);
+          } else {
+            const float v = __uint_as_float(xo[j][e]);
+            ssl = fmaf(v, v, ssl);
+          }
+        }
+      }
+    wave_tree([&](auto other) { ssl += __uint_as_float(other(__float_as_uint(ssl))); });
+  }
+
   // 1 / rms(x) of this lane's row, from its norm partials
   auto row_rinv = [&]() -> float {
     float ss = 0.f;
     if constexpr (ONE) {
-      ss = lane < H / 32 ? __uint_as_float(ssv[0][0]) + __uint_as_float(ssv[0][2]) : 0.f;
-      wave_tree([&](auto other) { ss += __uint_as_float(other(__float_as_uint(ss))); });
+      ss = ssl;
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -884,13 +906,16 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   if (wpr > 1) {
     // K parts of a row tile: (((k0 + k1) + k2) + k3), in the wave of part 0
     f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);  // [4 waves][2][64 lanes]
+    float* red_ss = (float*)((uint8_t*)misc + kRedSsLds);  // ONE: [4 waves][64 lanes]
     if (wave_live) {
+      if constexpr (NORM && ONE) red_ss[wave * 64 + lane] = ssl;
       red_acc[(wave * 2 + 0) * 64 + lane] = acc0;
       if constexpr (NB == 2) red_acc[(wave * 2 + 1) * 64 + lane] = acc1;
     }
     __syncthreads();
     if (wave_live && ks == 0) {
       for (int k = 1; k < wpr; ++k) {
+        if constexpr (NORM && ONE) ssl = ssl + red_ss[(rt * wpr + k) * 64 + lane];
         const f32x4 a = red_acc[((rt * wpr + k) * 2 + 0) * 64 + lane];
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + a[v];
@@ -907,8 +932,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       // The norm partials of the row (every producer tile's) are needed only
       // now: the K loop started as soon as this wave's own operand units were
       // in.  (ks == 0: the waves that store the tile.)
-      if constexpr (ONE) await_all(pl, pend(ssv, rs, sso, in_tag, wave_live && ks == 0, 1));
-      else await_all(pl, pend<ASM>(ssv, rs, sso, in_tag, live && ks == 0, nsq / 2));
+      if constexpr (!ONE) await_all(pl, pend<ASM>(ssv, rs, sso, in_tag, live && ks == 0, nsq / 2));
       rinv = row_rinv();
     }
   }
@@ -1006,10 +1030,11 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e]);
       }
-      const float sq = tile_ssq(h, 16, 4);
+      // (the row's norm partial: one-row frames read none, so store none)
+      const float sq = ONE ? 0.f : tile_ssq(h, 16, 4);
       if (live) {
         st_sop4<BF>(make_rsrc(out, hbytes), row, (int)slots, H, h);
-        if (q == 0)
+        if (!ONE && q == 0)
           st8c(make_rsrc(ssq_slot(pl, out_ssq), (uint32_t)Rmax * ss_row), (uint32_t)row * ss_row + tk.tile * 8,
                u32x2{__float_as_uint(sq), my_tag});
       }
@@ -1337,10 +1362,11 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
 // ------------------------------------------------------------------ draw + embed
 
 // Writes embedding row `code` of table j as the input of position j + 1 (when
-// there is one, tagged, with its sum-of-squares partials) and adds it to the
+// there is one, tagged, with its sum-of-squares partials unless SS is false:
+// one-row frames take the sum from the operand itself) and adds it to the
 // row's fp32 embedding sum.  All draws of a row run in one workgroup, so the
 // sum is carried in program order with ordinary loads and stores.
-template <int BF>
+template <int BF, bool SS = true>
 __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr, int j, int row, int code,
                                           bool first, uint32_t my_tag) {
   constexpr int ESZ = BF ? 2 : 4;
@@ -1372,26 +1398,26 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
       for (int i = 0; i < 4; ++i) ev[i] = 0.f;
     }
     if (in && feeds) st_sop4<BF>(rx, row, k, H, ev);
-    const float sq = tile_ssq(ev, 1, 4);
+    const float sq = SS ? tile_ssq(ev, 1, 4) : 0.f;
     if (in) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(first ? ev[i] : __uint_as_float(sv[i]) + ev[i]);
       st16(rs, (uint32_t)(row * H + k) * 4, sv);
-      if (feeds && (threadIdx.x & 3) == 0)
+      if (SS && feeds && (threadIdx.x & 3) == 0)
         st8c(make_rsrc(ssq_slot(pl, j + 1), (uint32_t)pl.Rmax * (H / 16) * 8), (uint32_t)(row * (H / 16) + k / 16) * 8,
              u32x2{__float_as_uint(sq), my_tag});
     }
   }
 }
 
-template <int BF>
+template <int BF, bool SS>
 __device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                             uint64_t* tr) {
   const int row = (int)tk.tile;
   if (row < fr.rows) {
     int code = fr.code0[row];
     code = code < 0 ? 0 : (code >= pl.V ? pl.V - 1 : code);
-    embed_row<BF>(pl, fr, 0, row, code, true, tag_of(epoch, tk.phase));
+    embed_row<BF, SS>(pl, fr, 0, row, code, true, tag_of(epoch, tk.phase));
   }
   stamp(tr, 5);
 }
@@ -1898,7 +1924,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
         st8c(make_rsrc(fr.offset, (uint32_t)fr.rows * 8), (uint32_t)row * 8, u32x2{(uint32_t)o, (uint32_t)(o >> 32)});
       }
     }
-    embed_row<BF>(pl, fr, p, row, code, false, tag_of(epoch, tk.phase));
+    embed_row<BF, ASM>(pl, fr, p, row, code, false, tag_of(epoch, tk.phase));
   } else if (row < fr.rows) {
     if (threadIdx.x < 64) {
       // the head tiles' (value, index) candidates of this row, tile order
@@ -1937,7 +1963,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
     __syncthreads();
-    embed_row<BF>(pl, fr, p, row, (int)misc[1], false, tag_of(epoch, tk.phase));
+    embed_row<BF, ASM>(pl, fr, p, row, (int)misc[1], false, tag_of(epoch, tk.phase));
   }
   stamp(tr, 5);
 }
@@ -1957,7 +1983,7 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
       if (PLAIN || pl.d == 128) attn_task<BF, 128, !ONE, NOQK>(pl, fr, tk, epoch, tr);
       else attn_task<BF, 64, !ONE, NOQK>(pl, fr, tk, epoch, tr);
       break;
-    case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
+    case T_EMBED0: embed0_task<BF, !ONE>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
 // (one-row frames: only a task of row group 0 has the row)
 #define CP_PROJ(K)                                                                                  \
