@@ -75,8 +75,10 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
  * operand units are in and wait for the row's norm partials (one from every
  * producer tile) only before the epilogue, the per-chunk start of section
  * "What's left in the frame, open" (first item).  Same results, bit for bit.
- * One-row frames always run this way (measured faster there); frames of more
- * rows only with this flag (measured slower at 64 rows on MI355X). */
+ * Frames of more than one row only with this flag (measured slower at 64
+ * rows on MI355X).  One-row frames need no partials at all: their normed
+ * projections take the row's sum of squares from the operand units they
+ * stream, so the flag changes nothing for them. */
 #define CP_FLAG_LATE_NORM 0x2u
 /* Every hand-off writes through to memory: no split-K partials or q/k/v kept
  * in one XCD's L2 for readers on that XCD.  A plan also runs this way when,
