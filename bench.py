@@ -291,7 +291,7 @@ def main():
     import torch
     from persistent_megakernel_streaming_amd import cp, synth
 
-    everything = {"p64", "p1", "p128", "s64", "pp64", "pp1", "late", "nolocal", "rg", "cross", "qk", "l10", "floor", "chain",
+    everything = {"p64", "p1", "p128", "s64", "pp64", "pp1", "nolocal", "rg", "cross", "qk", "l10", "floor", "chain",
                   "cold", "pct"}
     only = set(args.only.split(",")) if args.only else everything
     steps, warm, reps = args.steps, args.warmup, args.repeats
@@ -337,13 +337,6 @@ def main():
             extra["per_frame_us_1row"] = {"p50": float(np.percentile(t, 50)), "p99": float(np.percentile(t, 99)),
                                           "frames": len(t)}
         plan1.close()
-    if "late" in only:
-        # normed projections waiting for the norm partials after the K loop
-        for c, mr in ((cfg64, 64), (cfg1, 1)):
-            pl = cp.Plan(c, wdev, exec_mode="persistent", max_rows=mr, flags=cp.CP_FLAG_LATE_NORM)
-            io = cp.make_io(c, synth.make_inputs(c), logits=False)
-            res[f"late_norm_persistent_us_{mr}"] = _time_frames(pl, io, max(20, steps // 2), warm, 3)
-            pl.close()
     if "p128" in only:
         # the 128-row frame (two groups of 64 rows per projection task)
         c = synth.CONFIGS["l5_r128"]

@@ -71,15 +71,6 @@ typedef enum { CP_EXEC_PERSISTENT = 0, CP_EXEC_PER_PHASE = 1 } cp_exec;
 
 /* Plan flags. */
 #define CP_FLAG_TRACE 0x1u /* record eight timestamps per task (persistent executor; see cp_frame_io.trace) */
-/* Normed projections (qkv, gate/up, heads) start their K loop once their own
- * operand units are in and wait for the row's norm partials (one from every
- * producer tile) only before the epilogue, the per-chunk start of section
- * "What's left in the frame, open" (first item).  Same results, bit for bit.
- * Frames of more than one row only with this flag (measured slower at 64
- * rows on MI355X).  One-row frames need no partials at all: their normed
- * projections take the row's sum of squares from the operand units they
- * stream, so the flag changes nothing for them. */
-#define CP_FLAG_LATE_NORM 0x2u
 /* Every hand-off writes through to memory: no split-K partials or q/k/v kept
  * in one XCD's L2 for readers on that XCD.  A plan also runs this way when,
  * at its creation, the device did not deal workgroup i to XCD (i + r) mod 8

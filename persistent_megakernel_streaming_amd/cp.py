@@ -22,7 +22,6 @@ STATUS = {0: "CP_OK", 1: "CP_ERR_INVALID_ARGUMENT", 2: "CP_ERR_UNSUPPORTED", 3: 
 CP_DTYPE_F32, CP_DTYPE_BF16 = 0, 1
 CP_EXEC_PERSISTENT, CP_EXEC_PER_PHASE = 0, 1
 CP_FLAG_TRACE = 1
-CP_FLAG_LATE_NORM = 2
 CP_FLAG_NO_LOCAL = 4
 CP_FLAG_ROW_GROUPS = 8
 ABI_VERSION = 3

@@ -115,7 +115,7 @@ struct DevPlan {
   int n_wg;
   int n_tasks;
   int tasks_in_lds;             // every workgroup's list fits kTaskLds: the executor copies it to LDS
-  int late_norm;                // CP_FLAG_LATE_NORM: normed projections wait for norm partials after the K loop
+  int layout_pad0;              // unused (see layout_pad1)
   int local_ok;                 // XCD-local hand-offs allowed (not CP_FLAG_NO_LOCAL)
   int grp_rows;                 // CP_FLAG_ROW_GROUPS: rows per projection task (0: all, in passes of 64)
   // task lists
@@ -152,7 +152,10 @@ struct DevPlan {
   uint64_t* qkn;                // QK-norm: [2][Rmax][nq + nkv][d/16] per-tile sums of squares of q, k heads
   void* vc;
   uint64_t* part;               // split-K partials, each buffer [H/16 tiles][nsplit][Rmax][16] words
-  uint32_t* ssq;                // [P + 6][Rmax][H/16] words: sum-of-squares partials of residual rows
+  // Unused.  With this word and layout_pad0 left out of the kernel argument,
+  // the executor's code came out 23 us per 64-row frame slower (measured
+  // A/B, same sources otherwise).
+  uint32_t* layout_pad1;
   uint64_t* zbuf;               // [Rmax][V] words: logits of the current head
   uint64_t* cand;               // [Rmax][n_head_tiles][2] words: (value, index) of each head tile
   uint64_t* trace;              // plan-owned trace staging (unused if no trace)

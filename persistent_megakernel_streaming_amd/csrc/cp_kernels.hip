@@ -329,24 +329,6 @@ __device__ __forceinline__ f32x4 mma(const u32x4& w, const u32x4& x, f32x4 acc) 
   }
 }
 
-// Sum of squares of a residual row comes from its producers as H/16 partials
-// (one per 16-column tile, tile order), stored as tagged words; ssq slot ids:
-// position inputs 0 .. P-1, residual after down P + 2*parity + layer parity,
-// residual after o P + 4 + parity.
-__device__ __forceinline__ uint32_t* ssq_slot(const DevPlan& pl, int slot) {
-  return pl.ssq + (size_t)slot * pl.Rmax * (pl.H / 16) * 2;
-}
-
-// Sum of squares of the four values a lane stores, added over the `span`
-// lanes (xor distances first, 2 first, ...) that share one 16-column tile.
-__device__ __forceinline__ float tile_ssq(const float (&v)[4], int first, int span) {
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s = fmaf(v[e], v[e], s);
-  for (int m = first; m < first * span; m <<= 1) s += shfl_xor_f(s, m);
-  return s;
-}
-
 // Tag check of the first n of N tagged 16-byte units: true when every word
 // carries `tag`.
 template <int N>
@@ -593,7 +575,7 @@ __device__ __forceinline__ void await_all(const DevPlan& pl, Ps&&... ps) {
 // plans without it: 2392 -> 2369 us per 64-row frame).
 template <int BF, int KIND, bool ONE = false, bool ASM = !ONE, bool NOQK = false>
 __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, bool lnorm,
+                                          uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl,
                                           int r0, int gr) {
   constexpr int ESZ = BF ? 2 : 4;     // bytes per activation element
   constexpr int E = 16 / ESZ;         // elements per 16-byte payload chunk
@@ -639,15 +621,14 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   uint8_t* const hmid = (uint8_t*)pl.hmid;
   const uint8_t* xsrc;
   uint32_t ld;                     // operand row length (elements)
-  int kt = H, k0 = 0, in_ssq = 0;
+  int kt = H, k0 = 0;
   if constexpr (KIND == T_QKV) {
     xsrc = (l == 0) ? xin + (size_t)p * hbytes : hres + plane(l - 1, p) * hbytes;
-    in_ssq = (l == 0) ? p : P + 2 * par + ((l - 1) & 1);
     ld = H;
   } else if constexpr (KIND == T_GU) {
-    xsrc = hmid + plane(l, p) * hbytes; in_ssq = P + 4 + par; ld = H;
+    xsrc = hmid + plane(l, p) * hbytes; ld = H;
   } else if constexpr (KIND == T_HEAD) {
-    xsrc = hres + plane(pl.L - 1, p) * hbytes; in_ssq = P + 2 * par + ((pl.L - 1) & 1); ld = H;
+    xsrc = hres + plane(pl.L - 1, p) * hbytes; ld = H;
   } else if constexpr (KIND == T_O) {
     // (the many-row executor runs down tasks through this instantiation too:
     // one body for both split-K kinds keeps the kernel's code smaller,
@@ -736,19 +717,6 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       for (int s = 0; s < DEPTH; ++s) load0(xs[s], s);
     }
   }
-  // Sum-of-squares partials of a normalised operand (H/16 per row, written
-  // with the rows): lane group q adds H/64 of them.  (ONE: not read; the
-  // row's sum of squares comes from its operand units, below.)
-  u32x4 ssv[8];
-  const int nsq = H / 64;
-  const uint32_t ss_row = (uint32_t)(H / 16) * 8;
-  const rsrc_t rs = make_rsrc(ssq_slot(pl, in_ssq), (uint32_t)rows * ss_row);
-  const uint32_t ss0 = (uint32_t)row * ss_row + (uint32_t)(q * nsq) * 8;
-  auto sso = [=](int i) -> uint32_t { return ONE ? (uint32_t)(lane % (H / 32)) * 16 : ss0 + i * 16; };
-  if constexpr (NORM && !ONE) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ssv[i] = ld16(rs, sso(2 * i < nsq ? i : nsq / 2 - 1));  // (past nsq: not waited for)
-  }
   // RoPE angles of a qkv tile's two rotary pairs per lane.
   float rope_cs[2] = {1.f, 1.f}, rope_sn[2] = {0.f, 0.f};
   if constexpr (KIND == T_QKV) {
@@ -761,35 +729,34 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       rope_sn[pr] = pl.rope[(p * (d / 2) + i0 + pr) * 2 + 1];
     }
   }
-  // The data is its own signal: wait for the first group and the norm
-  // partials, then for this task's weight tile (issued during the previous
-  // task) to be in LDS.  With tagged operands the tile's copy is older than
+  // The data is its own signal: wait for the first group, then for this
+  // task's weight tile (issued during the previous task) to be in LDS.  With tagged operands the tile's copy is older than
   // every load of group 0 (the executor issues it before it dispatches the
   // task, and a task's loads are its own code, behind that dispatch), so
   // group 0 having arrived covers this wave's part of it and the later groups
   // stay in flight.  A wave with no live rows issued no operand loads but
   // still copied its share of the tile, and waits for every load; so do
   // one-row frames and untagged operands.  (wave_live is wave-uniform.)
-  // (late: the norm partials are awaited after the K loop instead, with
-  // CP_FLAG_LATE_NORM, where it measured slower: 2545 vs 2509 us at 64 rows;
-  // one-row frames need no partials, and take rms(x) after the K loop)
-  const bool late = NORM && (ONE || lnorm);
   if constexpr (ONE)
     await_all(pl, spend<BF>(xo, rx, oo, wave_live, nj1));
   else
-    await_all(pl, spend<BF, ASM>(xs[0], rx, uoff(0), XLL && live),
-              pend<ASM>(ssv, rs, sso, in_tag, NORM && live && !late, nsq / 2));
+    await_all(pl, spend<BF, ASM>(xs[0], rx, uoff(0), XLL && live));
   if (XLL && !ONE && wave_live) wait_for(xs[0][0]);
   else wait_vm();
   __syncthreads();
   stamp(tr, 2);
 
-  // ONE: the row's sum of squares for RMSNorm from the operand pieces this
-  // wave holds (each piece of its chunks once), added over the wave; the
-  // waves that split K add theirs after the K loop.  No wait for the
-  // producers' norm partials then: 1575 -> 1547 us per one-row frame.  (At
-  // 64 rows the squares in the K loop cost more than the partials' wait
-  // saves: 2349 -> 2422 us.)
+  // RMSNorm needs the sum of squares of each row over all of K.  The
+  // projection streams the whole row anyway, so it takes the sum from its
+  // own operand units instead of waiting for partial sums from the tiles
+  // that produced the row (which would be a wait on every producer tile
+  // before the first MFMA).  Many rows: one more MFMA per chunk, x x^T, whose
+  // diagonal holds the rows' sums (2349 -> 2217 us per 64-row frame, and
+  // 2166 with the producers no longer writing partials; squares taken with
+  // vector ALU instructions in the K loop instead: 2422).  ONE: each wave
+  // holds its pieces of row 0 whole after the first load and adds their
+  // squares there (1575 -> 1547 us per one-row frame).  Waves that split K
+  // add their sums after the K loop, in wave order.
   float ssl = 0.f;
   if constexpr (NORM && ONE) {
 #pragma unroll
@@ -810,32 +777,15 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     wave_tree([&](auto other) { ssl += __uint_as_float(other(__float_as_uint(ssl))); });
   }
 
-  // 1 / rms(x) of this lane's row, from its norm partials
-  auto row_rinv = [&]() -> float {
-    float ss = 0.f;
-    if constexpr (ONE) {
-      ss = ssl;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (2 * i < nsq) ss += __uint_as_float(ssv[i][0]) + __uint_as_float(ssv[i][2]);
-      ss += shfl_xor_f(ss, 16);
-      ss += shfl_xor_f(ss, 32);
-    }
-    return 1.0f / sqrtf(ss / (float)H + pl.eps);
-  };
-  float rinv = 1.f;
-  if constexpr (NORM)
-    if (!late) rinv = row_rinv();
-
   const uint8_t* wt = slot + lane * 16 + (size_t)c0 * NB * 1024;
-  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, accs = {0, 0, 0, 0};
   auto step = [&](u32x4 (&xr)[NU], int g) {
     if constexpr (XLL) await_all(pl, spend<BF, ASM>(xr, rx, uoff(g), live));
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const int c = g * NU + i;
       const u32x4 x = xr[i];
+      if constexpr (NORM && !ONE) accs = mma<BF>(x, x, accs);
       const u32x4 w0 = *(const u32x4*)(wt + c * NB * 1024);
       if constexpr (NB == 2) {
         const u32x4 w1 = *(const u32x4*)(wt + (c * 2 + 1) * 1024);
@@ -903,19 +853,26 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     }
   }
   stamp(tr, 4);
+  if constexpr (NORM && !ONE) {
+    // the row's sum of squares: the diagonal of the Gram block x x^T, entry
+    // (rl, rl) in lane (rl / 4) * 16 + rl, element rl % 4
+    const int v = rl & 3;
+    const float mine = v == 0 ? accs[0] : (v == 1 ? accs[1] : (v == 2 ? accs[2] : accs[3]));
+    ssl = __shfl(mine, (rl >> 2) * 16 + rl, 64);
+  }
   if (wpr > 1) {
     // K parts of a row tile: (((k0 + k1) + k2) + k3), in the wave of part 0
     f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);  // [4 waves][2][64 lanes]
     float* red_ss = (float*)((uint8_t*)misc + kRedSsLds);  // ONE: [4 waves][64 lanes]
     if (wave_live) {
-      if constexpr (NORM && ONE) red_ss[wave * 64 + lane] = ssl;
+      if constexpr (NORM) red_ss[wave * 64 + lane] = ssl;
       red_acc[(wave * 2 + 0) * 64 + lane] = acc0;
       if constexpr (NB == 2) red_acc[(wave * 2 + 1) * 64 + lane] = acc1;
     }
     __syncthreads();
     if (wave_live && ks == 0) {
       for (int k = 1; k < wpr; ++k) {
-        if constexpr (NORM && ONE) ssl = ssl + red_ss[(rt * wpr + k) * 64 + lane];
+        if constexpr (NORM) ssl = ssl + red_ss[(rt * wpr + k) * 64 + lane];
         const f32x4 a = red_acc[((rt * wpr + k) * 2 + 0) * 64 + lane];
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc0[v] = acc0[v] + a[v];
@@ -927,16 +884,8 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
   }
-  if constexpr (NORM) {
-    if (late) {
-      // The norm partials of the row (every producer tile's) are needed only
-      // now: the K loop started as soon as this wave's own operand units were
-      // in.  (ks == 0: the waves that store the tile.)
-      if constexpr (!ONE) await_all(pl, pend<ASM>(ssv, rs, sso, in_tag, live && ks == 0, nsq / 2));
-      rinv = row_rinv();
-    }
-  }
   if constexpr (NORM) {  // W (g . x / rms(x)) = (W g) x / rms(x): the gain is in the packed tile
+    const float rinv = 1.0f / sqrtf(ssl / (float)H + pl.eps);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       acc0[v] = acc0[v] * rinv;
@@ -952,22 +901,20 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
     const bool owner = tk.split == 0;
     uint64_t part_off;
     void* out;
-    int out_ssq;
     const void* resid = nullptr;
     if constexpr (KIND == T_O) {
       if (ONE || tk.type == T_O) {
         part_off = pl.part_o_off + (uint64_t)par * pl.part_stride; out = hmid + plane(l, p) * hbytes;
-        out_ssq = P + 4 + par;
         resid = (l == 0) ? xin + (size_t)p * hbytes : hres + plane(l - 1, p) * hbytes;
       } else {  // a down task (many-row executor)
         part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; out = hres + plane(l, p) * hbytes;
-        out_ssq = P + 2 * par + (l & 1); resid = hmid + plane(l, p) * hbytes;
+        resid = hmid + plane(l, p) * hbytes;
       }
     } else if constexpr (KIND == T_DOWN) {
       part_off = pl.part_d_off + (uint64_t)par * pl.part_stride; out = hres + plane(l, p) * hbytes;
-      out_ssq = P + 2 * par + (l & 1); resid = hmid + plane(l, p) * hbytes;
+      resid = hmid + plane(l, p) * hbytes;
     } else {
-      part_off = pl.part_in_off; out = xin; out_ssq = 0;
+      part_off = pl.part_in_off; out = xin;
     }
     const rsrc_t rp = make_rsrc(pl.part + part_off, (uint32_t)pl.part_stride * 8);
     const uint32_t pbase = (uint32_t)((tk.tile * tk.nsplit * Rmax + row) * 16 + 4 * q) * 8;
@@ -1030,14 +977,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = act_val<BF>(s[e]);
       }
-      // (the row's norm partial: one-row frames read none, so store none)
-      const float sq = ONE ? 0.f : tile_ssq(h, 16, 4);
-      if (live) {
-        st_sop4<BF>(make_rsrc(out, hbytes), row, (int)slots, H, h);
-        if (!ONE && q == 0)
-          st8c(make_rsrc(ssq_slot(pl, out_ssq), (uint32_t)Rmax * ss_row), (uint32_t)row * ss_row + tk.tile * 8,
-               u32x2{__float_as_uint(sq), my_tag});
-      }
+      if (live) st_sop4<BF>(make_rsrc(out, hbytes), row, (int)slots, H, h);
     }
   } else {
     if (epi_wave && live) {
@@ -1362,13 +1302,11 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
 // ------------------------------------------------------------------ draw + embed
 
 // Writes embedding row `code` of table j as the input of position j + 1 (when
-// there is one, tagged, with its sum-of-squares partials unless SS is false:
-// one-row frames take the sum from the operand itself) and adds it to the
-// row's fp32 embedding sum.  All draws of a row run in one workgroup, so the
+// there is one, in operand order) and adds it to the row's fp32 embedding sum.  All draws of a row run in one workgroup, so the
 // sum is carried in program order with ordinary loads and stores.
-template <int BF, bool SS = true>
+template <int BF>
 __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr, int j, int row, int code,
-                                          bool first, uint32_t my_tag) {
+                                          bool first) {
   constexpr int ESZ = BF ? 2 : 4;
   const int H = pl.H, V = pl.V;
   const rsrc_t re = make_rsrc(pl.embed, (uint32_t)pl.P * V * H * ESZ);
@@ -1398,26 +1336,22 @@ __device__ __forceinline__ void embed_row(const DevPlan& pl, const DevFrame& fr,
       for (int i = 0; i < 4; ++i) ev[i] = 0.f;
     }
     if (in && feeds) st_sop4<BF>(rx, row, k, H, ev);
-    const float sq = SS ? tile_ssq(ev, 1, 4) : 0.f;
     if (in) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = __float_as_uint(first ? ev[i] : __uint_as_float(sv[i]) + ev[i]);
       st16(rs, (uint32_t)(row * H + k) * 4, sv);
-      if (SS && feeds && (threadIdx.x & 3) == 0)
-        st8c(make_rsrc(ssq_slot(pl, j + 1), (uint32_t)pl.Rmax * (H / 16) * 8), (uint32_t)(row * (H / 16) + k / 16) * 8,
-             u32x2{__float_as_uint(sq), my_tag});
     }
   }
 }
 
-template <int BF, bool SS>
+template <int BF>
 __device__ __forceinline__ void embed0_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
                                             uint64_t* tr) {
   const int row = (int)tk.tile;
   if (row < fr.rows) {
     int code = fr.code0[row];
     code = code < 0 ? 0 : (code >= pl.V ? pl.V - 1 : code);
-    embed_row<BF, SS>(pl, fr, 0, row, code, true, tag_of(epoch, tk.phase));
+    embed_row<BF>(pl, fr, 0, row, code, true);
   }
   stamp(tr, 5);
 }
@@ -1924,7 +1858,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
         st8c(make_rsrc(fr.offset, (uint32_t)fr.rows * 8), (uint32_t)row * 8, u32x2{(uint32_t)o, (uint32_t)(o >> 32)});
       }
     }
-    embed_row<BF, ASM>(pl, fr, p, row, code, false, tag_of(epoch, tk.phase));
+    embed_row<BF>(pl, fr, p, row, code, false);
   } else if (row < fr.rows) {
     if (threadIdx.x < 64) {
       // the head tiles' (value, index) candidates of this row, tile order
@@ -1963,7 +1897,7 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
       }
     }
     __syncthreads();
-    embed_row<BF, ASM>(pl, fr, p, row, (int)misc[1], false, tag_of(epoch, tk.phase));
+    embed_row<BF>(pl, fr, p, row, (int)misc[1], false);
   }
   stamp(tr, 5);
 }
@@ -1977,24 +1911,24 @@ __device__ __forceinline__ void draw_task(const DevPlan& pl, const DevFrame& fr,
 template <int BF, bool ONE, bool PLAIN = false, bool NOQK = false>
 // lcl: XCD-local hand-offs allowed in this frame.
 __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, const DevTask& tk, uint32_t epoch,
-                                         uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl, bool lnorm) {
+                                         uint8_t* slot, uint32_t* misc, uint64_t* tr, bool lcl) {
   switch (tk.type) {
     case T_ATTN:
       if (PLAIN || pl.d == 128) attn_task<BF, 128, !ONE, NOQK>(pl, fr, tk, epoch, tr);
       else attn_task<BF, 64, !ONE, NOQK>(pl, fr, tk, epoch, tr);
       break;
-    case T_EMBED0: embed0_task<BF, !ONE>(pl, fr, tk, epoch, tr); break;
+    case T_EMBED0: embed0_task<BF>(pl, fr, tk, epoch, tr); break;
     case T_DRAW: draw_task<BF, !ONE>(pl, fr, tk, epoch, slot, misc, tr); break;
 // (one-row frames: only a task of row group 0 has the row)
 #define CP_PROJ(K)                                                                                  \
   if constexpr (ONE) {                                                                              \
-    if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, 0, 64); \
+    if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, 0, 64); \
   } else if (pl.grp_rows) {                                                                         \
     const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;                                     \
-    if (r0 < fr.rows) proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, r0, pl.grp_rows); \
+    if (r0 < fr.rows) proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows); \
   } else {                                                                                          \
     for (int rh = 0; rh * 64 < fr.rows; ++rh)                                                       \
-      proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, rh * 64, 64);  \
+      proj_task<BF, K, ONE, !ONE, NOQK>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh * 64, 64);  \
   }
     case T_QKV: CP_PROJ(T_QKV) break;
     case T_O: CP_PROJ(T_O) break;
@@ -2010,13 +1944,13 @@ __device__ __forceinline__ void run_task(const DevPlan& pl, const DevFrame& fr, 
 #undef CP_PROJ
     default:
       if constexpr (ONE) {
-        if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, 0, 64);
+        if ((tk.flags >> kTaskGroupShift) == 0) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, 0, 64);
       } else if (pl.grp_rows) {
         const int r0 = (tk.flags >> kTaskGroupShift) * pl.grp_rows;
-        if (r0 < fr.rows) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, r0, pl.grp_rows);
+        if (r0 < fr.rows) proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, r0, pl.grp_rows);
       } else {
         for (int rh = 0; rh * 64 < fr.rows; ++rh)
-          proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, lnorm, rh * 64, 64);
+          proj_task<BF, T_INPROJ, false, !ONE>(pl, fr, tk, epoch, slot, misc, tr, lcl, rh * 64, 64);
       }
       break;
   }
@@ -2069,8 +2003,7 @@ __device__ __forceinline__ void advance_epoch(const DevPlan& pl, uint32_t epoch,
   }
 }
 
-// PLAIN: no trace stamps, no CP_FLAG_LATE_NORM (many-row frames), XCD-local
-// hand-offs allowed and head_dim 128; those choices are then constants in
+// PLAIN: no trace stamps, XCD-local hand-offs allowed and head_dim 128; those choices are then constants in
 // the task bodies (as runtime checks, 64-row frames measured 76 us slower,
 // the local-hand-off check alone cost one-row frames 44 us, and the unused
 // head_dim-64 attention 19 us per 64-row frame: the kernel's code is larger
@@ -2125,7 +2058,7 @@ __global__ __launch_bounds__(kThreads, 1) void persistent_kernel(DevPlan pl, Dev
     const DevTask nxt = more ? task_at(i + 1) : DevTask{};
     const Next nx = {nxt, more, lds + (s ^ 1) * kSlotBytes};
     stamp(tr, 1);
-    run_task<BF, ONE, PLAIN, NOQK>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl, !PLAIN && pl.late_norm != 0);
+    run_task<BF, ONE, PLAIN, NOQK>(pl, fr, cur, epoch, lds + s * kSlotBytes, misc, tr, lcl);
     __syncthreads();  // LDS (tile slot, reductions) of this task is free again
     stamp(tr, 6);
     // The next task's tile copy goes out once every wave has issued this
@@ -2172,7 +2105,7 @@ __global__ __launch_bounds__(kThreads, 1) void phase_kernel(DevPlan pl, DevFrame
   const uint32_t epoch = __hip_atomic_load(pl.state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const DevTask tk = tasks[blockIdx.x];
   issue_tile(pl, tk, lds);
-  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr, false, pl.late_norm != 0);  // (per-phase tasks carry no local flags)
+  run_task<BF, ONE>(pl, fr, tk, epoch, lds, misc, nullptr, false);  // (per-phase tasks carry no local flags)
 }
 
 // The per-phase executor's last launches of a frame: the sentinel refill of
@@ -2230,8 +2163,7 @@ namespace cpms {
 hipError_t launch_persistent(const DevPlan& pl, const DevFrame& fr, hipStream_t s) {
   const dim3 g(pl.n_wg), t(kThreads);
   const bool one = fr.rows == 1 && pl.tasks_in_lds;
-  // (one-row frames always wait late for the norm partials)
-  const bool plain = pl.tasks_in_lds && !pl.trace_on && (one || !pl.late_norm) && pl.local_ok && pl.d == 128;
+  const bool plain = pl.tasks_in_lds && !pl.trace_on && pl.local_ok && pl.d == 128;
   const bool nq = plain && !one && !pl.qk_norm;
 #define X(B, T, O, PL, NQK)                                                                        \
   if (pl.bf16 == B && (pl.tasks_in_lds != 0) == T && one == O && plain == PL && nq == NQK) {       \

@@ -289,7 +289,7 @@ static cp_status validate(const cp_config* c, std::string& msg) {
   // an o split (n_q_heads / 4 heads) must read at most kMaxWaits kv heads
   const int gq = c->n_q_heads / c->n_kv_heads, hps = c->n_q_heads / 4;
   if ((hps - 1) / gq + 2 > kMaxWaits && hps / gq > kMaxWaits) { msg = "kv grouping not supported"; return CP_ERR_UNSUPPORTED; }
-  if (c->flags & ~(CP_FLAG_TRACE | CP_FLAG_LATE_NORM | CP_FLAG_NO_LOCAL | CP_FLAG_ROW_GROUPS)) {
+  if (c->flags & ~(CP_FLAG_TRACE | CP_FLAG_NO_LOCAL | CP_FLAG_ROW_GROUPS)) {
     msg = "unknown flag";
     return CP_ERR_UNSUPPORTED;
   }
@@ -1016,7 +1016,6 @@ static cp_status alloc_scratch(cp_plan* P) {
   dp.part_o_off = 0;
   dp.part_d_off = 2 * part_one;
   dp.part_in_off = 4 * part_one;
-  TRY(alloc(P, &p, (size_t)(Pn + 6) * R * (H / 16) * 8, true)); dp.ssq = (uint32_t*)p;
   TRY(alloc(P, &p, (size_t)R * V * 8, true)); dp.zbuf = (uint64_t*)p;
   TRY(alloc(P, &p, (size_t)R * (V / 16) * 16, true)); dp.cand = (uint64_t*)p;
   TRY(alloc(P, &p, 256 * 4)); dp.state = (uint32_t*)p;
@@ -1134,7 +1133,6 @@ static cp_status create_impl(cp_plan* P, const cp_config* cfg, const cp_weights*
   TRY(pack_weights(P, w));
   TRY(check_schedule(P));
   dp.tasks_in_lds = (int64_t)P->max_tasks_wg * (int64_t)sizeof(DevTask) <= kTaskLds;
-  dp.late_norm = (cfg->flags & CP_FLAG_LATE_NORM) ? 1 : 0;
   dp.local_ok = (cfg->flags & CP_FLAG_NO_LOCAL) ? 0 : 1;
   TRY(alloc_scratch(P));
   HIPCHK(P, hipDeviceSynchronize());

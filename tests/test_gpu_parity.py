@@ -236,22 +236,20 @@ def test_persistent_equals_per_phase_bitwise():
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("rows,exec_mode", [(1, "persistent"), (40, "persistent"), (64, "persistent"),
-                                           (13, "per_phase")])
-def test_late_norm_wait_equals_default_bitwise(rows, exec_mode):
-    """CP_FLAG_LATE_NORM (normed projections wait for the row's norm partials
-    after the K loop, not before it) changes when a task waits, never what it
-    computes: every output equals the default plan's, bit for bit."""
-    cp = _cp()
+@pytest.mark.parametrize("rows,exec_mode", [(2, "persistent"), (20, "persistent"), (33, "persistent"),
+                                           (20, "per_phase")])
+def test_rms_from_operand_rows_with_waves_splitting_k(rows, exec_mode):
+    """The normed projections take each row's sum of squares from the operand
+    units they stream (an extra x x^T MFMA per chunk); at 2 and 20 rows the
+    waves of a row tile split K (four and two ways) and add their sums in LDS,
+    at 33 rows one wave covers the whole row and the last row tile is ragged.
+    Every row's logits and K/V against the oracle."""
     cfg = synth.CONFIGS["l5_r64"]
     w, wdev, ow = _weights(cfg)
     inputs = synth.make_inputs(cfg, rows=rows, seed=21)
-    a = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=rows, kv=True)
-    b = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=rows, kv=True, flags=cp.CP_FLAG_LATE_NORM)
-    for k in a:
-        assert np.array_equal(a[k], b[k]), k
-    if rows == 64:
-        _check(cfg, ow, inputs, b, range(0, 64, 9), 0.05, kv=True)
+    gpu = _gpu_frame(cfg, wdev, inputs, exec_mode, max_rows=rows, kv=True)
+    err, frac = _check(cfg, ow, inputs, gpu, range(rows), 0.05, kv=True)
+    print(f"l5 r{rows} {exec_mode}: max logit err {err:.4f}, decided {frac:.2f}")
 
 
 @pytest.mark.parametrize("rows", [64, 1])
