@@ -25,7 +25,7 @@
  *                       reloads until none is left.  After the frame every
  *                       workgroup meets at one counter and refills its share
  *                       of those buffers with the sentinel.  Every other value
- *                       (q, K/V, split-K and norm partials, logits) is stored
+ *                       (q, K/V, split-K partials, logits) is stored
  *                       next to a 32-bit tag (epoch * 1024 + the writer's
  *                       phase), and the reader reloads the words until every
  *                       tag is the one it expects.  No fence is on the path.
@@ -180,7 +180,7 @@ typedef struct {
                                 timestamps of the device's 100 MHz constant clock, written by the task's
                                 workgroup:
                                   0 task start, 1 dispatched (next task's record read),
-                                  2 dependencies met (projections: first operand group, norm partials and
+                                  2 dependencies met (projections: first operand group and
                                     weight tile in place; attention: Q, K, V of its first pair; draw: the
                                     head's logits or candidates),
                                   3 first operand group consumed, 4 K loop done (projections),
