@@ -1140,20 +1140,23 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
     const int hq = g * gq + pi % gq;
     if (row >= fr.rows) continue;  // wave-uniform
     const uint32_t kvrow = (uint32_t)((l * Rmax + row) * nkv + g) * P;
-    // Q and K of this lane's quarter
+    // Q and K of this lane's quarter of the head dims
     constexpr int NQ = BF ? 8 : 16;  // 16-byte tagged loads per score lane at most
     u32x4 qv[NQ], kv[NQ];
-    const uint32_t q0 = ((uint32_t)(row * pl.nq * d + hq * d + c * dq)) * ESZ * 2;
-    const uint32_t k0 = ((uint32_t)((kvrow + t) * d + c * dq)) * ESZ * 2;
-    auto qo = [=](int i) { return q0 + i * 16; };
+    // (chunk i of lane quarter c is the head's 16-byte unit 4 i + c: one
+    // load instruction reads 64 contiguous bytes of each position's K row,
+    // not 16 bytes of 64 different cache lines)
+    const uint32_t q0 = ((uint32_t)(row * pl.nq * d + hq * d)) * ESZ * 2 + c * 16;
+    const uint32_t k0 = ((uint32_t)((kvrow + t) * d)) * ESZ * 2 + c * 16;
+    auto qo = [=](int i) { return q0 + i * 64; };
     // (loads without branches: units past nld repeat the last one and
     // positions past p read position p; neither is part of the wait)
     const uint32_t kclamp = (uint32_t)(min(t, p) - t) * (uint32_t)(d * ESZ * 2);
     // QK-norm: position p (and the clamped lanes past it) read the staging
     // buffer, written by the qkv phase with its tag
     const bool rawk = qkn && t >= p;
-    const uint32_t kr0 = kvbytes + ((uint32_t)((((p & 1) * Rmax + row) * nkv + g) * d + c * dq)) * ESZ * 2;
-    auto ko = [=](int i) { return rawk ? kr0 + i * 16 : k0 + kclamp + i * 16; };
+    const uint32_t kr0 = kvbytes + ((uint32_t)((((p & 1) * Rmax + row) * nkv + g) * d)) * ESZ * 2 + c * 16;
+    auto ko = [=](int i) { return rawk ? kr0 + i * 64 : k0 + kclamp + i * 64; };
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int iu = i < nld ? i : nld - 1;
@@ -1223,7 +1226,7 @@ __device__ __forceinline__ void attn_task(const DevPlan& pl, const DevFrame& fr,
       if (t == p && pi % gq == 0) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i)
-          if (i < nld) st16c(rk, k0 + i * 16, ll_pair(kv[i][0], kv[i][2], kv_tag));
+          if (i < nld) st16c(rk, k0 + i * 64, ll_pair(kv[i][0], kv[i][2], kv_tag));
       }
     }
     if (pi < 4) stamp(tr, 2);
