@@ -608,11 +608,10 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   const int H = pl.H, Rmax = pl.Rmax, P = pl.P;
   const int l = tk.layer, p = tk.pos;
   const uint32_t my_tag = tag_of(epoch, tk.phase);
-  const uint32_t in_tag = tag_of(epoch, tk.ph_in0);
 
-  // Operand buffers have a plane per layer and position; the tagged norm
-  // partials and split-K partials that positions 0 and 1 (in flight
-  // together) would share are doubled and picked by position parity.
+  // Operand buffers have a plane per layer and position; the tagged split-K
+  // partials that positions 0 and 1 (in flight together) would share are
+  // doubled and picked by position parity.
   const int par = p & 1;
   const uint32_t hbytes = sop_bytes<BF>(Rmax, H);
   auto plane = [&](int ll, int pp) -> size_t { return (size_t)(ll * P + pp); };
@@ -863,7 +862,7 @@ __device__ __forceinline__ void proj_task(const DevPlan& pl, const DevFrame& fr,
   if (wpr > 1) {
     // K parts of a row tile: (((k0 + k1) + k2) + k3), in the wave of part 0
     f32x4* red_acc = (f32x4*)((uint8_t*)misc + kRedAccLds);  // [4 waves][2][64 lanes]
-    float* red_ss = (float*)((uint8_t*)misc + kRedSsLds);  // ONE: [4 waves][64 lanes]
+    float* red_ss = (float*)((uint8_t*)misc + kRedSsLds);  // [4 waves][64 lanes]
     if (wave_live) {
       if constexpr (NORM) red_ss[wave * 64 + lane] = ssl;
       red_acc[(wave * 2 + 0) * 64 + lane] = acc0;
