@@ -200,18 +200,20 @@ def _measured_read_rate(nbytes, reps=20):
 CHAIN_VARIANTS = [  # (name, xcd_local, cp_chain_run variant)
     ("all_to_all_sc1_sc1", 0, 0), ("all_to_all_sys_sys", 0, 4),
     ("xcd_local_sc1_sc1", 1, 0), ("xcd_local_plain_sc1", 1, 1), ("xcd_local_plain_sc0", 1, 2),
-    ("xcd_local_plain_sys", 1, 3)]
+    ("xcd_local_plain_sys", 1, 3), ("all_to_all_counter_fence", 0, 5)]
 
 
 def _chain_us_per_phase(n_phases, launches=10):
     """µs per phase of empty chains of tagged-word hand-offs over 256 one-wave
-    workgroups, for each store / load cache policy and scope: best of
-    `launches`; None where a wait gave up (stores its readers never saw)."""
+    workgroups, for each store / load cache policy and scope, and of the same
+    all-to-all chain handed off through a counter with release / acquire
+    fences: best of `launches`; None where a wait gave up (stores its readers
+    never saw)."""
     import torch
     from persistent_megakernel_streaming_amd import cp
     out = {}
     for name, local, variant in CHAIN_VARIANTS:
-        slots = torch.zeros(2 * 256 * 4, dtype=torch.int32, device="cuda")
+        slots = torch.zeros(2 * 256 * 4 + 4, dtype=torch.int32, device="cuda")  # (+ the counter of variant 5)
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
         base, best = 0, float("inf")
         for i in range(launches + 2):

@@ -363,10 +363,17 @@ cp_status cp_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* 
  *   2  plain stores, workgroup-coherent loads;
  *   3  plain stores, system-coherent loads;
  *   4  system-coherent stores and loads;
- * variants 1-3 need xcd_local (plain stores stay in the writer's XCD).
- * slots: device memory of 2 * n_workgroups * 16 bytes, zero before the first
- * launch; tags must grow from launch to launch (tag_base of the next launch
- * >= this tag_base + n_phases, at most 2^32 - 1 in all).  error_word: a
+ *   5  the hand-off through counters in global memory of [PR] "How it works"
+ *      for comparison: each workgroup stores its word, takes a release fence
+ *      and adds one to a counter; the others poll the counter, take an
+ *      acquire fence and read the words (all-to-all only).
+ * variants 1-3 need xcd_local (plain stores stay in the writer's XCD);
+ * variant 5 refuses it.
+ * slots: device memory of 2 * n_workgroups * 16 bytes (variant 5: 16 more,
+ * the counter), zero before the first launch; tags must grow from launch to
+ * launch (tag_base of the next launch >= this tag_base + n_phases, at most
+ * 2^32 - 1 in all; variant 5: exactly this tag_base + n_phases, the first
+ * launch's 0, and tag_base + n_phases at most 2^32 / n_workgroups).  error_word: a
  * device uint32 set to 1 if a wait gave up (every wait is bounded, about
  * 65536 polls).  Allocates nothing; does not synchronise. */
 cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t tag_base, int xcd_local, int variant,

@@ -1406,7 +1406,8 @@ cp_status cp_chain_run(uint32_t* slots, int n_workgroups, int n_phases, uint32_t
                        uint32_t* error_word, void* stream) {
   if (!slots || !error_word || n_workgroups < 1 || n_workgroups > 256 || n_phases < 1 ||
       (xcd_local && n_workgroups % 8) || (uint64_t)tag_base + (uint64_t)n_phases > 0xffffffffull || variant < 0 ||
-      variant > 4 || (variant >= 1 && variant <= 3 && !xcd_local))
+      variant > 5 || (variant >= 1 && variant <= 3 && !xcd_local) ||
+      (variant == 5 && (xcd_local || ((uint64_t)tag_base + (uint64_t)n_phases) * (uint64_t)n_workgroups > 0xffffffffull)))
     return CP_ERR_INVALID_ARGUMENT;
   return launch_chain(slots, n_workgroups, n_phases, tag_base, xcd_local, variant, error_word, (hipStream_t)stream) ==
                  hipSuccess

@@ -177,3 +177,20 @@ def test_inline_asm_vector_memory_blocks_start_with_the_guard(tmp_path):
     bad.write_text('asm volatile("s_nop 4\\ns_load_dwordx4 %0, %2, 0x0\\ns_load_dwordx2 %1, %2, 0x10"\n'
                    '             : "=&s"(a), "=&s"(b) : "s"(t));\n')
     assert build.check_asm_guards(str(bad)) == 1
+
+
+@pytest.mark.parametrize("args", [
+    (256, 8, 0, 1, 5),        # the counter form is all-to-all only
+    (256, 8, 0, 0, 6),        # no such variant
+    (256, 8, 0, 0, 1),        # plain stores need the XCD-local chain
+    (256, 8, (1 << 24) - 8, 0, 5),  # the counter would pass 2^32
+    (0, 8, 0, 0, 0),          # no workgroups
+])
+def test_chain_probe_refusals(args):
+    """cp_chain_run refuses, before any launch, a variant it does not have or
+    a combination the hand-off it measures cannot run (no device needed)."""
+    from persistent_megakernel_streaming_amd import cp
+    n_wg, n_ph, base, local, variant = args
+    lib = cp.lib()
+    st = lib.cp_chain_run(C.c_void_p(16), n_wg, n_ph, base, local, variant, C.c_void_p(16), None)
+    assert st == cp.CP_ERR_INVALID_ARGUMENT
